@@ -1,0 +1,242 @@
+"""CPU oracle for the exact-integer block-quantized projection.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, ``__graft_entry__.smoke()`` and the
+benchmark's CPU-baseline leg may import this package.  The product library
+never loads it, and it shares no code with the GPU path: the C part
+(``oracle.c``) and the Python parts here are written from the pages'
+definitions alone.
+
+Sources, cited by page title and section:
+  [UORLUT01]  "D11 integer table serving (UORLUT01)", "How it works".
+  [Handshake] "Vendor-Invariant Integer Inference for MindChain: Handshake v0",
+              Claims C1-C4, "Construction".
+  [tritify]   "Deterministic, Reproducible Inference in Exact Integer
+              Arithmetic, and Verifiable Distributed Inference as Its
+              Consequence" (arXiv 2611.13730), sections 3.1, 3.2, 3.4, 4.
+
+Parity status of each function (what pins it is in tests/test_oracle_*.py):
+  q8, q4, silu_mul, limb_split, silu_lut, ffn_layer, moe_pairs -- pinned;
+  q8_fp32 (the float negative control) -- canonical and tree_walk orders are
+  pinned against numpy float32 sequences; the other orders: parity unpinned.
+"""
+from __future__ import annotations
+
+import ctypes
+import hashlib
+import os
+import subprocess
+from functools import lru_cache
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+ORDERS = {
+    "canonical": 0, "reversed": 1, "tiled_shuffled": 2, "split_k": 3,
+    "tree_walk": 4, "row_order": 5, "column_stream": 6,
+}
+SCHEDULES = ("canonical", "reversed", "tiled_shuffled", "split_k", "tree_walk")
+MULS = {"native": 0, "radix16": 1}
+ORC_OK, ORC_EINVAL, ORC_ERANGE, ORC_ENOMEM = 0, 1, 2, 3
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so (plain scalar C, no vectorizer)."""
+    if force or not os.path.exists(_LIB):
+        cmd = ["gcc", "-std=c11", "-O2", "-fno-tree-vectorize", "-ffp-contract=off",
+               "-fno-fast-math", "-fPIC", "-shared", "-pthread", _SRC, "-o", _LIB + ".tmp"]
+        subprocess.run(cmd, check=True)
+        os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+@lru_cache(maxsize=1)
+def _lib() -> ctypes.CDLL:
+    if not os.path.exists(_LIB):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.orc_q8.argtypes = [P, P, P, P, P, I64, I64, I64, I, ctypes.c_uint64, I, I]
+    lib.orc_q4.argtypes = [P, P, P, P, I64, I64, I64, I, I]
+    lib.orc_silu_mul.argtypes = [P, P, P, P, I64]
+    lib.orc_limb_split.argtypes = [P, P, I64, I]
+    lib.orc_q8_fp32.argtypes = [P, P, P, P, I64, I64, I64, I, ctypes.c_uint64]
+    lib.orc_mul128_radix16.argtypes = [ctypes.c_uint64] * 4 + [P]
+    lib.orc_mul128_radix16.restype = None
+    for f in ("orc_q8", "orc_q4", "orc_silu_mul", "orc_limb_split", "orc_q8_fp32"):
+        getattr(lib, f).restype = I
+    return lib
+
+
+def _c(a: np.ndarray, dtype) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype != dtype:
+        raise TypeError(f"expected {np.dtype(dtype)}, got {a.dtype}")
+    return a
+
+
+def _check(st: int, what: str) -> None:
+    if st == ORC_ERANGE:
+        raise OracleError(f"{what}: result outside int64 (ERANGE)")
+    if st != ORC_OK:
+        raise OracleError(f"{what}: status {st}")
+
+
+def q8(codes: np.ndarray, scales: np.ndarray, x: np.ndarray, order: str = "canonical",
+       seed: int = 0xE1, mul: str = "native", threads: int = 1) -> np.ndarray:
+    """y[t][i] = floor((sum_b S[i][b] sum_{j in b} q[i][j] x[t][j] + 2^23) / 2^24).
+
+    codes int8 [N][K], scales int32 [N][K/32], x int64 [T][K] -> int64 [T][N].
+    [UORLUT01] "One projection (definition)"; [Handshake] C1 / "The frozen
+    profile" (Q24 block scales, Q16 int64 activations, exact accumulation).
+    """
+    codes, scales, x = _c(codes, np.int8), _c(scales, np.int32), _c(x, np.int64)
+    N, K = codes.shape
+    T = x.shape[0]
+    assert x.shape == (T, K) and scales.shape == (N, K // 32)
+    y = np.zeros((T, N), dtype=np.int64)
+    st = _lib().orc_q8(codes.ctypes.data, scales.ctypes.data, x.ctypes.data, y.ctypes.data, None,
+                       N, K, T, ORDERS[order], seed, MULS[mul], threads)
+    _check(st, "q8")
+    return y
+
+
+def q4(nib: np.ndarray, sme: np.ndarray, x: np.ndarray, derivation: str = "definition",
+       threads: int = 1) -> np.ndarray:
+    """y[t][i] = sum_g m 2^e sum_{j in g} q[i][j] x[t][j], exact, no rounding.
+
+    nib uint8 [N][K/2], sme uint8 [N][K/32], x int32 [T][K] -> int64 [T][N].
+    derivation "definition" or "table_read" ([UORLUT01] "One projection").
+    """
+    nib, sme, x = _c(nib, np.uint8), _c(sme, np.uint8), _c(x, np.int32)
+    N = nib.shape[0]
+    K = nib.shape[1] * 2
+    T = x.shape[0]
+    assert x.shape == (T, K) and sme.shape == (N, K // 32)
+    y = np.zeros((T, N), dtype=np.int64)
+    st = _lib().orc_q4(nib.ctypes.data, sme.ctypes.data, x.ctypes.data, y.ctypes.data,
+                       N, K, T, {"definition": 0, "table_read": 1}[derivation], threads)
+    _check(st, "q4")
+    return y
+
+
+def silu_mul(g: np.ndarray, u: np.ndarray, lut: np.ndarray) -> np.ndarray:
+    """h = floor(LUT[clamp(floor((g+16)/32), +-32768) + 32768] * u / 2^16)."""
+    g, u, lut = _c(g, np.int64), _c(u, np.int64), _c(lut, np.int32)
+    assert g.shape == u.shape and lut.shape == (65537,)
+    h = np.zeros(g.shape, dtype=np.int64)
+    _check(_lib().orc_silu_mul(g.ctypes.data, u.ctypes.data, lut.ctypes.data, h.ctypes.data, g.size), "silu_mul")
+    return h
+
+
+def limb_split(x: np.ndarray, L: int) -> tuple[np.ndarray, bool]:
+    """Balanced base-256 digits d [L][n] in [-128, 127], x = sum 256^l d_l.
+
+    Returns (digits, in_range)."""
+    x = _c(x.reshape(-1), np.int64)
+    d = np.zeros((L, x.size), dtype=np.int8)
+    st = _lib().orc_limb_split(x.ctypes.data, d.ctypes.data, x.size, L)
+    if st not in (ORC_OK, ORC_ERANGE):
+        raise OracleError(f"limb_split: status {st}")
+    return d, st == ORC_OK
+
+
+def q8_fp32(codes: np.ndarray, scales: np.ndarray, x: np.ndarray, order: str = "canonical",
+            seed: int = 0xE1) -> np.ndarray:
+    """The float32 shadow of the Q8 sum in one schedule's order ([Handshake] C3)."""
+    codes, scales, x = _c(codes, np.int8), _c(scales, np.int32), _c(x, np.int64)
+    N, K = codes.shape
+    T = x.shape[0]
+    y = np.zeros((T, N), dtype=np.float32)
+    _check(_lib().orc_q8_fp32(codes.ctypes.data, scales.ctypes.data, x.ctypes.data, y.ctypes.data,
+                              N, K, T, ORDERS[order], seed), "q8_fp32")
+    return y
+
+
+def mul128_radix16(a: int, b: int) -> int:
+    """The C oracle's radix-16 multiples-table product of two unsigned 128-bit
+    values, mod 2^128 ([UORLUT01] "Products of two runtime values")."""
+    m = (1 << 64) - 1
+    out = (ctypes.c_uint64 * 2)()
+    _lib().orc_mul128_radix16(a & m, (a >> 64) & m, b & m, (b >> 64) & m, out)
+    return out[0] | (out[1] << 64)
+
+
+@lru_cache(maxsize=1)
+def silu_lut() -> np.ndarray:
+    """The 65537-entry SiLU table: LUT[k + 32768] = round(silu(k / 2^11) * 2^16).
+
+    [Handshake] C1 and C4: a Decimal-committed table, Q11 input over +-16,
+    Q16 output.  silu(z) = z / (1 + e^-z), evaluated here with 50-digit
+    decimal arithmetic and rounded to the nearest integer; the only exact
+    half-way case would need silu(z) 2^16 to be a half-integer, which does
+    not occur (checked by the tests), so the tie rule never acts.
+    """
+    from decimal import Decimal, getcontext, ROUND_HALF_EVEN
+    getcontext().prec = 50
+    out = np.empty(65537, dtype=np.int32)
+    scale = Decimal(65536)
+    for k in range(-32768, 32769):
+        z = Decimal(k) / Decimal(2048)
+        v = z / (Decimal(1) + (-z).exp()) * scale
+        out[k + 32768] = int(v.to_integral_value(rounding=ROUND_HALF_EVEN))
+    out.setflags(write=False)
+    return out
+
+
+def digest(a: np.ndarray) -> str:
+    """SHA-256 of the array's raw little-endian bytes, row-major, no header."""
+    a = np.ascontiguousarray(a)
+    return hashlib.sha256(a.astype(a.dtype.newbyteorder("<"), copy=False).tobytes()).hexdigest()
+
+
+def ffn_layer(x: np.ndarray, wg, wu, wd, lut: np.ndarray, threads: int = 1):
+    """One Q8 FFN layer: g = Q8(Wg, x), u = Q8(Wu, x), h = silu(g)*u >> 16,
+    d = Q8(Wd, h), x_next = x + d (a residual stream; the pages' per-layer
+    digests come from a residual transformer, [Handshake] C2).
+
+    wg, wu, wd are (codes, scales) pairs.  Returns (g, u, h, d, x_next)."""
+    g = q8(wg[0], wg[1], x, threads=threads)
+    u = q8(wu[0], wu[1], x, threads=threads)
+    h = silu_mul(g, u, lut)
+    d = q8(wd[0], wd[1], h, threads=threads)
+    xn = x + d
+    return g, u, h, d, xn
+
+
+def moe_pairs(x: np.ndarray, route: np.ndarray, experts, lut: np.ndarray, pairs=None,
+              down_rows=None, threads: int = 1) -> np.ndarray:
+    """Routed expert FFNs: out[t][k] = Wd_e (silu(Wg_e x_t) * (Wu_e x_t) >> 16)
+    for e = route[t][k] ([tritify] 3.2 "Mixture-of-Experts": each selected
+    expert is an exact-integer MLP).  No combine: the router weights are not
+    part of this workload.
+
+    experts(e) -> ((gc, gs), (uc, us), (dc, ds)).  pairs: optional list of
+    (t, k) to compute; down_rows: optional subset of output rows.  Returns
+    an int64 array [len(pairs)][n_rows]."""
+    T, topk = route.shape
+    if pairs is None:
+        pairs = [(t, k) for t in range(T) for k in range(topk)]
+    outs = []
+    cache = {}
+    for (t, k) in pairs:
+        e = int(route[t, k])
+        if e not in cache:
+            cache.clear()
+            cache[e] = experts(e)
+        (gc, gs), (uc, us), (dc, ds) = cache[e]
+        xt = x[t:t + 1]
+        g = q8(gc, gs, xt, threads=threads)
+        u = q8(uc, us, xt, threads=threads)
+        h = silu_mul(g, u, lut)
+        if down_rows is None:
+            outs.append(q8(dc, ds, h, threads=threads)[0])
+        else:
+            outs.append(q8(dc[down_rows], ds[down_rows], h, threads=threads)[0])
+    return np.stack(outs) if outs else np.zeros((0, 0), np.int64)

@@ -1,0 +1,61 @@
+"""Write the stored expected values under tests/golden/ (CPU only).
+
+Calls only the oracle (and the shared seeded input generators): no value
+written here comes from the GPU path.  Run:  python tests/golden/make_golden.py
+"""
+import json
+import os
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, os.path.dirname(os.path.dirname(HERE)))
+
+import numpy as np  # noqa: E402
+
+import oracle  # noqa: E402
+import synth  # noqa: E402
+
+
+def main(threads: int = 8) -> None:
+    lut = oracle.silu_lut()
+    with open(os.path.join(HERE, "silu_lut.sha256"), "w") as f:
+        f.write(oracle.digest(lut) + "  silu_lut int32[65537] little-endian\n")
+
+    out = {}
+    (w, s), x = synth.q8_896_inputs()
+    out["q8_896x896"] = {"inputs": synth.input_sha256(w, s, x), "y": oracle.digest(oracle.q8(w, s, x))}
+
+    mats, x = synth.qkv_inputs()
+    rec = {"inputs_x": synth.input_sha256(x)}
+    for name, (c, sc) in mats.items():
+        rec[name] = oracle.digest(oracle.q8(c, sc, x))
+        rec[name + "_fp32"] = {o: oracle.digest(oracle.q8_fp32(c, sc, x, o)) for o in oracle.SCHEDULES}
+    out["qkv_gate"] = rec
+
+    rec = {}
+    for name, (n, k) in synth.Q4_SHAPES.items():
+        nib, sme = synth.q4_d512_matrix(name)
+        for t in (1, 64):
+            rec[f"{name}_t{t}"] = oracle.digest(oracle.q4(nib, sme, synth.q4_d512_x(k, t), threads=threads))
+    out["q4_d512"] = rec
+
+    x = synth.qwen_ffn_x0()
+    layers = []
+    for layer in range(synth.QWEN_LAYERS):
+        wg, wu, wd = synth.qwen_ffn_layer(layer)
+        g, u, h, d, x = oracle.ffn_layer(x, wg, wu, wd, lut, threads=threads)
+        layers.append({"d": oracle.digest(d), "x_next": oracle.digest(x)})
+        print("ffn layer", layer, layers[-1]["x_next"][:16], flush=True)
+    out["qwen05b_ffn"] = {"layers": layers}
+
+    w, s = synth.dense_w()
+    x1 = synth.dense_x(1)
+    out["dense_14336x4096"] = {"t1_y": oracle.digest(oracle.q8(w, s, x1, threads=threads))}
+
+    with open(os.path.join(HERE, "oracle_digests.json"), "w") as f:
+        json.dump(out, f, indent=1, sort_keys=True)
+        f.write("\n")
+
+
+if __name__ == "__main__":
+    main()
