@@ -1,0 +1,245 @@
+"""Python binding of libexact_int.so: the exact-integer block-quantized
+projection on AMD Instinct MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/exact_int.h.  PyTorch provides
+device memory and streams.  There is no CPU path: without the built library
+or a HIP device every compute call raises.
+
+torch is imported before the library is loaded, so that the library binds to
+the HIP runtime torch already loaded and shares its streams and allocations.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from functools import lru_cache
+
+import torch
+
+__all__ = [
+    "EIError", "PackedWeights", "lib", "pack_q8", "pack_q4", "gemm_q8", "gemm_q4",
+    "limb_split", "silu_lut", "silu_mul", "digest", "sha256_host", "workspace_bytes",
+    "SCHEDULES", "DEV_LIMB_RANGE", "DEV_OUT_RANGE",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libexact_int.so")
+
+EI_OK, EI_EINVAL, EI_ERANGE, EI_EDEVICE, EI_ENOSPACE = 0, 1, 2, 3, 4
+DEV_LIMB_RANGE, DEV_OUT_RANGE = 1, 2
+SCHEDULES = {"default": 0, "canonical": 1, "reversed": 2, "tiled_shuffled": 3, "split_k": 4, "tree_walk": 5}
+FORMAT_Q8, FORMAT_Q4 = 1, 2
+
+
+class EIError(RuntimeError):
+    """A library call failed (host-detected code, or a device status bit)."""
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [("packed", ctypes.c_void_p), ("n", ctypes.c_int64), ("k", ctypes.c_int64),
+                ("n_pad", ctypes.c_int64), ("nb", ctypes.c_int64), ("smax", ctypes.c_uint32),
+                ("format", ctypes.c_int32)]
+
+
+# name -> (restype, argtypes); mirrors include/exact_int.h
+P, I64, I32, SZ, U64 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t, ctypes.c_uint64
+WP = ctypes.POINTER(Weights)
+SIGNATURES = {
+    "ei_packed_bytes": (SZ, [I64, I64]),
+    "ei_q8_pack": (I32, [P, P, I64, I64, P, SZ, WP, P]),
+    "ei_q4_pack": (I32, [P, P, I64, I64, P, SZ, WP, P]),
+    "ei_limb_split": (I32, [P, P, I64, I32, P, P]),
+    "ei_gemm_workspace_bytes": (SZ, [WP, I64, I32, I32]),
+    "int_gemm_q8": (I32, [WP, P, P, I64, I32, I32, U64, P, SZ, P, P]),
+    "int_gemm_q4": (I32, [WP, P, P, I64, I32, I32, U64, P, SZ, P, P]),
+    "ei_silu_lut_build": (I32, [P, P]),
+    "silu_lut_epilogue": (I32, [P, P, P, P, I64, P, P]),
+    "output_digest": (I32, [P, SZ, P, P]),
+    "ei_sha256_host": (None, [P, SZ, P]),
+    "ei_status_string": (ctypes.c_char_p, [I32]),
+    "ei_version": (I32, []),
+}
+
+
+@lru_cache(maxsize=1)
+def lib() -> ctypes.CDLL:
+    """Load libexact_int.so (building it first only if it is absent)."""
+    if not os.path.exists(LIB_PATH):
+        from . import build as _build
+        _build.build()
+    L = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    return L
+
+
+def _check(code: int, what: str) -> None:
+    if code != EI_OK:
+        raise EIError(f"{what}: {lib().ei_status_string(code).decode()} ({code})")
+
+
+def _dev(t: torch.Tensor, dtype: torch.dtype, name: str) -> int:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise EIError(f"{name} must be a HIP device tensor")
+    if t.dtype != dtype:
+        raise EIError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise EIError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream() -> int:
+    if not torch.cuda.is_available():
+        raise EIError("no HIP device: the exact-integer kernels need an MI355X")
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _raise_status(status: torch.Tensor, what: str) -> None:
+    v = int(status.item())
+    if v:
+        bits = [n for b, n in ((DEV_LIMB_RANGE, "activation outside the declared limb range"),
+                               (DEV_OUT_RANGE, "result outside int64")) if v & b]
+        raise EIError(f"{what}: " + "; ".join(bits))
+
+
+class PackedWeights:
+    """A packed weight matrix: the device buffer and its host descriptor."""
+
+    def __init__(self, buf: torch.Tensor, desc: Weights):
+        self.buf = buf          # keeps the device memory alive
+        self.desc = desc
+
+    @property
+    def n(self) -> int:
+        return self.desc.n
+
+    @property
+    def k(self) -> int:
+        return self.desc.k
+
+    @property
+    def fmt(self) -> int:
+        return self.desc.format
+
+
+def _pack(fn: str, codes: torch.Tensor, scales: torch.Tensor, n: int, k: int, cdt, sdt) -> PackedWeights:
+    s = _stream()
+    pc, ps = _dev(codes, cdt, "codes"), _dev(scales, sdt, "scales")
+    nbytes = lib().ei_packed_bytes(n, k)
+    if nbytes == 0:
+        raise EIError(f"{fn}: bad shape n={n} k={k}")
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=codes.device)
+    desc = Weights()
+    _check(getattr(lib(), fn)(pc, ps, n, k, buf.data_ptr(), nbytes, ctypes.byref(desc), s), fn)
+    return PackedWeights(buf, desc)
+
+
+def pack_q8(codes: torch.Tensor, scales: torch.Tensor) -> PackedWeights:
+    """codes int8 [n][k], scales int32 [n][k/32] (device) -> packed weights."""
+    n, k = codes.shape
+    return _pack("ei_q8_pack", codes, scales, n, k, torch.int8, torch.int32)
+
+
+def pack_q4(nib: torch.Tensor, sme: torch.Tensor) -> PackedWeights:
+    """nibbles uint8 [n][k/2], scale bytes uint8 [n][k/32] (device) -> packed weights."""
+    n, kh = nib.shape
+    return _pack("ei_q4_pack", nib, sme, n, 2 * kh, torch.uint8, torch.uint8)
+
+
+def workspace_bytes(w: PackedWeights, t: int, limbs: int = 3, schedule: str = "default") -> int:
+    return int(lib().ei_gemm_workspace_bytes(ctypes.byref(w.desc), t, limbs, SCHEDULES[schedule]))
+
+
+def _gemm(fn: str, w: PackedWeights, x: torch.Tensor, xdt, limbs: int, schedule: str, seed: int,
+          out, workspace, status) -> torch.Tensor:
+    s = _stream()
+    t, k = x.shape
+    if k != w.k:
+        raise EIError(f"{fn}: x has k={k}, weights k={w.k}")
+    px = _dev(x, xdt, "x")
+    y = out if out is not None else torch.empty((t, w.n), dtype=torch.int64, device=x.device)
+    py = _dev(y, torch.int64, "y")
+    if tuple(y.shape) != (t, w.n):
+        raise EIError(f"{fn}: y must be [{t}][{w.n}]")
+    need = workspace_bytes(w, t, limbs, schedule)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    pw = workspace.data_ptr() if workspace is not None else None
+    wsz = workspace.numel() if workspace is not None else 0
+    check = status is None
+    if check:
+        status = torch.zeros(1, dtype=torch.int32, device=x.device)
+    _check(getattr(lib(), fn)(ctypes.byref(w.desc), px, py, t, limbs, SCHEDULES[schedule], seed,
+                              pw, wsz, status.data_ptr(), s), fn)
+    if check:
+        _raise_status(status, fn)
+    return y
+
+
+def gemm_q8(w: PackedWeights, x: torch.Tensor, limbs: int = 3, schedule: str = "default", seed: int = 0xE1,
+            out=None, workspace=None, status=None) -> torch.Tensor:
+    """y = (sum_b S sum_j q x + 2^23) >> 24 for Q16 int64 activations x [t][k]."""
+    return _gemm("int_gemm_q8", w, x, torch.int64, limbs, schedule, seed, out, workspace, status)
+
+
+def gemm_q4(w: PackedWeights, x: torch.Tensor, limbs: int = 3, schedule: str = "default", seed: int = 0xE1,
+            out=None, workspace=None, status=None) -> torch.Tensor:
+    """y = sum_g m 2^e sum_j q x (exact) for int32 activations x [t][k]."""
+    return _gemm("int_gemm_q4", w, x, torch.int32, limbs, schedule, seed, out, workspace, status)
+
+
+def limb_split(x: torch.Tensor, limbs: int = 3):
+    """Balanced base-256 limbs of int64 x: (d int8 [limbs][n], status int32 [1])."""
+    s = _stream()
+    xf = x.reshape(-1)
+    d = torch.empty((limbs, xf.numel()), dtype=torch.int8, device=x.device)
+    status = torch.zeros(1, dtype=torch.int32, device=x.device)
+    _check(lib().ei_limb_split(_dev(xf, torch.int64, "x"), d.data_ptr(), xf.numel(), limbs, status.data_ptr(), s),
+           "ei_limb_split")
+    return d, status
+
+
+def silu_lut(device="cuda") -> torch.Tensor:
+    """The 65537-entry SiLU table, built on the device."""
+    s = _stream()
+    lut = torch.empty(65537, dtype=torch.int32, device=device)
+    _check(lib().ei_silu_lut_build(lut.data_ptr(), s), "ei_silu_lut_build")
+    return lut
+
+
+def silu_mul(g: torch.Tensor, u: torch.Tensor, lut: torch.Tensor, out=None, status=None) -> torch.Tensor:
+    """h = (lut[clamp((g + 16) >> 5)] * u) >> 16, elementwise (int64)."""
+    s = _stream()
+    if g.shape != u.shape:
+        raise EIError("silu_mul: gate and up shapes differ")
+    h = out if out is not None else torch.empty_like(g)
+    check = status is None
+    if check:
+        status = torch.zeros(1, dtype=torch.int32, device=g.device)
+    _check(lib().silu_lut_epilogue(_dev(g, torch.int64, "gate"), _dev(u, torch.int64, "up"),
+                                   _dev(lut, torch.int32, "lut"), _dev(h, torch.int64, "h"), g.numel(),
+                                   status.data_ptr(), s), "silu_lut_epilogue")
+    if check:
+        _raise_status(status, "silu_lut_epilogue")
+    return h
+
+
+def digest(t: torch.Tensor) -> str:
+    """SHA-256 (hex) of a device tensor's raw little-endian bytes (synchronises)."""
+    s = _stream()
+    if not t.is_contiguous():
+        raise EIError("digest: tensor must be contiguous")
+    out = (ctypes.c_uint8 * 32)()
+    _check(lib().output_digest(t.data_ptr(), t.numel() * t.element_size(), out, s), "output_digest")
+    return bytes(out).hex()
+
+
+def sha256_host(data: bytes) -> str:
+    """The library's SHA-256 of a host byte string (host-only)."""
+    out = (ctypes.c_uint8 * 32)()
+    buf = ctypes.create_string_buffer(data, len(data))
+    lib().ei_sha256_host(buf, len(data), out)
+    return bytes(out).hex()

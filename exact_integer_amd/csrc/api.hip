@@ -1,0 +1,261 @@
+// extern "C" entry points of libexact_int.so (declared in include/exact_int.h).
+// Host-side validation, workspace layout and schedule dispatch; all
+// arithmetic runs in the kernels of the other translation units.
+#include <cstdlib>
+#include <cstring>
+
+#include "ei_internal.h"
+
+using namespace ei;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+constexpr int kSmallT = 4;   // token counts up to this use the GEMV kernel
+constexpr int kSplitParts = 8;
+
+struct WsLayout {
+  size_t limb_off = 0, perm_off = 0, part_off = 0, total = 0;
+  bool mfma = false;
+  int64_t t_pad = 0, ntiles = 0;
+};
+
+WsLayout layout_for(const ei_weights* w, int64_t t, int limbs, int schedule) {
+  WsLayout L;
+  L.mfma = t > kSmallT;
+  L.t_pad = round_up(t, kTile);
+  size_t off = 0;
+  if (L.mfma) {
+    L.limb_off = off;
+    off = align_up(off + (size_t)limbs * (size_t)L.t_pad * (size_t)w->k);
+    L.ntiles = ((w->n_pad / kTile + 1) / 2) * ((L.t_pad / kTile + 1) / 2);
+  } else {
+    L.ntiles = w->n_pad / kTile;
+  }
+  if (schedule == EI_SCHED_TILED_SHUFFLED) {
+    L.perm_off = off;
+    off = align_up(off + sizeof(int32_t) * (size_t)(L.ntiles + w->nb));
+  }
+  if (schedule == EI_SCHED_SPLIT_K) {
+    L.part_off = off;
+    off = align_up(off + sizeof(int64_t) * (size_t)kSplitParts * limbs * (size_t)t * (size_t)w->n);
+  }
+  if (schedule == EI_SCHED_TREE) {
+    L.part_off = off;
+    off = align_up(off + sizeof(int64_t) * (size_t)w->nb * limbs * (size_t)t * (size_t)w->n);
+  }
+  L.total = off;
+  return L;
+}
+
+int check_weights(const ei_weights* w, int format) {
+  if (!w || !w->packed || w->format != format) return EI_EINVAL;
+  if (w->n < 1 || w->k < 32 || w->k % 32 != 0 || w->nb != w->k / 32 || w->n_pad != round_up(w->n, kTile))
+    return EI_EINVAL;
+  if (w->k > kMaxK) return EI_ERANGE;
+  return EI_OK;
+}
+
+int run_gemm(const ei_weights* w, const void* x, int x_is_i32, int64_t* y, int64_t t, int limbs, int schedule,
+             uint64_t seed, void* ws, size_t ws_bytes, int32_t* status, hipStream_t s, int out_mode) {
+  if (!x || !y || t < 1) return EI_EINVAL;
+  if (limbs < 1 || limbs > 8) return EI_EINVAL;
+  if (limbs > kMaxLimbs) return EI_ERANGE;
+  if (schedule < EI_SCHED_DEFAULT || schedule > EI_SCHED_TREE) return EI_EINVAL;
+  const WsLayout lay = layout_for(w, t, limbs, schedule);
+  if (lay.total > 0 && (!ws || ws_bytes < lay.total)) return EI_ENOSPACE;
+  uint8_t* wsb = static_cast<uint8_t*>(ws);
+
+  GemmArgs a;
+  std::memset(&a, 0, sizeof a);
+  const uint8_t* base = static_cast<const uint8_t*>(w->packed);
+  a.codes = reinterpret_cast<const int8_t*>(base + kHeaderBytes);
+  a.scales = reinterpret_cast<const int32_t*>(base + kHeaderBytes + w->n_pad * w->k);
+  a.x = x;
+  a.x_is_i32 = x_is_i32;
+  a.y = y;
+  a.status = status;
+  a.n = w->n;
+  a.k = w->k;
+  a.t = t;
+  a.n_pad = w->n_pad;
+  a.t_pad = lay.t_pad;
+  a.nb = w->nb;
+  a.b0 = 0;
+  a.b1 = w->nb;
+  a.out_mode = out_mode;
+  a.order = ORDER_ASC;
+
+  hipError_t e = hipSuccess;
+  if (lay.mfma) {
+    a.limb_tiles = reinterpret_cast<const int8_t*>(wsb + lay.limb_off);
+    e = launch_limb_tiles(x, x_is_i32, t, w->k, limbs, reinterpret_cast<int8_t*>(wsb + lay.limb_off), lay.t_pad,
+                          status, s);
+    if (e != hipSuccess) return EI_EDEVICE;
+  }
+  auto launch = [&](const GemmArgs& args) { return lay.mfma ? launch_gemm_mfma(args, limbs, s) : launch_gemv(args, limbs, s); };
+
+  switch (schedule) {
+    case EI_SCHED_DEFAULT:
+    case EI_SCHED_CANONICAL:
+      e = launch(a);
+      break;
+    case EI_SCHED_REVERSED:
+      a.order = ORDER_DESC;
+      e = launch(a);
+      break;
+    case EI_SCHED_TILED_SHUFFLED: {
+      int32_t* tperm = reinterpret_cast<int32_t*>(wsb + lay.perm_off);
+      int32_t* kperm = tperm + lay.ntiles;
+      e = launch_make_perm(tperm, lay.ntiles, seed, s);
+      if (e == hipSuccess) e = launch_make_perm(kperm, w->nb, seed ^ 0x5851F42D4C957F2Dull, s);
+      a.tperm = tperm;
+      a.kperm = kperm;
+      a.order = ORDER_PERM;
+      if (e == hipSuccess) e = launch(a);
+      break;
+    }
+    case EI_SCHED_SPLIT_K: {
+      int64_t* part = reinterpret_cast<int64_t*>(wsb + lay.part_off);
+      a.part = part;
+      a.out_mode = OUT_PARTIAL;
+      for (int p = 0; p < kSplitParts && e == hipSuccess; ++p) {
+        a.b0 = p * w->nb / kSplitParts;
+        a.b1 = (p + 1) * w->nb / kSplitParts;
+        a.part_index = p;
+        e = launch(a);
+      }
+      if (e == hipSuccess) e = launch_combine_partials(part, kSplitParts, y, t, w->n, limbs, out_mode, status, s);
+      break;
+    }
+    case EI_SCHED_TREE: {
+      int64_t* terms = reinterpret_cast<int64_t*>(wsb + lay.part_off);
+      a.part = terms;
+      a.out_mode = OUT_TERMS;
+      e = launch(a);
+      if (e == hipSuccess) e = launch_tree_terms(terms, w->nb, y, t, w->n, limbs, out_mode, status, s);
+      break;
+    }
+  }
+  return e == hipSuccess ? EI_OK : EI_EDEVICE;
+}
+
+int do_pack(int format, const void* codes, const void* scales, int64_t n, int64_t k, void* packed,
+            size_t packed_bytes_, ei_weights* out, hipStream_t s) {
+  if (!codes || !scales || !packed || !out) return EI_EINVAL;
+  if (n < 1 || k < 32 || k % 32 != 0) return EI_EINVAL;
+  if (!aligned(packed, 256) || (format == EI_FORMAT_Q8 && !aligned(codes, 16))) return EI_EINVAL;
+  if (packed_bytes_ < ei::packed_bytes(n, k)) return EI_ENOSPACE;
+  hipError_t e = format == EI_FORMAT_Q8
+                     ? launch_pack_q8(static_cast<const int8_t*>(codes), static_cast<const int32_t*>(scales), n, k,
+                                      packed, s)
+                     : launch_pack_q4(static_cast<const uint8_t*>(codes), static_cast<const uint8_t*>(scales), n, k,
+                                      packed, s);
+  if (e != hipSuccess) return EI_EDEVICE;
+  PackedHeader h;
+  if (hipMemcpyAsync(&h, packed, sizeof h, hipMemcpyDeviceToHost, s) != hipSuccess) return EI_EDEVICE;
+  if (hipStreamSynchronize(s) != hipSuccess) return EI_EDEVICE;
+  if (h.magic != kMagic || h.n != n || h.k != k) return EI_EDEVICE;
+  out->packed = packed;
+  out->n = n;
+  out->k = k;
+  out->n_pad = h.n_pad;
+  out->nb = h.nb;
+  out->smax = h.smax;
+  out->format = format;
+  return EI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ei_packed_bytes(int64_t n, int64_t k) {
+  if (n < 1 || k < 32 || k % 32 != 0) return 0;
+  return ei::packed_bytes(n, k);
+}
+
+int ei_q8_pack(const int8_t* codes, const int32_t* scales, int64_t n, int64_t k, void* packed, size_t packed_bytes,
+               ei_weights* out, ei_stream stream) {
+  return do_pack(EI_FORMAT_Q8, codes, scales, n, k, packed, packed_bytes, out, static_cast<hipStream_t>(stream));
+}
+
+int ei_q4_pack(const uint8_t* nib, const uint8_t* sme, int64_t n, int64_t k, void* packed, size_t packed_bytes,
+               ei_weights* out, ei_stream stream) {
+  return do_pack(EI_FORMAT_Q4, nib, sme, n, k, packed, packed_bytes, out, static_cast<hipStream_t>(stream));
+}
+
+int ei_limb_split(const int64_t* x, int8_t* d, int64_t n, int limbs, int32_t* d_status, ei_stream stream) {
+  if (!x || !d || n < 0) return EI_EINVAL;
+  if (limbs < 1 || limbs > 8) return EI_EINVAL;
+  return launch_limb_split_flat(x, d, n, limbs, d_status, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? EI_OK
+             : EI_EDEVICE;
+}
+
+size_t ei_gemm_workspace_bytes(const ei_weights* w, int64_t t, int limbs, int schedule) {
+  if (!w || t < 1 || limbs < 1) return 0;
+  return layout_for(w, t, limbs, schedule).total;
+}
+
+int int_gemm_q8(const ei_weights* w, const int64_t* x, int64_t* y, int64_t t, int limbs, int schedule,
+                uint64_t shuffle_seed, void* workspace, size_t workspace_bytes, int32_t* d_status, ei_stream stream) {
+  const int c = check_weights(w, EI_FORMAT_Q8);
+  if (c != EI_OK) return c;
+  return run_gemm(w, x, 0, y, t, limbs, schedule, shuffle_seed, workspace, workspace_bytes, d_status,
+                  static_cast<hipStream_t>(stream), OUT_ROUND_Q24);
+}
+
+int int_gemm_q4(const ei_weights* w, const int32_t* x, int64_t* y, int64_t t, int limbs, int schedule,
+                uint64_t shuffle_seed, void* workspace, size_t workspace_bytes, int32_t* d_status, ei_stream stream) {
+  const int c = check_weights(w, EI_FORMAT_Q4);
+  if (c != EI_OK) return c;
+  return run_gemm(w, x, 1, y, t, limbs, schedule, shuffle_seed, workspace, workspace_bytes, d_status,
+                  static_cast<hipStream_t>(stream), OUT_EXACT);
+}
+
+int ei_silu_lut_build(int32_t* lut, ei_stream stream) {
+  if (!lut) return EI_EINVAL;
+  return launch_silu_lut(lut, static_cast<hipStream_t>(stream)) == hipSuccess ? EI_OK : EI_EDEVICE;
+}
+
+int silu_lut_epilogue(const int64_t* gate, const int64_t* up, const int32_t* lut, int64_t* h, int64_t n,
+                      int32_t* d_status, ei_stream stream) {
+  if (!gate || !up || !lut || !h || n < 0) return EI_EINVAL;
+  return launch_silu_mul(gate, up, lut, h, n, d_status, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? EI_OK
+             : EI_EDEVICE;
+}
+
+int output_digest(const void* dptr, size_t nbytes, uint8_t* out, ei_stream stream) {
+  if (!out || (!dptr && nbytes)) return EI_EINVAL;
+  if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return EI_EDEVICE;
+  void* host = std::malloc(nbytes ? nbytes : 1);
+  if (!host) return EI_ENOSPACE;
+  if (nbytes && hipMemcpy(host, dptr, nbytes, hipMemcpyDeviceToHost) != hipSuccess) {
+    std::free(host);
+    return EI_EDEVICE;
+  }
+  ei::sha256(host, nbytes, out);
+  std::free(host);
+  return EI_OK;
+}
+
+void ei_sha256_host(const void* data, size_t nbytes, uint8_t* out) { ei::sha256(data, nbytes, out); }
+
+const char* ei_status_string(int code) {
+  switch (code) {
+    case EI_OK: return "ok";
+    case EI_EINVAL: return "invalid argument";
+    case EI_ERANGE: return "outside the exactness envelope";
+    case EI_EDEVICE: return "HIP runtime error";
+    case EI_ENOSPACE: return "workspace or buffer too small";
+    default: return "unknown status";
+  }
+}
+
+int ei_version(void) { return 100; }
+
+}  // extern "C"

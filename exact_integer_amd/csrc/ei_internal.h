@@ -1,0 +1,109 @@
+// Internal declarations shared by the library's translation units.
+// Not installed; the public interface is include/exact_int.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "exact_int.h"
+
+namespace ei {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+constexpr uint32_t kMagic = 0x31514945u;   // "EIQ1"
+constexpr int kHeaderBytes = 256;
+constexpr int kTile = 32;                   // rows per row group, tokens per token group, columns per block
+constexpr int kTileBytes = 1024;            // one 32x32 int8 tile in MFMA lane order
+constexpr int64_t kMaxK = 262144;           // per-limb int64 sums exact up to here (2^13 blocks x 2^50)
+constexpr int kMaxLimbs = 4;                // limb counts instantiated by this build
+
+// The packed weight buffer starts with this header (device memory).
+struct PackedHeader {
+  uint32_t magic;
+  int32_t format;
+  int64_t n, k, n_pad, nb;
+  uint32_t smax;     // max |scale| (written by the pack pass with atomicMax)
+  uint32_t pad0;
+  int64_t codes_off, scales_off;
+};
+static_assert(sizeof(PackedHeader) <= kHeaderBytes, "header too large");
+
+inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+inline size_t packed_bytes(int64_t n, int64_t k) {
+  int64_t n_pad = round_up(n, kTile);
+  return (size_t)kHeaderBytes + (size_t)n_pad * (size_t)k + (size_t)n_pad * (size_t)(k / 32) * 4u;
+}
+
+// Output modes of the projection kernels.
+enum OutMode : int {
+  OUT_ROUND_Q24 = 0,   // y = floor((acc + 2^23) / 2^24)       (Q8)
+  OUT_EXACT = 1,       // y = acc, checked to fit int64          (Q4)
+  OUT_PARTIAL = 2,     // per-limb int64 partial sums to workspace [part][L][T][N]
+  OUT_TERMS = 3        // per-limb int64 per-block terms to workspace [b][L][T][N]
+};
+
+// Block visiting orders inside a kernel.
+enum BlockOrder : int { ORDER_ASC = 0, ORDER_DESC = 1, ORDER_PERM = 2 };
+
+// Everything a projection kernel launch needs.
+struct GemmArgs {
+  const int8_t* codes;       // packed code tiles
+  const int32_t* scales;     // packed scales
+  const void* x;             // int64 (Q8) or int32 (Q4) activations [T][K]
+  int x_is_i32;
+  const int8_t* limb_tiles;  // [L][t_pad/32][nb][1 KB] (MFMA path)
+  int64_t* y;                // [T][N]
+  int64_t* part;             // OUT_PARTIAL / OUT_TERMS destination
+  const int32_t* kperm;      // ORDER_PERM: block order [nb]
+  const int32_t* tperm;      // tile order for the shuffled schedule (or null)
+  int32_t* status;           // device status word (or null)
+  int64_t n, k, t, n_pad, t_pad, nb;
+  int64_t b0, b1;            // block range [b0, b1)
+  int part_index;            // OUT_PARTIAL: which partial this launch writes
+  int out_mode, order;
+};
+
+// Launchers (each defined in the translation unit that holds its kernel).
+hipError_t launch_pack_q8(const int8_t* codes, const int32_t* scales, int64_t n, int64_t k,
+                          void* packed, hipStream_t s);
+hipError_t launch_pack_q4(const uint8_t* nib, const uint8_t* sme, int64_t n, int64_t k,
+                          void* packed, hipStream_t s);
+hipError_t launch_limb_split_flat(const int64_t* x, int8_t* d, int64_t n, int limbs,
+                                  int32_t* status, hipStream_t s);
+hipError_t launch_limb_tiles(const void* x, int x_is_i32, int64_t t, int64_t k, int limbs,
+                             int8_t* tiles, int64_t t_pad, int32_t* status, hipStream_t s);
+hipError_t launch_gemv(const GemmArgs& a, int limbs, hipStream_t s);
+hipError_t launch_gemm_mfma(const GemmArgs& a, int limbs, hipStream_t s);
+hipError_t launch_combine_partials(const int64_t* part, int nparts, int64_t* y, int64_t t, int64_t n,
+                                   int limbs, int out_mode, int32_t* status, hipStream_t s);
+hipError_t launch_tree_terms(int64_t* terms, int64_t nb, int64_t* y, int64_t t, int64_t n,
+                             int limbs, int out_mode, int32_t* status, hipStream_t s);
+hipError_t launch_make_perm(int32_t* perm, int64_t n, uint64_t seed, hipStream_t s);
+hipError_t launch_silu_lut(int32_t* lut, hipStream_t s);
+hipError_t launch_silu_mul(const int64_t* g, const int64_t* u, const int32_t* lut, int64_t* h,
+                           int64_t n, int32_t* status, hipStream_t s);
+
+void sha256(const void* data, size_t n, uint8_t out[32]);
+
+// ---------------------------------------------------------------- device
+// Combine per-limb int64 sums A_l into sum_l 2^(8l) A_l (int128) and apply
+// the output rounding.  Returns false if the result does not fit int64.
+__device__ inline bool finish_output(__int128 acc, int mode, int64_t* out) {
+  __int128 v = acc;
+  if (mode == OUT_ROUND_Q24) v = (acc + ((__int128)1 << 23)) >> 24;   // arithmetic: floor
+  const __int128 lo = -((__int128)1 << 63), hi = ((__int128)1 << 63) - 1;
+  if (v < lo || v > hi) { *out = 0; return false; }
+  *out = (int64_t)v;
+  return true;
+}
+
+__device__ inline void flag(int32_t* status, int bits) {
+  if (status) atomicOr(status, bits);
+}
+
+}  // namespace ei

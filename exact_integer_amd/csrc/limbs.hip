@@ -1,0 +1,110 @@
+// Activation limb split (the quantiser in front of the int8 contraction).
+//
+// An integer activation x is written as balanced base-256 digits
+// d_l in [-128, 127], x = sum_{l<L} 256^l d_l.  The digit set is a complete
+// residue system mod 256, so the digits are unique: d_0 = ((x + 128) mod 256)
+// - 128, then x <- (x - d_0) / 256 (exact), and so on.  After L digits the
+// remainder must be zero, otherwise x is outside the L-limb range and the
+// device status gets EI_DEV_LIMB_RANGE.  With the digits, the contraction
+// sum_j q_j x_j becomes L int8 x int8 contractions whose int32 block sums
+// are exact (|sum over 32| <= 32 * 128 * 128 < 2^19).
+#include "ei_internal.h"
+
+namespace ei {
+
+// Digits of v; returns true if v fits L limbs.
+template <int L>
+__device__ inline bool split_digits(int64_t v, int (&d)[L]) {
+  uint64_t r = (uint64_t)v;
+#pragma unroll
+  for (int l = 0; l < L; ++l) {
+    int dl = (int)((r + 128u) & 255u) - 128;
+    d[l] = dl;
+    r = (uint64_t)(((int64_t)(r - (uint64_t)(int64_t)dl)) >> 8);   // exact division by 256
+  }
+  return r == 0;
+}
+
+__global__ void limb_split_flat_kernel(const int64_t* __restrict__ x, int8_t* __restrict__ d, int64_t n, int limbs,
+                                       int32_t* status) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  uint64_t r = (uint64_t)x[i];
+  for (int l = 0; l < limbs; ++l) {
+    int dl = (int)((r + 128u) & 255u) - 128;
+    d[(int64_t)l * n + i] = (int8_t)dl;
+    r = (uint64_t)(((int64_t)(r - (uint64_t)(int64_t)dl)) >> 8);
+  }
+  if (r != 0) flag(status, EI_DEV_LIMB_RANGE);
+}
+
+// One thread per (token t < t_pad, block b, half h): 16 activations into 16
+// bytes of each of the L limb tiles, at lane t%32 + 32h of tile (l, t/32, b).
+template <int L, typename XT>
+__global__ void limb_tiles_kernel(const XT* __restrict__ x, int64_t t, int64_t k, int8_t* __restrict__ tiles,
+                                  int64_t t_pad, int32_t* status) {
+  const int64_t nb = k / 32;
+  int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= t_pad * nb * 2) return;
+  const int h = (int)(gid & 1);
+  const int64_t b = (gid >> 1) % nb;
+  const int64_t tok = (gid >> 1) / nb;
+  const int64_t tg = tok / kTile;
+  const int lane = (int)(tok % kTile) + 32 * h;
+  uint32_t words[L][4];
+#pragma unroll
+  for (int l = 0; l < L; ++l)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) words[l][w] = 0;
+  bool ok = true;
+  if (tok < t) {
+    const XT* src = x + tok * k + b * 32 + 16 * h;
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      int d[L];
+      ok &= split_digits<L>((int64_t)src[p], d);
+#pragma unroll
+      for (int l = 0; l < L; ++l) words[l][p >> 2] |= ((uint32_t)(uint8_t)(int8_t)d[l]) << (8 * (p & 3));
+    }
+  }
+  if (!ok) flag(status, EI_DEV_LIMB_RANGE);
+  const int64_t tgs = t_pad / kTile;
+#pragma unroll
+  for (int l = 0; l < L; ++l) {
+    v4i v = {(int)words[l][0], (int)words[l][1], (int)words[l][2], (int)words[l][3]};
+    int8_t* dst = tiles + ((((int64_t)l * tgs + tg) * nb + b) * 64 + lane) * 16;
+    *reinterpret_cast<v4i*>(dst) = v;
+  }
+}
+
+hipError_t launch_limb_split_flat(const int64_t* x, int8_t* d, int64_t n, int limbs, int32_t* status,
+                                  hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(limb_split_flat_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, x, d, n, limbs,
+                     status);
+  return hipGetLastError();
+}
+
+template <typename XT>
+static void launch_tiles_t(const XT* x, int64_t t, int64_t k, int limbs, int8_t* tiles, int64_t t_pad,
+                           int32_t* status, hipStream_t s) {
+  const int64_t threads = t_pad * (k / 32) * 2;
+  const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+  switch (limbs) {
+    case 1: hipLaunchKernelGGL((limb_tiles_kernel<1, XT>), grid, block, 0, s, x, t, k, tiles, t_pad, status); break;
+    case 2: hipLaunchKernelGGL((limb_tiles_kernel<2, XT>), grid, block, 0, s, x, t, k, tiles, t_pad, status); break;
+    case 3: hipLaunchKernelGGL((limb_tiles_kernel<3, XT>), grid, block, 0, s, x, t, k, tiles, t_pad, status); break;
+    default: hipLaunchKernelGGL((limb_tiles_kernel<4, XT>), grid, block, 0, s, x, t, k, tiles, t_pad, status); break;
+  }
+}
+
+hipError_t launch_limb_tiles(const void* x, int x_is_i32, int64_t t, int64_t k, int limbs, int8_t* tiles,
+                             int64_t t_pad, int32_t* status, hipStream_t s) {
+  if (x_is_i32)
+    launch_tiles_t(static_cast<const int32_t*>(x), t, k, limbs, tiles, t_pad, status, s);
+  else
+    launch_tiles_t(static_cast<const int64_t*>(x), t, k, limbs, tiles, t_pad, status, s);
+  return hipGetLastError();
+}
+
+}  // namespace ei

@@ -1,0 +1,92 @@
+// Partial-sum combination for the split-K and tree schedules, and the seeded
+// permutation used by the shuffled schedule ("Vendor-Invariant Integer
+// Inference for MindChain: Handshake v0", Construction / Schedule gate: the
+// same GEMM under canonical, reversed, tiled_shuffled, split_k and tree_walk
+// schedules must give one digest).
+#include "ei_internal.h"
+
+namespace ei {
+
+// y[t][i] from per-limb partials part[p][l][t][i], p summed from the last
+// partial down to the first; each partial sum is exact in int64.
+__global__ void combine_partials_kernel(const int64_t* __restrict__ part, int nparts, int64_t* __restrict__ y,
+                                        int64_t t, int64_t n, int limbs, int out_mode, int32_t* status) {
+  int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= t * n) return;
+  __int128 v = 0;
+  for (int l = 0; l < limbs; ++l) {
+    int64_t s = 0;
+    for (int p = nparts - 1; p >= 0; --p) s += part[((int64_t)p * limbs + l) * t * n + e];
+    v += (__int128)s << (8 * l);
+  }
+  int64_t out;
+  if (!finish_output(v, out_mode, &out)) flag(status, EI_DEV_OUT_RANGE);
+  y[e] = out;
+}
+
+// Pairwise tree over the per-block terms terms[b][l][t][i]: pairs (0,1),
+// (2,3), ... at every level, an odd last term passes up unchanged.  Each
+// thread owns one (t, i) and reduces its L columns in place.
+__global__ void tree_terms_kernel(int64_t* __restrict__ terms, int64_t nb, int64_t* __restrict__ y, int64_t t,
+                                  int64_t n, int limbs, int out_mode, int32_t* status) {
+  int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= t * n) return;
+  const int64_t stride = (int64_t)limbs * t * n;   // between consecutive blocks
+  __int128 v = 0;
+  for (int l = 0; l < limbs; ++l) {
+    int64_t* col = terms + (int64_t)l * t * n + e;
+    int64_t cnt = nb;
+    while (cnt > 1) {
+      int64_t m = 0;
+      for (; 2 * m + 1 < cnt; ++m) col[m * stride] = col[2 * m * stride] + col[(2 * m + 1) * stride];
+      if (cnt & 1) { col[m * stride] = col[(cnt - 1) * stride]; ++m; }
+      cnt = m;
+    }
+    v += (__int128)(nb > 0 ? col[0] : 0) << (8 * l);
+  }
+  int64_t out;
+  if (!finish_output(v, out_mode, &out)) flag(status, EI_DEV_OUT_RANGE);
+  y[e] = out;
+}
+
+// splitmix64 (Steele, Lea and Flood, 2014) followed by a Fisher-Yates shuffle:
+// perm is a seeded permutation of 0 .. n-1.  One thread; n is a tile or block
+// count.
+__global__ void make_perm_kernel(int32_t* perm, int64_t n, uint64_t seed) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  for (int64_t i = 0; i < n; ++i) perm[i] = (int32_t)i;
+  uint64_t st = seed;
+  for (int64_t i = n - 1; i > 0; --i) {
+    uint64_t z = (st += 0x9E3779B97F4A7C15ull);
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    const int64_t j = (int64_t)(z % (uint64_t)(i + 1));
+    const int32_t tmp = perm[i];
+    perm[i] = perm[j];
+    perm[j] = tmp;
+  }
+}
+
+hipError_t launch_combine_partials(const int64_t* part, int nparts, int64_t* y, int64_t t, int64_t n, int limbs,
+                                   int out_mode, int32_t* status, hipStream_t s) {
+  const int64_t total = t * n;
+  hipLaunchKernelGGL(combine_partials_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, part, nparts, y,
+                     t, n, limbs, out_mode, status);
+  return hipGetLastError();
+}
+
+hipError_t launch_tree_terms(int64_t* terms, int64_t nb, int64_t* y, int64_t t, int64_t n, int limbs, int out_mode,
+                             int32_t* status, hipStream_t s) {
+  const int64_t total = t * n;
+  hipLaunchKernelGGL(tree_terms_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, terms, nb, y, t, n,
+                     limbs, out_mode, status);
+  return hipGetLastError();
+}
+
+hipError_t launch_make_perm(int32_t* perm, int64_t n, uint64_t seed, hipStream_t s) {
+  hipLaunchKernelGGL(make_perm_kernel, dim3(1), dim3(64), 0, s, perm, n, seed);
+  return hipGetLastError();
+}
+
+}  // namespace ei

@@ -1,0 +1,235 @@
+/*
+ * exact_int.h -- C ABI of the exact-integer block-quantized projection
+ * library for AMD Instinct MI355X (gfx950).
+ *
+ * The library computes the projection stated on the pages
+ *
+ *     y_i = rnd( sum_b S_ib * sum_{j in b} q_ij * x_j )
+ *
+ * exactly, so that its output bits do not depend on loop order, tiling or
+ * split-K.  Sources (cited by page title and section):
+ *   [UORLUT01]  "D11 integer table serving (UORLUT01)", "How it works":
+ *               "Export" (4-bit codes in groups of 32, one-byte scale with
+ *               a 4-bit mantissa and a 4-bit exponent) and "One projection
+ *               (definition)" (y_i = sum_j w_ij x_j, w_ij = s_g q_ij,
+ *               s_g = m 2^e).
+ *   [Handshake] "Vendor-Invariant Integer Inference for MindChain:
+ *               Handshake v0", claim C1 and "Construction / The frozen
+ *               profile" (Q8_0 codes in blocks of 32, FP16 block scales
+ *               frozen into Q24 integers, Q16 activations in int64, exact
+ *               accumulation with no saturation, Decimal-committed SiLU
+ *               table); C3 and "Schedule gate" (five adversarial
+ *               schedules); C4 (the SiLU table's clip behaviour).
+ *   [tritify]   "Deterministic, Reproducible Inference in Exact Integer
+ *               Arithmetic, and Verifiable Distributed Inference as Its
+ *               Consequence" (arXiv 2611.13730), 3.1 "Arithmetic
+ *               specification" (i128 reference accumulator, i64 hot path
+ *               within a proven range bound), 3.2 "Mixture-of-Experts",
+ *               4 (SHA-256 of the integer output).
+ *
+ * Conventions (all entry points):
+ *   - Pointers are DEVICE pointers owned by the caller unless a comment says
+ *     "host".  The library never frees caller memory.  Arrays are dense,
+ *     row-major, little-endian, and 16-byte aligned unless stated.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are
+ *     asynchronous on `stream` unless a comment says "synchronous".
+ *   - The return value reports errors the host can see at once (EI_EINVAL,
+ *     EI_ERANGE, EI_ENOSPACE, EI_EDEVICE); nothing is launched when it is
+ *     not EI_OK.  Errors only the device can see (an activation outside the
+ *     declared limb range, a result outside int64) are OR-ed into the
+ *     device word `d_status` (may be NULL to skip), which the caller reads
+ *     after synchronising; the outputs are then unspecified.
+ *   - No entry point allocates device memory except where a comment says
+ *     so; scratch space is the caller's `workspace` of at least the size
+ *     the matching *_workspace_bytes() returns.
+ *   - The library holds no mutable global state; calls on different streams
+ *     may run concurrently.  Calls that share a workspace must be ordered.
+ *   - Weight matrices have K (the reduction dimension) a multiple of 32:
+ *     the block structure of the formats.  N and T may be anything >= 1.
+ */
+#ifndef EXACT_INT_H
+#define EXACT_INT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* ei_stream;   /* a hipStream_t */
+
+/* Return codes. */
+enum {
+  EI_OK = 0,
+  EI_EINVAL = 1,    /* null pointer, bad size or enum, K % 32 != 0, misaligned */
+  EI_ERANGE = 2,    /* request outside the proven-exact envelope (see below)  */
+  EI_EDEVICE = 3,   /* a HIP runtime call failed                               */
+  EI_ENOSPACE = 4   /* workspace or output buffer too small                    */
+};
+
+/* Bits OR-ed into *d_status by the device. */
+enum {
+  EI_DEV_LIMB_RANGE = 1,    /* an activation does not fit the declared limbs */
+  EI_DEV_OUT_RANGE = 2      /* a result does not fit int64                   */
+};
+
+/* Accumulation schedules ([Handshake] "Schedule gate": canonical, reversed,
+ * tiled_shuffled, split_k, tree_walk).  Every schedule returns identical
+ * bits; EI_SCHED_DEFAULT is the fastest kernel for the shape. */
+enum {
+  EI_SCHED_DEFAULT = 0,
+  EI_SCHED_CANONICAL = 1,       /* blocks ascending                               */
+  EI_SCHED_REVERSED = 2,        /* blocks descending                              */
+  EI_SCHED_TILED_SHUFFLED = 3,  /* output tiles and K blocks in a seeded order    */
+  EI_SCHED_SPLIT_K = 4,         /* 8 K-ranges as separate partials, then summed   */
+  EI_SCHED_TREE = 5             /* per-block terms summed in a pairwise tree      */
+};
+
+enum { EI_FORMAT_Q8 = 1, EI_FORMAT_Q4 = 2 };
+
+/* Host-side descriptor of a packed weight matrix, filled by ei_q8_pack or
+ * ei_q4_pack.  `packed` points into the caller's device buffer. */
+typedef struct ei_weights {
+  const void* packed;   /* device: packed tiles, see ei_q8_pack            */
+  int64_t n;            /* output rows                                     */
+  int64_t k;            /* reduction length, a multiple of 32              */
+  int64_t n_pad;        /* n rounded up to a multiple of 32                */
+  int64_t nb;           /* k / 32 blocks                                   */
+  uint32_t smax;        /* max |scale| over all blocks (Q4: max 2^e)       */
+  int32_t format;       /* EI_FORMAT_Q8 or EI_FORMAT_Q4                    */
+} ei_weights;
+
+/* ------------------------------------------------------------ weights */
+
+/* Bytes of device memory ei_q8_pack / ei_q4_pack need for an n x k matrix. */
+size_t ei_packed_bytes(int64_t n, int64_t k);
+
+/*
+ * Repack a Q8 matrix ([Handshake] C1: 8-bit codes, one Q24 int32 scale per
+ * 32-wide block along K) into the kernels' layout, once, at load time.
+ *   codes   device int8 [n][k]
+ *   scales  device int32 [n][k/32]
+ *   packed  device buffer of >= ei_packed_bytes(n, k) bytes, 256-B aligned;
+ *           after the call it holds a 256-byte header, then the code tiles
+ *           [n_pad/32][k/32][64 lanes][16 B] (lane l holds row l%32 and
+ *           columns 16*(l/32) .. +15 of the block), then the scales
+ *           [n_pad/32][k/32][32] int32; rows >= n are zero.
+ *   out     host: the descriptor to pass to the GEMM entry points.
+ * Synchronous (it reads back the largest scale).  Errors: EI_EINVAL for a
+ * null pointer, n < 1, k < 32 or k % 32 != 0; EI_ENOSPACE if packed_bytes is
+ * too small; EI_EDEVICE on a HIP failure.
+ */
+int ei_q8_pack(const int8_t* codes, const int32_t* scales, int64_t n, int64_t k,
+               void* packed, size_t packed_bytes, ei_weights* out, ei_stream stream);
+
+/*
+ * Repack a UORLUT01-style 4-bit matrix ([UORLUT01] "Export": 4-bit codes in
+ * groups of 32 with a one-byte scale, mantissa m and exponent e, s = m 2^e).
+ *   nib     device uint8 [n][k/2]: two's-complement nibbles, element 2j in
+ *           the low nibble of byte j
+ *   sme     device uint8 [n][k/32]: m in the low nibble, e in the high nibble
+ * The mantissa is folded into the codes (m q lies in [-120, 105], an int8)
+ * and the scale kept as 2^e, so sum_g m 2^e sum_j q x is computed exactly
+ * as sum_g 2^e sum_j (m q) x.  Layout, sync and errors as ei_q8_pack.
+ */
+int ei_q4_pack(const uint8_t* nib, const uint8_t* sme, int64_t n, int64_t k,
+               void* packed, size_t packed_bytes, ei_weights* out, ei_stream stream);
+
+/* ------------------------------------------------------ activations */
+
+/*
+ * Balanced base-256 limb split, the activation quantiser: digits d_l in
+ * [-128, 127] with x = sum_{l<L} 256^l d_l (unique).  Q16 activations with
+ * |x| <= 2^22 need L = 3 (range [-8421504, 8355711]).
+ *   x       device int64 [n]
+ *   d       device int8 [L][n]
+ * An x outside the L-limb range sets EI_DEV_LIMB_RANGE.  L in 1..8.
+ */
+int ei_limb_split(const int64_t* x, int8_t* d, int64_t n, int limbs,
+                  int32_t* d_status, ei_stream stream);
+
+/* ------------------------------------------------------ projections */
+
+/* Workspace bytes int_gemm_q8 / int_gemm_q4 need for T tokens. */
+size_t ei_gemm_workspace_bytes(const ei_weights* w, int64_t t, int limbs, int schedule);
+
+/*
+ * Q8 projection ([UORLUT01] "One projection (definition)"; [Handshake] C1,
+ * "The frozen profile"):
+ *     acc[t][i] = sum_b S[i][b] * sum_{j in b} q[i][j] * x[t][j]   (exact)
+ *     y[t][i]   = (acc[t][i] + 2^23) >> 24   (arithmetic shift: floor)
+ *   w        host: descriptor from ei_q8_pack (format EI_FORMAT_Q8)
+ *   x        device int64 [t][k], Q16 activations
+ *   y        device int64 [t][n]
+ *   limbs    activation limbs L in 1..8; every x must satisfy the L-limb
+ *            range (3 limbs: [-8421504, 8355711], which holds |x| <= 2^22)
+ *   schedule EI_SCHED_*; shuffle_seed seeds EI_SCHED_TILED_SHUFFLED
+ * Exactness: per-limb partial sums are carried in int64 and are exact for
+ * any int32 scales while k <= 262144 (each term |S P| < 2^31 2^19 = 2^50);
+ * the limbs are combined in int128 and rounded once.  EI_ERANGE if
+ * k > 262144.  A y outside int64 sets EI_DEV_OUT_RANGE.
+ */
+int int_gemm_q8(const ei_weights* w, const int64_t* x, int64_t* y, int64_t t, int limbs,
+                int schedule, uint64_t shuffle_seed, void* workspace, size_t workspace_bytes,
+                int32_t* d_status, ei_stream stream);
+
+/*
+ * 4-bit projection ([UORLUT01] "One projection (definition)"), exact, not
+ * rounded:  y[t][i] = sum_g m[i][g] 2^e[i][g] sum_{j in g} q[i][j] x[t][j]
+ *   w        descriptor from ei_q4_pack (format EI_FORMAT_Q4)
+ *   x        device int32 [t][k]; limbs as in int_gemm_q8 (3 covers
+ *            |x| < 2^23; the workload's x in [-2^15, 2^15) needs 3 too, as
+ *            2 limbs stop at 32639)
+ *   y        device int64 [t][n]
+ * Other arguments and errors as int_gemm_q8.
+ */
+int int_gemm_q4(const ei_weights* w, const int32_t* x, int64_t* y, int64_t t, int limbs,
+                int schedule, uint64_t shuffle_seed, void* workspace, size_t workspace_bytes,
+                int32_t* d_status, ei_stream stream);
+
+/* ------------------------------------------------------- epilogues */
+
+/*
+ * Build the 65537-entry SiLU table ([Handshake] C1, C4: Q11 input over
+ * +-16, Q16 output): lut[k + 32768] = round(silu(k / 2^11) * 2^16),
+ * silu(z) = z / (1 + e^-z), k in [-32768, 32768].
+ *   lut     device int32 [65537]
+ */
+int ei_silu_lut_build(int32_t* lut, ei_stream stream);
+
+/*
+ * SiLU-gated product ([Handshake] C1, C4), elementwise over n values:
+ *     idx  = clamp(floor((g + 16) / 32), -32768, 32768)   (Q16 -> Q11, add-half)
+ *     h    = floor(lut[idx + 32768] * u / 2^16)            (Q16)
+ *   gate, up, h  device int64 [n];  lut device int32 [65537]
+ * An h outside int64 sets EI_DEV_OUT_RANGE.
+ */
+int silu_lut_epilogue(const int64_t* gate, const int64_t* up, const int32_t* lut, int64_t* h,
+                      int64_t n, int32_t* d_status, ei_stream stream);
+
+/* -------------------------------------------------------- digests */
+
+/*
+ * SHA-256 of the raw bytes of a device buffer ([tritify] 4: the integer
+ * output carries a reproducing SHA-256).  Synchronous: waits for `stream`,
+ * copies the bytes to host memory (allocated and freed inside the call)
+ * and hashes them.
+ *   out     host uint8 [32]
+ */
+int output_digest(const void* dptr, size_t nbytes, uint8_t* out, ei_stream stream);
+
+/* SHA-256 (FIPS 180-4) of a host buffer; host-only, no device work. */
+void ei_sha256_host(const void* data, size_t nbytes, uint8_t* out);
+
+/* Human-readable name of a return code. */
+const char* ei_status_string(int code);
+
+/* Library ABI version (major * 100 + minor). */
+int ei_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_INT_H */
