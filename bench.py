@@ -77,6 +77,26 @@ def cpu_baseline(q, s, x1, x512, rows: int):
     }, y1
 
 
+def copy_calibration(torch, dev) -> int:
+    """A plain copy of known size: each launch reads and writes 256 MiB.  The
+    HBM byte counters of this copy give the scale factor for the counters
+    read on the projection kernels."""
+    nbytes = 256 << 20
+    src = torch.randint(0, 255, (nbytes,), dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 5
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "launches": 5,
+                      "ms_per_copy": round(ms, 4), "copy_gbs_read_plus_write": round(2 * nbytes / ms / 1e6, 1)}))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -86,6 +106,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--profile", action="store_true", help="short run for rocprofv3 (no baseline, few steps)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of 256 MiB, 5 times (the reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -103,6 +125,8 @@ def main() -> int:
         print("bench.py: no HIP device", file=sys.stderr)
         return 1
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        return copy_calibration(torch, dev)
 
     def to_dev(a):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)

@@ -66,7 +66,15 @@ struct GemmArgs {
   int64_t b0, b1;            // block range [b0, b1)
   int part_index;            // OUT_PARTIAL: which partial this launch writes
   int out_mode, order;
+  int chunk;                 // GEMV: blocks per wave per LDS limb chunk (a multiple of its prefetch depth)
 };
+
+// pos-th block visited by a kernel in the block range [b0, b1) of `a`.
+__device__ inline int64_t block_at(const GemmArgs& a, int64_t pos) {
+  if (a.order == ORDER_DESC) return a.b1 - 1 - pos;
+  if (a.order == ORDER_PERM) return a.kperm[a.b0 + pos];
+  return a.b0 + pos;
+}
 
 // Launchers (each defined in the translation unit that holds its kernel).
 hipError_t launch_pack_q8(const int8_t* codes, const int32_t* scales, int64_t n, int64_t k,
@@ -100,6 +108,42 @@ __device__ inline bool finish_output(__int128 acc, int mode, int64_t* out) {
   if (v < lo || v > hi) { *out = 0; return false; }
   *out = (int64_t)v;
   return true;
+}
+
+// Balanced base-256 digits d_l in [-128, 127] with v = sum_{l<L} 256^l d_l
+// (unique: the digit set is a complete residue system mod 256), for four
+// values at once, packed per limb: byte p of w[l] is d_l of v[p].  With u = v + 128 * (1 + 256 + ... + 256^(L-1)), the
+// ordinary base-256 digits of u are d_l + 128, and v fits L digits exactly
+// when 0 <= u < 2^(8L); d_l + 128 -> d_l as a byte is an XOR with 0x80.
+// The bytes are gathered with v_perm_b32 (selector byte k picks byte k of
+// the pair {S1 = bytes 0-3, S0 = bytes 4-7}; 0x0c gives zero).  L <= 4.
+template <int L>
+__device__ inline bool limb_words(const int64_t (&v)[4], uint32_t (&w)[L]) {
+  static_assert(L >= 1 && L <= 4, "limb_words handles 1..4 limbs");
+  constexpr uint64_t kBias = 0x8080808080808080ull >> (64 - 8 * L);
+  uint32_t lo[4];
+  uint64_t bad = 0;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint64_t u = (uint64_t)v[p] + kBias;
+    bad |= u >> (8 * L);
+    lo[p] = (uint32_t)u ^ 0x80808080u;
+  }
+#pragma unroll
+  for (int l = 0; l < L; ++l) {
+    const uint32_t sel = 0x0c0c0000u | ((uint32_t)(4 + l) << 8) | (uint32_t)l;   // [byte l of S1, byte l of S0, 0, 0]
+    const uint32_t a = __builtin_amdgcn_perm(lo[1], lo[0], sel);
+    const uint32_t b = __builtin_amdgcn_perm(lo[3], lo[2], sel);
+    w[l] = __builtin_amdgcn_perm(b, a, 0x05040100u);                             // [a0, a1, b0, b1]
+  }
+  return bad == 0;
+}
+
+// Buffer resource (V#) over `bytes` bytes at `base`, for raw buffer loads:
+// a scalar base and a per-load scalar offset leave only the lane offset in a
+// VGPR.  Word 3 is the gfx9 raw-buffer configuration (32-bit data format).
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
 
 __device__ inline void flag(int32_t* status, int bits) {

@@ -12,19 +12,25 @@
 
 namespace ei {
 
-// Digits of v; returns true if v fits L limbs.
+// L <= 4: one thread per 4 consecutive values, digits packed with limb_words.
 template <int L>
-__device__ inline bool split_digits(int64_t v, int (&d)[L]) {
-  uint64_t r = (uint64_t)v;
+__global__ void limb_split4_kernel(const int64_t* __restrict__ x, int8_t* __restrict__ d, int64_t n,
+                                   int32_t* status) {
+  const int64_t i0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (i0 >= n) return;
+  int64_t v[4];
 #pragma unroll
-  for (int l = 0; l < L; ++l) {
-    int dl = (int)((r + 128u) & 255u) - 128;
-    d[l] = dl;
-    r = (uint64_t)(((int64_t)(r - (uint64_t)(int64_t)dl)) >> 8);   // exact division by 256
-  }
-  return r == 0;
+  for (int p = 0; p < 4; ++p) v[p] = i0 + p < n ? x[i0 + p] : 0;
+  uint32_t w[L];
+  if (!limb_words<L>(v, w)) flag(status, EI_DEV_LIMB_RANGE);
+#pragma unroll
+  for (int l = 0; l < L; ++l)
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      if (i0 + p < n) d[(int64_t)l * n + i0 + p] = (int8_t)(uint8_t)(w[l] >> (8 * p));
 }
 
+// Any L in 1..8, one value per thread.
 __global__ void limb_split_flat_kernel(const int64_t* __restrict__ x, int8_t* __restrict__ d, int64_t n, int limbs,
                                        int32_t* status) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -60,11 +66,13 @@ __global__ void limb_tiles_kernel(const XT* __restrict__ x, int64_t t, int64_t k
   if (tok < t) {
     const XT* src = x + tok * k + b * 32 + 16 * h;
 #pragma unroll
-    for (int p = 0; p < 16; ++p) {
-      int d[L];
-      ok &= split_digits<L>((int64_t)src[p], d);
+    for (int q = 0; q < 4; ++q) {
+      const int64_t v[4] = {(int64_t)src[4 * q], (int64_t)src[4 * q + 1], (int64_t)src[4 * q + 2],
+                            (int64_t)src[4 * q + 3]};
+      uint32_t w[L];
+      ok &= limb_words<L>(v, w);
 #pragma unroll
-      for (int l = 0; l < L; ++l) words[l][p >> 2] |= ((uint32_t)(uint8_t)(int8_t)d[l]) << (8 * (p & 3));
+      for (int l = 0; l < L; ++l) words[l][q] = w[l];
     }
   }
   if (!ok) flag(status, EI_DEV_LIMB_RANGE);
@@ -80,8 +88,15 @@ __global__ void limb_tiles_kernel(const XT* __restrict__ x, int64_t t, int64_t k
 hipError_t launch_limb_split_flat(const int64_t* x, int8_t* d, int64_t n, int limbs, int32_t* status,
                                   hipStream_t s) {
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(limb_split_flat_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, x, d, n, limbs,
-                     status);
+  const dim3 g4((unsigned)(((n + 3) / 4 + 255) / 256)), b(256);
+  switch (limbs) {
+    case 1: hipLaunchKernelGGL(limb_split4_kernel<1>, g4, b, 0, s, x, d, n, status); break;
+    case 2: hipLaunchKernelGGL(limb_split4_kernel<2>, g4, b, 0, s, x, d, n, status); break;
+    case 3: hipLaunchKernelGGL(limb_split4_kernel<3>, g4, b, 0, s, x, d, n, status); break;
+    case 4: hipLaunchKernelGGL(limb_split4_kernel<4>, g4, b, 0, s, x, d, n, status); break;
+    default:
+      hipLaunchKernelGGL(limb_split_flat_kernel, dim3((unsigned)((n + 255) / 256)), b, 0, s, x, d, n, limbs, status);
+  }
   return hipGetLastError();
 }
 
