@@ -50,6 +50,18 @@ WsLayout layout_for(const ei_weights* w, int64_t t, int limbs, int schedule) {
   return L;
 }
 
+// The tiled prefill kernel keeps one int64 accumulator per output: exact
+// when every partial sum, bounded by nb * smax * 2^19 * (1 + 2^8 + 2^16),
+// stays below 2^63, and it forms S * 2^16 in int32, so smax < 2^15.
+constexpr int64_t kTiledMinT = 64;
+bool tiled_ok(const ei_weights* w, int64_t t, int limbs, int schedule) {
+  if (limbs != 3 || t < kTiledMinT) return false;
+  if (schedule != EI_SCHED_DEFAULT && schedule != EI_SCHED_CANONICAL) return false;
+  if (w->smax >= (1u << 15)) return false;
+  const __int128 bound = (__int128)w->nb * (__int128)w->smax * ((__int128)1 << 19) * 65793;
+  return bound < ((__int128)1 << 63);
+}
+
 int check_weights(const ei_weights* w, int format) {
   if (!w || !w->packed || w->format != format) return EI_EINVAL;
   if (w->n < 1 || w->k < 32 || w->k % 32 != 0 || w->nb != w->k / 32 || w->n_pad != round_up(w->n, kTile))
@@ -95,7 +107,11 @@ int run_gemm(const ei_weights* w, const void* x, int x_is_i32, int64_t* y, int64
                           status, s);
     if (e != hipSuccess) return EI_EDEVICE;
   }
-  auto launch = [&](const GemmArgs& args) { return lay.mfma ? launch_gemm_mfma(args, limbs, s) : launch_gemv(args, limbs, s); };
+  const bool tiled = lay.mfma && tiled_ok(w, t, limbs, schedule);
+  auto launch = [&](const GemmArgs& args) {
+    if (tiled) return launch_gemm_tiled(args, s);
+    return lay.mfma ? launch_gemm_mfma(args, limbs, s) : launch_gemv(args, limbs, s);
+  };
 
   switch (schedule) {
     case EI_SCHED_DEFAULT:

@@ -87,6 +87,7 @@ hipError_t launch_limb_tiles(const void* x, int x_is_i32, int64_t t, int64_t k, 
                              int8_t* tiles, int64_t t_pad, int32_t* status, hipStream_t s);
 hipError_t launch_gemv(const GemmArgs& a, int limbs, hipStream_t s);
 hipError_t launch_gemm_mfma(const GemmArgs& a, int limbs, hipStream_t s);
+hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t s);   // 3 limbs, see tiled_ok()
 hipError_t launch_combine_partials(const int64_t* part, int nparts, int64_t* y, int64_t t, int64_t n,
                                    int limbs, int out_mode, int32_t* status, hipStream_t s);
 hipError_t launch_tree_terms(int64_t* terms, int64_t nb, int64_t* y, int64_t t, int64_t n,

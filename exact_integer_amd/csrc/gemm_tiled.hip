@@ -1,0 +1,220 @@
+// Tiled exact projection for many tokens: the prefill GEMM.
+//
+// Computes, for three activation limbs d_0, d_1, d_2 (x = d_0 + 2^8 d_1 +
+// 2^16 d_2) and every (token t, row i),
+//     acc[t][i] = sum_b S[i][b] * (P_0 + 2^8 P_1 + 2^16 P_2)[t][i][b],
+//     P_l[t][i][b] = sum_{j in b} q[i][j] * d_l[t][j]          (int32, exact)
+// in ONE int64 accumulator, then y = floor((acc + 2^23) / 2^24) (or acc).
+// Exactness: |P_l| <= 32 * 128 * 128 = 2^19, so every partial sum of acc is
+// bounded by nb * smax * 2^19 * (1 + 2^8 + 2^16); the host launches this
+// kernel only when that bound is below 2^63 and smax < 2^15 (so that
+// S * 2^16 is an int32).  P_0 + 2^8 P_1 < 2^28 is formed in int32.  Every
+// step is exact integer arithmetic, so the result is the same bits as any
+// other evaluation order.
+//
+// Work split.  A workgroup of 4 waves owns a tile of 32 RT WR rows x
+// 32 TT (4 / WR) tokens; each wave owns RT x TT 32x32 MFMA tiles.  Per
+// 32-wide block the workgroup needs its code tiles, 3 limb tiles per token
+// tile (1 KB each, already in MFMA lane order in global memory) and the
+// scales of its rows; they are copied global -> LDS with direct-to-LDS
+// buffer loads (no VGPR round trip, scalar block offsets) into a ring of
+// NBUF one-block buffers, NBUF - 1 blocks ahead of use.  Per block a wave
+// issues 3 RT TT v_mfma_i32_32x32x32_i8 and, per output element, one
+// v_lshl_add_u32 and two v_mad_i64_i32: this VALU epilogue, which the matrix
+// cores only partly overlap, is the critical resource.
+#include "ei_internal.h"
+
+namespace ei {
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// Direct-to-LDS copy of 16 bytes per lane from buffer r at voffset +
+// soffset; lane i writes LDS bytes dst + 16 i .. +15.  (A device function of
+// its own: the host pass of the kernel must not see the LDS address space.)
+__device__ inline void copy16_to_lds(__amdgpu_buffer_rsrc_t r, uint8_t* dst, uint32_t voffset, uint32_t soffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)dst, 16, voffset, soffset, 0, 0);
+}
+
+// Workgroup barrier once at most N of this wave's vector-memory operations
+// (here: direct-to-LDS copies of later blocks) are outstanding and its LDS
+// reads are done.  __syncthreads would wait for every copy in flight.
+template <int N>
+__device__ inline void barrier_after_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Shape of a tiled launch: each of the 4 waves owns RT x TT MFMA tiles; the
+// waves are arranged WR x (4 / WR) over rows x tokens.
+template <int RT, int TT, int WR>
+struct TiledShape {
+  static constexpr int WT = 4 / WR;
+  static constexpr int kRowTiles = RT * WR, kTokTiles = TT * WT;        // per workgroup
+  static constexpr int kRows = 32 * kRowTiles, kToks = 32 * kTokTiles;
+  static constexpr int kCodeOff = 0, kLimbOff = kRowTiles * 1024;
+  static constexpr int kScaleOff = kLimbOff + 3 * kTokTiles * 1024;
+  static constexpr int kCopies = kRowTiles + 3 * kTokTiles;            // 1 KB tiles per block
+  static constexpr int kPerWave = (kCopies + 3) / 4;
+  static constexpr int kPad = kPerWave * 4 - kCopies;                  // dummy copies
+  static constexpr int kBlockBytes = kScaleOff + kRowTiles * 128 + kPad * 1024;
+};
+
+template <int RT, int TT, int WR, int NBUF, bool kExact>
+__global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs a) {
+  using Sh = TiledShape<RT, TT, WR>;
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wave % WR, wt = wave / WR;
+
+  // ---- tile of this workgroup
+  const int64_t tbs = (a.t_pad + Sh::kToks - 1) / Sh::kToks;
+  const int64_t rb = blockIdx.x / tbs, tb = blockIdx.x % tbs;
+  const int64_t rgs = a.n_pad / kTile, tgs = a.t_pad / kTile;
+
+  // ---- copies of one block: every wave issues kPerWave tile copies
+  // (j = wave + 4 i; j < kRowTiles: code tile j, then the limb tiles, then
+  // dummy copies into a pad area) and one copy of the scales of its own row
+  // tiles, so that every wave has the same number of loads per block.  Row
+  // and token groups past the matrix re-read the last one (results unused).
+  // Scalar offsets of tile j at block 0; block b adds b * 1 KB.
+  const __amdgpu_buffer_rsrc_t rcode = make_rsrc(a.codes, (uint32_t)(a.n_pad * a.nb * 1024));
+  const __amdgpu_buffer_rsrc_t rlimb = make_rsrc(a.limb_tiles, (uint32_t)(3 * a.t_pad * a.nb * 32));
+  const __amdgpu_buffer_rsrc_t rscal = make_rsrc(a.scales, (uint32_t)(a.n_pad * a.nb * 4));
+  uint32_t soff[Sh::kPerWave];
+  bool is_code[Sh::kPerWave];
+  int dst_off[Sh::kPerWave];
+#pragma unroll
+  for (int i = 0; i < Sh::kPerWave; ++i) {
+    const int j = wave + 4 * i;
+    is_code[i] = true;
+    if (j < Sh::kRowTiles) {
+      int64_t rg = Sh::kRowTiles * rb + j;
+      rg = rg < rgs ? rg : rgs - 1;
+      soff[i] = (uint32_t)(rg * a.nb * 1024);
+      dst_off[i] = Sh::kCodeOff + j * 1024;
+    } else if (j < Sh::kCopies) {
+      const int jj = j - Sh::kRowTiles;
+      const int l = jj / Sh::kTokTiles, tt = jj % Sh::kTokTiles;
+      int64_t tg = Sh::kTokTiles * tb + tt;
+      tg = tg < tgs ? tg : tgs - 1;
+      is_code[i] = false;
+      soff[i] = (uint32_t)(((int64_t)l * tgs + tg) * a.nb * 1024);
+      dst_off[i] = Sh::kLimbOff + (l * Sh::kTokTiles + tt) * 1024;
+    } else {   // dummy: re-read this workgroup's first code tile into the pad area
+      int64_t rg = Sh::kRowTiles * rb;
+      rg = rg < rgs ? rg : rgs - 1;
+      soff[i] = (uint32_t)(rg * a.nb * 1024);
+      dst_off[i] = Sh::kScaleOff + Sh::kRowTiles * 128 + (j - Sh::kCopies) * 1024;
+    }
+  }
+  // scales: lane i < 8 RT copies 16 B of the wave's row tile RT wr + i / 8
+  // (the row group's offset rides in the lane offset, the block's in the
+  // scalar one); the direct-to-LDS copy puts lane i at sdst + 16 i
+  uint32_t svoff;
+  {
+    const int jr = RT * wr + (lane >> 3) % RT;
+    int64_t rg = Sh::kRowTiles * rb + jr;
+    rg = rg < rgs ? rg : rgs - 1;
+    svoff = (uint32_t)(rg * a.nb * 128) + (lane & 7) * 16;
+  }
+  const int sdst = Sh::kScaleOff + RT * wr * 128;
+  auto issue = [&](int64_t b) {
+    uint8_t* blk = lds + (int)(b % NBUF) * Sh::kBlockBytes;
+#pragma unroll
+    for (int i = 0; i < Sh::kPerWave; ++i)
+      copy16_to_lds(is_code[i] ? rcode : rlimb, blk + dst_off[i], lane * 16, soff[i] + (uint32_t)b * 1024u);
+    if (lane < 8 * RT)   // one load instruction per wave either way: the per-wave count stays uniform
+      copy16_to_lds(rscal, blk + sdst, svoff, (uint32_t)b * 128u);
+  };
+
+  int64_t acc[RT][TT][16];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[rt][tt][r] = 0;
+  const v16i zero = {};
+
+  const int64_t nb = a.nb;
+  for (int64_t b = 0; b < NBUF - 1 && b < nb; ++b) issue(b);
+  for (int64_t b = 0; b < nb; ++b) {
+    // this wave's copies of block b have landed when at most the later
+    // blocks' copies are outstanding; the barrier then covers all waves and
+    // frees the buffer of block b - 1 for block b + NBUF - 1
+    // (__syncthreads would also wait for the copies still in flight)
+    if (b + NBUF - 2 < nb)
+      barrier_after_vmcnt<(NBUF - 2) * (Sh::kPerWave + 1)>();
+    else
+      barrier_after_vmcnt<0>();
+    if (b + NBUF - 1 < nb) issue(b + NBUF - 1);
+
+    const uint8_t* blk = lds + (int)(b % NBUF) * Sh::kBlockBytes;
+    v4i q[RT];
+    int32_t S[RT], S16[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int jr = RT * wr + rt;
+      q[rt] = *reinterpret_cast<const v4i*>(blk + Sh::kCodeOff + jr * 1024 + lane * 16);
+      S[rt] = *reinterpret_cast<const int32_t*>(blk + Sh::kScaleOff + (jr * 32 + (lane & 31)) * 4);
+      S16[rt] = (int32_t)((uint32_t)S[rt] << 16);
+    }
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      const int jt = TT * wt + tt;
+      v4i d[3];
+#pragma unroll
+      for (int l = 0; l < 3; ++l)
+        d[l] = *reinterpret_cast<const v4i*>(blk + Sh::kLimbOff + (l * Sh::kTokTiles + jt) * 1024 + lane * 16);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const v16i D0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(d[0], q[rt], zero, 0, 0, 0);
+        const v16i D1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(d[1], q[rt], zero, 0, 0, 0);
+        const v16i D2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(d[2], q[rt], zero, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int32_t p01 = D0[r] + (int32_t)((uint32_t)D1[r] << 8);
+          acc[rt][tt][r] += (int64_t)S[rt] * p01 + (int64_t)S16[rt] * D2[r];
+        }
+      }
+    }
+  }
+
+  // ---- store: lane holds row 32 jr + lane % 32 and tokens 32 jt + 8 (r / 4)
+  // + 4 (lane / 32) + r % 4 of the workgroup tile
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int64_t row = rb * Sh::kRows + (RT * wr + rt) * 32 + (lane & 31);
+    if (row >= a.n) continue;
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t tok = tb * Sh::kToks + (TT * wt + tt) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (tok >= a.t) continue;
+        int64_t out;
+        if (!finish_output((__int128)acc[rt][tt][r], kExact ? OUT_EXACT : OUT_ROUND_Q24, &out))
+          flag(a.status, EI_DEV_OUT_RANGE);
+        a.y[tok * a.n + row] = out;
+      }
+  }
+}
+
+template <int RT, int TT, int WR, int NBUF>
+hipError_t launch_tiled_shape(const GemmArgs& a, hipStream_t s) {
+  using Sh = TiledShape<RT, TT, WR>;
+  const int64_t rbs = (a.n_pad + Sh::kRows - 1) / Sh::kRows, tbs = (a.t_pad + Sh::kToks - 1) / Sh::kToks;
+  const dim3 grid((unsigned)(rbs * tbs)), block(256);
+  const size_t lds = (size_t)NBUF * Sh::kBlockBytes;
+  if (a.out_mode == OUT_EXACT)
+    hipLaunchKernelGGL((gemm_tiled_kernel<RT, TT, WR, NBUF, true>), grid, block, lds, s, a);
+  else
+    hipLaunchKernelGGL((gemm_tiled_kernel<RT, TT, WR, NBUF, false>), grid, block, lds, s, a);
+  return hipGetLastError();
+}
+
+// Launch shape: one 32x32 tile per wave, 128 rows x 32 tokens per workgroup,
+// copies one block ahead (the fastest of the shapes measured on MI355X).
+hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t s) { return launch_tiled_shape<1, 1, 4, 2>(a, s); }
+
+}  // namespace ei

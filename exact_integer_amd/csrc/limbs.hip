@@ -44,19 +44,22 @@ __global__ void limb_split_flat_kernel(const int64_t* __restrict__ x, int8_t* __
   if (r != 0) flag(status, EI_DEV_LIMB_RANGE);
 }
 
-// One thread per (token t < t_pad, block b, half h): 16 activations into 16
-// bytes of each of the L limb tiles, at lane t%32 + 32h of tile (l, t/32, b).
+// One thread per (token group tg, block b, tile lane): lane = t % 32 + 32 h
+// takes the 16 activations of token 32 tg + t % 32, half h of block b, into
+// 16 bytes of each of the L limb tiles (l, tg, b).  Consecutive threads write
+// consecutive 16-byte pieces of a tile; each reads one 128-byte (int64) or
+// 64-byte (int32) run of x.
 template <int L, typename XT>
 __global__ void limb_tiles_kernel(const XT* __restrict__ x, int64_t t, int64_t k, int8_t* __restrict__ tiles,
                                   int64_t t_pad, int32_t* status) {
   const int64_t nb = k / 32;
   int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= t_pad * nb * 2) return;
-  const int h = (int)(gid & 1);
-  const int64_t b = (gid >> 1) % nb;
-  const int64_t tok = (gid >> 1) / nb;
-  const int64_t tg = tok / kTile;
-  const int lane = (int)(tok % kTile) + 32 * h;
+  const int lane = (int)(gid & 63);
+  const int h = lane >> 5;
+  const int64_t b = (gid >> 6) % nb;
+  const int64_t tg = (gid >> 6) / nb;
+  const int64_t tok = tg * kTile + (lane & 31);
   uint32_t words[L][4];
 #pragma unroll
   for (int l = 0; l < L; ++l)
