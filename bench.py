@@ -36,34 +36,78 @@ N, K = 14336, 4096
 LIMBS = 3                      # Q16 activations with |x| <= 2^22 need 3 balanced base-256 limbs
 W_BYTES = N * K + N * (K // 32) * 4          # canonical Q8: 1 B/code + 4 B/32-block scale
 GEMV_KERNEL = "gemv_kernel"
-GEMM_KERNEL = "gemm_mfma_kernel"
+GEMM_KERNEL = "gemm_tiled_kernel"
+# the source file each timed kernel is built from: a stored HBM-traffic figure
+# is used only while that file is unchanged
+KERNEL_SOURCES = {GEMV_KERNEL: "gemv.hip", GEMM_KERNEL: "gemm_tiled.hip"}
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def kernel_source_hash() -> str:
-    p = os.path.join(ROOT, "exact_integer_amd", "csrc", "gemm.hip")
+def kernel_source_hash(kernel: str) -> str:
+    p = os.path.join(ROOT, "exact_integer_amd", "csrc", KERNEL_SOURCES[kernel])
     return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
 
 
 def stored_traffic(kernel: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel source; else None."""
-    p = os.path.join(ROOT, "profiles", "traffic.json")
-    if not os.path.exists(p):
+    if not os.path.exists(TRAFFIC_JSON):
         return None
-    rec = json.load(open(p)).get(kernel)
-    if not rec or rec.get("source_sha") != kernel_source_hash():
+    rec = json.load(open(TRAFFIC_JSON)).get(kernel)
+    if not rec or rec.get("source_sha") != kernel_source_hash(kernel):
         return None
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(q, s, x1, x512, rows: int):
-    import numpy as np
+def summarize_counters(fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy_write_dir: str) -> int:
+    """Turn four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE, each on
+    `bench.py --profile` and on `bench.py --copy-calibration`) into HBM bytes per
+    launch of the timed kernels, scaled by what the same counters read for the
+    256 MiB copy, and write profiles/traffic.json."""
+    import csv
+    import statistics
+
+    def per_kernel(d):
+        out = {}
+        for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))):
+            out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return out
+
+    def copy_kib(d):
+        vals = [v for k, vs in per_kernel(d).items() if "copyBuffer" in k for v in vs]
+        return statistics.median(vals)
+
+    true_kib = (256 << 20) / 1024
+    f_fac, w_fac = true_kib / copy_kib(copy_fetch_dir), true_kib / copy_kib(copy_write_dir)
+    fetch, write = per_kernel(fetch_dir), per_kernel(write_dir)
+    out = {"_calibration": {"copy_bytes": 256 << 20, "fetch_scale": round(f_fac, 4), "write_scale": round(w_fac, 4)}}
+    for kern in (GEMV_KERNEL, GEMM_KERNEL):
+        fk = [v for k, vs in fetch.items() if kern in k for v in vs]
+        wk = [v for k, vs in write.items() if kern in k for v in vs]
+        if not fk or not wk:
+            continue
+        f_b, w_b = statistics.median(fk) * 1024 * f_fac, statistics.median(wk) * 1024 * w_fac
+        out[kern] = {"bytes_per_launch": int(f_b + w_b), "fetch_bytes": int(f_b), "write_bytes": int(w_b),
+                     "launches_sampled": len(fk), "source_sha": kernel_source_hash(kern)}
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(out, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps(out))
+    return 0
+
+
+def cpu_baseline(q, s, x1, x512, rows: int, decode_seconds: float = 8.0):
+    """The CPU oracle, as it stands, on the host cores: T=1 passes over the whole
+    matrix repeated for about `decode_seconds`, and one T=512 pass over the
+    first `rows` rows.  Threads own disjoint output rows."""
     import oracle
     cores = min(os.cpu_count() or 1, 16)
-    reps = 10
-    t0 = time.perf_counter()
-    for _ in range(reps):
+    reps, t0 = 0, time.perf_counter()
+    while True:
         y1 = oracle.q8(q, s, x1, threads=cores)
+        reps += 1
+        if time.perf_counter() - t0 >= decode_seconds:
+            break
     t_dec = (time.perf_counter() - t0) / reps
     t0 = time.perf_counter()
     oracle.q8(q[:rows], s[:rows], x512, threads=cores)
@@ -71,7 +115,8 @@ def cpu_baseline(q, s, x1, x512, rows: int):
     useful = LIMBS * 2.0 * 512 * rows * K
     return {
         "value": W_BYTES / t_dec / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
-        "sample": f"T=1: all {N} rows x {reps} repeats; T=512: rows 0..{rows - 1} of {N} (rate per row-sample)",
+        "sample": f"T=1: all {N} rows x {reps} passes ({reps * t_dec:.1f} s); "
+                  f"T=512: rows 0..{rows - 1} of {N}, one pass ({t_pre:.1f} s)",
         "t1_ms": t_dec * 1e3, "t512_useful_tops": useful / t_pre / 1e12,
         "t512_logical_tops": useful / LIMBS / t_pre / 1e12, "t512_sample_s": t_pre,
     }, y1
@@ -104,11 +149,15 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--copies", type=int, default=12, help="distinct resident weight copies for the T=1 pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=2048)
+    ap.add_argument("--cpu-rows", type=int, default=N, help="rows of the T=512 oracle sample")
     ap.add_argument("--profile", action="store_true", help="short run for rocprofv3 (no baseline, few steps)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 256 MiB, 5 times (the reference for HBM byte counters)")
+    ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="rocprofv3 --pmc output directories -> profiles/traffic.json (no GPU needed)")
     args = ap.parse_args()
+    if args.summarize_counters:
+        return summarize_counters(*args.summarize_counters)
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the projection would shard by rows across GPUs, see the design notes)", file=sys.stderr)

@@ -18,16 +18,16 @@ from functools import lru_cache
 import torch
 
 __all__ = [
-    "EIError", "PackedWeights", "lib", "pack_q8", "pack_q4", "gemm_q8", "gemm_q4",
-    "limb_split", "silu_lut", "silu_mul", "digest", "sha256_host", "workspace_bytes",
-    "SCHEDULES", "DEV_LIMB_RANGE", "DEV_OUT_RANGE",
+    "EIError", "PackedWeights", "lib", "pack_q8", "pack_q4", "pack_q8_stacked", "gemm_q8", "gemm_q4",
+    "gemm_q8_grouped", "limb_split", "silu_lut", "silu_mul", "digest", "sha256_host", "workspace_bytes",
+    "grouped_workspace_bytes", "SCHEDULES", "DEV_LIMB_RANGE", "DEV_OUT_RANGE", "DEV_ROUTE",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libexact_int.so")
 
 EI_OK, EI_EINVAL, EI_ERANGE, EI_EDEVICE, EI_ENOSPACE = 0, 1, 2, 3, 4
-DEV_LIMB_RANGE, DEV_OUT_RANGE = 1, 2
+DEV_LIMB_RANGE, DEV_OUT_RANGE, DEV_ROUTE = 1, 2, 4
 SCHEDULES = {"default": 0, "canonical": 1, "reversed": 2, "tiled_shuffled": 3, "split_k": 4, "tree_walk": 5}
 FORMAT_Q8, FORMAT_Q4 = 1, 2
 
@@ -39,7 +39,7 @@ class EIError(RuntimeError):
 class Weights(ctypes.Structure):
     _fields_ = [("packed", ctypes.c_void_p), ("n", ctypes.c_int64), ("k", ctypes.c_int64),
                 ("n_pad", ctypes.c_int64), ("nb", ctypes.c_int64), ("smax", ctypes.c_uint32),
-                ("format", ctypes.c_int32)]
+                ("format", ctypes.c_int32), ("experts", ctypes.c_int64), ("expert_stride", ctypes.c_int64)]
 
 
 # name -> (restype, argtypes); mirrors include/exact_int.h
@@ -49,6 +49,10 @@ SIGNATURES = {
     "ei_packed_bytes": (SZ, [I64, I64]),
     "ei_q8_pack": (I32, [P, P, I64, I64, P, SZ, WP, P]),
     "ei_q4_pack": (I32, [P, P, I64, I64, P, SZ, WP, P]),
+    "ei_packed_bytes_stacked": (SZ, [I64, I64, I64]),
+    "ei_q8_pack_stacked": (I32, [P, P, I64, I64, I64, P, SZ, WP, P]),
+    "ei_grouped_workspace_bytes": (SZ, [WP, I64, I32, I32]),
+    "int_gemm_q8_grouped": (I32, [WP, P, P, I64, I32, P, I32, P, SZ, P, P]),
     "ei_limb_split": (I32, [P, P, I64, I32, P, P]),
     "ei_gemm_workspace_bytes": (SZ, [WP, I64, I32, I32]),
     "int_gemm_q8": (I32, [WP, P, P, I64, I32, I32, U64, P, SZ, P, P]),
@@ -101,7 +105,8 @@ def _raise_status(status: torch.Tensor, what: str) -> None:
     v = int(status.item())
     if v:
         bits = [n for b, n in ((DEV_LIMB_RANGE, "activation outside the declared limb range"),
-                               (DEV_OUT_RANGE, "result outside int64")) if v & b]
+                               (DEV_OUT_RANGE, "result outside int64"),
+                               (DEV_ROUTE, "expert id outside [0, E)")) if v & b]
         raise EIError(f"{what}: " + "; ".join(bits))
 
 
@@ -147,6 +152,53 @@ def pack_q4(nib: torch.Tensor, sme: torch.Tensor) -> PackedWeights:
     """nibbles uint8 [n][k/2], scale bytes uint8 [n][k/32] (device) -> packed weights."""
     n, kh = nib.shape
     return _pack("ei_q4_pack", nib, sme, n, 2 * kh, torch.uint8, torch.uint8)
+
+
+def pack_q8_stacked(codes: torch.Tensor, scales: torch.Tensor) -> PackedWeights:
+    """codes int8 [E][n][k], scales int32 [E][n][k/32] (device) -> E packed experts in one buffer."""
+    s = _stream()
+    e, n, k = codes.shape
+    pc, ps = _dev(codes, torch.int8, "codes"), _dev(scales, torch.int32, "scales")
+    nbytes = lib().ei_packed_bytes_stacked(e, n, k)
+    if nbytes == 0:
+        raise EIError(f"ei_q8_pack_stacked: bad shape e={e} n={n} k={k}")
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=codes.device)
+    desc = Weights()
+    _check(lib().ei_q8_pack_stacked(pc, ps, e, n, k, buf.data_ptr(), nbytes, ctypes.byref(desc), s),
+           "ei_q8_pack_stacked")
+    return PackedWeights(buf, desc)
+
+
+def grouped_workspace_bytes(w: PackedWeights, rows: int, topk: int, limbs: int = 3) -> int:
+    return int(lib().ei_grouped_workspace_bytes(ctypes.byref(w.desc), rows, topk, limbs))
+
+
+def gemm_q8_grouped(w: PackedWeights, x: torch.Tensor, route: torch.Tensor, limbs: int = 3, out=None,
+                    workspace=None, status=None) -> torch.Tensor:
+    """Routed projection: y[r*topk + s] = Q8 projection of expert route[r][s] on x[r] (int64 [rows*topk][n])."""
+    s = _stream()
+    rows, k = x.shape
+    if k != w.k:
+        raise EIError(f"int_gemm_q8_grouped: x has k={k}, weights k={w.k}")
+    if route.dim() != 2 or route.shape[0] != rows:
+        raise EIError("int_gemm_q8_grouped: route must be [rows][topk]")
+    topk = route.shape[1]
+    px, pr = _dev(x, torch.int64, "x"), _dev(route, torch.int32, "route")
+    y = out if out is not None else torch.empty((rows * topk, w.n), dtype=torch.int64, device=x.device)
+    py = _dev(y, torch.int64, "y")
+    if tuple(y.shape) != (rows * topk, w.n):
+        raise EIError(f"int_gemm_q8_grouped: y must be [{rows * topk}][{w.n}]")
+    need = grouped_workspace_bytes(w, rows, topk, limbs)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    check = status is None
+    if check:
+        status = torch.zeros(1, dtype=torch.int32, device=x.device)
+    _check(lib().int_gemm_q8_grouped(ctypes.byref(w.desc), px, pr, rows, topk, py, limbs, workspace.data_ptr(),
+                                     workspace.numel(), status.data_ptr(), s), "int_gemm_q8_grouped")
+    if check:
+        _raise_status(status, "int_gemm_q8_grouped")
+    return y
 
 
 def workspace_bytes(w: PackedWeights, t: int, limbs: int = 3, schedule: str = "default") -> int:

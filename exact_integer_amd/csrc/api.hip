@@ -50,16 +50,22 @@ WsLayout layout_for(const ei_weights* w, int64_t t, int limbs, int schedule) {
   return L;
 }
 
-// The tiled prefill kernel keeps one int64 accumulator per output: exact
-// when every partial sum, bounded by nb * smax * 2^19 * (1 + 2^8 + 2^16),
-// stays below 2^63, and it forms S * 2^16 in int32, so smax < 2^15.
+// The tiled prefill kernel (3 limbs, default/canonical schedule, T >= 64)
+// keeps one int64 accumulator per output when that is exact -- every partial
+// sum, bounded by nb * smax * 2^19 * (1 + 2^8 + 2^16), stays below 2^63, and
+// S * 2^16 fits an int32 (smax < 2^15) -- and one per limb otherwise (exact
+// for any int32 scale, nb <= 2^13).  Its buffer offsets are 32-bit.
 constexpr int64_t kTiledMinT = 64;
-bool tiled_ok(const ei_weights* w, int64_t t, int limbs, int schedule) {
-  if (limbs != 3 || t < kTiledMinT) return false;
-  if (schedule != EI_SCHED_DEFAULT && schedule != EI_SCHED_CANONICAL) return false;
+bool single_acc_ok(const ei_weights* w) {
   if (w->smax >= (1u << 15)) return false;
   const __int128 bound = (__int128)w->nb * (__int128)w->smax * ((__int128)1 << 19) * 65793;
   return bound < ((__int128)1 << 63);
+}
+bool tiled_ok(const ei_weights* w, int64_t t, int limbs, int schedule) {
+  if (limbs != 3 || t < kTiledMinT) return false;
+  if (schedule != EI_SCHED_DEFAULT && schedule != EI_SCHED_CANONICAL) return false;
+  const int64_t t_pad = round_up(t, kTile);
+  return w->n_pad * w->k < ((int64_t)1 << 32) && 3 * t_pad * w->k < ((int64_t)1 << 32);
 }
 
 int check_weights(const ei_weights* w, int format) {
@@ -108,8 +114,9 @@ int run_gemm(const ei_weights* w, const void* x, int x_is_i32, int64_t* y, int64
     if (e != hipSuccess) return EI_EDEVICE;
   }
   const bool tiled = lay.mfma && tiled_ok(w, t, limbs, schedule);
+  const bool single = tiled && single_acc_ok(w);
   auto launch = [&](const GemmArgs& args) {
-    if (tiled) return launch_gemm_tiled(args, s);
+    if (tiled) return launch_gemm_tiled(args, single, s);
     return lay.mfma ? launch_gemm_mfma(args, limbs, s) : launch_gemv(args, limbs, s);
   };
 
@@ -181,7 +188,33 @@ int do_pack(int format, const void* codes, const void* scales, int64_t n, int64_
   out->nb = h.nb;
   out->smax = h.smax;
   out->format = format;
+  out->experts = 1;
+  out->expert_stride = (int64_t)align_up(ei::packed_bytes(n, k));
   return EI_OK;
+}
+
+// Grouped (expert) workspace: sorted pairs, segment offsets, the token-tile
+// table, the tile count and the gathered limb tiles.
+struct GroupedLayout {
+  size_t sorted_off, offsets_off, texp_off, trow0_off, trows_off, ntiles_off, limb_off, total;
+  int64_t pairs, tiles_max;
+};
+
+GroupedLayout grouped_layout(const ei_weights* w, int64_t rows, int topk, int limbs) {
+  GroupedLayout g;
+  g.pairs = rows * topk;
+  g.tiles_max = (g.pairs + kTile - 1) / kTile + (w->experts < g.pairs ? w->experts : g.pairs);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
+  g.sorted_off = take(sizeof(int32_t) * (size_t)g.pairs);
+  g.offsets_off = take(sizeof(int32_t) * (size_t)(w->experts + 1));
+  g.texp_off = take(sizeof(int32_t) * (size_t)g.tiles_max);
+  g.trow0_off = take(sizeof(int32_t) * (size_t)g.tiles_max);
+  g.trows_off = take(sizeof(int32_t) * (size_t)g.tiles_max);
+  g.ntiles_off = take(sizeof(int32_t));
+  g.limb_off = take((size_t)limbs * (size_t)g.tiles_max * (size_t)w->k * kTile);
+  g.total = off;
+  return g;
 }
 
 }  // namespace
@@ -201,6 +234,94 @@ int ei_q8_pack(const int8_t* codes, const int32_t* scales, int64_t n, int64_t k,
 int ei_q4_pack(const uint8_t* nib, const uint8_t* sme, int64_t n, int64_t k, void* packed, size_t packed_bytes,
                ei_weights* out, ei_stream stream) {
   return do_pack(EI_FORMAT_Q4, nib, sme, n, k, packed, packed_bytes, out, static_cast<hipStream_t>(stream));
+}
+
+size_t ei_packed_bytes_stacked(int64_t experts, int64_t n, int64_t k) {
+  if (experts < 1 || n < 1 || k < 32 || k % 32 != 0) return 0;
+  return (size_t)experts * align_up(ei::packed_bytes(n, k));
+}
+
+int ei_q8_pack_stacked(const int8_t* codes, const int32_t* scales, int64_t experts, int64_t n, int64_t k,
+                       void* packed, size_t packed_bytes, ei_weights* out, ei_stream stream) {
+  if (!codes || !scales || !packed || !out || experts < 1) return EI_EINVAL;
+  if (n < 1 || k < 32 || k % 32 != 0) return EI_EINVAL;
+  if (packed_bytes < ei_packed_bytes_stacked(experts, n, k)) return EI_ENOSPACE;
+  const size_t stride = align_up(ei::packed_bytes(n, k));
+  ei_weights one;
+  uint32_t smax = 0;
+  for (int64_t e = 0; e < experts; ++e) {
+    const int c = do_pack(EI_FORMAT_Q8, codes + e * n * k, scales + e * n * (k / 32), n, k,
+                          static_cast<uint8_t*>(packed) + e * stride, stride, &one, static_cast<hipStream_t>(stream));
+    if (c != EI_OK) return c;
+    smax = one.smax > smax ? one.smax : smax;
+  }
+  *out = one;
+  out->packed = packed;
+  out->smax = smax;
+  out->experts = experts;
+  out->expert_stride = (int64_t)stride;
+  return EI_OK;
+}
+
+size_t ei_grouped_workspace_bytes(const ei_weights* w, int64_t rows, int topk, int limbs) {
+  if (!w || rows < 1 || topk < 1 || limbs < 1) return 0;
+  return grouped_layout(w, rows, topk, limbs).total;
+}
+
+int int_gemm_q8_grouped(const ei_weights* w, const int64_t* x, const int32_t* route, int64_t rows, int topk,
+                        int64_t* y, int limbs, void* workspace, size_t workspace_bytes, int32_t* d_status,
+                        ei_stream stream) {
+  const int c = check_weights(w, EI_FORMAT_Q8);
+  if (c != EI_OK) return c;
+  if (!x || !route || !y || rows < 1 || topk < 1 || w->experts < 1) return EI_EINVAL;
+  if (limbs != 3) return limbs < 1 || limbs > 8 ? EI_EINVAL : EI_ERANGE;
+  if (rows * topk > ((int64_t)1 << 14) || w->experts > ((int64_t)1 << 17)) return EI_ERANGE;
+  if (w->n_pad * w->k >= ((int64_t)1 << 32)) return EI_ERANGE;
+  const GroupedLayout g = grouped_layout(w, rows, topk, limbs);
+  if (3 * g.tiles_max * w->k * kTile >= ((int64_t)1 << 32)) return EI_ERANGE;
+  if (!workspace || workspace_bytes < g.total) return EI_ENOSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  int32_t* sorted = reinterpret_cast<int32_t*>(ws + g.sorted_off);
+  int32_t* offs = reinterpret_cast<int32_t*>(ws + g.offsets_off);
+  int32_t* texp = reinterpret_cast<int32_t*>(ws + g.texp_off);
+  int32_t* trow0 = reinterpret_cast<int32_t*>(ws + g.trow0_off);
+  int32_t* trows = reinterpret_cast<int32_t*>(ws + g.trows_off);
+  int32_t* ntiles = reinterpret_cast<int32_t*>(ws + g.ntiles_off);
+  int8_t* limb = reinterpret_cast<int8_t*>(ws + g.limb_off);
+  if (launch_moe_sort(route, g.pairs, w->experts, sorted, offs, texp, trow0, trows, ntiles, d_status, s) !=
+      hipSuccess)
+    return EI_EDEVICE;
+  if (launch_grouped_limb_tiles(x, w->k, topk, sorted, trow0, trows, ntiles, g.tiles_max, limb, d_status, s) !=
+      hipSuccess)
+    return EI_EDEVICE;
+  GemmArgs a;
+  std::memset(&a, 0, sizeof a);
+  const uint8_t* base = static_cast<const uint8_t*>(w->packed);
+  a.codes = reinterpret_cast<const int8_t*>(base + kHeaderBytes);
+  a.scales = reinterpret_cast<const int32_t*>(base + kHeaderBytes + w->n_pad * w->k);
+  a.x = x;
+  a.limb_tiles = limb;
+  a.y = y;
+  a.status = d_status;
+  a.n = w->n;
+  a.k = w->k;
+  a.t = g.pairs;
+  a.n_pad = w->n_pad;
+  a.t_pad = g.tiles_max * kTile;
+  a.nb = w->nb;
+  a.b0 = 0;
+  a.b1 = w->nb;
+  a.out_mode = OUT_ROUND_Q24;
+  a.order = ORDER_ASC;
+  a.tile_expert = texp;
+  a.tile_row0 = trow0;
+  a.tile_rows = trows;
+  a.sorted_pair = sorted;
+  a.ntiles = ntiles;
+  a.tiles_max = g.tiles_max;
+  a.expert_stride = w->expert_stride;
+  return launch_gemm_grouped(a, single_acc_ok(w), s) == hipSuccess ? EI_OK : EI_EDEVICE;
 }
 
 int ei_limb_split(const int64_t* x, int8_t* d, int64_t n, int limbs, int32_t* d_status, ei_stream stream) {
@@ -272,6 +393,6 @@ const char* ei_status_string(int code) {
   }
 }
 
-int ei_version(void) { return 100; }
+int ei_version(void) { return 101; }
 
 }  // extern "C"

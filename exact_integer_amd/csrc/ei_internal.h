@@ -67,6 +67,16 @@ struct GemmArgs {
   int part_index;            // OUT_PARTIAL: which partial this launch writes
   int out_mode, order;
   int chunk;                 // GEMV: blocks per wave per LDS limb chunk (a multiple of its prefetch depth)
+  // grouped (expert) launches: token tile j holds sorted pairs
+  // tile_row0[j] .. + tile_rows[j] - 1 of expert tile_expert[j]; sorted pair
+  // i is original pair sorted_pair[i], whose output row it is
+  const int32_t* tile_expert;
+  const int32_t* tile_row0;
+  const int32_t* tile_rows;
+  const int32_t* sorted_pair;
+  const int32_t* ntiles;     // device: tiles in use (<= tiles_max)
+  int64_t tiles_max;
+  int64_t expert_stride;     // bytes between the packed images of two experts
 };
 
 // pos-th block visited by a kernel in the block range [b0, b1) of `a`.
@@ -87,7 +97,14 @@ hipError_t launch_limb_tiles(const void* x, int x_is_i32, int64_t t, int64_t k, 
                              int8_t* tiles, int64_t t_pad, int32_t* status, hipStream_t s);
 hipError_t launch_gemv(const GemmArgs& a, int limbs, hipStream_t s);
 hipError_t launch_gemm_mfma(const GemmArgs& a, int limbs, hipStream_t s);
-hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t s);   // 3 limbs, see tiled_ok()
+hipError_t launch_gemm_tiled(const GemmArgs& a, bool single_acc, hipStream_t s);   // 3 limbs, see tiled_ok()
+hipError_t launch_gemm_grouped(const GemmArgs& a, bool single_acc, hipStream_t s);  // 3 limbs
+hipError_t launch_moe_sort(const int32_t* route, int64_t pairs, int64_t experts, int32_t* sorted_pair,
+                           int32_t* offsets, int32_t* tile_expert, int32_t* tile_row0, int32_t* tile_rows,
+                           int32_t* ntiles, int32_t* status, hipStream_t s);
+hipError_t launch_grouped_limb_tiles(const int64_t* x, int64_t k, int topk, const int32_t* sorted_pair,
+                                     const int32_t* tile_row0, const int32_t* tile_rows, const int32_t* ntiles,
+                                     int64_t tiles_max, int8_t* tiles, int32_t* status, hipStream_t s);
 hipError_t launch_combine_partials(const int64_t* part, int nparts, int64_t* y, int64_t t, int64_t n,
                                    int limbs, int out_mode, int32_t* status, hipStream_t s);
 hipError_t launch_tree_terms(int64_t* terms, int64_t nb, int64_t* y, int64_t t, int64_t n,

@@ -58,7 +58,10 @@ struct TiledShape {
   static constexpr int kBlockBytes = kScaleOff + kRowTiles * 128 + kPad * 1024;
 };
 
-template <int RT, int TT, int WR, int NBUF, bool kExact>
+// NACC = 1: one int64 accumulator (host-checked bound above); NACC = 3: one
+// per limb, exact for any int32 scale while nb <= 2^13.  kGrouped: each token
+// tile belongs to one expert, whose packed image and output rows it looks up.
+template <int RT, int TT, int WR, int NBUF, bool kExact, int NACC, bool kGrouped>
 __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs a) {
   using Sh = TiledShape<RT, TT, WR>;
   extern __shared__ __align__(16) uint8_t lds[];
@@ -67,9 +70,18 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs a) {
   const int wr = wave % WR, wt = wave / WR;
 
   // ---- tile of this workgroup
-  const int64_t tbs = (a.t_pad + Sh::kToks - 1) / Sh::kToks;
+  const int64_t tbs = kGrouped ? a.tiles_max : (a.t_pad + Sh::kToks - 1) / Sh::kToks;
   const int64_t rb = blockIdx.x / tbs, tb = blockIdx.x % tbs;
-  const int64_t rgs = a.n_pad / kTile, tgs = a.t_pad / kTile;
+  const int64_t rgs = a.n_pad / kTile, tgs = kGrouped ? a.tiles_max : a.t_pad / kTile;
+  const int8_t* codes = a.codes;
+  const int32_t* scales = a.scales;
+  if (kGrouped) {
+    static_assert(!kGrouped || (TT == 1 && WR == 4), "grouped launches use one token tile per workgroup");
+    if (tb >= *a.ntiles) return;   // the whole workgroup: no tile here
+    const int64_t e = a.tile_expert[tb];
+    codes += e * a.expert_stride;
+    scales = reinterpret_cast<const int32_t*>(reinterpret_cast<const int8_t*>(scales) + e * a.expert_stride);
+  }
 
   // ---- copies of one block: every wave issues kPerWave tile copies
   // (j = wave + 4 i; j < kRowTiles: code tile j, then the limb tiles, then
@@ -77,9 +89,9 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs a) {
   // tiles, so that every wave has the same number of loads per block.  Row
   // and token groups past the matrix re-read the last one (results unused).
   // Scalar offsets of tile j at block 0; block b adds b * 1 KB.
-  const __amdgpu_buffer_rsrc_t rcode = make_rsrc(a.codes, (uint32_t)(a.n_pad * a.nb * 1024));
-  const __amdgpu_buffer_rsrc_t rlimb = make_rsrc(a.limb_tiles, (uint32_t)(3 * a.t_pad * a.nb * 32));
-  const __amdgpu_buffer_rsrc_t rscal = make_rsrc(a.scales, (uint32_t)(a.n_pad * a.nb * 4));
+  const __amdgpu_buffer_rsrc_t rcode = make_rsrc(codes, (uint32_t)(a.n_pad * a.nb * 1024));
+  const __amdgpu_buffer_rsrc_t rlimb = make_rsrc(a.limb_tiles, (uint32_t)(3 * tgs * a.nb * 1024));
+  const __amdgpu_buffer_rsrc_t rscal = make_rsrc(scales, (uint32_t)(a.n_pad * a.nb * 4));
   uint32_t soff[Sh::kPerWave];
   bool is_code[Sh::kPerWave];
   int dst_off[Sh::kPerWave];
@@ -127,13 +139,15 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs a) {
       copy16_to_lds(rscal, blk + sdst, svoff, (uint32_t)b * 128u);
   };
 
-  int64_t acc[RT][TT][16];
+  int64_t acc[NACC][RT][TT][16];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
+  for (int c = 0; c < NACC; ++c)
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt)
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[rt][tt][r] = 0;
+      for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[c][rt][tt][r] = 0;
   const v16i zero = {};
 
   const int64_t nb = a.nb;
@@ -173,8 +187,14 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs a) {
         const v16i D2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(d[2], q[rt], zero, 0, 0, 0);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int32_t p01 = D0[r] + (int32_t)((uint32_t)D1[r] << 8);
-          acc[rt][tt][r] += (int64_t)S[rt] * p01 + (int64_t)S16[rt] * D2[r];
+          if (NACC == 1) {
+            const int32_t p01 = D0[r] + (int32_t)((uint32_t)D1[r] << 8);
+            acc[0][rt][tt][r] += (int64_t)S[rt] * p01 + (int64_t)S16[rt] * D2[r];
+          } else {
+            acc[0][rt][tt][r] += (int64_t)S[rt] * D0[r];
+            acc[NACC > 1 ? 1 : 0][rt][tt][r] += (int64_t)S[rt] * D1[r];
+            acc[NACC > 2 ? 2 : 0][rt][tt][r] += (int64_t)S[rt] * D2[r];
+          }
         }
       }
     }
@@ -190,31 +210,47 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs a) {
     for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t tok = tb * Sh::kToks + (TT * wt + tt) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (tok >= a.t) continue;
+        const int tloc = (TT * wt + tt) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        int64_t orow;   // output row of this token (grouped: the original pair)
+        if (kGrouped) {
+          if (tloc >= a.tile_rows[tb]) continue;
+          orow = a.sorted_pair[a.tile_row0[tb] + tloc];
+        } else {
+          orow = tb * Sh::kToks + tloc;
+          if (orow >= a.t) continue;
+        }
+        __int128 v = acc[0][rt][tt][r];
+        if (NACC > 1) v += (__int128)acc[NACC > 1 ? 1 : 0][rt][tt][r] << 8;
+        if (NACC > 2) v += (__int128)acc[NACC > 2 ? 2 : 0][rt][tt][r] << 16;
         int64_t out;
-        if (!finish_output((__int128)acc[rt][tt][r], kExact ? OUT_EXACT : OUT_ROUND_Q24, &out))
-          flag(a.status, EI_DEV_OUT_RANGE);
-        a.y[tok * a.n + row] = out;
+        if (!finish_output(v, kExact ? OUT_EXACT : OUT_ROUND_Q24, &out)) flag(a.status, EI_DEV_OUT_RANGE);
+        a.y[orow * a.n + row] = out;
       }
   }
 }
 
-template <int RT, int TT, int WR, int NBUF>
+template <int RT, int TT, int WR, int NBUF, int NACC = 1, bool kGrouped = false>
 hipError_t launch_tiled_shape(const GemmArgs& a, hipStream_t s) {
   using Sh = TiledShape<RT, TT, WR>;
-  const int64_t rbs = (a.n_pad + Sh::kRows - 1) / Sh::kRows, tbs = (a.t_pad + Sh::kToks - 1) / Sh::kToks;
+  const int64_t rbs = (a.n_pad + Sh::kRows - 1) / Sh::kRows;
+  const int64_t tbs = kGrouped ? a.tiles_max : (a.t_pad + Sh::kToks - 1) / Sh::kToks;
   const dim3 grid((unsigned)(rbs * tbs)), block(256);
   const size_t lds = (size_t)NBUF * Sh::kBlockBytes;
   if (a.out_mode == OUT_EXACT)
-    hipLaunchKernelGGL((gemm_tiled_kernel<RT, TT, WR, NBUF, true>), grid, block, lds, s, a);
+    hipLaunchKernelGGL((gemm_tiled_kernel<RT, TT, WR, NBUF, true, NACC, kGrouped>), grid, block, lds, s, a);
   else
-    hipLaunchKernelGGL((gemm_tiled_kernel<RT, TT, WR, NBUF, false>), grid, block, lds, s, a);
+    hipLaunchKernelGGL((gemm_tiled_kernel<RT, TT, WR, NBUF, false, NACC, kGrouped>), grid, block, lds, s, a);
   return hipGetLastError();
 }
 
 // Launch shape: one 32x32 tile per wave, 128 rows x 32 tokens per workgroup,
 // copies one block ahead (the fastest of the shapes measured on MI355X).
-hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t s) { return launch_tiled_shape<1, 1, 4, 2>(a, s); }
+hipError_t launch_gemm_tiled(const GemmArgs& a, bool single_acc, hipStream_t s) {
+  return single_acc ? launch_tiled_shape<1, 1, 4, 2, 1>(a, s) : launch_tiled_shape<1, 1, 4, 2, 3>(a, s);
+}
+
+hipError_t launch_gemm_grouped(const GemmArgs& a, bool single_acc, hipStream_t s) {
+  return single_acc ? launch_tiled_shape<1, 1, 4, 2, 1, true>(a, s) : launch_tiled_shape<1, 1, 4, 2, 3, true>(a, s);
+}
 
 }  // namespace ei

@@ -71,7 +71,8 @@ enum {
 /* Bits OR-ed into *d_status by the device. */
 enum {
   EI_DEV_LIMB_RANGE = 1,    /* an activation does not fit the declared limbs */
-  EI_DEV_OUT_RANGE = 2      /* a result does not fit int64                   */
+  EI_DEV_OUT_RANGE = 2,     /* a result does not fit int64                   */
+  EI_DEV_ROUTE = 4          /* a routed pair names an expert outside [0, E)  */
 };
 
 /* Accumulation schedules ([Handshake] "Schedule gate": canonical, reversed,
@@ -98,6 +99,9 @@ typedef struct ei_weights {
   int64_t nb;           /* k / 32 blocks                                   */
   uint32_t smax;        /* max |scale| over all blocks (Q4: max 2^e)       */
   int32_t format;       /* EI_FORMAT_Q8 or EI_FORMAT_Q4                    */
+  int64_t experts;      /* matrices stacked in the buffer (1 unless packed */
+                        /* with ei_q8_pack_stacked)                         */
+  int64_t expert_stride;/* bytes from one stacked matrix to the next       */
 } ei_weights;
 
 /* ------------------------------------------------------------ weights */
@@ -135,6 +139,26 @@ int ei_q8_pack(const int8_t* codes, const int32_t* scales, int64_t n, int64_t k,
  */
 int ei_q4_pack(const uint8_t* nib, const uint8_t* sme, int64_t n, int64_t k,
                void* packed, size_t packed_bytes, ei_weights* out, ei_stream stream);
+
+/* Bytes for `experts` stacked n x k matrices (ei_q8_pack_stacked). */
+size_t ei_packed_bytes_stacked(int64_t experts, int64_t n, int64_t k);
+
+/*
+ * Repack E same-shape Q8 matrices, the experts of a Mixture-of-Experts layer
+ * ([tritify] 3.2 "Mixture-of-Experts": every selected expert is an exact-
+ * integer MLP), into one buffer: matrix e is packed exactly as ei_q8_pack
+ * would, at byte offset e * expert_stride (expert_stride = ei_packed_bytes(n,
+ * k) rounded up to 256).
+ *   codes   device int8 [E][n][k]
+ *   scales  device int32 [E][n][k/32]
+ *   packed  device buffer of >= ei_packed_bytes_stacked(E, n, k) bytes,
+ *           256-B aligned
+ *   out     host: descriptor with experts = E; smax is the largest scale of
+ *           all experts
+ * Synchronous.  Errors as ei_q8_pack; EI_EINVAL for E < 1.
+ */
+int ei_q8_pack_stacked(const int8_t* codes, const int32_t* scales, int64_t experts, int64_t n, int64_t k,
+                       void* packed, size_t packed_bytes, ei_weights* out, ei_stream stream);
 
 /* ------------------------------------------------------ activations */
 
@@ -187,6 +211,33 @@ int int_gemm_q8(const ei_weights* w, const int64_t* x, int64_t* y, int64_t t, in
 int int_gemm_q4(const ei_weights* w, const int32_t* x, int64_t* y, int64_t t, int limbs,
                 int schedule, uint64_t shuffle_seed, void* workspace, size_t workspace_bytes,
                 int32_t* d_status, ei_stream stream);
+
+/* Workspace bytes int_gemm_q8_grouped needs for `rows` activation rows routed
+ * to `topk` experts each. */
+size_t ei_grouped_workspace_bytes(const ei_weights* w, int64_t rows, int topk, int limbs);
+
+/*
+ * Routed (grouped) Q8 projection, the expert GEMM of a Mixture-of-Experts
+ * layer ([tritify] 3.2 "Mixture-of-Experts"; the Q8 profile of [Handshake]
+ * C1): for every activation row r and slot s, with e = route[r][s],
+ *     y[r * topk + s][i] = (sum_b S_e[i][b] sum_{j in b} q_e[i][j] x[r][j]
+ *                           + 2^23) >> 24
+ * exactly, i.e. int_gemm_q8 of expert e on row r.  The pairs (r, s) are
+ * grouped by expert on the device (a stable sort, ties by pair index), each
+ * group runs as MFMA token tiles against its expert's tiles, and every result
+ * lands in its pair's own output row, so y does not depend on the grouping.
+ *   w        descriptor from ei_q8_pack_stacked (experts = E)
+ *   x        device int64 [rows][k], Q16 activations
+ *   route    device int32 [rows][topk], expert ids in [0, E)
+ *   y        device int64 [rows * topk][n]
+ *   limbs    3 (Q16 activations with |x| <= 2^22)
+ * rows * topk <= 16384 and E <= 2^17, else EI_ERANGE; other host errors as
+ * int_gemm_q8.  An expert id outside [0, E) sets EI_DEV_ROUTE (that pair's
+ * output row is left unwritten).
+ */
+int int_gemm_q8_grouped(const ei_weights* w, const int64_t* x, const int32_t* route, int64_t rows, int topk,
+                        int64_t* y, int limbs, void* workspace, size_t workspace_bytes, int32_t* d_status,
+                        ei_stream stream);
 
 /* ------------------------------------------------------- epilogues */
 

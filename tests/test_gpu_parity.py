@@ -225,3 +225,109 @@ def test_repeat_runs_identical(ei):
         xd = dev(synth.dense_x(t))
         say("repeat", t)
         assert len({ei.digest(ei.gemm_q8(w, xd)) for _ in range(3)}) == 1
+
+
+# ------------------------------------------------- tiled kernel accumulators
+
+def test_q8_tiled_per_limb_accumulators_extreme_scales(ei):
+    # scales at the int32 ends: the tiled kernel must take its per-limb
+    # accumulator form (one shared int64 would not be exact here)
+    N, K, T = 100, 256, 70
+    r = np.random.default_rng(12)
+    q = r.choice(np.array([-128, 127, -127, 3, 0], np.int8), size=(N, K))
+    s = r.choice(np.array([-(2**31), 2**31 - 1, 1, -1, 40000], np.int64), size=(N, K // 32)).astype(np.int32)
+    x = r.choice(np.array([8355711, -8421504, 0, 1, -1, 2**22], np.int64), size=(T, K))
+    say("tiled per-limb accumulators")
+    w = ei.pack_q8(dev(q), dev(s))
+    assert (host(ei.gemm_q8(w, dev(x))) == oracle.q8(q, s, x)).all()
+
+
+# ------------------------------------------------------------- routed (MoE)
+
+def _grouped_reference(codes, scales, x, route):
+    """Oracle rows y[r*topk + s] = Q8(expert route[r][s], x[r]), one oracle
+    call per expert on the rows routed to it."""
+    rows, topk = route.shape
+    y = np.zeros((rows * topk, codes.shape[1]), np.int64)
+    for e in np.unique(route):
+        rr, ss = np.nonzero(route == e)
+        y[rr * topk + ss] = oracle.q8(codes[e], scales[e], x[rr])
+    return y
+
+
+@pytest.mark.parametrize("shape", [(5, 37, 3, 70, 96), (3, 50, 2, 33, 64), (9, 12, 4, 130, 288)])
+def test_q8_grouped_small(ei, shape):
+    E, rows, topk, N, K = shape
+    r = np.random.default_rng(E * 100 + rows)
+    codes = np.stack([synth.q8_codes(r, N, K) for _ in range(E)])
+    scales = np.stack([synth.q8_scales(r, N, K) for _ in range(E)])
+    x = synth.q16_acts(r, rows, K)
+    route = np.stack([np.sort(r.choice(E, topk, replace=False)) for _ in range(rows)]).astype(np.int32)
+    say("grouped", shape)
+    w = ei.pack_q8_stacked(dev(codes), dev(scales))
+    y = host(ei.gemm_q8_grouped(w, dev(x), dev(route)))
+    assert (y == _grouped_reference(codes, scales, x, route)).all()
+
+
+def test_q8_grouped_skewed_and_extreme(ei):
+    # one expert takes most pairs (several token tiles), one takes none, and
+    # the scales force the per-limb accumulators
+    E, rows, topk, N, K = 4, 80, 2, 64, 128
+    r = np.random.default_rng(21)
+    codes = np.stack([r.integers(-128, 128, (N, K), dtype=np.int16).astype(np.int8) for _ in range(E)])
+    scales = np.stack([r.integers(-(2**31), 2**31, (N, K // 32), dtype=np.int64).astype(np.int32)
+                       for _ in range(E)])
+    x = r.integers(-8421504, 8355712, (rows, K), dtype=np.int64)
+    route = np.zeros((rows, topk), np.int32)
+    route[:, 0] = 0
+    route[:, 1] = np.where(np.arange(rows) % 5 == 0, 3, 1)
+    say("grouped skewed")
+    w = ei.pack_q8_stacked(dev(codes), dev(scales))
+    y = host(ei.gemm_q8_grouped(w, dev(x), dev(route)))
+    assert (y == _grouped_reference(codes, scales, x, route)).all()
+
+
+def test_q8_grouped_bad_expert_is_flagged(ei):
+    E, rows, topk, N, K = 3, 8, 2, 32, 64
+    r = np.random.default_rng(22)
+    codes = np.stack([synth.q8_codes(r, N, K) for _ in range(E)])
+    scales = np.stack([synth.q8_scales(r, N, K) for _ in range(E)])
+    route = np.tile(np.array([[0, 1]], np.int32), (rows, 1))
+    route[3, 1] = 3
+    say("grouped bad expert")
+    w = ei.pack_q8_stacked(dev(codes), dev(scales))
+    with pytest.raises(ei.EIError):
+        ei.gemm_q8_grouped(w, dev(synth.q16_acts(r, rows, K)), dev(route))
+
+
+def test_olmoe_grouped_ffn_sampled_pairs(ei, lut):
+    # 64 experts (gate/up 1024x2048, down 2048x1024), 512 tokens, top-8: the
+    # full routed FFN on the GPU, sampled pairs against the oracle
+    E, H, I = synth.OLMOE_E, synth.OLMOE_H, synth.OLMOE_I
+    mats = [synth.olmoe_expert(e) for e in range(E)]
+    gc = np.stack([m[0][0] for m in mats]); gs = np.stack([m[0][1] for m in mats])
+    uc = np.stack([m[1][0] for m in mats]); us = np.stack([m[1][1] for m in mats])
+    dc = np.stack([m[2][0] for m in mats]); ds = np.stack([m[2][1] for m in mats])
+    x, route = synth.olmoe_x(), synth.olmoe_route()
+    say("olmoe pack")
+    wg, wu, wd = ei.pack_q8_stacked(dev(gc), dev(gs)), ei.pack_q8_stacked(dev(uc), dev(us)), \
+        ei.pack_q8_stacked(dev(dc), dev(ds))
+    xd, rd = dev(x), dev(route)
+    say("olmoe grouped ffn")
+    g = ei.gemm_q8_grouped(wg, xd, rd)
+    u = ei.gemm_q8_grouped(wu, xd, rd)
+    h = ei.silu_mul(g, u, ei.silu_lut())
+    out = host(ei.gemm_q8_grouped(wd, h, rd.reshape(-1, 1)))
+    assert out.shape == (synth.OLMOE_T * synth.OLMOE_TOPK, H)
+    rs = np.random.default_rng(23)
+    pairs = [(int(t), int(k)) for t, k in zip(rs.integers(0, synth.OLMOE_T, 16), rs.integers(0, 8, 16))]
+    pairs += [(0, 0), (511, 7)]
+    ref = oracle.moe_pairs(x, route, lambda e: mats[e], lut, pairs=pairs, threads=8)
+    for (t, k), want in zip(pairs, ref):
+        assert (out[t * 8 + k] == want).all(), (t, k)
+    # the gate projection of one expert equals the dense projection of that
+    # expert on its routed tokens (a property that holds at any size)
+    e = int(route[3, 0])
+    tt, kk = np.nonzero(route == e)
+    dense = host(ei.gemm_q8(ei.pack_q8(dev(gc[e]), dev(gs[e])), dev(x[tt])))
+    assert (host(g)[tt * 8 + kk] == dense).all()
