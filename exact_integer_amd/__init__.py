@@ -19,7 +19,7 @@ import torch
 
 __all__ = [
     "EIError", "PackedWeights", "lib", "pack_q8", "pack_q4", "pack_q8_stacked", "gemm_q8", "gemm_q4",
-    "gemm_q8_grouped", "limb_split", "silu_lut", "silu_mul", "digest", "sha256_host", "workspace_bytes",
+    "gemm_q8_grouped", "fp32_shadow", "limb_split", "silu_lut", "silu_mul", "digest", "sha256_host", "workspace_bytes",
     "grouped_workspace_bytes", "SCHEDULES", "DEV_LIMB_RANGE", "DEV_OUT_RANGE", "DEV_ROUTE",
 ]
 
@@ -59,6 +59,7 @@ SIGNATURES = {
     "int_gemm_q4": (I32, [WP, P, P, I64, I32, I32, U64, P, SZ, P, P]),
     "ei_silu_lut_build": (I32, [P, P]),
     "silu_lut_epilogue": (I32, [P, P, P, P, I64, P, P]),
+    "ei_q8_fp32_shadow": (I32, [P, P, P, P, I64, I64, I64, I32, U64, P]),
     "output_digest": (I32, [P, SZ, P, P]),
     "ei_sha256_host": (None, [P, SZ, P]),
     "ei_status_string": (ctypes.c_char_p, [I32]),
@@ -277,6 +278,19 @@ def silu_mul(g: torch.Tensor, u: torch.Tensor, lut: torch.Tensor, out=None, stat
     if check:
         _raise_status(status, "silu_lut_epilogue")
     return h
+
+
+def fp32_shadow(codes: torch.Tensor, scales: torch.Tensor, x: torch.Tensor, schedule: str = "canonical",
+                seed: int = 0xE1) -> torch.Tensor:
+    """The float32 shadow of the Q8 projection in one schedule's order (contrast only)."""
+    s = _stream()
+    n, k = codes.shape
+    t = x.shape[0]
+    y = torch.empty((t, n), dtype=torch.float32, device=x.device)
+    _check(lib().ei_q8_fp32_shadow(_dev(codes, torch.int8, "codes"), _dev(scales, torch.int32, "scales"),
+                                   _dev(x, torch.int64, "x"), y.data_ptr(), n, k, t, SCHEDULES[schedule], seed, s),
+           "ei_q8_fp32_shadow")
+    return y
 
 
 def digest(t: torch.Tensor) -> str:

@@ -366,6 +366,17 @@ int silu_lut_epilogue(const int64_t* gate, const int64_t* up, const int32_t* lut
              : EI_EDEVICE;
 }
 
+int ei_q8_fp32_shadow(const int8_t* codes, const int32_t* scales, const int64_t* x, float* y, int64_t n, int64_t k,
+                      int64_t t, int schedule, uint64_t shuffle_seed, ei_stream stream) {
+  if (!codes || !scales || !x || !y || n < 1 || t < 1 || k < 32 || k % 32 != 0) return EI_EINVAL;
+  if (schedule < EI_SCHED_DEFAULT || schedule > EI_SCHED_TREE) return EI_EINVAL;
+  if ((k + 127) / 128 > 16384) return EI_ERANGE;   // the tile permutation lives in LDS
+  return launch_shadow(codes, scales, x, y, n, k, t, schedule, shuffle_seed, static_cast<hipStream_t>(stream)) ==
+                 hipSuccess
+             ? EI_OK
+             : EI_EDEVICE;
+}
+
 int output_digest(const void* dptr, size_t nbytes, uint8_t* out, ei_stream stream) {
   if (!out || (!dptr && nbytes)) return EI_EINVAL;
   if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return EI_EDEVICE;

@@ -259,6 +259,26 @@ int ei_silu_lut_build(int32_t* lut, ei_stream stream);
 int silu_lut_epilogue(const int64_t* gate, const int64_t* up, const int32_t* lut, int64_t* h,
                       int64_t n, int32_t* d_status, ei_stream stream);
 
+/*
+ * FP32 shadow of the Q8 projection, the negative control of the schedule gate
+ * ([Handshake] C3 and "Construction / Schedule gate": the same GEMM in float
+ * under the five schedules splinters into several bit patterns).  Contrast
+ * only: nothing on the exact path uses it.
+ *     y[t][i] = the float32 sum of fl32(fl32(S[i][b] q[i][j] 2^-24) *
+ *               fl32(x[t][j] 2^-16)) over j, one float32 rounding per product
+ *               and per addition, in the schedule's order (EI_SCHED_DEFAULT
+ *               and CANONICAL: j ascending; REVERSED: j descending;
+ *               TILED_SHUFFLED: 128-column tiles in the splitmix64/Fisher-
+ *               Yates permutation drawn from shuffle_seed; SPLIT_K: 8
+ *               block-range partials added last to first; TREE: per-block sums
+ *               in a pairwise tree)
+ *   codes   device int8 [n][k] (canonical, not packed); scales device int32
+ *           [n][k/32]; x device int64 [t][k]; y device float32 [t][n]
+ * Errors: EI_EINVAL for null pointers, bad sizes or schedule.
+ */
+int ei_q8_fp32_shadow(const int8_t* codes, const int32_t* scales, const int64_t* x, float* y, int64_t n, int64_t k,
+                      int64_t t, int schedule, uint64_t shuffle_seed, ei_stream stream);
+
 /* -------------------------------------------------------- digests */
 
 /*

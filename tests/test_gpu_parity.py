@@ -331,3 +331,33 @@ def test_olmoe_grouped_ffn_sampled_pairs(ei, lut):
     tt, kk = np.nonzero(route == e)
     dense = host(ei.gemm_q8(ei.pack_q8(dev(gc[e]), dev(gs[e])), dev(x[tt])))
     assert (host(g)[tt * 8 + kk] == dense).all()
+
+
+# ------------------------------------------------------------- FP32 shadow
+
+def test_fp32_shadow_matches_oracle_orders_and_splinters(ei):
+    # the float negative control of the schedule gate: each schedule's float32
+    # sum matches the oracle's float32 sum in that order bit for bit, and the
+    # five schedules do not all agree (the integer digests do)
+    mats, x = synth.qkv_inputs()
+    xd = dev(x)
+    for name, (c, sc) in mats.items():
+        cd, sd = dev(c), dev(sc)
+        digests = set()
+        for order in oracle.SCHEDULES:
+            say("fp32 shadow", name, order)
+            dg = ei.digest(ei.fp32_shadow(cd, sd, xd, order, seed=0xE1))
+            assert dg == GOLDEN["qkv_gate"][name + "_fp32"][order], (name, order)
+            digests.add(dg)
+        assert len(digests) >= 2, name
+
+
+@pytest.mark.parametrize("shape", [(37, 96, 3), (5, 3200, 2), (64, 4096, 1)])
+def test_fp32_shadow_small_all_orders(ei, shape):
+    N, K, T = shape
+    r = np.random.default_rng(N + K + T)
+    q, s, x = synth.q8_codes(r, N, K), synth.q8_scales(r, N, K), synth.q16_acts(r, T, K)
+    for order in oracle.SCHEDULES:
+        say("fp32 shadow small", shape, order)
+        y = host(ei.fp32_shadow(dev(q), dev(s), dev(x), order, seed=0x77))
+        assert (y.view(np.uint32) == oracle.q8_fp32(q, s, x, order, seed=0x77).view(np.uint32)).all(), order
