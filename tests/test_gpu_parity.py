@@ -361,3 +361,24 @@ def test_fp32_shadow_small_all_orders(ei, shape):
         say("fp32 shadow small", shape, order)
         y = host(ei.fp32_shadow(dev(q), dev(s), dev(x), order, seed=0x77))
         assert (y.view(np.uint32) == oracle.q8_fp32(q, s, x, order, seed=0x77).view(np.uint32)).all(), order
+
+
+def test_gemv_repeated_calls_and_flagged_call(ei):
+    # back-to-back GEMV calls of different T with one shared workspace; a
+    # call whose activations are out of range is flagged, not fatal, and the
+    # calls after it are still exact
+    N, K = 1000, 2048
+    r = np.random.default_rng(31)
+    q, s = synth.q8_codes(r, N, K), synth.q8_scales(r, N, K)
+    w = ei.pack_q8(dev(q), dev(s))
+    ws = torch.zeros(max(ei.workspace_bytes(w, 4), 1), dtype=torch.uint8, device="cuda")
+    for t in (1, 3, 4, 1, 2):
+        x = synth.q16_acts(r, t, K)
+        say("gemv reuse", t)
+        assert (host(ei.gemm_q8(w, dev(x), workspace=ws)) == oracle.q8(q, s, x)).all(), t
+    bad = synth.q16_acts(r, 1, K)
+    bad[0, 7] = 2**40
+    with pytest.raises(ei.EIError):
+        ei.gemm_q8(w, dev(bad), workspace=ws)
+    x = synth.q16_acts(r, 2, K)
+    assert (host(ei.gemm_q8(w, dev(x), workspace=ws)) == oracle.q8(q, s, x)).all()
