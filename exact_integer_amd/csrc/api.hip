@@ -50,17 +50,9 @@ WsLayout layout_for(const ei_weights* w, int64_t t, int limbs, int schedule) {
   return L;
 }
 
-// The tiled prefill kernel (3 limbs, default/canonical schedule, T >= 64)
-// keeps one int64 accumulator per output when that is exact -- every partial
-// sum, bounded by nb * smax * 2^19 * (1 + 2^8 + 2^16), stays below 2^63, and
-// S * 2^16 fits an int32 (smax < 2^15) -- and one per limb otherwise (exact
-// for any int32 scale, nb <= 2^13).  Its buffer offsets are 32-bit.
+// The tiled prefill kernel: 3 limbs, default/canonical schedule, T >= 64, and
+// 32-bit buffer offsets.
 constexpr int64_t kTiledMinT = 64;
-bool single_acc_ok(const ei_weights* w) {
-  if (w->smax >= (1u << 15)) return false;
-  const __int128 bound = (__int128)w->nb * (__int128)w->smax * ((__int128)1 << 19) * 65793;
-  return bound < ((__int128)1 << 63);
-}
 bool tiled_ok(const ei_weights* w, int64_t t, int limbs, int schedule) {
   if (limbs != 3 || t < kTiledMinT) return false;
   if (schedule != EI_SCHED_DEFAULT && schedule != EI_SCHED_CANONICAL) return false;
@@ -114,9 +106,8 @@ int run_gemm(const ei_weights* w, const void* x, int x_is_i32, int64_t* y, int64
     if (e != hipSuccess) return EI_EDEVICE;
   }
   const bool tiled = lay.mfma && tiled_ok(w, t, limbs, schedule);
-  const bool single = tiled && single_acc_ok(w);
   auto launch = [&](const GemmArgs& args) {
-    if (tiled) return launch_gemm_tiled(args, single, s);
+    if (tiled) return launch_gemm_tiled(args, s);
     return lay.mfma ? launch_gemm_mfma(args, limbs, s) : launch_gemv(args, limbs, s);
   };
 
@@ -321,7 +312,7 @@ int int_gemm_q8_grouped(const ei_weights* w, const int64_t* x, const int32_t* ro
   a.ntiles = ntiles;
   a.tiles_max = g.tiles_max;
   a.expert_stride = w->expert_stride;
-  return launch_gemm_grouped(a, single_acc_ok(w), s) == hipSuccess ? EI_OK : EI_EDEVICE;
+  return launch_gemm_grouped(a, s) == hipSuccess ? EI_OK : EI_EDEVICE;
 }
 
 int ei_limb_split(const int64_t* x, int8_t* d, int64_t n, int limbs, int32_t* d_status, ei_stream stream) {

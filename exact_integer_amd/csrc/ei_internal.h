@@ -97,8 +97,8 @@ hipError_t launch_limb_tiles(const void* x, int x_is_i32, int64_t t, int64_t k, 
                              int8_t* tiles, int64_t t_pad, int32_t* status, hipStream_t s);
 hipError_t launch_gemv(const GemmArgs& a, int limbs, hipStream_t s);
 hipError_t launch_gemm_mfma(const GemmArgs& a, int limbs, hipStream_t s);
-hipError_t launch_gemm_tiled(const GemmArgs& a, bool single_acc, hipStream_t s);   // 3 limbs, see tiled_ok()
-hipError_t launch_gemm_grouped(const GemmArgs& a, bool single_acc, hipStream_t s);  // 3 limbs
+hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t s);    // 3 limbs, see tiled_ok()
+hipError_t launch_gemm_grouped(const GemmArgs& a, hipStream_t s);  // 3 limbs
 hipError_t launch_moe_sort(const int32_t* route, int64_t pairs, int64_t experts, int32_t* sorted_pair,
                            int32_t* offsets, int32_t* tile_expert, int32_t* tile_row0, int32_t* tile_rows,
                            int32_t* ntiles, int32_t* status, hipStream_t s);

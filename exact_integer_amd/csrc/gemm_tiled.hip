@@ -1,16 +1,17 @@
 // Tiled exact projection for many tokens: the prefill GEMM.
 //
 // Computes, for three activation limbs d_0, d_1, d_2 (x = d_0 + 2^8 d_1 +
-// 2^16 d_2) and every (token t, row i),
-//     acc[t][i] = sum_b S[i][b] * (P_0 + 2^8 P_1 + 2^16 P_2)[t][i][b],
+// 2^16 d_2) and every (token t, row i), the per-limb sums
+//     A_l[t][i] = sum_b S[i][b] * P_l[t][i][b],
 //     P_l[t][i][b] = sum_{j in b} q[i][j] * d_l[t][j]          (int32, exact)
-// in ONE int64 accumulator, then y = floor((acc + 2^23) / 2^24) (or acc).
-// Exactness: |P_l| <= 32 * 128 * 128 = 2^19, so every partial sum of acc is
-// bounded by nb * smax * 2^19 * (1 + 2^8 + 2^16); the host launches this
-// kernel only when that bound is below 2^63 and smax < 2^15 (so that
-// S * 2^16 is an int32).  P_0 + 2^8 P_1 < 2^28 is formed in int32.  Every
-// step is exact integer arithmetic, so the result is the same bits as any
-// other evaluation order.
+// in int64 (|S P_l| < 2^31 * 2^19 = 2^50, so any partial sum over up to 2^13
+// blocks is exact for any int32 scale), then acc = A_0 + 2^8 A_1 + 2^16 A_2
+// in int128 and y = floor((acc + 2^23) / 2^24) (or acc).  Every step is exact
+// integer arithmetic, so the result is the same bits as any other
+// evaluation order.  (One shared int64 accumulator, with P_0 + 2^8 P_1 formed
+// in int32, needs one VALU op less per element but measured slower on
+// MI355X: its two dependent 64-bit multiply-adds per element stall where
+// three independent ones do not.)
 //
 // Work split.  A workgroup of 4 waves owns a tile of 32 RT WR rows x
 // 32 TT (4 / WR) tokens; each wave owns RT x TT 32x32 MFMA tiles.  Per
@@ -19,9 +20,9 @@
 // scales of its rows; they are copied global -> LDS with direct-to-LDS
 // buffer loads (no VGPR round trip, scalar block offsets) into a ring of
 // NBUF one-block buffers, NBUF - 1 blocks ahead of use.  Per block a wave
-// issues 3 RT TT v_mfma_i32_32x32x32_i8 and, per output element, one
-// v_lshl_add_u32 and two v_mad_i64_i32: this VALU epilogue, which the matrix
-// cores only partly overlap, is the critical resource.
+// issues 3 RT TT v_mfma_i32_32x32x32_i8 and, per output element, three
+// v_mad_i64_i32: this VALU epilogue, which the matrix cores only partly
+// overlap, is the critical resource.
 #include "ei_internal.h"
 
 namespace ei {
@@ -58,10 +59,10 @@ struct TiledShape {
   static constexpr int kBlockBytes = kScaleOff + kRowTiles * 128 + kPad * 1024;
 };
 
-// NACC = 1: one int64 accumulator (host-checked bound above); NACC = 3: one
-// per limb, exact for any int32 scale while nb <= 2^13.  kGrouped: each token
-// tile belongs to one expert, whose packed image and output rows it looks up.
-template <int RT, int TT, int WR, int NBUF, bool kExact, int NACC, bool kGrouped>
+// kGrouped: each token tile belongs to one expert, whose packed image and
+// output rows it looks up.  PIPE: the epilogue of block b runs after the
+// MFMAs of block b + 1 are issued.  XMAP: XCD-contiguous tile order.
+template <int RT, int TT, int WR, int NBUF, bool kExact, bool kGrouped, bool PIPE, bool XMAP>
 __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs a) {
   using Sh = TiledShape<RT, TT, WR>;
   extern __shared__ __align__(16) uint8_t lds[];
@@ -71,7 +72,13 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs a) {
 
   // ---- tile of this workgroup
   const int64_t tbs = kGrouped ? a.tiles_max : (a.t_pad + Sh::kToks - 1) / Sh::kToks;
-  const int64_t rb = blockIdx.x / tbs, tb = blockIdx.x % tbs;
+  // XMAP: workgroup g runs on XCD g % 8; give each XCD a contiguous run of
+  // tiles (token tiles fastest), so a row block's code tiles are fetched into
+  // one XCD's L2 and reused there by the token tiles that follow
+  const int64_t rbs = (a.n_pad + Sh::kRows - 1) / Sh::kRows, ntiles = rbs * tbs;
+  int64_t g = blockIdx.x;
+  if (XMAP && ntiles % 8 == 0) g = (g % 8) * (ntiles / 8) + g / 8;
+  const int64_t rb = g / tbs, tb = g % tbs;
   const int64_t rgs = a.n_pad / kTile, tgs = kGrouped ? a.tiles_max : a.t_pad / kTile;
   const int8_t* codes = a.codes;
   const int32_t* scales = a.scales;
@@ -139,9 +146,9 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs a) {
       copy16_to_lds(rscal, blk + sdst, svoff, (uint32_t)b * 128u);
   };
 
-  int64_t acc[NACC][RT][TT][16];
+  int64_t acc[3][RT][TT][16];
 #pragma unroll
-  for (int c = 0; c < NACC; ++c)
+  for (int c = 0; c < 3; ++c)
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -151,52 +158,67 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs a) {
   const v16i zero = {};
 
   const int64_t nb = a.nb;
-  for (int64_t b = 0; b < NBUF - 1 && b < nb; ++b) issue(b);
-  for (int64_t b = 0; b < nb; ++b) {
-    // this wave's copies of block b have landed when at most the later
-    // blocks' copies are outstanding; the barrier then covers all waves and
-    // frees the buffer of block b - 1 for block b + NBUF - 1
+  // Block b: wait for its copies (all waves), start the copy of block
+  // b + NBUF - 1 into the buffer block b - 1 used, read the operands and
+  // scales into registers, issue the MFMAs.  The epilogue of a block needs
+  // only registers, so with PIPE it runs one block later, while the matrix
+  // cores work on the next block; two named register sets (A, B) keep the
+  // loop free of copies.
+  using Dset = v16i[RT][TT][3];
+  auto step = [&](int64_t b, Dset& D, int32_t (&S)[RT]) {
     // (__syncthreads would also wait for the copies still in flight)
     if (b + NBUF - 2 < nb)
       barrier_after_vmcnt<(NBUF - 2) * (Sh::kPerWave + 1)>();
     else
       barrier_after_vmcnt<0>();
     if (b + NBUF - 1 < nb) issue(b + NBUF - 1);
-
     const uint8_t* blk = lds + (int)(b % NBUF) * Sh::kBlockBytes;
     v4i q[RT];
-    int32_t S[RT], S16[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       const int jr = RT * wr + rt;
       q[rt] = *reinterpret_cast<const v4i*>(blk + Sh::kCodeOff + jr * 1024 + lane * 16);
       S[rt] = *reinterpret_cast<const int32_t*>(blk + Sh::kScaleOff + (jr * 32 + (lane & 31)) * 4);
-      S16[rt] = (int32_t)((uint32_t)S[rt] << 16);
     }
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
       const int jt = TT * wt + tt;
-      v4i d[3];
 #pragma unroll
-      for (int l = 0; l < 3; ++l)
-        d[l] = *reinterpret_cast<const v4i*>(blk + Sh::kLimbOff + (l * Sh::kTokTiles + jt) * 1024 + lane * 16);
+      for (int l = 0; l < 3; ++l) {
+        const v4i d = *reinterpret_cast<const v4i*>(blk + Sh::kLimbOff + (l * Sh::kTokTiles + jt) * 1024 + lane * 16);
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const v16i D0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(d[0], q[rt], zero, 0, 0, 0);
-        const v16i D1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(d[1], q[rt], zero, 0, 0, 0);
-        const v16i D2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(d[2], q[rt], zero, 0, 0, 0);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if (NACC == 1) {
-            const int32_t p01 = D0[r] + (int32_t)((uint32_t)D1[r] << 8);
-            acc[0][rt][tt][r] += (int64_t)S[rt] * p01 + (int64_t)S16[rt] * D2[r];
-          } else {
-            acc[0][rt][tt][r] += (int64_t)S[rt] * D0[r];
-            acc[NACC > 1 ? 1 : 0][rt][tt][r] += (int64_t)S[rt] * D1[r];
-            acc[NACC > 2 ? 2 : 0][rt][tt][r] += (int64_t)S[rt] * D2[r];
-          }
-        }
+        for (int rt = 0; rt < RT; ++rt) D[rt][tt][l] = __builtin_amdgcn_mfma_i32_32x32x32_i8(d, q[rt], zero, 0, 0, 0);
       }
+    }
+  };
+  auto epilogue = [&](const Dset& D, const int32_t (&S)[RT]) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+#pragma unroll
+          for (int l = 0; l < 3; ++l) acc[l][rt][tt][r] += (int64_t)S[rt] * D[rt][tt][l][r];
+  };
+
+  for (int64_t b = 0; b < NBUF - 1 && b < nb; ++b) issue(b);
+  Dset DA, DB;
+  int32_t SA[RT], SB[RT];
+  if (PIPE) {
+    step(0, DA, SA);
+    for (int64_t b = 0; b < nb; b += 2) {
+      if (b + 1 < nb) step(b + 1, DB, SB);
+      epilogue(DA, SA);
+      if (b + 1 < nb) {
+        if (b + 2 < nb) step(b + 2, DA, SA);
+        epilogue(DB, SB);
+      }
+    }
+  } else {
+    for (int64_t b = 0; b < nb; ++b) {
+      step(b, DA, SA);
+      epilogue(DA, SA);
     }
   }
 
@@ -219,9 +241,8 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs a) {
           orow = tb * Sh::kToks + tloc;
           if (orow >= a.t) continue;
         }
-        __int128 v = acc[0][rt][tt][r];
-        if (NACC > 1) v += (__int128)acc[NACC > 1 ? 1 : 0][rt][tt][r] << 8;
-        if (NACC > 2) v += (__int128)acc[NACC > 2 ? 2 : 0][rt][tt][r] << 16;
+        const __int128 v = (__int128)acc[0][rt][tt][r] + ((__int128)acc[1][rt][tt][r] << 8) +
+                           ((__int128)acc[2][rt][tt][r] << 16);
         int64_t out;
         if (!finish_output(v, kExact ? OUT_EXACT : OUT_ROUND_Q24, &out)) flag(a.status, EI_DEV_OUT_RANGE);
         a.y[orow * a.n + row] = out;
@@ -229,7 +250,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs a) {
   }
 }
 
-template <int RT, int TT, int WR, int NBUF, int NACC = 1, bool kGrouped = false>
+template <int RT, int TT, int WR, int NBUF, bool kGrouped = false, bool PIPE = false, bool XMAP = false>
 hipError_t launch_tiled_shape(const GemmArgs& a, hipStream_t s) {
   using Sh = TiledShape<RT, TT, WR>;
   const int64_t rbs = (a.n_pad + Sh::kRows - 1) / Sh::kRows;
@@ -237,20 +258,17 @@ hipError_t launch_tiled_shape(const GemmArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)(rbs * tbs)), block(256);
   const size_t lds = (size_t)NBUF * Sh::kBlockBytes;
   if (a.out_mode == OUT_EXACT)
-    hipLaunchKernelGGL((gemm_tiled_kernel<RT, TT, WR, NBUF, true, NACC, kGrouped>), grid, block, lds, s, a);
+    hipLaunchKernelGGL((gemm_tiled_kernel<RT, TT, WR, NBUF, true, kGrouped, PIPE, XMAP>), grid, block, lds, s, a);
   else
-    hipLaunchKernelGGL((gemm_tiled_kernel<RT, TT, WR, NBUF, false, NACC, kGrouped>), grid, block, lds, s, a);
+    hipLaunchKernelGGL((gemm_tiled_kernel<RT, TT, WR, NBUF, false, kGrouped, PIPE, XMAP>), grid, block, lds, s, a);
   return hipGetLastError();
 }
 
 // Launch shape: one 32x32 tile per wave, 128 rows x 32 tokens per workgroup,
-// copies one block ahead (the fastest of the shapes measured on MI355X).
-hipError_t launch_gemm_tiled(const GemmArgs& a, bool single_acc, hipStream_t s) {
-  return single_acc ? launch_tiled_shape<1, 1, 4, 2, 1>(a, s) : launch_tiled_shape<1, 1, 4, 2, 3>(a, s);
-}
+// copies one block ahead, no software pipelining, natural tile order (the
+// fastest of the variants measured on MI355X).
+hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t s) { return launch_tiled_shape<1, 1, 4, 2>(a, s); }
 
-hipError_t launch_gemm_grouped(const GemmArgs& a, bool single_acc, hipStream_t s) {
-  return single_acc ? launch_tiled_shape<1, 1, 4, 2, 1, true>(a, s) : launch_tiled_shape<1, 1, 4, 2, 3, true>(a, s);
-}
+hipError_t launch_gemm_grouped(const GemmArgs& a, hipStream_t s) { return launch_tiled_shape<1, 1, 4, 2, true>(a, s); }
 
 }  // namespace ei
