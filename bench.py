@@ -142,6 +142,135 @@ def copy_calibration(torch, dev) -> int:
     return 0
 
 
+def _time_graph(torch, fn, steps: int, warmup: int):
+    """Record fn once as a HIP graph, replay it warmup + steps times; median ms
+    per replay from HIP events on the capturing stream."""
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        g.replay()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(); g.replay(); b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    return ms[len(ms) // 2], wall / steps * 1e3
+
+
+def bench_olmoe(args, torch, np, ei, synth, dev) -> int:
+    """The OLMoE-shaped routed FFN: 64 experts (gate/up 1024x2048, down
+    2048x1024, Q8), 512 tokens, top-8: grouped gate and up projections, the
+    SiLU-gated product, grouped down projection.  HBM-bound: every expert's
+    weights are read once per step."""
+    import oracle
+    E, H, I, T, TOPK = synth.OLMOE_E, synth.OLMOE_H, synth.OLMOE_I, synth.OLMOE_T, synth.OLMOE_TOPK
+    mats = [synth.olmoe_expert(e) for e in range(E)]
+
+    def stack(m, k):
+        return torch.from_numpy(np.ascontiguousarray(np.stack([mm[m][k] for mm in mats]))).to(dev)
+    wg, wu, wd = (ei.pack_q8_stacked(stack(m, 0), stack(m, 1)) for m in range(3))
+    x, route = synth.olmoe_x(), synth.olmoe_route()
+    xd, rd = torch.from_numpy(x).to(dev), torch.from_numpy(route).to(dev)
+    rd1 = rd.reshape(-1, 1).contiguous()
+    P = T * TOPK
+    g = torch.empty((P, I), dtype=torch.int64, device=dev)
+    u, h = torch.empty_like(g), torch.empty_like(g)
+    out = torch.empty((P, H), dtype=torch.int64, device=dev)
+    ws_a = torch.empty(ei.grouped_workspace_bytes(wg, T, TOPK), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(ei.grouped_workspace_bytes(wd, P, 1), dtype=torch.uint8, device=dev)
+    lut = ei.silu_lut(dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def step():
+        ei.gemm_q8_grouped(wg, xd, rd, out=g, workspace=ws_a, status=status)
+        ei.gemm_q8_grouped(wu, xd, rd, out=u, workspace=ws_a, status=status)
+        ei.silu_mul(g, u, lut, out=h, status=status)
+        ei.gemm_q8_grouped(wd, h, rd1, out=out, workspace=ws_b, status=status)
+
+    ms, wall_ms = _time_graph(torch, step, args.steps, args.warmup)
+    if int(status.item()) != 0:
+        print(f"bench.py: device status {int(status.item())}", file=sys.stderr)
+        return 1
+    rs = np.random.default_rng(5)
+    pairs = [(int(t), int(k)) for t, k in zip(rs.integers(0, T, 6), rs.integers(0, TOPK, 6))]
+    ref = oracle.moe_pairs(x, route, lambda e: mats[e], oracle.silu_lut(), pairs=pairs,
+                           threads=min(os.cpu_count() or 1, 16))
+    got = out.cpu().numpy()
+    ok = all((got[t * TOPK + k] == r).all() for (t, k), r in zip(pairs, ref))
+    wbytes = 3 * E * I * H * (1 + 4 / 32)
+    useful = LIMBS * 2.0 * P * 3 * I * H
+    gbs = wbytes / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "routed expert FFN: weight GB/s", "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall_ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int8xint8->int32, int64 accumulate",
+        "data": "synthetic (seeded Q8 experts, Q16 activations, uniform top-8 routing)",
+        "config": {"workload": "olmoe_grouped_ffn", "experts": E, "hidden": H, "intermediate": I, "tokens": T,
+                   "top_k": TOPK, "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "step_ms": round(ms, 4),
+                     "weight_bytes": int(wbytes)},
+        "useful_tops": round(useful / (ms * 1e-3) / 1e12, 2),
+        "parity": {"sampled_pairs_equal_oracle": ok, "pairs_checked": len(pairs)}}))
+    return 0 if ok else 1
+
+
+def bench_qwen_ffn(args, torch, np, ei, synth, dev) -> int:
+    """The Qwen2.5-0.5B-shaped FFN chain: 24 layers of gate and up (4864x896)
+    and down (896x4864) Q8 projections at T=30 with the SiLU-gated product and
+    the residual add, fresh weights per layer (353 MB, read once per step)."""
+    import json as _json
+    layers = []
+    for layer in range(synth.QWEN_LAYERS):
+        (gc, gs), (uc, us), (dc, ds) = synth.qwen_ffn_layer(layer)
+        t = [torch.from_numpy(a).to(dev) for a in (gc, gs, uc, us, dc, ds)]
+        layers.append((ei.pack_q8(t[0], t[1]), ei.pack_q8(t[2], t[3]), ei.pack_q8(t[4], t[5])))
+    x0 = torch.from_numpy(synth.qwen_ffn_x0()).to(dev)
+    T, D, F = synth.QWEN_T, synth.QWEN_D, synth.QWEN_F
+    x = torch.empty_like(x0)
+    g = torch.empty((T, F), dtype=torch.int64, device=dev)
+    u, h = torch.empty_like(g), torch.empty_like(g)
+    d = torch.empty((T, D), dtype=torch.int64, device=dev)
+    wsz = max(ei.workspace_bytes(layers[0][0], T), ei.workspace_bytes(layers[0][2], T), 1)
+    ws = torch.empty(wsz, dtype=torch.uint8, device=dev)
+    lut = ei.silu_lut(dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def step():
+        x.copy_(x0)
+        for wg, wu, wd in layers:
+            ei.gemm_q8(wg, x, out=g, workspace=ws, status=status)
+            ei.gemm_q8(wu, x, out=u, workspace=ws, status=status)
+            ei.silu_mul(g, u, lut, out=h, status=status)
+            ei.gemm_q8(wd, h, out=d, workspace=ws, status=status)
+            x.add_(d)
+
+    ms, wall_ms = _time_graph(torch, step, args.steps, args.warmup)
+    gold = _json.load(open(os.path.join(ROOT, "tests", "golden", "oracle_digests.json")))["qwen05b_ffn"]["layers"]
+    ok = int(status.item()) == 0 and ei.digest(x) == gold[-1]["x_next"]
+    wbytes = synth.QWEN_LAYERS * 3 * F * D * (1 + 4 / 32)
+    gbs = wbytes / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "24-layer Q8 FFN chain: weight GB/s", "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall_ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int8xint8->int32, int64 accumulate",
+        "data": "synthetic (seeded Q8 layers, Q16 activations)",
+        "config": {"workload": "qwen05b_ffn_24_layers", "tokens": T, "hidden": D, "intermediate": F,
+                   "layers": synth.QWEN_LAYERS, "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "step_ms": round(ms, 4),
+                     "weight_bytes": int(wbytes)},
+        "parity": {"final_digest_equals_oracle": ok}}))
+    return 0 if ok else 1
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -155,6 +284,9 @@ def main() -> int:
                     help="only run a plain device copy of 256 MiB, 5 times (the reference for HBM byte counters)")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="rocprofv3 --pmc output directories -> profiles/traffic.json (no GPU needed)")
+    ap.add_argument("--workload", choices=("dense", "olmoe", "qwen_ffn"), default="dense",
+                    help="dense: the 14336x4096 decode + prefill step (default); olmoe / qwen_ffn: the routed "
+                         "expert FFN or the 24-layer FFN chain, timed the same way")
     args = ap.parse_args()
     if args.summarize_counters:
         return summarize_counters(*args.summarize_counters)
@@ -176,6 +308,10 @@ def main() -> int:
     dev = torch.device("cuda:0")
     if args.copy_calibration:
         return copy_calibration(torch, dev)
+    if args.workload == "olmoe":
+        return bench_olmoe(args, torch, np, ei, synth, dev)
+    if args.workload == "qwen_ffn":
+        return bench_qwen_ffn(args, torch, np, ei, synth, dev)
 
     def to_dev(a):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)

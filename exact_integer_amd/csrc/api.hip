@@ -16,9 +16,27 @@ inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 constexpr int kSmallT = 4;   // token counts up to this use the GEMV kernel
 constexpr int kSplitParts = 8;
 
+// The tiled prefill kernel: 3 limbs, default/canonical schedule, T >= 64, and
+// 32-bit buffer offsets.
+constexpr int64_t kTiledMinT = 64;
+bool tiled_ok(const ei_weights* w, int64_t t, int limbs, int schedule) {
+  if (limbs != 3 || t < kTiledMinT) return false;
+  if (schedule != EI_SCHED_DEFAULT && schedule != EI_SCHED_CANONICAL) return false;
+  const int64_t t_pad = round_up(t, kTile);
+  return w->n_pad * w->k < ((int64_t)1 << 32) && 3 * t_pad * w->k < ((int64_t)1 << 32);
+}
+
+// Which kernel runs a projection: the GEMV for T <= 4; for larger T under the
+// default/canonical schedule the tiled kernel where it applies, else the
+// skinny split-K kernel; the other schedules use the generic MFMA kernel,
+// which visits the blocks in the schedule's order.
+enum GemmPath { PATH_GEMV, PATH_TILED, PATH_SKINNY, PATH_MFMA };
+
 struct WsLayout {
   size_t limb_off = 0, perm_off = 0, part_off = 0, total = 0;
   bool mfma = false;
+  GemmPath path = PATH_GEMV;
+  int splits = 1;   // skinny: workgroup-level K splits (partials when > 1)
   int64_t t_pad = 0, ntiles = 0;
 };
 
@@ -26,6 +44,13 @@ WsLayout layout_for(const ei_weights* w, int64_t t, int limbs, int schedule) {
   WsLayout L;
   L.mfma = t > kSmallT;
   L.t_pad = round_up(t, kTile);
+  const bool plain = schedule == EI_SCHED_DEFAULT || schedule == EI_SCHED_CANONICAL;
+  if (!L.mfma)
+    L.path = PATH_GEMV;
+  else if (tiled_ok(w, t, limbs, schedule))
+    L.path = PATH_TILED;
+  else
+    L.path = plain ? PATH_SKINNY : PATH_MFMA;
   size_t off = 0;
   if (L.mfma) {
     L.limb_off = off;
@@ -33,6 +58,13 @@ WsLayout layout_for(const ei_weights* w, int64_t t, int limbs, int schedule) {
     L.ntiles = ((w->n_pad / kTile + 1) / 2) * ((L.t_pad / kTile + 1) / 2);
   } else {
     L.ntiles = w->n_pad / kTile;
+  }
+  if (L.path == PATH_SKINNY) {
+    L.splits = skinny_splits(w->n_pad, L.t_pad, w->nb);
+    if (L.splits > 1) {
+      L.part_off = off;
+      off = align_up(off + sizeof(int64_t) * (size_t)L.splits * limbs * (size_t)t * (size_t)w->n);
+    }
   }
   if (schedule == EI_SCHED_TILED_SHUFFLED) {
     L.perm_off = off;
@@ -48,16 +80,6 @@ WsLayout layout_for(const ei_weights* w, int64_t t, int limbs, int schedule) {
   }
   L.total = off;
   return L;
-}
-
-// The tiled prefill kernel: 3 limbs, default/canonical schedule, T >= 64, and
-// 32-bit buffer offsets.
-constexpr int64_t kTiledMinT = 64;
-bool tiled_ok(const ei_weights* w, int64_t t, int limbs, int schedule) {
-  if (limbs != 3 || t < kTiledMinT) return false;
-  if (schedule != EI_SCHED_DEFAULT && schedule != EI_SCHED_CANONICAL) return false;
-  const int64_t t_pad = round_up(t, kTile);
-  return w->n_pad * w->k < ((int64_t)1 << 32) && 3 * t_pad * w->k < ((int64_t)1 << 32);
 }
 
 int check_weights(const ei_weights* w, int format) {
@@ -105,16 +127,28 @@ int run_gemm(const ei_weights* w, const void* x, int x_is_i32, int64_t* y, int64
                           status, s);
     if (e != hipSuccess) return EI_EDEVICE;
   }
-  const bool tiled = lay.mfma && tiled_ok(w, t, limbs, schedule);
   auto launch = [&](const GemmArgs& args) {
-    if (tiled) return launch_gemm_tiled(args, s);
+    if (lay.path == PATH_TILED) return launch_gemm_tiled(args, s);
     return lay.mfma ? launch_gemm_mfma(args, limbs, s) : launch_gemv(args, limbs, s);
   };
 
   switch (schedule) {
     case EI_SCHED_DEFAULT:
     case EI_SCHED_CANONICAL:
-      e = launch(a);
+      if (lay.path == PATH_SKINNY) {
+        if (lay.splits > 1) {
+          int64_t* part = reinterpret_cast<int64_t*>(wsb + lay.part_off);
+          a.part = part;
+          a.out_mode = OUT_PARTIAL;
+          e = launch_gemm_skinny(a, limbs, lay.splits, s);
+          if (e == hipSuccess)
+            e = launch_combine_partials(part, lay.splits, y, t, w->n, limbs, out_mode, status, s);
+        } else {
+          e = launch_gemm_skinny(a, limbs, 1, s);
+        }
+      } else {
+        e = launch(a);
+      }
       break;
     case EI_SCHED_REVERSED:
       a.order = ORDER_DESC;

@@ -99,6 +99,8 @@ hipError_t launch_gemv(const GemmArgs& a, int limbs, hipStream_t s);
 hipError_t launch_gemm_mfma(const GemmArgs& a, int limbs, hipStream_t s);
 hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t s);    // 3 limbs, see tiled_ok()
 hipError_t launch_gemm_grouped(const GemmArgs& a, hipStream_t s);  // 3 limbs
+int skinny_splits(int64_t n_pad, int64_t t_pad, int64_t nb);       // workgroup K splits of the skinny kernel
+hipError_t launch_gemm_skinny(const GemmArgs& a, int limbs, int splits, hipStream_t s);  // a.part when splits > 1
 hipError_t launch_moe_sort(const int32_t* route, int64_t pairs, int64_t experts, int32_t* sorted_pair,
                            int32_t* offsets, int32_t* tile_expert, int32_t* tile_row0, int32_t* tile_rows,
                            int32_t* ntiles, int32_t* status, hipStream_t s);

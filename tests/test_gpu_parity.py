@@ -118,6 +118,38 @@ def test_q8_four_limbs_wide_activations(ei):
         assert (host(ei.gemm_q8(ei.pack_q8(dev(q), dev(s)), dev(x), 4)) == oracle.q8(q, s, x)).all()
 
 
+def _limb_bounds(L):
+    # balanced base-256: L digits in [-128, 127] reach [-128 (256^L - 1)/255, 127 (256^L - 1)/255]
+    m = (256 ** L - 1) // 255
+    return -128 * m, 127 * m
+
+
+@pytest.mark.parametrize("shape", [(40, 8192, 30, 3), (70, 4096, 17, 2), (33, 2048, 64, 4), (64, 1024, 5, 1),
+                                   (96, 2560, 48, 3), (7, 160, 63, 3)])
+def test_q8_skinny_split_k(ei, shape):
+    # few row tiles and a long K: the workgroups split the blocks and write
+    # per-limb partials that a second kernel combines; limbs 1 to 4, activations
+    # spanning each limb count's whole range
+    N, K, T, L = shape
+    r = np.random.default_rng(N + K + T + L)
+    q, s = synth.q8_codes(r, N, K), synth.q8_scales(r, N, K)
+    lo, hi = _limb_bounds(L)
+    x = r.integers(lo, hi + 1, size=(T, K)).astype(np.int64)
+    x[0, :4] = [lo, hi, 0, -1]
+    w = ei.pack_q8(dev(q), dev(s))
+    say("q8 skinny", shape, "workspace", ei.workspace_bytes(w, T, L))
+    assert (host(ei.gemm_q8(w, dev(x), L)) == oracle.q8(q, s, x)).all()
+
+
+def test_q4_skinny_split_k(ei):
+    N, K, T = 50, 4096, 12
+    r = np.random.default_rng(12)
+    nib, sme, x = synth.q4_codes_packed(r, N, K), synth.q4_scale_bytes(r, N, K), synth.i32_acts(r, T, K)
+    w = ei.pack_q4(dev(nib), dev(sme))
+    say("q4 skinny", (N, K, T))
+    assert (host(ei.gemm_q4(w, dev(x), 3)) == oracle.q4(nib, sme, x)).all()
+
+
 def test_q8_limb_range_is_flagged(ei):
     r = np.random.default_rng(7)
     q, s = synth.q8_codes(r, 32, 64), synth.q8_scales(r, 32, 64)
