@@ -16,10 +16,61 @@ namespace ei {
 
 constexpr int kMoeSortThreads = 1024;
 constexpr int64_t kMoeMaxPairs = 1 << 14;   // pair index field of the sort key
+constexpr int kMoePer = (int)(kMoeMaxPairs / kMoeSortThreads);   // keys per thread, at most
 
-// One workgroup: bitonic sort of the keys in LDS, then segment offsets and the
-// token-tile table.  Keys of pairs with an expert outside [0, E) become
-// E * 2^14 + p (they sort last and join no tile) and set EI_DEV_ROUTE.
+// Exclusive scans over the workgroup in thread order: a sum of packed
+// counters (four 16-bit fields; no field may exceed 65535 in total) and a
+// maximum.  wave_tot: LDS scratch of one word per wave.  Two barriers each.
+__device__ inline uint64_t block_exclusive_sum(uint64_t v, uint64_t* total, uint64_t* wave_tot) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint64_t inc = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint64_t u = __shfl_up(inc, d, 64);
+    if (lane >= d) inc += u;
+  }
+  if (lane == 63) wave_tot[wave] = inc;
+  __syncthreads();
+  uint64_t base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kMoeSortThreads / 64; ++w) {
+    base += w < wave ? wave_tot[w] : 0;
+    tot += wave_tot[w];
+  }
+  __syncthreads();
+  *total = tot;
+  return base + inc - v;
+}
+
+__device__ inline int64_t block_exclusive_max(int64_t v, uint64_t* wave_tot) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int64_t inc = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int64_t u = __shfl_up(inc, d, 64);
+    if (lane >= d && u > inc) inc = u;
+  }
+  int64_t ex = __shfl_up(inc, 1, 64);
+  if (lane == 0) ex = -1;
+  if (lane == 63) wave_tot[wave] = (uint64_t)inc;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kMoeSortThreads / 64; ++w)
+    if (w < wave && (int64_t)wave_tot[w] > ex) ex = (int64_t)wave_tot[w];
+  __syncthreads();
+  return ex;
+}
+
+// One workgroup: a stable LSD radix sort of the keys expert * 2^14 + p (two
+// bits of the expert field per pass), then segment offsets and the token-tile
+// table.  The input is in pair order, so the result is ordered by expert and,
+// within an expert, by pair index.  Keys of pairs with an expert outside
+// [0, E) become E * 2^14 + p (they sort last and join no tile) and set
+// EI_DEV_ROUTE.
+//
+// Each thread holds a contiguous run of `per` keys in registers; a pass
+// counts the run's digits, scans the counts over the workgroup and writes
+// every key to its place in its digit's region (a stable 4-way split).
 __global__ __launch_bounds__(kMoeSortThreads) void moe_sort_kernel(const int32_t* __restrict__ route, int64_t pairs,
                                                                   int64_t experts, int32_t* __restrict__ sorted_pair,
                                                                   int32_t* __restrict__ offsets,
@@ -27,40 +78,59 @@ __global__ __launch_bounds__(kMoeSortThreads) void moe_sort_kernel(const int32_t
                                                                   int32_t* __restrict__ tile_row0,
                                                                   int32_t* __restrict__ tile_rows,
                                                                   int32_t* __restrict__ ntiles, int32_t* status) {
-  extern __shared__ uint32_t keys[];   // n2 = next power of two >= pairs
+  extern __shared__ uint32_t keys[];   // per * 1024 keys; positions >= pairs hold all-ones sentinels
+  __shared__ uint64_t wave_tot[kMoeSortThreads / 64];
   const int tid = threadIdx.x;
-  int n2 = 1;
-  while (n2 < pairs) n2 <<= 1;
+  const int per = (int)((pairs + kMoeSortThreads - 1) / kMoeSortThreads);
+  const int r0 = tid * per;
+  uint32_t k[kMoePer];
   bool bad = false;
-  for (int i = tid; i < n2; i += kMoeSortThreads) {
-    if (i < pairs) {
+#pragma unroll
+  for (int u = 0; u < kMoePer; ++u) {
+    k[u] = 0xFFFFFFFFu;
+    const int i = r0 + u;
+    if (u < per && i < pairs) {
       int64_t e = route[i];
       if (e < 0 || e >= experts) {
         bad = true;
         e = experts;
       }
-      keys[i] = (uint32_t)(e << 14) | (uint32_t)i;
-    } else {
-      keys[i] = 0xFFFFFFFFu;
+      k[u] = (uint32_t)(e << 14) | (uint32_t)i;
     }
   }
   if (bad) flag(status, EI_DEV_ROUTE);
-  __syncthreads();
-  for (int size = 2; size <= n2; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < n2; i += kMoeSortThreads) {
-        const int j = i ^ stride;
-        if (j > i) {
-          const bool up = (i & size) == 0;
-          const uint32_t a = keys[i], b = keys[j];
-          if ((a > b) == up) {
-            keys[i] = b;
-            keys[j] = a;
-          }
-        }
+  int bits = 0;
+  while (((int64_t)1 << bits) <= experts) ++bits;   // expert fields 0 .. E
+  for (int bit = 0; bit < bits; bit += 2) {
+    const int sh = 14 + bit;
+    uint64_t c = 0;
+#pragma unroll
+    for (int u = 0; u < kMoePer; ++u)
+      if (u < per) c += (uint64_t)1 << (16 * ((k[u] >> sh) & 3u));
+    uint64_t tot;
+    const uint64_t pre = block_exclusive_sum(c, &tot, wave_tot);
+    const int t0 = (int)(tot & 0xFFFF), t1 = (int)((tot >> 16) & 0xFFFF), t2 = (int)((tot >> 32) & 0xFFFF);
+    int p0 = (int)(pre & 0xFFFF);
+    int p1 = t0 + (int)((pre >> 16) & 0xFFFF);
+    int p2 = t0 + t1 + (int)((pre >> 32) & 0xFFFF);
+    int p3 = t0 + t1 + t2 + (int)(pre >> 48);
+#pragma unroll
+    for (int u = 0; u < kMoePer; ++u) {
+      if (u < per) {
+        const uint32_t d = (k[u] >> sh) & 3u;
+        const int dst = d == 0 ? p0 : d == 1 ? p1 : d == 2 ? p2 : p3;
+        keys[dst] = k[u];
+        p0 += d == 0;
+        p1 += d == 1;
+        p2 += d == 2;
+        p3 += d == 3;
       }
-      __syncthreads();
     }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kMoePer; ++u)
+      if (u < per) k[u] = keys[r0 + u];
+    // the next pass rewrites keys only after its scan's barriers
   }
   // sorted pairs; offsets[e] = first sorted position whose expert is >= e
   for (int i = tid; i <= pairs; i += kMoeSortThreads) {
@@ -70,19 +140,38 @@ __global__ __launch_bounds__(kMoeSortThreads) void moe_sort_kernel(const int32_t
     const int64_t hi = ei < experts ? ei : experts;
     for (int64_t e = ep + 1; e <= hi; ++e) offsets[e] = i;
   }
-  __syncthreads();
-  if (tid == 0) {
-    int32_t j = 0;
-    for (int64_t e = 0; e < experts; ++e) {
-      const int32_t beg = offsets[e], cnt = offsets[e + 1] - beg;
-      for (int32_t s = 0; s < cnt; s += kTile, ++j) {
-        tile_expert[j] = (int32_t)e;
-        tile_row0[j] = beg + s;
-        tile_rows[j] = cnt - s < kTile ? cnt - s : kTile;
-      }
-    }
-    *ntiles = j;
+  // Token tiles: sorted position i opens a tile when its expert is valid and
+  // i minus the start of its expert's segment is a multiple of 32.  Segment
+  // starts come from a max-scan of the segment boundaries; tiles are numbered
+  // by a scan of the per-thread counts, so they come out in sorted order.
+  const int64_t i1 = r0 + per < pairs ? r0 + per : pairs;
+  auto expert_at = [&](int64_t i) { return (int64_t)(keys[i] >> 14); };
+  auto boundary = [&](int64_t i) { return i == 0 || expert_at(i) != expert_at(i - 1); };
+  int64_t last = -1;
+  for (int64_t i = r0; i < i1; ++i)
+    if (boundary(i)) last = i;
+  const int64_t carry = block_exclusive_max(last, wave_tot);
+  int64_t seg = carry;
+  int cnt = 0;
+  for (int64_t i = r0; i < i1; ++i) {
+    if (boundary(i)) seg = i;
+    cnt += expert_at(i) < experts && ((i - seg) & (kTile - 1)) == 0;
   }
+  uint64_t total;
+  int64_t j = (int64_t)block_exclusive_sum((uint64_t)cnt, &total, wave_tot);
+  seg = carry;
+  for (int64_t i = r0; i < i1; ++i) {
+    if (boundary(i)) seg = i;
+    const int64_t e = expert_at(i);
+    if (e >= experts || ((i - seg) & (kTile - 1)) != 0) continue;
+    int rows = 1;
+    while (rows < kTile && i + rows < pairs && expert_at(i + rows) == e) ++rows;
+    tile_expert[j] = (int32_t)e;
+    tile_row0[j] = (int32_t)i;
+    tile_rows[j] = rows;
+    ++j;
+  }
+  if (tid == 0) *ntiles = (int32_t)total;
 }
 
 // Limb tiles of the grouped activations: thread (tile j, block b, lane) takes
@@ -129,9 +218,9 @@ __global__ void grouped_limb_tiles_kernel(const int64_t* __restrict__ x, int64_t
 hipError_t launch_moe_sort(const int32_t* route, int64_t pairs, int64_t experts, int32_t* sorted_pair,
                            int32_t* offsets, int32_t* tile_expert, int32_t* tile_row0, int32_t* tile_rows,
                            int32_t* ntiles, int32_t* status, hipStream_t s) {
-  int64_t n2 = 1;
-  while (n2 < pairs) n2 <<= 1;
-  hipLaunchKernelGGL(moe_sort_kernel, dim3(1), dim3(kMoeSortThreads), (size_t)n2 * 4, s, route, pairs, experts,
+  const int64_t per = (pairs + kMoeSortThreads - 1) / kMoeSortThreads;
+  hipLaunchKernelGGL(moe_sort_kernel, dim3(1), dim3(kMoeSortThreads), (size_t)(per * kMoeSortThreads) * 4, s, route,
+                     pairs, experts,
                      sorted_pair, offsets, tile_expert, tile_row0, tile_rows, ntiles, status);
   return hipGetLastError();
 }

@@ -319,6 +319,23 @@ def test_q8_grouped_skewed_and_extreme(ei):
     assert (y == _grouped_reference(codes, scales, x, route)).all()
 
 
+@pytest.mark.parametrize("shape", [(100, 1500, 2, 32, 64), (1, 70, 3, 40, 32), (7, 8192, 2, 32, 32)])
+def test_q8_grouped_sort_sizes(ei, shape):
+    # pair counts that leave ragged per-thread runs in the grouping sort, up to
+    # the 2^14-pair maximum; a single expert; 100 experts (a non-power-of-two
+    # expert field); unsorted routes that may repeat an expert within a row
+    E, rows, topk, N, K = shape
+    r = np.random.default_rng(E + rows)
+    codes = np.stack([synth.q8_codes(r, N, K) for _ in range(E)])
+    scales = np.stack([synth.q8_scales(r, N, K) for _ in range(E)])
+    x = synth.q16_acts(r, rows, K)
+    route = (r.integers(0, E, (rows, topk)) ** 2 % E).astype(np.int32)   # skewed toward some experts
+    say("grouped sort sizes", shape)
+    w = ei.pack_q8_stacked(dev(codes), dev(scales))
+    y = host(ei.gemm_q8_grouped(w, dev(x), dev(route)))
+    assert (y == _grouped_reference(codes, scales, x, route)).all()
+
+
 def test_q8_grouped_bad_expert_is_flagged(ei):
     E, rows, topk, N, K = 3, 8, 2, 32, 64
     r = np.random.default_rng(22)
