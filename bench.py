@@ -178,21 +178,14 @@ def bench_olmoe(args, torch, np, ei, synth, dev) -> int:
     wg, wu, wd = (ei.pack_q8_stacked(stack(m, 0), stack(m, 1)) for m in range(3))
     x, route = synth.olmoe_x(), synth.olmoe_route()
     xd, rd = torch.from_numpy(x).to(dev), torch.from_numpy(route).to(dev)
-    rd1 = rd.reshape(-1, 1).contiguous()
     P = T * TOPK
-    g = torch.empty((P, I), dtype=torch.int64, device=dev)
-    u, h = torch.empty_like(g), torch.empty_like(g)
     out = torch.empty((P, H), dtype=torch.int64, device=dev)
-    ws_a = torch.empty(ei.grouped_workspace_bytes(wg, T, TOPK), dtype=torch.uint8, device=dev)
-    ws_b = torch.empty(ei.grouped_workspace_bytes(wd, P, 1), dtype=torch.uint8, device=dev)
+    ws = torch.empty(ei.moe_ffn_workspace_bytes(wg, wd, T, TOPK), dtype=torch.uint8, device=dev)
     lut = ei.silu_lut(dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
 
     def step():
-        ei.gemm_q8_grouped(wg, xd, rd, out=g, workspace=ws_a, status=status)
-        ei.gemm_q8_grouped(wu, xd, rd, out=u, workspace=ws_a, status=status)
-        ei.silu_mul(g, u, lut, out=h, status=status)
-        ei.gemm_q8_grouped(wd, h, rd1, out=out, workspace=ws_b, status=status)
+        ei.moe_ffn_q8(wg, wu, wd, xd, rd, lut, out=out, workspace=ws, status=status)
 
     ms, wall_ms = _time_graph(torch, step, args.steps, args.warmup)
     if int(status.item()) != 0:
@@ -234,27 +227,21 @@ def bench_qwen_ffn(args, torch, np, ei, synth, dev) -> int:
         layers.append((ei.pack_q8(t[0], t[1]), ei.pack_q8(t[2], t[3]), ei.pack_q8(t[4], t[5])))
     x0 = torch.from_numpy(synth.qwen_ffn_x0()).to(dev)
     T, D, F = synth.QWEN_T, synth.QWEN_D, synth.QWEN_F
-    x = torch.empty_like(x0)
-    g = torch.empty((T, F), dtype=torch.int64, device=dev)
-    u, h = torch.empty_like(g), torch.empty_like(g)
-    d = torch.empty((T, D), dtype=torch.int64, device=dev)
-    wsz = max(ei.workspace_bytes(layers[0][0], T), ei.workspace_bytes(layers[0][2], T), 1)
-    ws = torch.empty(wsz, dtype=torch.uint8, device=dev)
+    bufs = [torch.empty_like(x0), torch.empty_like(x0)]
+    ws = torch.empty(max(ei.ffn_workspace_bytes(layers[0][0], layers[0][2], T), 1), dtype=torch.uint8, device=dev)
     lut = ei.silu_lut(dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
 
-    def step():
-        x.copy_(x0)
-        for wg, wu, wd in layers:
-            ei.gemm_q8(wg, x, out=g, workspace=ws, status=status)
-            ei.gemm_q8(wu, x, out=u, workspace=ws, status=status)
-            ei.silu_mul(g, u, lut, out=h, status=status)
-            ei.gemm_q8(wd, h, out=d, workspace=ws, status=status)
-            x.add_(d)
+    def step():   # layer l reads x_l and writes x_{l+1}; the first reads x0
+        src = x0
+        for i, (wg, wu, wd) in enumerate(layers):
+            dst = bufs[i % 2]
+            ei.ffn_q8(wg, wu, wd, src, lut, out=dst, workspace=ws, status=status)
+            src = dst
 
     ms, wall_ms = _time_graph(torch, step, args.steps, args.warmup)
     gold = _json.load(open(os.path.join(ROOT, "tests", "golden", "oracle_digests.json")))["qwen05b_ffn"]["layers"]
-    ok = int(status.item()) == 0 and ei.digest(x) == gold[-1]["x_next"]
+    ok = int(status.item()) == 0 and ei.digest(bufs[(synth.QWEN_LAYERS - 1) % 2]) == gold[-1]["x_next"]
     wbytes = synth.QWEN_LAYERS * 3 * F * D * (1 + 4 / 32)
     gbs = wbytes / (ms * 1e-3) / 1e9
     print(json.dumps({

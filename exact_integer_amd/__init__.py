@@ -62,6 +62,10 @@ SIGNATURES = {
     "ei_q8_fp32_shadow": (I32, [P, P, P, P, I64, I64, I64, I32, U64, P]),
     "output_digest": (I32, [P, SZ, P, P]),
     "ei_sha256_host": (None, [P, SZ, P]),
+    "ei_ffn_workspace_bytes": (SZ, [WP, WP, I64]),
+    "int_ffn_q8": (I32, [WP, WP, WP, P, P, P, I64, P, SZ, P, P]),
+    "ei_moe_ffn_workspace_bytes": (SZ, [WP, WP, I64, I32]),
+    "int_moe_ffn_q8": (I32, [WP, WP, WP, P, P, I64, I32, P, P, P, SZ, P, P]),
     "ei_status_string": (ctypes.c_char_p, [I32]),
     "ei_version": (I32, []),
 }
@@ -199,6 +203,67 @@ def gemm_q8_grouped(w: PackedWeights, x: torch.Tensor, route: torch.Tensor, limb
                                      workspace.numel(), status.data_ptr(), s), "int_gemm_q8_grouped")
     if check:
         _raise_status(status, "int_gemm_q8_grouped")
+    return y
+
+
+def ffn_workspace_bytes(wg: PackedWeights, wd: PackedWeights, t: int) -> int:
+    return int(lib().ei_ffn_workspace_bytes(ctypes.byref(wg.desc), ctypes.byref(wd.desc), t))
+
+
+def ffn_q8(wg: PackedWeights, wu: PackedWeights, wd: PackedWeights, x: torch.Tensor, lut: torch.Tensor, out=None,
+           workspace=None, status=None) -> torch.Tensor:
+    """One FFN layer: y = x + Q8(wd, silu_mul(Q8(wg, x), Q8(wu, x))) (int64 [t][d])."""
+    s = _stream()
+    t, d = x.shape
+    if d != wg.k or wu.k != wg.k or wu.n != wg.n or wd.k != wg.n or wd.n != wg.k:
+        raise EIError("int_ffn_q8: shapes must be wg, wu [f][d], wd [d][f], x [t][d]")
+    px, pl = _dev(x, torch.int64, "x"), _dev(lut, torch.int32, "lut")
+    y = out if out is not None else torch.empty((t, d), dtype=torch.int64, device=x.device)
+    py = _dev(y, torch.int64, "y")
+    if tuple(y.shape) != (t, d):
+        raise EIError(f"int_ffn_q8: y must be [{t}][{d}]")
+    if workspace is None:
+        workspace = torch.empty(max(ffn_workspace_bytes(wg, wd, t), 1), dtype=torch.uint8, device=x.device)
+    check = status is None
+    if check:
+        status = torch.zeros(1, dtype=torch.int32, device=x.device)
+    _check(lib().int_ffn_q8(ctypes.byref(wg.desc), ctypes.byref(wu.desc), ctypes.byref(wd.desc), px, pl, py, t,
+                            workspace.data_ptr(), workspace.numel(), status.data_ptr(), s), "int_ffn_q8")
+    if check:
+        _raise_status(status, "int_ffn_q8")
+    return y
+
+
+def moe_ffn_workspace_bytes(wg: PackedWeights, wd: PackedWeights, rows: int, topk: int) -> int:
+    return int(lib().ei_moe_ffn_workspace_bytes(ctypes.byref(wg.desc), ctypes.byref(wd.desc), rows, topk))
+
+
+def moe_ffn_q8(wg: PackedWeights, wu: PackedWeights, wd: PackedWeights, x: torch.Tensor, route: torch.Tensor,
+               lut: torch.Tensor, out=None, workspace=None, status=None) -> torch.Tensor:
+    """Routed FFN: y[r*topk + s] = expert route[r][s]'s gated MLP on x[r] (int64 [rows*topk][d])."""
+    s = _stream()
+    rows, d = x.shape
+    if d != wg.k or wu.k != wg.k or wu.n != wg.n or wd.k != wg.n or wd.n != wg.k:
+        raise EIError("int_moe_ffn_q8: shapes must be wg, wu [E][f][d], wd [E][d][f], x [rows][d]")
+    if route.dim() != 2 or route.shape[0] != rows:
+        raise EIError("int_moe_ffn_q8: route must be [rows][topk]")
+    topk = route.shape[1]
+    px, pr, pl = _dev(x, torch.int64, "x"), _dev(route, torch.int32, "route"), _dev(lut, torch.int32, "lut")
+    y = out if out is not None else torch.empty((rows * topk, d), dtype=torch.int64, device=x.device)
+    py = _dev(y, torch.int64, "y")
+    if tuple(y.shape) != (rows * topk, d):
+        raise EIError(f"int_moe_ffn_q8: y must be [{rows * topk}][{d}]")
+    if workspace is None:
+        workspace = torch.empty(max(moe_ffn_workspace_bytes(wg, wd, rows, topk), 1), dtype=torch.uint8,
+                                device=x.device)
+    check = status is None
+    if check:
+        status = torch.zeros(1, dtype=torch.int32, device=x.device)
+    _check(lib().int_moe_ffn_q8(ctypes.byref(wg.desc), ctypes.byref(wu.desc), ctypes.byref(wd.desc), px, pr, rows,
+                                topk, pl, py, workspace.data_ptr(), workspace.numel(), status.data_ptr(), s),
+           "int_moe_ffn_q8")
+    if check:
+        _raise_status(status, "int_moe_ffn_q8")
     return y
 
 

@@ -90,8 +90,12 @@ int check_weights(const ei_weights* w, int format) {
   return EI_OK;
 }
 
+// y = projection of x (+ resid when resid is not null: the skinny kernel and
+// the partial combiner add it as they write y, other paths in a pass of
+// their own).
 int run_gemm(const ei_weights* w, const void* x, int x_is_i32, int64_t* y, int64_t t, int limbs, int schedule,
-             uint64_t seed, void* ws, size_t ws_bytes, int32_t* status, hipStream_t s, int out_mode) {
+             uint64_t seed, void* ws, size_t ws_bytes, int32_t* status, hipStream_t s, int out_mode,
+             const int64_t* resid = nullptr) {
   if (!x || !y || t < 1) return EI_EINVAL;
   if (limbs < 1 || limbs > 8) return EI_EINVAL;
   if (limbs > kMaxLimbs) return EI_ERANGE;
@@ -142,13 +146,14 @@ int run_gemm(const ei_weights* w, const void* x, int x_is_i32, int64_t* y, int64
           a.out_mode = OUT_PARTIAL;
           e = launch_gemm_skinny(a, limbs, lay.splits, s);
           if (e == hipSuccess)
-            e = launch_combine_partials(part, lay.splits, y, t, w->n, limbs, out_mode, status, s);
+            e = launch_combine_partials(part, lay.splits, y, t, w->n, limbs, out_mode, resid, status, s);
         } else {
+          a.resid = resid;
           e = launch_gemm_skinny(a, limbs, 1, s);
         }
-      } else {
-        e = launch(a);
+        return e == hipSuccess ? EI_OK : EI_EDEVICE;
       }
+      e = launch(a);
       break;
     case EI_SCHED_REVERSED:
       a.order = ORDER_DESC;
@@ -175,8 +180,8 @@ int run_gemm(const ei_weights* w, const void* x, int x_is_i32, int64_t* y, int64
         a.part_index = p;
         e = launch(a);
       }
-      if (e == hipSuccess) e = launch_combine_partials(part, kSplitParts, y, t, w->n, limbs, out_mode, status, s);
-      break;
+      if (e == hipSuccess) e = launch_combine_partials(part, kSplitParts, y, t, w->n, limbs, out_mode, resid, status, s);
+      return e == hipSuccess ? EI_OK : EI_EDEVICE;
     }
     case EI_SCHED_TREE: {
       int64_t* terms = reinterpret_cast<int64_t*>(wsb + lay.part_off);
@@ -187,6 +192,7 @@ int run_gemm(const ei_weights* w, const void* x, int x_is_i32, int64_t* y, int64
       break;
     }
   }
+  if (e == hipSuccess && resid) e = launch_add_residual(y, resid, t * w->n, status, s);
   return e == hipSuccess ? EI_OK : EI_EDEVICE;
 }
 
@@ -240,6 +246,120 @@ GroupedLayout grouped_layout(const ei_weights* w, int64_t rows, int topk, int li
   g.limb_off = take((size_t)limbs * (size_t)g.tiles_max * (size_t)w->k * kTile);
   g.total = off;
   return g;
+}
+
+int grouped_check(const ei_weights* w, int64_t rows, int topk, int limbs) {
+  const int c = check_weights(w, EI_FORMAT_Q8);
+  if (c != EI_OK) return c;
+  if (rows < 1 || topk < 1 || w->experts < 1) return EI_EINVAL;
+  if (limbs != 3) return limbs < 1 || limbs > 8 ? EI_EINVAL : EI_ERANGE;
+  if (rows * topk > ((int64_t)1 << 14) || w->experts > ((int64_t)1 << 17)) return EI_ERANGE;
+  if (w->n_pad * w->k >= ((int64_t)1 << 32)) return EI_ERANGE;
+  const int64_t tiles_max = grouped_layout(w, rows, topk, limbs).tiles_max;
+  if (3 * tiles_max * w->k * kTile >= ((int64_t)1 << 32)) return EI_ERANGE;
+  return EI_OK;
+}
+
+// Pointers into a grouped workspace laid out by grouped_layout.
+struct Grouping {
+  int32_t *sorted, *offs, *texp, *trow0, *trows, *ntiles;
+  int8_t* limb;
+};
+
+Grouping grouping_at(void* workspace, const GroupedLayout& g) {
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  Grouping p;
+  p.sorted = reinterpret_cast<int32_t*>(ws + g.sorted_off);
+  p.offs = reinterpret_cast<int32_t*>(ws + g.offsets_off);
+  p.texp = reinterpret_cast<int32_t*>(ws + g.texp_off);
+  p.trow0 = reinterpret_cast<int32_t*>(ws + g.trow0_off);
+  p.trows = reinterpret_cast<int32_t*>(ws + g.trows_off);
+  p.ntiles = reinterpret_cast<int32_t*>(ws + g.ntiles_off);
+  p.limb = reinterpret_cast<int8_t*>(ws + g.limb_off);
+  return p;
+}
+
+// The grouped projection of w over the limb tiles in p (already gathered for
+// the sorted pairs): y[pair][n].
+hipError_t launch_grouped_projection(const ei_weights* w, const GroupedLayout& g, const Grouping& p, int64_t* y,
+                                     int32_t* status, hipStream_t s) {
+  GemmArgs a;
+  std::memset(&a, 0, sizeof a);
+  const uint8_t* base = static_cast<const uint8_t*>(w->packed);
+  a.codes = reinterpret_cast<const int8_t*>(base + kHeaderBytes);
+  a.scales = reinterpret_cast<const int32_t*>(base + kHeaderBytes + w->n_pad * w->k);
+  a.limb_tiles = p.limb;
+  a.y = y;
+  a.status = status;
+  a.n = w->n;
+  a.k = w->k;
+  a.t = g.pairs;
+  a.n_pad = w->n_pad;
+  a.t_pad = g.tiles_max * kTile;
+  a.nb = w->nb;
+  a.b0 = 0;
+  a.b1 = w->nb;
+  a.out_mode = OUT_ROUND_Q24;
+  a.order = ORDER_ASC;
+  a.tile_expert = p.texp;
+  a.tile_row0 = p.trow0;
+  a.tile_rows = p.trows;
+  a.sorted_pair = p.sorted;
+  a.ntiles = p.ntiles;
+  a.tiles_max = g.tiles_max;
+  a.expert_stride = w->expert_stride;
+  return launch_gemm_grouped(a, s);
+}
+
+// FFN workspace: h [t][f], then g and u [t][f] unless the gate and up
+// projections run fused, then the projections' own workspace.
+struct FfnLayout {
+  bool fused;
+  size_t h_off, g_off, u_off, gemm_off, total;
+};
+
+FfnLayout ffn_layout(const ei_weights* wg, const ei_weights* wd, int64_t t) {
+  FfnLayout f;
+  const WsLayout lg = layout_for(wg, t, 3, EI_SCHED_DEFAULT), ld = layout_for(wd, t, 3, EI_SCHED_DEFAULT);
+  f.fused = lg.path == PATH_SKINNY && lg.splits == 1;
+  const size_t hb = align_up(sizeof(int64_t) * (size_t)t * (size_t)wg->n);
+  f.h_off = 0;
+  f.g_off = f.u_off = hb;
+  size_t off = hb;
+  if (!f.fused) {
+    f.u_off = off + hb;
+    off += 2 * hb;
+  }
+  f.gemm_off = off;
+  f.total = off + (lg.total > ld.total ? lg.total : ld.total);
+  return f;
+}
+
+int ffn_check(const ei_weights* wg, const ei_weights* wu, const ei_weights* wd) {
+  int c = check_weights(wg, EI_FORMAT_Q8);
+  if (c == EI_OK) c = check_weights(wu, EI_FORMAT_Q8);
+  if (c == EI_OK) c = check_weights(wd, EI_FORMAT_Q8);
+  if (c != EI_OK) return c;
+  if (wu->n != wg->n || wu->k != wg->k || wd->k != wg->n || wd->n != wg->k) return EI_EINVAL;
+  return EI_OK;
+}
+
+// Routed FFN workspace: one grouping (its limb area sized for the wider of
+// the two inputs), then g, u and h [pairs][f].
+struct MoeLayout {
+  GroupedLayout g;
+  size_t g_off, u_off, h_off, total;
+};
+
+MoeLayout moe_layout(const ei_weights* wg, const ei_weights* wd, int64_t rows, int topk) {
+  MoeLayout m;
+  m.g = grouped_layout(wd->k > wg->k ? wd : wg, rows, topk, 3);
+  const size_t hb = align_up(sizeof(int64_t) * (size_t)m.g.pairs * (size_t)wg->n);
+  m.g_off = m.g.total;
+  m.u_off = m.g_off + hb;
+  m.h_off = m.u_off + hb;
+  m.total = m.h_off + hb;
+  return m;
 }
 
 }  // namespace
@@ -296,57 +416,116 @@ size_t ei_grouped_workspace_bytes(const ei_weights* w, int64_t rows, int topk, i
 int int_gemm_q8_grouped(const ei_weights* w, const int64_t* x, const int32_t* route, int64_t rows, int topk,
                         int64_t* y, int limbs, void* workspace, size_t workspace_bytes, int32_t* d_status,
                         ei_stream stream) {
-  const int c = check_weights(w, EI_FORMAT_Q8);
+  if (!x || !route || !y) return EI_EINVAL;
+  const int c = grouped_check(w, rows, topk, limbs);
   if (c != EI_OK) return c;
-  if (!x || !route || !y || rows < 1 || topk < 1 || w->experts < 1) return EI_EINVAL;
-  if (limbs != 3) return limbs < 1 || limbs > 8 ? EI_EINVAL : EI_ERANGE;
-  if (rows * topk > ((int64_t)1 << 14) || w->experts > ((int64_t)1 << 17)) return EI_ERANGE;
-  if (w->n_pad * w->k >= ((int64_t)1 << 32)) return EI_ERANGE;
   const GroupedLayout g = grouped_layout(w, rows, topk, limbs);
-  if (3 * g.tiles_max * w->k * kTile >= ((int64_t)1 << 32)) return EI_ERANGE;
   if (!workspace || workspace_bytes < g.total) return EI_ENOSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const Grouping p = grouping_at(workspace, g);
+  hipError_t e = launch_moe_sort(route, g.pairs, w->experts, p.sorted, p.offs, p.texp, p.trow0, p.trows, p.ntiles,
+                                 d_status, s);
+  if (e == hipSuccess)
+    e = launch_grouped_limb_tiles(x, w->k, topk, p.sorted, p.trow0, p.trows, p.ntiles, g.tiles_max, p.limb, d_status,
+                                  s);
+  if (e == hipSuccess) e = launch_grouped_projection(w, g, p, y, d_status, s);
+  return e == hipSuccess ? EI_OK : EI_EDEVICE;
+}
+
+size_t ei_ffn_workspace_bytes(const ei_weights* wg, const ei_weights* wd, int64_t t) {
+  if (!wg || !wd || t < 1) return 0;
+  return ffn_layout(wg, wd, t).total;
+}
+
+int int_ffn_q8(const ei_weights* wg, const ei_weights* wu, const ei_weights* wd, const int64_t* x,
+               const int32_t* lut, int64_t* y, int64_t t, void* workspace, size_t workspace_bytes,
+               int32_t* d_status, ei_stream stream) {
+  if (!x || !lut || !y || t < 1) return EI_EINVAL;
+  const int c = ffn_check(wg, wu, wd);
+  if (c != EI_OK) return c;
+  const FfnLayout f = ffn_layout(wg, wd, t);
+  if (!workspace || workspace_bytes < f.total) return EI_ENOSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  int32_t* sorted = reinterpret_cast<int32_t*>(ws + g.sorted_off);
-  int32_t* offs = reinterpret_cast<int32_t*>(ws + g.offsets_off);
-  int32_t* texp = reinterpret_cast<int32_t*>(ws + g.texp_off);
-  int32_t* trow0 = reinterpret_cast<int32_t*>(ws + g.trow0_off);
-  int32_t* trows = reinterpret_cast<int32_t*>(ws + g.trows_off);
-  int32_t* ntiles = reinterpret_cast<int32_t*>(ws + g.ntiles_off);
-  int8_t* limb = reinterpret_cast<int8_t*>(ws + g.limb_off);
-  if (launch_moe_sort(route, g.pairs, w->experts, sorted, offs, texp, trow0, trows, ntiles, d_status, s) !=
-      hipSuccess)
-    return EI_EDEVICE;
-  if (launch_grouped_limb_tiles(x, w->k, topk, sorted, trow0, trows, ntiles, g.tiles_max, limb, d_status, s) !=
-      hipSuccess)
-    return EI_EDEVICE;
-  GemmArgs a;
-  std::memset(&a, 0, sizeof a);
-  const uint8_t* base = static_cast<const uint8_t*>(w->packed);
-  a.codes = reinterpret_cast<const int8_t*>(base + kHeaderBytes);
-  a.scales = reinterpret_cast<const int32_t*>(base + kHeaderBytes + w->n_pad * w->k);
-  a.x = x;
-  a.limb_tiles = limb;
-  a.y = y;
-  a.status = d_status;
-  a.n = w->n;
-  a.k = w->k;
-  a.t = g.pairs;
-  a.n_pad = w->n_pad;
-  a.t_pad = g.tiles_max * kTile;
-  a.nb = w->nb;
-  a.b0 = 0;
-  a.b1 = w->nb;
-  a.out_mode = OUT_ROUND_Q24;
-  a.order = ORDER_ASC;
-  a.tile_expert = texp;
-  a.tile_row0 = trow0;
-  a.tile_rows = trows;
-  a.sorted_pair = sorted;
-  a.ntiles = ntiles;
-  a.tiles_max = g.tiles_max;
-  a.expert_stride = w->expert_stride;
-  return launch_gemm_grouped(a, s) == hipSuccess ? EI_OK : EI_EDEVICE;
+  int64_t* h = reinterpret_cast<int64_t*>(ws + f.h_off);
+  void* gws = ws + f.gemm_off;
+  const size_t gws_bytes = workspace_bytes - f.gemm_off;
+  if (f.fused) {
+    // gate and up in one pass, the SiLU-gated product in its epilogue
+    const WsLayout lay = layout_for(wg, t, 3, EI_SCHED_DEFAULT);
+    int8_t* limb = static_cast<int8_t*>(gws) + lay.limb_off;
+    if (launch_limb_tiles(x, 0, t, wg->k, 3, limb, lay.t_pad, d_status, s) != hipSuccess) return EI_EDEVICE;
+    GemmArgs a;
+    std::memset(&a, 0, sizeof a);
+    const uint8_t* bg = static_cast<const uint8_t*>(wg->packed);
+    const uint8_t* bu = static_cast<const uint8_t*>(wu->packed);
+    a.codes = reinterpret_cast<const int8_t*>(bg + kHeaderBytes);
+    a.scales = reinterpret_cast<const int32_t*>(bg + kHeaderBytes + wg->n_pad * wg->k);
+    a.codes2 = reinterpret_cast<const int8_t*>(bu + kHeaderBytes);
+    a.scales2 = reinterpret_cast<const int32_t*>(bu + kHeaderBytes + wu->n_pad * wu->k);
+    a.lut = lut;
+    a.limb_tiles = limb;
+    a.y = h;
+    a.status = d_status;
+    a.n = wg->n;
+    a.k = wg->k;
+    a.t = t;
+    a.n_pad = wg->n_pad;
+    a.t_pad = lay.t_pad;
+    a.nb = wg->nb;
+    a.b0 = 0;
+    a.b1 = wg->nb;
+    a.out_mode = OUT_ROUND_Q24;
+    if (launch_gemm_skinny_gateup(a, s) != hipSuccess) return EI_EDEVICE;
+  } else {
+    int64_t* g = reinterpret_cast<int64_t*>(ws + f.g_off);
+    int64_t* u = reinterpret_cast<int64_t*>(ws + f.u_off);
+    int r = run_gemm(wg, x, 0, g, t, 3, EI_SCHED_DEFAULT, 0, gws, gws_bytes, d_status, s, OUT_ROUND_Q24);
+    if (r == EI_OK) r = run_gemm(wu, x, 0, u, t, 3, EI_SCHED_DEFAULT, 0, gws, gws_bytes, d_status, s, OUT_ROUND_Q24);
+    if (r != EI_OK) return r;
+    if (launch_silu_mul(g, u, lut, h, t * wg->n, d_status, s) != hipSuccess) return EI_EDEVICE;
+  }
+  return run_gemm(wd, h, 0, y, t, 3, EI_SCHED_DEFAULT, 0, gws, gws_bytes, d_status, s, OUT_ROUND_Q24, x);
+}
+
+size_t ei_moe_ffn_workspace_bytes(const ei_weights* wg, const ei_weights* wd, int64_t rows, int topk) {
+  if (!wg || !wd || rows < 1 || topk < 1) return 0;
+  return moe_layout(wg, wd, rows, topk).total;
+}
+
+int int_moe_ffn_q8(const ei_weights* wg, const ei_weights* wu, const ei_weights* wd, const int64_t* x,
+                   const int32_t* route, int64_t rows, int topk, const int32_t* lut, int64_t* y, void* workspace,
+                   size_t workspace_bytes, int32_t* d_status, ei_stream stream) {
+  if (!x || !route || !lut || !y) return EI_EINVAL;
+  int c = ffn_check(wg, wu, wd);
+  if (c == EI_OK) c = grouped_check(wg, rows, topk, 3);
+  if (c == EI_OK) c = grouped_check(wd, rows * topk, 1, 3);
+  if (c != EI_OK) return c;
+  if (wu->experts != wg->experts || wd->experts != wg->experts) return EI_EINVAL;
+  const MoeLayout m = moe_layout(wg, wd, rows, topk);
+  if (!workspace || workspace_bytes < m.total) return EI_ENOSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const Grouping p = grouping_at(workspace, m.g);
+  int64_t* g = reinterpret_cast<int64_t*>(ws + m.g_off);
+  int64_t* u = reinterpret_cast<int64_t*>(ws + m.u_off);
+  int64_t* h = reinterpret_cast<int64_t*>(ws + m.h_off);
+  const int64_t pairs = m.g.pairs;
+  // one grouping serves all three projections: pair p of the down projection
+  // is row p of h, in the same sorted order
+  hipError_t e = launch_moe_sort(route, pairs, wg->experts, p.sorted, p.offs, p.texp, p.trow0, p.trows, p.ntiles,
+                                 d_status, s);
+  if (e == hipSuccess)
+    e = launch_grouped_limb_tiles(x, wg->k, topk, p.sorted, p.trow0, p.trows, p.ntiles, m.g.tiles_max, p.limb,
+                                  d_status, s);
+  if (e == hipSuccess) e = launch_grouped_projection(wg, m.g, p, g, d_status, s);
+  if (e == hipSuccess) e = launch_grouped_projection(wu, m.g, p, u, d_status, s);
+  if (e == hipSuccess) e = launch_silu_mul(g, u, lut, h, pairs * wg->n, d_status, s);
+  if (e == hipSuccess)
+    e = launch_grouped_limb_tiles(h, wd->k, 1, p.sorted, p.trow0, p.trows, p.ntiles, m.g.tiles_max, p.limb,
+                                  d_status, s);
+  if (e == hipSuccess) e = launch_grouped_projection(wd, m.g, p, y, d_status, s);
+  return e == hipSuccess ? EI_OK : EI_EDEVICE;
 }
 
 int ei_limb_split(const int64_t* x, int8_t* d, int64_t n, int limbs, int32_t* d_status, ei_stream stream) {
@@ -429,6 +608,6 @@ const char* ei_status_string(int code) {
   }
 }
 
-int ei_version(void) { return 101; }
+int ei_version(void) { return 102; }
 
 }  // extern "C"

@@ -77,6 +77,13 @@ struct GemmArgs {
   const int32_t* ntiles;     // device: tiles in use (<= tiles_max)
   int64_t tiles_max;
   int64_t expert_stride;     // bytes between the packed images of two experts
+  // fused FFN launches: a second weight matrix of the same shape (the up
+  // projection) whose result meets the first's in the SiLU-gated product,
+  // and a residual added to the final output (y = resid + result)
+  const int8_t* codes2;
+  const int32_t* scales2;
+  const int32_t* lut;
+  const int64_t* resid;
 };
 
 // pos-th block visited by a kernel in the block range [b0, b1) of `a`.
@@ -108,7 +115,9 @@ hipError_t launch_grouped_limb_tiles(const int64_t* x, int64_t k, int topk, cons
                                      const int32_t* tile_row0, const int32_t* tile_rows, const int32_t* ntiles,
                                      int64_t tiles_max, int8_t* tiles, int32_t* status, hipStream_t s);
 hipError_t launch_combine_partials(const int64_t* part, int nparts, int64_t* y, int64_t t, int64_t n,
-                                   int limbs, int out_mode, int32_t* status, hipStream_t s);
+                                   int limbs, int out_mode, const int64_t* resid, int32_t* status, hipStream_t s);
+hipError_t launch_add_residual(int64_t* y, const int64_t* resid, int64_t n, int32_t* status, hipStream_t s);
+hipError_t launch_gemm_skinny_gateup(const GemmArgs& a, hipStream_t s);   // 3 limbs, one split
 hipError_t launch_tree_terms(int64_t* terms, int64_t nb, int64_t* y, int64_t t, int64_t n,
                              int limbs, int out_mode, int32_t* status, hipStream_t s);
 hipError_t launch_make_perm(int32_t* perm, int64_t n, uint64_t seed, hipStream_t s);
@@ -170,6 +179,24 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t by
 
 __device__ inline void flag(int32_t* status, int bits) {
   if (status) atomicOr(status, bits);
+}
+
+// v as int64, or false if it does not fit.
+__device__ inline bool fit_i64(__int128 v, int64_t* out) {
+  const __int128 lo = -((__int128)1 << 63), hi = ((__int128)1 << 63) - 1;
+  if (v < lo || v > hi) { *out = 0; return false; }
+  *out = (int64_t)v;
+  return true;
+}
+
+// SiLU-gated product: h = floor(lut[clamp(floor((g + 16) / 32), -32768,
+// 32768) + 32768] * u / 2^16); false if h does not fit int64.
+__device__ inline bool silu_gate(int64_t g, int64_t u, const int32_t* __restrict__ lut, int64_t* h) {
+  // floor((g + 16) / 32) without overflowing at the int64 ends
+  int64_t idx = (g >> 5) + ((g & 31) >= 16 ? 1 : 0);
+  idx = idx < -32768 ? -32768 : (idx > 32768 ? 32768 : idx);
+  const __int128 p = (__int128)lut[idx + 32768] * (__int128)u;
+  return fit_i64(p >> 16, h);   // arithmetic shift: floor
 }
 
 }  // namespace ei

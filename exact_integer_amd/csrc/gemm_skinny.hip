@@ -27,17 +27,24 @@ struct SkinnyBatch {
   v4i d[D][L];
 };
 
-template <int L, int W, int D>
-__global__ __launch_bounds__(64 * W) void gemm_skinny_kernel(GemmArgs a) {
-  __shared__ int64_t red[(W - 1) * 16 * 64];
+// G = 1: one projection; y = result, or resid + result, or per-limb partials.
+// G = 2: the gate (codes, scales) and up (codes2, scales2) projections of an
+// FFN layer, W waves each, meet in the epilogue: y = h, the SiLU-gated
+// product of the two rounded results (one workgroup split only).
+template <int L, int W, int D, int G>
+__global__ __launch_bounds__(64 * W * G) void gemm_skinny_kernel(GemmArgs a) {
+  __shared__ int64_t red[G][(W - 1) * 16 * 64];
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int m = wave_all / W, wave = wave_all % W;   // matrix, wave within it
   const int64_t rg = blockIdx.x, part = blockIdx.y, ks = gridDim.y, tg = blockIdx.z;
   const int64_t tgs = a.t_pad / kTile;
   const int64_t g0 = part * a.nb / ks, g1 = (part + 1) * a.nb / ks;
   const int64_t w0 = g0 + wave * (g1 - g0) / W, w1 = g0 + (wave + 1) * (g1 - g0) / W;
-  const v4i* cbase = reinterpret_cast<const v4i*>(a.codes) + rg * a.nb * 64 + lane;
-  const int32_t* sbase = a.scales + rg * a.nb * 32 + (lane & 31);
+  const int8_t* codes = G == 2 && m == 1 ? a.codes2 : a.codes;
+  const int32_t* scales = G == 2 && m == 1 ? a.scales2 : a.scales;
+  const v4i* cbase = reinterpret_cast<const v4i*>(codes) + rg * a.nb * 64 + lane;
+  const int32_t* sbase = scales + rg * a.nb * 32 + (lane & 31);
   const v4i* lbase = reinterpret_cast<const v4i*>(a.limb_tiles) + tg * a.nb * 64 + lane;
   const int64_t lstride = tgs * a.nb * 64;   // between limbs
 
@@ -81,25 +88,62 @@ __global__ __launch_bounds__(64 * W) void gemm_skinny_kernel(GemmArgs a) {
     }
   }
 
-  // waves 1 .. W-1 hand their sums to wave 0, one limb at a time
+  // waves 1 .. W-1 of each matrix hand their sums to its wave 0, one limb at
+  // a time
 #pragma unroll
   for (int l = 0; l < L; ++l) {
     if (wave > 0) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) red[((wave - 1) * 16 + r) * 64 + lane] = acc[l][r];
+      for (int r = 0; r < 16; ++r) red[m][((wave - 1) * 16 + r) * 64 + lane] = acc[l][r];
     }
     __syncthreads();
     if (wave == 0) {
       for (int w = 1; w < W; ++w)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[l][r] += red[((w - 1) * 16 + r) * 64 + lane];
+        for (int r = 0; r < 16; ++r) acc[l][r] += red[m][((w - 1) * 16 + r) * 64 + lane];
     }
     __syncthreads();
   }
-  if (wave != 0) return;
 
   // D[m = token][n = row]: row lane % 32, token 8(r/4) + 4(lane/32) + r%4
   const int64_t row = rg * kTile + (lane & 31);
+  auto rounded = [&](int r, int64_t* out) {
+    __int128 v = 0;
+#pragma unroll
+    for (int l = 0; l < L; ++l) v += (__int128)acc[l][r] << (8 * l);
+    return finish_output(v, a.out_mode, out);
+  };
+  if constexpr (G == 2) {
+    // the up projection's wave 0 leaves its rounded results in LDS for the
+    // gate's (the same lanes hold the same outputs)
+    bool ok = true;
+    if (m == 1 && wave == 0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        int64_t u;
+        ok = rounded(r, &u) && ok;
+        red[0][r * 64 + lane] = u;
+      }
+    }
+    __syncthreads();
+    if (m == 1 || wave != 0) {
+      if (m == 1 && wave == 0 && !ok && row < a.n) flag(a.status, EI_DEV_OUT_RANGE);
+      return;
+    }
+    if (row >= a.n) return;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t tok = tg * kTile + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      if (tok >= a.t) continue;
+      int64_t g, h;
+      bool good = rounded(r, &g);
+      good = silu_gate(g, red[0][r * 64 + lane], a.lut, &h) && good;
+      if (!good) flag(a.status, EI_DEV_OUT_RANGE);
+      a.y[tok * a.n + row] = h;
+    }
+    return;
+  }
+  if (wave != 0) return;
   if (row >= a.n) return;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -109,11 +153,10 @@ __global__ __launch_bounds__(64 * W) void gemm_skinny_kernel(GemmArgs a) {
 #pragma unroll
       for (int l = 0; l < L; ++l) a.part[((part * L + l) * a.t + tok) * a.n + row] = acc[l][r];
     } else {
-      __int128 v = 0;
-#pragma unroll
-      for (int l = 0; l < L; ++l) v += (__int128)acc[l][r] << (8 * l);
       int64_t out;
-      if (!finish_output(v, a.out_mode, &out)) flag(a.status, EI_DEV_OUT_RANGE);
+      bool ok = rounded(r, &out);
+      if (a.resid) ok = fit_i64((__int128)a.resid[tok * a.n + row] + out, &out) && ok;
+      if (!ok) flag(a.status, EI_DEV_OUT_RANGE);
       a.y[tok * a.n + row] = out;
     }
   }
@@ -135,11 +178,18 @@ hipError_t launch_gemm_skinny(const GemmArgs& a, int limbs, int splits, hipStrea
   const dim3 grid((unsigned)(a.n_pad / kTile), (unsigned)splits, (unsigned)(a.t_pad / kTile));
   const dim3 block(64 * kSkinnyWaves);
   switch (limbs) {
-    case 1: hipLaunchKernelGGL((gemm_skinny_kernel<1, kSkinnyWaves, kSkinnyDepth>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((gemm_skinny_kernel<2, kSkinnyWaves, kSkinnyDepth>), grid, block, 0, s, a); break;
-    case 3: hipLaunchKernelGGL((gemm_skinny_kernel<3, kSkinnyWaves, kSkinnyDepth>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((gemm_skinny_kernel<4, kSkinnyWaves, kSkinnyDepth>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((gemm_skinny_kernel<1, kSkinnyWaves, kSkinnyDepth, 1>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((gemm_skinny_kernel<2, kSkinnyWaves, kSkinnyDepth, 1>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((gemm_skinny_kernel<3, kSkinnyWaves, kSkinnyDepth, 1>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((gemm_skinny_kernel<4, kSkinnyWaves, kSkinnyDepth, 1>), grid, block, 0, s, a); break;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_skinny_gateup(const GemmArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)(a.n_pad / kTile), 1, (unsigned)(a.t_pad / kTile));
+  hipLaunchKernelGGL((gemm_skinny_kernel<3, kSkinnyWaves, kSkinnyDepth, 2>), grid, dim3(64 * kSkinnyWaves * 2), 0, s,
+                     a);
   return hipGetLastError();
 }
 

@@ -8,9 +8,11 @@
 namespace ei {
 
 // y[t][i] from per-limb partials part[p][l][t][i], p summed from the last
-// partial down to the first; each partial sum is exact in int64.
+// partial down to the first; each partial sum is exact in int64.  With resid,
+// y = resid + (that result), checked to fit int64.
 __global__ void combine_partials_kernel(const int64_t* __restrict__ part, int nparts, int64_t* __restrict__ y,
-                                        int64_t t, int64_t n, int limbs, int out_mode, int32_t* status) {
+                                        int64_t t, int64_t n, int limbs, int out_mode,
+                                        const int64_t* __restrict__ resid, int32_t* status) {
   int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= t * n) return;
   __int128 v = 0;
@@ -20,7 +22,19 @@ __global__ void combine_partials_kernel(const int64_t* __restrict__ part, int np
     v += (__int128)s << (8 * l);
   }
   int64_t out;
-  if (!finish_output(v, out_mode, &out)) flag(status, EI_DEV_OUT_RANGE);
+  bool ok = finish_output(v, out_mode, &out);
+  if (resid) ok = fit_i64((__int128)resid[e] + out, &out) && ok;
+  if (!ok) flag(status, EI_DEV_OUT_RANGE);
+  y[e] = out;
+}
+
+// y += resid, checked to fit int64.
+__global__ void add_residual_kernel(int64_t* __restrict__ y, const int64_t* __restrict__ resid, int64_t n,
+                                    int32_t* status) {
+  int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= n) return;
+  int64_t out;
+  if (!fit_i64((__int128)y[e] + resid[e], &out)) flag(status, EI_DEV_OUT_RANGE);
   y[e] = out;
 }
 
@@ -69,10 +83,16 @@ __global__ void make_perm_kernel(int32_t* perm, int64_t n, uint64_t seed) {
 }
 
 hipError_t launch_combine_partials(const int64_t* part, int nparts, int64_t* y, int64_t t, int64_t n, int limbs,
-                                   int out_mode, int32_t* status, hipStream_t s) {
+                                   int out_mode, const int64_t* resid, int32_t* status, hipStream_t s) {
   const int64_t total = t * n;
   hipLaunchKernelGGL(combine_partials_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, part, nparts, y,
-                     t, n, limbs, out_mode, status);
+                     t, n, limbs, out_mode, resid, status);
+  return hipGetLastError();
+}
+
+hipError_t launch_add_residual(int64_t* y, const int64_t* resid, int64_t n, int32_t* status, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(add_residual_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, y, resid, n, status);
   return hipGetLastError();
 }
 

@@ -24,19 +24,9 @@ __global__ void silu_mul_kernel(const int64_t* __restrict__ g, const int64_t* __
                                 int32_t* status) {
   const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= n) return;
-  const int64_t gv = g[e];
-  // floor((g + 16) / 32) without overflowing at the int64 ends
-  int64_t idx = (gv >> 5) + ((gv & 31) >= 16 ? 1 : 0);
-  idx = idx < -32768 ? -32768 : (idx > 32768 ? 32768 : idx);
-  const __int128 p = (__int128)lut[idx + 32768] * (__int128)u[e];
-  const __int128 v = p >> 16;   // arithmetic: floor
-  const __int128 lo = -((__int128)1 << 63), hi = ((__int128)1 << 63) - 1;
-  if (v < lo || v > hi) {
-    flag(status, EI_DEV_OUT_RANGE);
-    h[e] = 0;
-  } else {
-    h[e] = (int64_t)v;
-  }
+  int64_t v;
+  if (!silu_gate(g[e], u[e], lut, &v)) flag(status, EI_DEV_OUT_RANGE);
+  h[e] = v;
 }
 
 hipError_t launch_silu_lut(int32_t* lut, hipStream_t s) {

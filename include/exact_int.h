@@ -259,6 +259,53 @@ int ei_silu_lut_build(int32_t* lut, ei_stream stream);
 int silu_lut_epilogue(const int64_t* gate, const int64_t* up, const int32_t* lut, int64_t* h,
                       int64_t n, int32_t* d_status, ei_stream stream);
 
+/* ------------------------------------------------------- FFN layers */
+
+/*
+ * One feed-forward layer of Q8 projections with the SiLU gate ([Handshake]
+ * C1 and C4: the committed SiLU table applied to the gate projection, the
+ * gated product, the down projection, the residual stream):
+ *   g = Q8(wg, x), u = Q8(wu, x), h = silu_lut_epilogue(g, u),
+ *   y = x + Q8(wd, h).
+ * Every value equals that sequence of int_gemm_q8 / silu_lut_epilogue calls
+ * and an int64 add; for 5 to 63 tokens the gate and up projections share one
+ * pass (the SiLU product in its epilogue, g and u never stored).
+ *   wg, wu   descriptors [f][d] from ei_q8_pack (the same shape)
+ *   wd       descriptor [d][f]
+ *   x        device int64 [t][d], Q16 activations with |x| <= 2^22
+ *   lut      device int32 [65537] from ei_silu_lut_build
+ *   y        device int64 [t][d]; must not overlap x
+ * Workspace: ei_ffn_workspace_bytes(wg, wd, t) bytes (EI_ENOSPACE if
+ * smaller).  EI_EINVAL for null pointers, t < 1 or mismatched shapes; a sum
+ * that leaves int64 sets EI_DEV_OUT_RANGE, an activation outside three limbs
+ * EI_DEV_LIMB_RANGE.
+ */
+size_t ei_ffn_workspace_bytes(const ei_weights* wg, const ei_weights* wd, int64_t t);
+int int_ffn_q8(const ei_weights* wg, const ei_weights* wu, const ei_weights* wd, const int64_t* x,
+               const int32_t* lut, int64_t* y, int64_t t, void* workspace, size_t workspace_bytes,
+               int32_t* d_status, ei_stream stream);
+
+/*
+ * The routed (mixture-of-experts) feed-forward layer ([tritify] 3.2
+ * "Mixture-of-Experts": each selected expert is an exact-integer MLP; the
+ * gate as in [Handshake] C1 and C4): for every pair (r, s), with
+ * e = route[r][s],
+ *   y[r * topk + s] = Q8(wd_e, silu_lut_epilogue(Q8(wg_e, x[r]), Q8(wu_e, x[r]))),
+ * no residual and no combination over s (the router's weights are not part
+ * of the layer).  The pairs are grouped by expert once for all three
+ * projections.
+ *   wg, wu   stacked descriptors [E][f][d] from ei_q8_pack_stacked
+ *   wd       stacked descriptor [E][d][f]
+ *   x        device int64 [rows][d]; route device int32 [rows][topk]
+ *   y        device int64 [rows * topk][d]
+ * Limits as int_gemm_q8_grouped; workspace ei_moe_ffn_workspace_bytes(wg,
+ * wd, rows, topk).  An expert id outside [0, E) sets EI_DEV_ROUTE.
+ */
+size_t ei_moe_ffn_workspace_bytes(const ei_weights* wg, const ei_weights* wd, int64_t rows, int topk);
+int int_moe_ffn_q8(const ei_weights* wg, const ei_weights* wu, const ei_weights* wd, const int64_t* x,
+                   const int32_t* route, int64_t rows, int topk, const int32_t* lut, int64_t* y, void* workspace,
+                   size_t workspace_bytes, int32_t* d_status, ei_stream stream);
+
 /*
  * FP32 shadow of the Q8 projection, the negative control of the schedule gate
  * ([Handshake] C3 and "Construction / Schedule gate": the same GEMM in float

@@ -224,6 +224,57 @@ def test_qwen_ffn_24_layers(ei):
         assert ei.digest(x) == exp["x_next"], layer
 
 
+@pytest.mark.parametrize("shape", [(96, 64, 1), (96, 64, 3), (160, 96, 30), (128, 64, 40), (64, 4096, 30),
+                                   (4096, 64, 30), (96, 160, 70), (32, 320, 5)])
+def test_ffn_q8_matches_the_separate_steps(ei, lut, shape):
+    # one layer through int_ffn_q8 against the oracle's gate, up, SiLU
+    # product, down projection and residual: the fused gate/up pass (5..63
+    # tokens with one workgroup split), the GEMV path, the tiled path, the
+    # unfused path, and split-K partials (with the residual) on the down
+    # projection
+    F, D, T = shape
+    r = np.random.default_rng(F + D + T)
+    mats = [(synth.q8_codes(r, F, D), synth.q8_scales(r, F, D)), (synth.q8_codes(r, F, D), synth.q8_scales(r, F, D)),
+            (synth.q8_codes(r, D, F), synth.q8_scales(r, D, F))]
+    x = synth.q16_acts(r, T, D)
+    wg, wu, wd = (ei.pack_q8(dev(c), dev(sc)) for c, sc in mats)
+    say("ffn", shape, "workspace", ei.ffn_workspace_bytes(wg, wd, T))
+    y = host(ei.ffn_q8(wg, wu, wd, dev(x), dev(lut)))
+    *_, xn = oracle.ffn_layer(x, mats[0], mats[1], mats[2], lut)
+    assert (y == xn).all()
+
+
+def test_qwen_ffn_24_layers_fused(ei):
+    lut = ei.silu_lut()
+    x = dev(synth.qwen_ffn_x0())
+    y = torch.empty_like(x)
+    for layer in range(synth.QWEN_LAYERS):
+        (gc, gs), (uc, us), (dc, ds) = synth.qwen_ffn_layer(layer)
+        wg, wu, wd = ei.pack_q8(dev(gc), dev(gs)), ei.pack_q8(dev(uc), dev(us)), ei.pack_q8(dev(dc), dev(ds))
+        say("fused ffn layer", layer)
+        ei.ffn_q8(wg, wu, wd, x, lut, out=y)
+        x, y = y, x
+        assert ei.digest(x) == GOLDEN["qwen05b_ffn"]["layers"][layer]["x_next"], layer
+
+
+@pytest.mark.parametrize("shape", [(5, 37, 3, 64, 96), (9, 12, 4, 32, 288), (100, 600, 2, 32, 64)])
+def test_moe_ffn_q8_small(ei, lut, shape):
+    E, rows, topk, F, D = shape
+    r = np.random.default_rng(E * 7 + rows)
+    mats = [[(synth.q8_codes(r, F, D), synth.q8_scales(r, F, D)), (synth.q8_codes(r, F, D), synth.q8_scales(r, F, D)),
+             (synth.q8_codes(r, D, F), synth.q8_scales(r, D, F))] for _ in range(E)]
+    x = synth.q16_acts(r, rows, D)
+    route = (r.integers(0, E, (rows, topk)) ** 2 % E).astype(np.int32)
+
+    def stack(m):
+        return (dev(np.stack([mm[m][0] for mm in mats])), dev(np.stack([mm[m][1] for mm in mats])))
+    wg, wu, wd = (ei.pack_q8_stacked(*stack(m)) for m in range(3))
+    say("moe ffn", shape)
+    y = host(ei.moe_ffn_q8(wg, wu, wd, dev(x), dev(route), dev(lut)))
+    ref = oracle.moe_pairs(x, route, lambda e: mats[e], lut)
+    assert (y == ref).all()
+
+
 def test_dense_t1(ei):
     q, s = synth.dense_w()
     w = ei.pack_q8(dev(q), dev(s))
@@ -380,6 +431,10 @@ def test_olmoe_grouped_ffn_sampled_pairs(ei, lut):
     tt, kk = np.nonzero(route == e)
     dense = host(ei.gemm_q8(ei.pack_q8(dev(gc[e]), dev(gs[e])), dev(x[tt])))
     assert (host(g)[tt * 8 + kk] == dense).all()
+    # the one-call routed FFN (one grouping for the three projections) gives
+    # the same rows as the three grouped calls
+    say("olmoe routed ffn, one call")
+    assert (host(ei.moe_ffn_q8(wg, wu, wd, xd, rd, dev(lut))) == out).all()
 
 
 # ------------------------------------------------------------- FP32 shadow
