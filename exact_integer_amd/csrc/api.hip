@@ -146,7 +146,8 @@ int run_gemm(const ei_weights* w, const void* x, int x_is_i32, int64_t* y, int64
           a.out_mode = OUT_PARTIAL;
           e = launch_gemm_skinny(a, limbs, lay.splits, s);
           if (e == hipSuccess)
-            e = launch_combine_partials(part, lay.splits, y, t, w->n, limbs, out_mode, resid, status, s);
+            e = limbs <= 3 ? launch_combine_hr(part, lay.splits, y, t, w->n, out_mode, resid, status, s)
+                           : launch_combine_partials(part, lay.splits, y, t, w->n, limbs, out_mode, resid, status, s);
         } else {
           a.resid = resid;
           e = launch_gemm_skinny(a, limbs, 1, s);

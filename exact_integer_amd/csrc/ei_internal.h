@@ -43,7 +43,8 @@ inline size_t packed_bytes(int64_t n, int64_t k) {
 enum OutMode : int {
   OUT_ROUND_Q24 = 0,   // y = floor((acc + 2^23) / 2^24)       (Q8)
   OUT_EXACT = 1,       // y = acc, checked to fit int64          (Q4)
-  OUT_PARTIAL = 2,     // per-limb int64 partial sums to workspace [part][L][T][N]
+  OUT_PARTIAL = 2,     // partial sums to workspace: per limb [part][L][T][N] (the skinny kernel
+                       // writes (h, r) pairs [part][2][T][N] for up to three limbs)
   OUT_TERMS = 3        // per-limb int64 per-block terms to workspace [b][L][T][N]
 };
 
@@ -107,7 +108,9 @@ hipError_t launch_gemm_mfma(const GemmArgs& a, int limbs, hipStream_t s);
 hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t s);    // 3 limbs, see tiled_ok()
 hipError_t launch_gemm_grouped(const GemmArgs& a, hipStream_t s);  // 3 limbs
 int skinny_splits(int64_t n_pad, int64_t t_pad, int64_t nb);       // workgroup K splits of the skinny kernel
-hipError_t launch_gemm_skinny(const GemmArgs& a, int limbs, int splits, hipStream_t s);  // a.part when splits > 1
+// a.part when splits > 1: (h, r) partials [splits][2][t][n] for up to three
+// limbs, per-limb partials [splits][limbs][t][n] for four
+hipError_t launch_gemm_skinny(const GemmArgs& a, int limbs, int splits, hipStream_t s);
 hipError_t launch_moe_sort(const int32_t* route, int64_t pairs, int64_t experts, int32_t* sorted_pair,
                            int32_t* offsets, int32_t* tile_expert, int32_t* tile_row0, int32_t* tile_rows,
                            int32_t* ntiles, int32_t* status, hipStream_t s);
@@ -116,6 +119,8 @@ hipError_t launch_grouped_limb_tiles(const int64_t* x, int64_t k, int topk, cons
                                      int64_t tiles_max, int8_t* tiles, int32_t* status, hipStream_t s);
 hipError_t launch_combine_partials(const int64_t* part, int nparts, int64_t* y, int64_t t, int64_t n,
                                    int limbs, int out_mode, const int64_t* resid, int32_t* status, hipStream_t s);
+hipError_t launch_combine_hr(const int64_t* part, int nparts, int64_t* y, int64_t t, int64_t n, int out_mode,
+                             const int64_t* resid, int32_t* status, hipStream_t s);   // (h, r) partials
 hipError_t launch_add_residual(int64_t* y, const int64_t* resid, int64_t n, int32_t* status, hipStream_t s);
 hipError_t launch_gemm_skinny_gateup(const GemmArgs& a, hipStream_t s);   // 3 limbs, one split
 hipError_t launch_tree_terms(int64_t* terms, int64_t nb, int64_t* y, int64_t t, int64_t n,
@@ -130,6 +135,14 @@ hipError_t launch_silu_mul(const int64_t* g, const int64_t* u, const int32_t* lu
 void sha256(const void* data, size_t n, uint8_t out[32]);
 
 // ---------------------------------------------------------------- device
+// v as int64, or false if it does not fit.
+__device__ inline bool fit_i64(__int128 v, int64_t* out) {
+  const __int128 lo = -((__int128)1 << 63), hi = ((__int128)1 << 63) - 1;
+  if (v < lo || v > hi) { *out = 0; return false; }
+  *out = (int64_t)v;
+  return true;
+}
+
 // Combine per-limb int64 sums A_l into sum_l 2^(8l) A_l (int128) and apply
 // the output rounding.  Returns false if the result does not fit int64.
 __device__ inline bool finish_output(__int128 acc, int mode, int64_t* out) {
@@ -139,6 +152,34 @@ __device__ inline bool finish_output(__int128 acc, int mode, int64_t* out) {
   if (v < lo || v > hi) { *out = 0; return false; }
   *out = (int64_t)v;
   return true;
+}
+
+// acc = a0 + 2^8 a1 + 2^16 a2 (any int64 a_l) as acc = 2^24 h + r without
+// 128-bit arithmetic: with a_l = h_l 2^(24-8l) + r_l, 0 <= r_l < 2^(24-8l)
+// (arithmetic shifts and masks), h = h_0 + h_1 + h_2 and r = r_0 + 2^8 r_1 +
+// 2^16 r_2 in [0, 3 * 2^24).  |h_l| < 2^39, 2^47, 2^55, so nothing overflows.
+// The pair is additive: sums of (h, r) over disjoint block ranges give the
+// (h, r) of the whole sum, with r below 2^24 times the number of terms.
+__device__ inline void split_hr(int64_t a0, int64_t a1, int64_t a2, int64_t* h, int64_t* r) {
+  *h = (a0 >> 24) + (a1 >> 16) + (a2 >> 8);
+  *r = (a0 & 0xFFFFFF) + ((a1 & 0xFFFF) << 8) + ((a2 & 0xFF) << 16);
+}
+
+// y from acc = 2^24 h + r (r >= 0): Q8 rounding floor((acc + 2^23) / 2^24) =
+// h + floor((r + 2^23) / 2^24), which cannot overflow for |h| < 2^62 and
+// r < 2^62; or the exact acc, checked to fit int64.
+__device__ inline bool finish_hr(int64_t h, int64_t r, int mode, int64_t* out) {
+  if (mode == OUT_ROUND_Q24) {
+    *out = h + ((r + ((int64_t)1 << 23)) >> 24);
+    return true;
+  }
+  return fit_i64((__int128)h * ((__int128)1 << 24) + r, out);
+}
+
+__device__ inline int64_t round_q24_3(int64_t a0, int64_t a1, int64_t a2) {
+  int64_t h, r;
+  split_hr(a0, a1, a2, &h, &r);
+  return h + ((r + ((int64_t)1 << 23)) >> 24);
 }
 
 // Balanced base-256 digits d_l in [-128, 127] with v = sum_{l<L} 256^l d_l
@@ -179,14 +220,6 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t by
 
 __device__ inline void flag(int32_t* status, int bits) {
   if (status) atomicOr(status, bits);
-}
-
-// v as int64, or false if it does not fit.
-__device__ inline bool fit_i64(__int128 v, int64_t* out) {
-  const __int128 lo = -((__int128)1 << 63), hi = ((__int128)1 << 63) - 1;
-  if (v < lo || v > hi) { *out = 0; return false; }
-  *out = (int64_t)v;
-  return true;
 }
 
 // SiLU-gated product: h = floor(lut[clamp(floor((g + 16) / 32), -32768,

@@ -6,9 +6,10 @@
 // takes one 32-row tile, one token tile and a range of blocks, its W waves
 // split that range again, and the waves' per-limb sums meet in LDS.  When the
 // row tiles alone are too few to occupy the chip, the block range is also split
-// across workgroups, which then write per-limb int64 partials
-// part[p][l][t][i] for the partial combiner (any grouping of the exact block
-// terms gives the same sum).
+// across workgroups, which then write partials for a combiner (any grouping
+// of the exact block terms gives the same sum).  For up to three limbs every
+// wave reduces its per-limb sums to the additive pair (h, r) with
+// acc = 2^24 h + r before they meet, and the four waves share the epilogue.
 //
 // Per block a wave loads one code tile, one scale per row and L activation
 // limb tiles (16 bytes per lane each), runs L v_mfma_i32_32x32x32_i8 (exact
@@ -27,13 +28,13 @@ struct SkinnyBatch {
   v4i d[D][L];
 };
 
-// G = 1: one projection; y = result, or resid + result, or per-limb partials.
+// G = 1: one projection; y = result, or resid + result, or partials (the
+// (h, r) pairs of split_hr for up to three limbs, per-limb sums for four).
 // G = 2: the gate (codes, scales) and up (codes2, scales2) projections of an
 // FFN layer, W waves each, meet in the epilogue: y = h, the SiLU-gated
 // product of the two rounded results (one workgroup split only).
 template <int L, int W, int D, int G>
 __global__ __launch_bounds__(64 * W * G) void gemm_skinny_kernel(GemmArgs a) {
-  __shared__ int64_t red[G][(W - 1) * 16 * 64];
   const int lane = threadIdx.x & 63;
   const int wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int m = wave_all / W, wave = wave_all % W;   // matrix, wave within it
@@ -78,86 +79,143 @@ __global__ __launch_bounds__(64 * W * G) void gemm_skinny_kernel(GemmArgs a) {
         }
       }
     };
+    // no load past the range: a copy still in flight at the reduction's
+    // barrier would hold every wave until it lands
     SkinnyBatch<L, D> A, B;
     load(A, w0);
-    for (int64_t pos = w0; pos < w1; pos += 2 * D) {
-      load(B, pos + D);
+    for (int64_t pos = w0;; pos += 2 * D) {
+      const bool more_b = pos + D < w1;
+      if (more_b) load(B, pos + D);
       compute(A, pos);
-      load(A, pos + 2 * D);
+      if (!more_b) break;
+      const bool more_a = pos + 2 * D < w1;
+      if (more_a) load(A, pos + 2 * D);
       compute(B, pos + D);
+      if (!more_a) break;
     }
-  }
-
-  // waves 1 .. W-1 of each matrix hand their sums to its wave 0, one limb at
-  // a time
-#pragma unroll
-  for (int l = 0; l < L; ++l) {
-    if (wave > 0) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) red[m][((wave - 1) * 16 + r) * 64 + lane] = acc[l][r];
-    }
-    __syncthreads();
-    if (wave == 0) {
-      for (int w = 1; w < W; ++w)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[l][r] += red[m][((w - 1) * 16 + r) * 64 + lane];
-    }
-    __syncthreads();
   }
 
   // D[m = token][n = row]: row lane % 32, token 8(r/4) + 4(lane/32) + r%4
   const int64_t row = rg * kTile + (lane & 31);
-  auto rounded = [&](int r, int64_t* out) {
-    __int128 v = 0;
+  auto token = [&](int r) { return tg * kTile + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); };
+
+  if constexpr (L <= 3) {
+    // Every wave turns its sums into the additive pair (h, r) of
+    // acc = 2^24 h + r, the pairs meet in LDS, and wave w finishes the four
+    // outputs 4w .. 4w + 3 of its lanes (all waves share the epilogue).
+    static_assert(W == 4, "one quarter of the 16 outputs per wave");
+    __shared__ int64_t xh[W][16][64];
+    __shared__ int32_t xr[W][16][64];
+    __shared__ int64_t xu[W][4][64];   // G = 2: the up projection's results
+    int64_t hs[4], rs[4];
+    auto exchange = [&](bool mine) {   // every thread calls it: two barriers
+      if (mine) {
 #pragma unroll
-    for (int l = 0; l < L; ++l) v += (__int128)acc[l][r] << (8 * l);
-    return finish_output(v, a.out_mode, out);
-  };
-  if constexpr (G == 2) {
-    // the up projection's wave 0 leaves its rounded results in LDS for the
-    // gate's (the same lanes hold the same outputs)
-    bool ok = true;
-    if (m == 1 && wave == 0) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        int64_t u;
-        ok = rounded(r, &u) && ok;
-        red[0][r * 64 + lane] = u;
+        for (int r = 0; r < 16; ++r) {
+          int64_t h, rr;
+          split_hr(acc[0][r], L > 1 ? acc[L > 1 ? 1 : 0][r] : 0, L > 2 ? acc[L > 2 ? 2 : 0][r] : 0, &h, &rr);
+          xh[wave][r][lane] = h;
+          xr[wave][r][lane] = (int32_t)rr;   // < 3 * 2^24
+        }
       }
-    }
-    __syncthreads();
-    if (m == 1 || wave != 0) {
-      if (m == 1 && wave == 0 && !ok && row < a.n) flag(a.status, EI_DEV_OUT_RANGE);
+      __syncthreads();
+      if (mine) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          hs[j] = 0;
+          rs[j] = 0;
+#pragma unroll
+          for (int w = 0; w < W; ++w) {
+            hs[j] += xh[w][4 * wave + j][lane];
+            rs[j] += xr[w][4 * wave + j][lane];
+          }
+        }
+      }
+      __syncthreads();
+    };
+    if constexpr (G == 2) {
+      // up first; its results wait in LDS for the gate's waves
+      exchange(m == 1);
+      if (m == 1) {
+        bool ok = true;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          int64_t u;
+          ok = finish_hr(hs[j], rs[j], a.out_mode, &u) && ok;
+          xu[wave][j][lane] = u;
+        }
+        if (!ok && row < a.n) flag(a.status, EI_DEV_OUT_RANGE);
+      }
+      exchange(m == 0);   // its first barrier also publishes xu
+      if (m == 1 || row >= a.n) return;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t tok = token(4 * wave + j);
+        if (tok >= a.t) continue;
+        int64_t g, h;
+        bool good = finish_hr(hs[j], rs[j], a.out_mode, &g);
+        good = silu_gate(g, xu[wave][j][lane], a.lut, &h) && good;
+        if (!good) flag(a.status, EI_DEV_OUT_RANGE);
+        a.y[tok * a.n + row] = h;
+      }
+      return;
+    } else {
+      exchange(true);
+      if (row >= a.n) return;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t tok = token(4 * wave + j);
+        if (tok >= a.t) continue;
+        if (a.out_mode == OUT_PARTIAL) {   // the (h, r) pair: part[p][2][t][n]
+          a.part[((part * 2 + 0) * a.t + tok) * a.n + row] = hs[j];
+          a.part[((part * 2 + 1) * a.t + tok) * a.n + row] = rs[j];
+        } else {
+          int64_t out;
+          bool ok = finish_hr(hs[j], rs[j], a.out_mode, &out);
+          if (a.resid) ok = fit_i64((__int128)a.resid[tok * a.n + row] + out, &out) && ok;
+          if (!ok) flag(a.status, EI_DEV_OUT_RANGE);
+          a.y[tok * a.n + row] = out;
+        }
+      }
       return;
     }
-    if (row >= a.n) return;
+  } else {
+    // four limbs: waves 1 .. W-1 hand their per-limb sums to wave 0, one limb
+    // at a time; wave 0 writes per-limb partials or the final result
+    static_assert(G == 1, "the fused gate/up pass takes three limbs");
+    __shared__ int64_t red[(W - 1) * 16 * 64];
+#pragma unroll
+    for (int l = 0; l < L; ++l) {
+      if (wave > 0) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) red[((wave - 1) * 16 + r) * 64 + lane] = acc[l][r];
+      }
+      __syncthreads();
+      if (wave == 0) {
+        for (int w = 1; w < W; ++w)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[l][r] += red[((w - 1) * 16 + r) * 64 + lane];
+      }
+      __syncthreads();
+    }
+    if (wave != 0 || row >= a.n) return;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int64_t tok = tg * kTile + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      const int64_t tok = token(r);
       if (tok >= a.t) continue;
-      int64_t g, h;
-      bool good = rounded(r, &g);
-      good = silu_gate(g, red[0][r * 64 + lane], a.lut, &h) && good;
-      if (!good) flag(a.status, EI_DEV_OUT_RANGE);
-      a.y[tok * a.n + row] = h;
-    }
-    return;
-  }
-  if (wave != 0) return;
-  if (row >= a.n) return;
+      if (a.out_mode == OUT_PARTIAL) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int64_t tok = tg * kTile + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-    if (tok >= a.t) continue;
-    if (a.out_mode == OUT_PARTIAL) {
+        for (int l = 0; l < L; ++l) a.part[((part * L + l) * a.t + tok) * a.n + row] = acc[l][r];
+      } else {
+        __int128 v = 0;
 #pragma unroll
-      for (int l = 0; l < L; ++l) a.part[((part * L + l) * a.t + tok) * a.n + row] = acc[l][r];
-    } else {
-      int64_t out;
-      bool ok = rounded(r, &out);
-      if (a.resid) ok = fit_i64((__int128)a.resid[tok * a.n + row] + out, &out) && ok;
-      if (!ok) flag(a.status, EI_DEV_OUT_RANGE);
-      a.y[tok * a.n + row] = out;
+        for (int l = 0; l < L; ++l) v += (__int128)acc[l][r] << (8 * l);
+        int64_t out;
+        bool ok = finish_output(v, a.out_mode, &out);
+        if (a.resid) ok = fit_i64((__int128)a.resid[tok * a.n + row] + out, &out) && ok;
+        if (!ok) flag(a.status, EI_DEV_OUT_RANGE);
+        a.y[tok * a.n + row] = out;
+      }
     }
   }
 }

@@ -7,22 +7,69 @@
 
 namespace ei {
 
-// y[t][i] from per-limb partials part[p][l][t][i], p summed from the last
-// partial down to the first; each partial sum is exact in int64.  With resid,
+// y[t][i] from per-limb partials part[p][l][t][i]; each partial sum is exact
+// in int64.  With resid,
 // y = resid + (that result), checked to fit int64.
 __global__ void combine_partials_kernel(const int64_t* __restrict__ part, int nparts, int64_t* __restrict__ y,
                                         int64_t t, int64_t n, int limbs, int out_mode,
                                         const int64_t* __restrict__ resid, int32_t* status) {
   int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= t * n) return;
-  __int128 v = 0;
-  for (int l = 0; l < limbs; ++l) {
-    int64_t s = 0;
-    for (int p = nparts - 1; p >= 0; --p) s += part[((int64_t)p * limbs + l) * t * n + e];
-    v += (__int128)s << (8 * l);
+  const int64_t tn = t * n;
+  int64_t sum[kMaxLimbs] = {};
+  // eight partials' loads in flight at a time (the order of the int64 sums
+  // is immaterial: each is exact)
+  for (int p0 = 0; p0 < nparts; p0 += 8) {
+#pragma unroll
+    for (int l = 0; l < kMaxLimbs; ++l) {
+      if (l >= limbs) break;
+      int64_t v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = p0 + j < nparts ? part[((int64_t)(p0 + j) * limbs + l) * tn + e] : 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sum[l] += v[j];
+    }
   }
   int64_t out;
-  bool ok = finish_output(v, out_mode, &out);
+  bool ok = true;
+  if (limbs <= 3 && out_mode == OUT_ROUND_Q24) {
+    out = round_q24_3(sum[0], limbs > 1 ? sum[1] : 0, limbs > 2 ? sum[2] : 0);
+  } else {
+    __int128 v = 0;
+#pragma unroll
+    for (int l = 0; l < kMaxLimbs; ++l)
+      if (l < limbs) v += (__int128)sum[l] << (8 * l);
+    ok = finish_output(v, out_mode, &out);
+  }
+  if (resid) ok = fit_i64((__int128)resid[e] + out, &out) && ok;
+  if (!ok) flag(status, EI_DEV_OUT_RANGE);
+  y[e] = out;
+}
+
+// y[t][i] from (h, r) partials part[p][2][t][i] (acc = 2^24 sum h + sum r;
+// the r are below 3 * 2^24 each), plus resid when given.
+__global__ void combine_hr_kernel(const int64_t* __restrict__ part, int nparts, int64_t* __restrict__ y, int64_t t,
+                                  int64_t n, int out_mode, const int64_t* __restrict__ resid, int32_t* status) {
+  int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= t * n) return;
+  const int64_t tn = t * n;
+  int64_t h = 0, r = 0;
+  for (int p0 = 0; p0 < nparts; p0 += 8) {   // eight partials' loads in flight
+    int64_t vh[8], vr[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bool in = p0 + j < nparts;
+      vh[j] = in ? part[(int64_t)(p0 + j) * 2 * tn + e] : 0;
+      vr[j] = in ? part[((int64_t)(p0 + j) * 2 + 1) * tn + e] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      h += vh[j];
+      r += vr[j];
+    }
+  }
+  int64_t out;
+  bool ok = finish_hr(h, r, out_mode, &out);
   if (resid) ok = fit_i64((__int128)resid[e] + out, &out) && ok;
   if (!ok) flag(status, EI_DEV_OUT_RANGE);
   y[e] = out;
@@ -87,6 +134,14 @@ hipError_t launch_combine_partials(const int64_t* part, int nparts, int64_t* y, 
   const int64_t total = t * n;
   hipLaunchKernelGGL(combine_partials_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, part, nparts, y,
                      t, n, limbs, out_mode, resid, status);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_hr(const int64_t* part, int nparts, int64_t* y, int64_t t, int64_t n, int out_mode,
+                             const int64_t* resid, int32_t* status, hipStream_t s) {
+  const int64_t total = t * n;
+  hipLaunchKernelGGL(combine_hr_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, part, nparts, y, t, n,
+                     out_mode, resid, status);
   return hipGetLastError();
 }
 
