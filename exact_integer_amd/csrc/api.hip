@@ -93,10 +93,12 @@ int check_weights(const ei_weights* w, int format) {
 // y = projection of x (+ resid when resid is not null: the skinny kernel and
 // the partial combiner add it as they write y, other paths in a pass of
 // their own).
+// With pre_limbs (T > 4 only), x is already split: its limb tiles
+// [limbs][t_pad/32][nb][1 KB] are read from there.
 int run_gemm(const ei_weights* w, const void* x, int x_is_i32, int64_t* y, int64_t t, int limbs, int schedule,
              uint64_t seed, void* ws, size_t ws_bytes, int32_t* status, hipStream_t s, int out_mode,
-             const int64_t* resid = nullptr) {
-  if (!x || !y || t < 1) return EI_EINVAL;
+             const int64_t* resid = nullptr, const int8_t* pre_limbs = nullptr) {
+  if ((!x && !pre_limbs) || !y || t < 1) return EI_EINVAL;
   if (limbs < 1 || limbs > 8) return EI_EINVAL;
   if (limbs > kMaxLimbs) return EI_ERANGE;
   if (schedule < EI_SCHED_DEFAULT || schedule > EI_SCHED_TREE) return EI_EINVAL;
@@ -125,11 +127,15 @@ int run_gemm(const ei_weights* w, const void* x, int x_is_i32, int64_t* y, int64
   a.order = ORDER_ASC;
 
   hipError_t e = hipSuccess;
-  if (lay.mfma) {
+  if (lay.mfma && pre_limbs) {
+    a.limb_tiles = pre_limbs;
+  } else if (lay.mfma) {
     a.limb_tiles = reinterpret_cast<const int8_t*>(wsb + lay.limb_off);
     e = launch_limb_tiles(x, x_is_i32, t, w->k, limbs, reinterpret_cast<int8_t*>(wsb + lay.limb_off), lay.t_pad,
                           status, s);
     if (e != hipSuccess) return EI_EDEVICE;
+  } else if (pre_limbs) {
+    return EI_EINVAL;
   }
   auto launch = [&](const GemmArgs& args) {
     if (lay.path == PATH_TILED) return launch_gemm_tiled(args, s);
@@ -312,8 +318,9 @@ hipError_t launch_grouped_projection(const ei_weights* w, const GroupedLayout& g
   return launch_gemm_grouped(a, s);
 }
 
-// FFN workspace: h [t][f], then g and u [t][f] unless the gate and up
-// projections run fused, then the projections' own workspace.
+// FFN workspace: fused gate/up, h as the down projection's limb tiles
+// [3][t_pad/32][f/32][1 KB]; otherwise h, g and u [t][f]; then the
+// projections' own workspace.
 struct FfnLayout {
   bool fused;
   size_t h_off, g_off, u_off, gemm_off, total;
@@ -322,14 +329,17 @@ struct FfnLayout {
 FfnLayout ffn_layout(const ei_weights* wg, const ei_weights* wd, int64_t t) {
   FfnLayout f;
   const WsLayout lg = layout_for(wg, t, 3, EI_SCHED_DEFAULT), ld = layout_for(wd, t, 3, EI_SCHED_DEFAULT);
-  f.fused = lg.path == PATH_SKINNY && lg.splits == 1;
-  const size_t hb = align_up(sizeof(int64_t) * (size_t)t * (size_t)wg->n);
+  f.fused = lg.path == PATH_SKINNY && lg.splits == 1 && ld.mfma;
   f.h_off = 0;
-  f.g_off = f.u_off = hb;
-  size_t off = hb;
-  if (!f.fused) {
-    f.u_off = off + hb;
-    off += 2 * hb;
+  size_t off;
+  if (f.fused) {
+    off = align_up((size_t)3 * (size_t)lg.t_pad * (size_t)wg->n);
+    f.g_off = f.u_off = off;
+  } else {
+    const size_t hb = align_up(sizeof(int64_t) * (size_t)t * (size_t)wg->n);
+    f.g_off = hb;
+    f.u_off = 2 * hb;
+    off = 3 * hb;
   }
   f.gemm_off = off;
   f.total = off + (lg.total > ld.total ? lg.total : ld.total);
@@ -448,7 +458,6 @@ int int_ffn_q8(const ei_weights* wg, const ei_weights* wu, const ei_weights* wd,
   if (!workspace || workspace_bytes < f.total) return EI_ENOSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  int64_t* h = reinterpret_cast<int64_t*>(ws + f.h_off);
   void* gws = ws + f.gemm_off;
   const size_t gws_bytes = workspace_bytes - f.gemm_off;
   if (f.fused) {
@@ -466,7 +475,7 @@ int int_ffn_q8(const ei_weights* wg, const ei_weights* wu, const ei_weights* wd,
     a.scales2 = reinterpret_cast<const int32_t*>(bu + kHeaderBytes + wu->n_pad * wu->k);
     a.lut = lut;
     a.limb_tiles = limb;
-    a.y = h;
+    a.limb_out = reinterpret_cast<int8_t*>(ws + f.h_off);
     a.status = d_status;
     a.n = wg->n;
     a.k = wg->k;
@@ -478,14 +487,16 @@ int int_ffn_q8(const ei_weights* wg, const ei_weights* wu, const ei_weights* wd,
     a.b1 = wg->nb;
     a.out_mode = OUT_ROUND_Q24;
     if (launch_gemm_skinny_gateup(a, s) != hipSuccess) return EI_EDEVICE;
-  } else {
-    int64_t* g = reinterpret_cast<int64_t*>(ws + f.g_off);
-    int64_t* u = reinterpret_cast<int64_t*>(ws + f.u_off);
-    int r = run_gemm(wg, x, 0, g, t, 3, EI_SCHED_DEFAULT, 0, gws, gws_bytes, d_status, s, OUT_ROUND_Q24);
-    if (r == EI_OK) r = run_gemm(wu, x, 0, u, t, 3, EI_SCHED_DEFAULT, 0, gws, gws_bytes, d_status, s, OUT_ROUND_Q24);
-    if (r != EI_OK) return r;
-    if (launch_silu_mul(g, u, lut, h, t * wg->n, d_status, s) != hipSuccess) return EI_EDEVICE;
+    return run_gemm(wd, nullptr, 0, y, t, 3, EI_SCHED_DEFAULT, 0, gws, gws_bytes, d_status, s, OUT_ROUND_Q24, x,
+                    reinterpret_cast<const int8_t*>(ws + f.h_off));
   }
+  int64_t* h = reinterpret_cast<int64_t*>(ws + f.h_off);
+  int64_t* g = reinterpret_cast<int64_t*>(ws + f.g_off);
+  int64_t* u = reinterpret_cast<int64_t*>(ws + f.u_off);
+  int r = run_gemm(wg, x, 0, g, t, 3, EI_SCHED_DEFAULT, 0, gws, gws_bytes, d_status, s, OUT_ROUND_Q24);
+  if (r == EI_OK) r = run_gemm(wu, x, 0, u, t, 3, EI_SCHED_DEFAULT, 0, gws, gws_bytes, d_status, s, OUT_ROUND_Q24);
+  if (r != EI_OK) return r;
+  if (launch_silu_mul(g, u, lut, h, t * wg->n, d_status, s) != hipSuccess) return EI_EDEVICE;
   return run_gemm(wd, h, 0, y, t, 3, EI_SCHED_DEFAULT, 0, gws, gws_bytes, d_status, s, OUT_ROUND_Q24, x);
 }
 

@@ -85,6 +85,7 @@ struct GemmArgs {
   const int32_t* scales2;
   const int32_t* lut;
   const int64_t* resid;
+  int8_t* limb_out;          // fused gate/up: h as limb tiles [3][t_pad/32][n/32][1 KB]
 };
 
 // pos-th block visited by a kernel in the block range [b0, b1) of `a`.

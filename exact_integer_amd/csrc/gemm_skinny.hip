@@ -31,8 +31,9 @@ struct SkinnyBatch {
 // G = 1: one projection; y = result, or resid + result, or partials (the
 // (h, r) pairs of split_hr for up to three limbs, per-limb sums for four).
 // G = 2: the gate (codes, scales) and up (codes2, scales2) projections of an
-// FFN layer, W waves each, meet in the epilogue: y = h, the SiLU-gated
-// product of the two rounded results (one workgroup split only).
+// FFN layer, W waves each, meet in the epilogue: h, the SiLU-gated product of
+// the two rounded results, goes out as the down projection's activation limb
+// tiles (limb_out; one workgroup split only, n a multiple of 32).
 template <int L, int W, int D, int G>
 __global__ __launch_bounds__(64 * W * G) void gemm_skinny_kernel(GemmArgs a) {
   const int lane = threadIdx.x & 63;
@@ -147,16 +148,47 @@ __global__ __launch_bounds__(64 * W * G) void gemm_skinny_kernel(GemmArgs a) {
         if (!ok && row < a.n) flag(a.status, EI_DEV_OUT_RANGE);
       }
       exchange(m == 0);   // its first barrier also publishes xu
-      if (m == 1 || row >= a.n) return;
+      // h is only the down projection's input: the gate's waves put the
+      // 32 x 32 tile of h in LDS (zero past t), and one wave splits it into
+      // the down projection's limb tiles (block rg of its K, token tile tg)
+      int64_t(*ht)[33] = reinterpret_cast<int64_t(*)[33]>(&xh[0][0][0]);   // [token][row], padded rows
+      if (m == 0) {
+        bool good = true;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t tok = token(4 * wave + j);
-        if (tok >= a.t) continue;
-        int64_t g, h;
-        bool good = finish_hr(hs[j], rs[j], a.out_mode, &g);
-        good = silu_gate(g, xu[wave][j][lane], a.lut, &h) && good;
+        for (int j = 0; j < 4; ++j) {
+          const int r = 4 * wave + j;
+          const int64_t tok = token(r);
+          int64_t h = 0;
+          if (tok < a.t && row < a.n) {
+            int64_t g;
+            good = finish_hr(hs[j], rs[j], a.out_mode, &g) && good;
+            good = silu_gate(g, xu[wave][j][lane], a.lut, &h) && good;
+          }
+          ht[8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)][lane & 31] = h;
+        }
         if (!good) flag(a.status, EI_DEV_OUT_RANGE);
-        a.y[tok * a.n + row] = h;
+      }
+      __syncthreads();
+      if (m == 0 && wave == 0) {
+        // lane: token lane % 32, rows 16 (lane / 32) .. + 15 of the tile
+        const int64_t* src = &ht[lane & 31][16 * (lane >> 5)];
+        uint32_t words[3][4];
+        bool ok = true;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t v[4] = {src[4 * q], src[4 * q + 1], src[4 * q + 2], src[4 * q + 3]};
+          uint32_t w[3];
+          ok = limb_words<3>(v, w) && ok;
+#pragma unroll
+          for (int l = 0; l < 3; ++l) words[l][q] = w[l];
+        }
+        if (!ok) flag(a.status, EI_DEV_LIMB_RANGE);
+        const int64_t nb_out = a.n_pad / kTile;
+#pragma unroll
+        for (int l = 0; l < 3; ++l) {
+          const v4i v = {(int)words[l][0], (int)words[l][1], (int)words[l][2], (int)words[l][3]};
+          reinterpret_cast<v4i*>(a.limb_out)[((l * tgs + tg) * nb_out + rg) * 64 + lane] = v;
+        }
       }
       return;
     } else {
