@@ -1,6 +1,6 @@
 // SiLU table and the SiLU-gated product ("Vendor-Invariant Integer Inference
 // for MindChain: Handshake v0", claims C1 and C4: a committed 65537-entry
-// table, Q11 input clipped to +-16, Q16 output; inputs beyond +16 read the end
+// table, Q11 input clamped at +-16, Q16 output; inputs beyond +16 read the end
 // entry, so the error there grows as x - 16).
 #include "ei_internal.h"
 

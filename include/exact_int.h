@@ -17,14 +17,14 @@
  *               Handshake v0", claim C1 and "Construction / The frozen
  *               profile" (Q8_0 codes in blocks of 32, FP16 block scales
  *               frozen into Q24 integers, Q16 activations in int64, exact
- *               accumulation with no saturation, Decimal-committed SiLU
- *               table); C3 and "Schedule gate" (five adversarial
+ *               accumulation with no saturation, a SiLU table committed
+ *               in decimal); C3 and "Schedule gate" (five adversarial
  *               schedules); C4 (the SiLU table's clip behaviour).
  *   [tritify]   "Deterministic, Reproducible Inference in Exact Integer
  *               Arithmetic, and Verifiable Distributed Inference as Its
  *               Consequence" (arXiv 2611.13730), 3.1 "Arithmetic
  *               specification" (i128 reference accumulator, i64 hot path
- *               within a proven range bound), 3.2 "Mixture-of-Experts",
+ *               with a proven bound on the range), 3.2 "Mixture-of-Experts",
  *               4 (SHA-256 of the integer output).
  *
  * Conventions (all entry points):

@@ -172,7 +172,7 @@ def mul128_radix16(a: int, b: int) -> int:
 def silu_lut() -> np.ndarray:
     """The 65537-entry SiLU table: LUT[k + 32768] = round(silu(k / 2^11) * 2^16).
 
-    [Handshake] C1 and C4: a Decimal-committed table, Q11 input over +-16,
+    [Handshake] C1 and C4: a table committed in decimal, Q11 input over +-16,
     Q16 output.  silu(z) = z / (1 + e^-z), evaluated here with 50-digit
     decimal arithmetic and rounded to the nearest integer; the only exact
     half-way case would need silu(z) 2^16 to be a half-integer, which does

@@ -437,7 +437,7 @@ int orc_q4(const uint8_t* nib, const uint8_t* sme, const int32_t* x, int64_t* y,
 /*
  * h = (silu(g) * u) >> 16 with silu read from the frozen table.
  * [Handshake] C1 and C4: SiLU is evaluated through a committed 65537-entry
- * table, Q11 input clipped to +-16, Q16 output; C4's clip behaviour (inputs
+ * table, Q11 input clamped at +-16, Q16 output; C4's clip behaviour (inputs
  * above +16 read the end entry, error growing as x - 16) fixes that the
  * index is clamped, not extrapolated.  Readings: the Q16 gate is brought to
  * Q11 by an add-half shift (as the same page's harness rescales Q16 to Q4),
