@@ -108,6 +108,27 @@ def test_q8_extremes_bit_exact(ei, shape):
         assert (host(ei.gemm_q8(w, dev(x), 3, sched)) == ref).all(), sched
 
 
+@pytest.mark.parametrize("sign", [-1, 1])
+def test_q8_max_k_extreme_accumulators(ei, sign):
+    # K = 262144 (8192 blocks, the largest the library accepts) with every
+    # term at its extreme: codes -128, scales -2^31, activations at one end of
+    # the 3-limb range.  With sign -1 every limb's sum is exactly -2^63, the
+    # int64 end; every path (GEMV, skinny with its splits, tiled) and, at T=5,
+    # every schedule must still give the oracle's bits.
+    N, K = 40, 262144
+    q = np.full((N, K), -128, np.int8)
+    s = np.full((N, K // 32), -(2**31), np.int32)
+    w = ei.pack_q8(dev(q), dev(s))
+    xv = -8421504 if sign < 0 else 8355711
+    for T in (1, 5, 64):
+        x = np.full((T, K), xv, np.int64)
+        ref = oracle.q8(q, s, x, threads=8)
+        scheds = SCHEDS if T == 5 else ["default"]
+        for sched in scheds:
+            say("q8 max K", sign, T, sched)
+            assert (host(ei.gemm_q8(w, dev(x), 3, sched)) == ref).all(), (T, sched)
+
+
 def test_q8_four_limbs_wide_activations(ei):
     r = np.random.default_rng(6)
     N, K = 64, 256
