@@ -15,7 +15,8 @@ Sources, cited by page title and section:
               Consequence" (arXiv 2611.13730), sections 3.1, 3.2, 3.4, 4.
 
 Parity status of each function (what pins it is in tests/test_oracle_*.py):
-  q8, q4, silu_mul, limb_split, silu_lut, ffn_layer, moe_pairs -- pinned;
+  q8, q4, silu_mul, limb_split, silu_lut, ffn_layer, moe_pairs, topk_route
+  -- pinned;
   q8_fp32 (the float negative control) -- canonical and tree_walk orders are
   pinned against numpy float32 sequences; the other orders: parity unpinned.
 """
@@ -208,6 +209,25 @@ def ffn_layer(x: np.ndarray, wg, wu, wd, lut: np.ndarray, threads: int = 1):
     d = q8(wd[0], wd[1], h, threads=threads)
     xn = x + d
     return g, u, h, d, xn
+
+
+def topk_route(scores: np.ndarray, k: int) -> np.ndarray:
+    """Integer top-k routing ([tritify] 3.2 "Mixture-of-Experts": the router
+    scores the experts in integer, the top-k selection compares integers and
+    breaks ties by index).  Reading: slot s of token t holds the expert of rank
+    s in the order (score descending, expert index ascending).
+
+    scores: int64 [T][E]; returns int32 [T][k].  Python integers throughout,
+    so the int64 ends compare without overflow."""
+    T, E = scores.shape
+    if not 1 <= k <= E:
+        raise OracleError(f"topk_route: need 1 <= k <= E, got k={k}, E={E}")
+    out = np.empty((T, k), np.int32)
+    for t in range(T):
+        row = [int(v) for v in scores[t]]
+        order = sorted(range(E), key=lambda e: (-row[e], e))
+        out[t] = order[:k]
+    return out
 
 
 def moe_pairs(x: np.ndarray, route: np.ndarray, experts, lut: np.ndarray, pairs=None,

@@ -186,6 +186,11 @@ def olmoe_x(t: int = OLMOE_T):
     return q16_acts(rng_for("olmoe_grouped", 0, "x"), t, OLMOE_H)
 
 
+def olmoe_router():
+    """The router's Q8 weights [64 experts][2048] (integer router scores)."""
+    return q8_matrix("olmoe_grouped", 0, "router", OLMOE_E, OLMOE_H)
+
+
 def olmoe_route(t: int = OLMOE_T):
     return routing(rng_for("olmoe_grouped", 0, "route"), t, OLMOE_E, OLMOE_TOPK)
 

@@ -48,6 +48,11 @@ def main(threads: int = 8) -> None:
         print("ffn layer", layer, layers[-1]["x_next"][:16], flush=True)
     out["qwen05b_ffn"] = {"layers": layers}
 
+    (rc, rs), xo = synth.olmoe_router(), synth.olmoe_x()
+    scores = oracle.q8(rc, rs, xo, threads=threads)
+    out["olmoe_router"] = {"scores": oracle.digest(scores),
+                           "route": oracle.digest(oracle.topk_route(scores, synth.OLMOE_TOPK))}
+
     w, s = synth.dense_w()
     x1 = synth.dense_x(1)
     out["dense_14336x4096"] = {"t1_y": oracle.digest(oracle.q8(w, s, x1, threads=threads))}

@@ -116,3 +116,42 @@ def test_mutant_is_caught(tmp_path, lut, name):
     text = open(SRC).read()
     assert text.count(old) == 1, f"mutation site for {name} not unique"
     assert not _pins_hold(_compile(tmp_path, name, text.replace(old, new)), lut)
+
+
+# --------------------------------------------- top-k routing (Python oracle)
+
+def _topk_checks(topk) -> bool:
+    """The routing pins, applied to a candidate implementation."""
+    import itertools
+    r = np.random.default_rng(33)
+    for _ in range(60):
+        E = int(r.integers(1, 6))
+        k = int(r.integers(1, E + 1))
+        sc = r.integers(-2, 3, (1, E)).astype(np.int64)
+        row = sc[0].tolist()
+        want = next(list(p[:k]) for p in itertools.permutations(range(E))
+                    if all(row[p[i]] > row[p[j]] or (row[p[i]] == row[p[j]] and p[i] < p[j])
+                           for i in range(E) for j in range(i + 1, E)))
+        if topk(sc, k)[0].tolist() != want:
+            return False
+    return True
+
+
+def _topk_mutant(key):
+    def f(scores, k):
+        out = np.empty((scores.shape[0], k), np.int32)
+        for t in range(scores.shape[0]):
+            row = [int(v) for v in scores[t]]
+            out[t] = sorted(range(len(row)), key=lambda e: key(row, e))[:k]
+        return out
+    return f
+
+
+@pytest.mark.parametrize("name,key", [
+    ("ties_to_higher_index", lambda row, e: (-row[e], -e)),
+    ("ascending_scores", lambda row, e: (row[e], e)),
+    ("index_only", lambda row, e: e),
+])
+def test_topk_mutants_are_caught(name, key):
+    assert _topk_checks(oracle.topk_route)
+    assert not _topk_checks(_topk_mutant(key)), name

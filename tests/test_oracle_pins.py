@@ -9,6 +9,8 @@ force with Python's arbitrary-precision integers on tiny inputs.
 import math
 import os
 
+import itertools
+
 import numpy as np
 import pytest
 
@@ -389,3 +391,38 @@ def test_ffn_layer_matches_bigint(lut):
     db = bigint.q8(wd[0].tolist(), wd[1].tolist(), hb)
     assert g.tolist() == gb and u.tolist() == ub and h.tolist() == hb and d.tolist() == db
     assert xn.tolist() == [[x[t, j] + db[t][j] for j in range(D)] for t in range(T)]
+
+
+# ------------------------------------------------------------- top-k routing
+
+def _topk_brute(scores, k):
+    # the unique permutation p with, for every i < j, p[i] ahead of p[j]:
+    # a higher score, or an equal score and a lower index; its first k
+    E = len(scores)
+    for p in itertools.permutations(range(E)):
+        if all(scores[p[i]] > scores[p[j]] or (scores[p[i]] == scores[p[j]] and p[i] < p[j])
+               for i in range(E) for j in range(i + 1, E)):
+            return list(p[:k])
+    raise AssertionError("no order found")
+
+
+def test_topk_route_brute_force_with_ties():
+    r = np.random.default_rng(31)
+    for _ in range(200):
+        E = int(r.integers(1, 7))
+        k = int(r.integers(1, E + 1))
+        sc = r.integers(-2, 3, (1, E)).astype(np.int64)   # a tiny range: many ties
+        assert oracle.topk_route(sc, k)[0].tolist() == _topk_brute(sc[0].tolist(), k)
+
+
+def test_topk_route_special_cases():
+    r = np.random.default_rng(32)
+    sc = r.integers(-1000, 1000, (50, 64)).astype(np.int64)
+    # k = 1 is the first maximum (numpy's argmax returns the first one)
+    assert (oracle.topk_route(sc, 1)[:, 0] == np.argmax(sc, axis=1)).all()
+    # k = E is a stable sort by descending score
+    assert (oracle.topk_route(sc, 64) == np.argsort(-sc, axis=1, kind="stable")).all()
+    # the int64 ends, all equal scores, and a constant row
+    ext = np.array([[np.iinfo(np.int64).min, np.iinfo(np.int64).max, 0, np.iinfo(np.int64).max, -1]], np.int64)
+    assert oracle.topk_route(ext, 5)[0].tolist() == [1, 3, 2, 4, 0]
+    assert oracle.topk_route(np.zeros((1, 9), np.int64), 4)[0].tolist() == [0, 1, 2, 3]
