@@ -62,6 +62,7 @@ SIGNATURES = {
     "ei_q8_fp32_shadow": (I32, [P, P, P, P, I64, I64, I64, I32, U64, P]),
     "output_digest": (I32, [P, SZ, P, P]),
     "ei_sha256_host": (None, [P, SZ, P]),
+    "ei_topk_route": (I32, [P, I64, I64, I32, P, P]),
     "ei_ffn_workspace_bytes": (SZ, [WP, WP, I64]),
     "int_ffn_q8": (I32, [WP, WP, WP, P, P, P, I64, P, SZ, P, P]),
     "ei_moe_ffn_workspace_bytes": (SZ, [WP, WP, I64, I32]),
@@ -204,6 +205,21 @@ def gemm_q8_grouped(w: PackedWeights, x: torch.Tensor, route: torch.Tensor, limb
     if check:
         _raise_status(status, "int_gemm_q8_grouped")
     return y
+
+
+def topk_route(scores: torch.Tensor, k: int, out=None) -> torch.Tensor:
+    """Integer top-k: route[t][s] = expert of rank s (score descending, index ascending), int32 [t][k]."""
+    s = _stream()
+    if scores.dim() != 2:
+        raise EIError("ei_topk_route: scores must be [t][e]")
+    t, e = scores.shape
+    ps = _dev(scores, torch.int64, "scores")
+    route = out if out is not None else torch.empty((t, k), dtype=torch.int32, device=scores.device)
+    pr = _dev(route, torch.int32, "route")
+    if tuple(route.shape) != (t, k):
+        raise EIError(f"ei_topk_route: route must be [{t}][{k}]")
+    _check(lib().ei_topk_route(ps, t, e, k, pr, s), "ei_topk_route")
+    return route
 
 
 def ffn_workspace_bytes(wg: PackedWeights, wd: PackedWeights, t: int) -> int:

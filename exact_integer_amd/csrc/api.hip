@@ -569,6 +569,12 @@ int int_gemm_q4(const ei_weights* w, const int32_t* x, int64_t* y, int64_t t, in
                   static_cast<hipStream_t>(stream), OUT_EXACT);
 }
 
+int ei_topk_route(const int64_t* scores, int64_t t, int64_t e, int k, int32_t* route, ei_stream stream) {
+  if (!scores || !route || t < 1 || e < 1 || k < 1 || k > e) return EI_EINVAL;
+  if (e > 2048) return EI_ERANGE;
+  return launch_topk(scores, t, e, k, route, static_cast<hipStream_t>(stream)) == hipSuccess ? EI_OK : EI_EDEVICE;
+}
+
 int ei_silu_lut_build(int32_t* lut, ei_stream stream) {
   if (!lut) return EI_EINVAL;
   return launch_silu_lut(lut, static_cast<hipStream_t>(stream)) == hipSuccess ? EI_OK : EI_EDEVICE;
@@ -620,6 +626,6 @@ const char* ei_status_string(int code) {
   }
 }
 
-int ei_version(void) { return 102; }
+int ei_version(void) { return 103; }
 
 }  // extern "C"

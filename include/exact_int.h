@@ -259,6 +259,22 @@ int ei_silu_lut_build(int32_t* lut, ei_stream stream);
 int silu_lut_epilogue(const int64_t* gate, const int64_t* up, const int32_t* lut, int64_t* h,
                       int64_t n, int32_t* d_status, ei_stream stream);
 
+/* ------------------------------------------------------- routing */
+
+/*
+ * Integer top-k routing ([tritify] 3.2 "Mixture-of-Experts": integer router
+ * scores, the top-k selection an integer comparison with ties broken by
+ * index).  route[t][s] = the expert of rank s of token t in the order (score
+ * descending, expert index ascending).  The scores are typically a Q8
+ * projection of the activations with the router's weights (int_gemm_q8 with
+ * n = E); the result is the route int_gemm_q8_grouped / int_moe_ffn_q8 take.
+ *   scores   device int64 [t][e]
+ *   route    device int32 [t][k]
+ * EI_EINVAL for null pointers, t < 1, e < 1, k < 1 or k > e; EI_ERANGE for
+ * e > 2048.  Asynchronous on stream; no workspace.
+ */
+int ei_topk_route(const int64_t* scores, int64_t t, int64_t e, int k, int32_t* route, ei_stream stream);
+
 /* ------------------------------------------------------- FFN layers */
 
 /*

@@ -458,6 +458,38 @@ def test_olmoe_grouped_ffn_sampled_pairs(ei, lut):
     assert (host(ei.moe_ffn_q8(wg, wu, wd, xd, rd, dev(lut))) == out).all()
 
 
+# ---------------------------------------------------------- top-k routing
+
+@pytest.mark.parametrize("shape", [(1, 1, 1), (37, 5, 3), (100, 64, 8), (50, 100, 7), (20, 300, 20),
+                                   (9, 2048, 64), (3, 130, 130)])
+def test_topk_route_matches_oracle(ei, shape):
+    # scores from a small range, so ties are everywhere: the lower index wins
+    T, E, k = shape
+    r = np.random.default_rng(T + E + k)
+    sc = r.integers(-3, 4, (T, E)).astype(np.int64)
+    say("topk", shape)
+    assert (host(ei.topk_route(dev(sc), k)) == oracle.topk_route(sc, k)).all()
+
+
+def test_topk_route_int64_ends(ei):
+    lo, hi = np.iinfo(np.int64).min, np.iinfo(np.int64).max
+    sc = np.array([[lo, hi, 0, hi, -1, lo, 1], [lo] * 7, [hi] * 7], np.int64)
+    for k in (1, 4, 7):
+        say("topk ends", k)
+        assert (host(ei.topk_route(dev(sc), k)) == oracle.topk_route(sc, k)).all()
+
+
+def test_olmoe_integer_router(ei):
+    # the router as a Q8 projection (64 experts x 2048) of the OLMoE
+    # activations, then integer top-8: scores and route digests = oracle's
+    (rc, rs), x = synth.olmoe_router(), synth.olmoe_x()
+    say("olmoe router")
+    scores = ei.gemm_q8(ei.pack_q8(dev(rc), dev(rs)), dev(x))
+    route = ei.topk_route(scores, synth.OLMOE_TOPK)
+    assert ei.digest(scores) == GOLDEN["olmoe_router"]["scores"]
+    assert ei.digest(route) == GOLDEN["olmoe_router"]["route"]
+
+
 # ------------------------------------------------------------- FP32 shadow
 
 def test_fp32_shadow_matches_oracle_orders_and_splinters(ei):
