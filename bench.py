@@ -164,6 +164,61 @@ def _time_graph(torch, fn, steps: int, warmup: int):
     return ms[len(ms) // 2], wall / steps * 1e3
 
 
+def bench_olmoe_router(args, torch, np, ei, synth, dev) -> int:
+    """The OLMoE-shaped routed FFN behind an integer router: the router's Q8
+    projection (64 x 2048) of the 512 tokens, integer top-8, then the routed
+    FFN on that route, all inside the timed step."""
+    import oracle
+    E, H, I, T, TOPK = synth.OLMOE_E, synth.OLMOE_H, synth.OLMOE_I, synth.OLMOE_T, synth.OLMOE_TOPK
+    mats = [synth.olmoe_expert(e) for e in range(E)]
+
+    def stack(m, k):
+        return torch.from_numpy(np.ascontiguousarray(np.stack([mm[m][k] for mm in mats]))).to(dev)
+    wg, wu, wd = (ei.pack_q8_stacked(stack(m, 0), stack(m, 1)) for m in range(3))
+    rc, rs = synth.olmoe_router()
+    wr = ei.pack_q8(torch.from_numpy(rc).to(dev), torch.from_numpy(rs).to(dev))
+    x = synth.olmoe_x()
+    xd = torch.from_numpy(x).to(dev)
+    scores = torch.empty((T, E), dtype=torch.int64, device=dev)
+    route = torch.empty((T, TOPK), dtype=torch.int32, device=dev)
+    out = torch.empty((T * TOPK, H), dtype=torch.int64, device=dev)
+    ws_r = torch.empty(max(ei.workspace_bytes(wr, T), 1), dtype=torch.uint8, device=dev)
+    ws = torch.empty(ei.moe_ffn_workspace_bytes(wg, wd, T, TOPK), dtype=torch.uint8, device=dev)
+    lut = ei.silu_lut(dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def step():
+        ei.gemm_q8(wr, xd, out=scores, workspace=ws_r, status=status)
+        ei.topk_route(scores, TOPK, out=route)
+        ei.moe_ffn_q8(wg, wu, wd, xd, route, lut, out=out, workspace=ws, status=status)
+
+    ms, wall_ms = _time_graph(torch, step, args.steps, args.warmup)
+    gold = json.load(open(os.path.join(ROOT, "tests", "golden", "oracle_digests.json")))["olmoe_router"]
+    route_ok = int(status.item()) == 0 and ei.digest(route) == gold["route"]
+    rs_ = np.random.default_rng(6)
+    pairs = [(int(t), int(k)) for t, k in zip(rs_.integers(0, T, 6), rs_.integers(0, TOPK, 6))]
+    ref = oracle.moe_pairs(x, route.cpu().numpy(), lambda e: mats[e], oracle.silu_lut(), pairs=pairs,
+                           threads=min(os.cpu_count() or 1, 16))
+    got = out.cpu().numpy()
+    ok = route_ok and all((got[t * TOPK + k] == r).all() for (t, k), r in zip(pairs, ref))
+    wbytes = 3 * E * I * H * (1 + 4 / 32) + E * H * (1 + 4 / 32)
+    gbs = wbytes / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "routed expert FFN with integer router: weight GB/s", "value": round(gbs, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8xint8->int32, int64 accumulate",
+        "data": "synthetic (seeded Q8 experts and router, Q16 activations; route from the integer router)",
+        "config": {"workload": "olmoe_router_ffn", "experts": E, "hidden": H, "intermediate": I, "tokens": T,
+                   "top_k": TOPK, "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "step_ms": round(ms, 4),
+                     "weight_bytes": int(wbytes)},
+        "parity": {"route_digest_equals_oracle": route_ok, "sampled_pairs_equal_oracle": ok,
+                   "pairs_checked": len(pairs)}}))
+    return 0 if ok else 1
+
+
 def bench_olmoe(args, torch, np, ei, synth, dev) -> int:
     """The OLMoE-shaped routed FFN: 64 experts (gate/up 1024x2048, down
     2048x1024, Q8), 512 tokens, top-8: grouped gate and up projections, the
@@ -271,9 +326,10 @@ def main() -> int:
                     help="only run a plain device copy of 256 MiB, 5 times (the reference for HBM byte counters)")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="rocprofv3 --pmc output directories -> profiles/traffic.json (no GPU needed)")
-    ap.add_argument("--workload", choices=("dense", "olmoe", "qwen_ffn"), default="dense",
+    ap.add_argument("--workload", choices=("dense", "olmoe", "olmoe_router", "qwen_ffn"), default="dense",
                     help="dense: the 14336x4096 decode + prefill step (default); olmoe / qwen_ffn: the routed "
-                         "expert FFN or the 24-layer FFN chain, timed the same way")
+                         "expert FFN or the 24-layer FFN chain, timed the same way; olmoe_router: the routed "
+                         "FFN behind the integer router")
     args = ap.parse_args()
     if args.summarize_counters:
         return summarize_counters(*args.summarize_counters)
@@ -297,6 +353,8 @@ def main() -> int:
         return copy_calibration(torch, dev)
     if args.workload == "olmoe":
         return bench_olmoe(args, torch, np, ei, synth, dev)
+    if args.workload == "olmoe_router":
+        return bench_olmoe_router(args, torch, np, ei, synth, dev)
     if args.workload == "qwen_ffn":
         return bench_qwen_ffn(args, torch, np, ei, synth, dev)
 

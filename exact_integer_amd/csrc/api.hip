@@ -16,13 +16,15 @@ inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 constexpr int kSmallT = 4;   // token counts up to this use the GEMV kernel
 constexpr int kSplitParts = 8;
 
-// The tiled prefill kernel: 3 limbs, default/canonical schedule, T >= 64, and
-// 32-bit buffer offsets.
-constexpr int64_t kTiledMinT = 64;
+// The tiled prefill kernel: 3 limbs, default/canonical schedule, T >= 64,
+// 32-bit buffer offsets, and enough 128-row x 32-token workgroups to occupy the
+// chip (fewer go to the skinny kernel, which also splits K).
+constexpr int64_t kTiledMinT = 64, kTiledMinWorkgroups = 128;
 bool tiled_ok(const ei_weights* w, int64_t t, int limbs, int schedule) {
   if (limbs != 3 || t < kTiledMinT) return false;
   if (schedule != EI_SCHED_DEFAULT && schedule != EI_SCHED_CANONICAL) return false;
   const int64_t t_pad = round_up(t, kTile);
+  if ((w->n_pad + 127) / 128 * (t_pad / kTile) < kTiledMinWorkgroups) return false;
   return w->n_pad * w->k < ((int64_t)1 << 32) && 3 * t_pad * w->k < ((int64_t)1 << 32);
 }
 

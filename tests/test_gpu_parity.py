@@ -334,9 +334,9 @@ def test_repeat_runs_identical(ei):
 # ------------------------------------------------- tiled kernel accumulators
 
 def test_q8_tiled_per_limb_accumulators_extreme_scales(ei):
-    # scales at the int32 ends: the tiled kernel must take its per-limb
-    # accumulator form (one shared int64 would not be exact here)
-    N, K, T = 100, 256, 70
+    # scales at the int32 ends through the tiled kernel (8 x 17 workgroups,
+    # ragged in rows and tokens): its per-limb int64 accumulators stay exact
+    N, K, T = 1000, 256, 520
     r = np.random.default_rng(12)
     q = r.choice(np.array([-128, 127, -127, 3, 0], np.int8), size=(N, K))
     s = r.choice(np.array([-(2**31), 2**31 - 1, 1, -1, 40000], np.int64), size=(N, K // 32)).astype(np.int32)
