@@ -15,8 +15,8 @@ Sources, cited by page title and section:
               Consequence" (arXiv 2611.13730), sections 3.1, 3.2, 3.4, 4.
 
 Parity status of each function (what pins it is in tests/test_oracle_*.py):
-  q8, q4, silu_mul, limb_split, silu_lut, ffn_layer, moe_pairs, topk_route
-  -- pinned;
+  q8, q4, silu_mul, limb_split, silu_lut, ffn_layer, moe_pairs, topk_route,
+  requant, rms_inverse, rmsnorm_q16 -- pinned;
   q8_fp32 (the float negative control) -- canonical and tree_walk orders are
   pinned against numpy float32 sequences; the other orders: parity unpinned.
 """
@@ -24,6 +24,7 @@ from __future__ import annotations
 
 import ctypes
 import hashlib
+import math
 import os
 import subprocess
 from functools import lru_cache
@@ -209,6 +210,56 @@ def ffn_layer(x: np.ndarray, wg, wu, wd, lut: np.ndarray, threads: int = 1):
     d = q8(wd[0], wd[1], h, threads=threads)
     xn = x + d
     return g, u, h, d, xn
+
+
+def requant(c, m: int, k: int):
+    """Fixed-point requantization round(c * m / 2^k), rounding half away from
+    zero ([tritify] 3.1, arithmetic specification: a 128-bit product, then a
+    round-half-away-from-zero arithmetic shift).  c: int array or int; Python
+    integers throughout (the exact product).  Returns int64 values; raises if
+    one does not fit."""
+    def one(v: int) -> int:
+        p = int(v) * int(m)
+        if k == 0:
+            r = p
+        else:
+            a = (abs(p) + (1 << (k - 1))) >> k
+            r = a if p >= 0 else -a
+        if not -(1 << 63) <= r < (1 << 63):
+            raise OracleError("requant: result outside int64")
+        return r
+    if np.ndim(c) == 0:
+        return one(c)
+    return np.array([one(v) for v in np.asarray(c).ravel()], np.int64).reshape(np.shape(c))
+
+
+RMS_SHIFT = 52   # inverse-RMS fixed point: 2^52 / rms, at least 2^29 for |x| <= 2^23
+
+
+def rms_inverse(ss: int, d: int, eps_q32: int) -> int:
+    """The integer inverse-RMS of a row ([tritify] 3.2 Normalization: an exact
+    integer sum of squares and an integer inverse square root folded into a
+    scale).  Reading: for Q16 codes X with ss = sum X^2, the real mean square
+    plus eps is (ss / d + eps_q32) / 2^32, and the scale is
+    inv = floor(sqrt(2^(2*52) * d / (ss + d * eps_q32))), i.e. 2^52 / rms in the
+    codes' units, by math.isqrt of the exact floor of the rational."""
+    return math.isqrt(((1 << (2 * RMS_SHIFT)) * d) // (ss + d * eps_q32))
+
+
+def rmsnorm_q16(x: np.ndarray, g: np.ndarray, eps_q32: int) -> np.ndarray:
+    """Integer RMSNorm of Q16 rows: Y_i = round_half_away(X_i * G_i * inv / 2^52)
+    with G the Q16 norm weight and inv = rms_inverse(sum X^2, d, eps), i.e.
+    Y = X * G / sqrt(mean(X^2) + eps * 2^32) in Q16, the scale applied by one
+    requantization ([tritify] 3.1, 3.2).  x int64 [T][d], g int32 [d],
+    eps_q32 >= 1.  Returns int64 [T][d]."""
+    T, d = x.shape
+    out = np.empty((T, d), np.int64)
+    gi = [int(v) for v in g]
+    for t in range(T):
+        row = [int(v) for v in x[t]]
+        inv = rms_inverse(sum(v * v for v in row), d, int(eps_q32))
+        out[t] = [requant(row[i] * gi[i], inv, RMS_SHIFT) for i in range(d)]
+    return out
 
 
 def topk_route(scores: np.ndarray, k: int) -> np.ndarray:

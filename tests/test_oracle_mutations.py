@@ -155,3 +155,53 @@ def _topk_mutant(key):
 def test_topk_mutants_are_caught(name, key):
     assert _topk_checks(oracle.topk_route)
     assert not _topk_checks(_topk_mutant(key)), name
+
+
+# ------------------------------------ requantization and RMSNorm (Python oracle)
+
+def _rms_checks(requant, rms_inverse) -> bool:
+    """The requant / inverse-RMS pins, applied to candidate implementations."""
+    from decimal import Decimal, getcontext
+    from fractions import Fraction
+    import math
+    getcontext().prec = 80
+    r = np.random.default_rng(44)
+    for _ in range(300):
+        c, m, k = int(r.integers(-(2**40), 2**40)), int(r.integers(1, 2**40)), int(r.integers(1, 60))
+        fr = Fraction(c * m, 2**k)
+        want = int(abs(fr) + Fraction(1, 2)) * (1 if fr >= 0 else -1)
+        if requant(c, m, k) != want:
+            return False
+    for _ in range(300):
+        d, eps = int(r.integers(1, 3000)), int(r.integers(1, 2**32))
+        ss = int(r.integers(0, d * 2**44))
+        if rms_inverse(ss, d, eps) != int((Decimal(2**104) * d / (ss + d * eps)).sqrt()):
+            return False
+    return True
+
+
+def _requant_half_even(c, m, k):
+    from fractions import Fraction
+    return round(Fraction(int(c) * int(m), 2**k))     # Python rounds half to even
+
+
+def _requant_floor(c, m, k):
+    return (int(c) * int(m)) >> k
+
+
+def _rms_no_d(ss, d, eps):
+    import math
+    return math.isqrt((1 << 104) // (ss + d * eps))
+
+
+def _rms_eps_unscaled(ss, d, eps):
+    import math
+    return math.isqrt(((1 << 104) * d) // (ss + eps))
+
+
+@pytest.mark.parametrize("name", ["half_even", "floor", "no_d", "eps_unscaled"])
+def test_rms_mutants_are_caught(name):
+    assert _rms_checks(oracle.requant, oracle.rms_inverse)
+    rq = {"half_even": _requant_half_even, "floor": _requant_floor}.get(name, oracle.requant)
+    ri = {"no_d": _rms_no_d, "eps_unscaled": _rms_eps_unscaled}.get(name, oracle.rms_inverse)
+    assert not _rms_checks(rq, ri), name

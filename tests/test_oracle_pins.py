@@ -6,10 +6,9 @@ that reduce to a library routine (numpy integer matmul), invariants the
 pages state (schedule invariance, row-order = column-stream), and brute
 force with Python's arbitrary-precision integers on tiny inputs.
 """
+import itertools
 import math
 import os
-
-import itertools
 
 import numpy as np
 import pytest
@@ -426,3 +425,73 @@ def test_topk_route_special_cases():
     ext = np.array([[np.iinfo(np.int64).min, np.iinfo(np.int64).max, 0, np.iinfo(np.int64).max, -1]], np.int64)
     assert oracle.topk_route(ext, 5)[0].tolist() == [1, 3, 2, 4, 0]
     assert oracle.topk_route(np.zeros((1, 9), np.int64), 4)[0].tolist() == [0, 1, 2, 3]
+
+
+# -------------------------------------------- requantization and RMSNorm
+
+def _half_away(fr):
+    """Round a Fraction half away from zero (exact)."""
+    from fractions import Fraction
+    a = abs(fr)
+    n = int(a + Fraction(1, 2))   # floor(|v| + 1/2)
+    return n if fr >= 0 else -n
+
+
+def test_requant_exact_halves_and_fractions():
+    from fractions import Fraction
+    # exact halves go away from zero; quarters to the nearer integer
+    assert [oracle.requant(v, 1, 1) for v in (3, -3, 1, -1, 2, -2)] == [2, -2, 1, -1, 1, -1]
+    assert [oracle.requant(v, 1, 2) for v in (5, -5, 6, -6, 7, -7)] == [1, -1, 2, -2, 2, -2]
+    r = np.random.default_rng(41)
+    for _ in range(2000):
+        c = int(r.integers(-(2**62), 2**62))
+        m = int(r.integers(1, 2**63 - 1))
+        k = int(r.integers(64, 126))
+        want = _half_away(Fraction(c * m, 2**k))
+        if -(2**63) <= want < 2**63:
+            assert oracle.requant(c, m, k) == want
+
+
+def test_rms_inverse_against_decimal_sqrt_and_float64():
+    from decimal import Decimal, getcontext
+    getcontext().prec = 80
+    r = np.random.default_rng(42)
+    worst = 0.0
+    for _ in range(3000):
+        d = int(r.integers(1, 5000))
+        ss = int(r.integers(0, d * 2**46))
+        eps = int(r.integers(1, 2**32))
+        inv = oracle.rms_inverse(ss, d, eps)
+        exact = (Decimal(2**104) * d / (ss + d * eps)).sqrt()
+        assert inv == int(exact)                       # the floor of the exact root
+        ref = 2.0**52 / math.sqrt(ss / d + eps)       # float64 1/sqrt, the pages' twin
+        worst = max(worst, abs(inv - ref) / ref)
+    assert worst < 2e-9                                # [tritify] Table 1: below 2e-9
+
+
+def test_rmsnorm_q16_against_exact_real_rounding():
+    from decimal import Decimal, getcontext
+    getcontext().prec = 80
+    r = np.random.default_rng(43)
+    for d in (1, 7, 64, 896):
+        x = np.clip(np.rint(r.normal(0, 1, (3, d)) * 2**16), -(2**22), 2**22).astype(np.int64)
+        g = r.integers(2**15, 2**17, d).astype(np.int32)
+        eps = 42950   # 1e-5 in Q32
+        y = oracle.rmsnorm_q16(x, g, eps)
+        for t in range(3):
+            ms = Decimal(sum(int(v) ** 2 for v in x[t])) / d + eps
+            rs = ms.sqrt()
+            for i in range(d):
+                v = Decimal(int(x[t, i])) * int(g[i]) / rs
+                want = int(v + Decimal("0.5")) if v >= 0 else -int(-v + Decimal("0.5"))
+                assert abs(int(y[t, i]) - want) <= 1
+
+
+def test_rmsnorm_q16_closed_form():
+    # X = 3 and eps = 16 in code units: mean square + eps = 25, rms = 5; with
+    # G = 5 * 2^16 every output is X * G / 5 = 3 * 2^16 after rounding
+    x = np.full((2, 9), 3, np.int64)
+    x[1] = -3
+    g = np.full(9, 5 * 2**16, np.int32)
+    y = oracle.rmsnorm_q16(x, g, 16)
+    assert (y[0] == 3 * 2**16).all() and (y[1] == -3 * 2**16).all()
