@@ -167,7 +167,7 @@ def _rms_checks(requant, rms_inverse) -> bool:
     getcontext().prec = 80
     r = np.random.default_rng(44)
     for _ in range(300):
-        c, m, k = int(r.integers(-(2**40), 2**40)), int(r.integers(1, 2**40)), int(r.integers(1, 60))
+        c, m, k = int(r.integers(-(2**40), 2**40)), int(r.integers(1, 2**40)), int(r.integers(24, 60))
         fr = Fraction(c * m, 2**k)
         want = int(abs(fr) + Fraction(1, 2)) * (1 if fr >= 0 else -1)
         if requant(c, m, k) != want:
