@@ -166,6 +166,9 @@ def _rms_checks(requant, rms_inverse) -> bool:
     import math
     getcontext().prec = 80
     r = np.random.default_rng(44)
+    for v in (1, 3, 5, 7, -1, -3, -5, -7):   # exact halves
+        if requant(v, 1, 1) != (abs(v) + 1) // 2 * (1 if v > 0 else -1):
+            return False
     for _ in range(300):
         c, m, k = int(r.integers(-(2**40), 2**40)), int(r.integers(1, 2**40)), int(r.integers(24, 60))
         fr = Fraction(c * m, 2**k)
