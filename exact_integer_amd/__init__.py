@@ -63,6 +63,8 @@ SIGNATURES = {
     "output_digest": (I32, [P, SZ, P, P]),
     "ei_sha256_host": (None, [P, SZ, P]),
     "ei_topk_route": (I32, [P, I64, I64, I32, P, P]),
+    "ei_requant": (I32, [P, I64, I32, P, I64, P, P]),
+    "ei_rmsnorm_q16": (I32, [P, P, I64, P, I64, I64, P, P]),
     "ei_ffn_workspace_bytes": (SZ, [WP, WP, I64]),
     "int_ffn_q8": (I32, [WP, WP, WP, P, P, P, I64, P, SZ, P, P]),
     "ei_moe_ffn_workspace_bytes": (SZ, [WP, WP, I64, I32]),
@@ -204,6 +206,41 @@ def gemm_q8_grouped(w: PackedWeights, x: torch.Tensor, route: torch.Tensor, limb
                                      workspace.numel(), status.data_ptr(), s), "int_gemm_q8_grouped")
     if check:
         _raise_status(status, "int_gemm_q8_grouped")
+    return y
+
+
+def requant(c: torch.Tensor, m: int, k: int, out=None, status=None) -> torch.Tensor:
+    """y = round_half_away(c * m / 2^k), int64, elementwise."""
+    s = _stream()
+    pc = _dev(c, torch.int64, "c")
+    y = out if out is not None else torch.empty_like(c)
+    py = _dev(y, torch.int64, "y")
+    if y.numel() != c.numel():
+        raise EIError("ei_requant: y must have c's size")
+    check = status is None
+    if check:
+        status = torch.zeros(1, dtype=torch.int32, device=c.device)
+    _check(lib().ei_requant(pc, m, k, py, c.numel(), status.data_ptr(), s), "ei_requant")
+    if check:
+        _raise_status(status, "ei_requant")
+    return y
+
+
+def rmsnorm_q16(x: torch.Tensor, g: torch.Tensor, eps_q32: int, out=None, status=None) -> torch.Tensor:
+    """Integer RMSNorm of Q16 rows with a Q16 weight g and eps in Q32 (int64 [t][d])."""
+    s = _stream()
+    t, d = x.shape
+    px, pg = _dev(x, torch.int64, "x"), _dev(g, torch.int32, "g")
+    if g.numel() != d:
+        raise EIError(f"ei_rmsnorm_q16: g must have {d} entries")
+    y = out if out is not None else torch.empty_like(x)
+    py = _dev(y, torch.int64, "y")
+    check = status is None
+    if check:
+        status = torch.zeros(1, dtype=torch.int32, device=x.device)
+    _check(lib().ei_rmsnorm_q16(px, pg, eps_q32, py, t, d, status.data_ptr(), s), "ei_rmsnorm_q16")
+    if check:
+        _raise_status(status, "ei_rmsnorm_q16")
     return y
 
 

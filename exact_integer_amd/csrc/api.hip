@@ -577,6 +577,21 @@ int ei_topk_route(const int64_t* scores, int64_t t, int64_t e, int k, int32_t* r
   return launch_topk(scores, t, e, k, route, static_cast<hipStream_t>(stream)) == hipSuccess ? EI_OK : EI_EDEVICE;
 }
 
+int ei_requant(const int64_t* c, int64_t m, int k, int64_t* y, int64_t n, int32_t* d_status, ei_stream stream) {
+  if (n < 0 || (n > 0 && (!c || !y)) || k < 0 || k > 126) return EI_EINVAL;
+  return launch_requant(c, m, k, y, n, d_status, static_cast<hipStream_t>(stream)) == hipSuccess ? EI_OK
+                                                                                                 : EI_EDEVICE;
+}
+
+int ei_rmsnorm_q16(const int64_t* x, const int32_t* g, int64_t eps_q32, int64_t* y, int64_t t, int64_t d,
+                   int32_t* d_status, ei_stream stream) {
+  if (!x || !g || !y || t < 1 || d < 1) return EI_EINVAL;
+  if (d > 65536 || eps_q32 < 1 || eps_q32 > ((int64_t)1 << 32)) return EI_ERANGE;
+  return launch_rmsnorm_q16(x, g, eps_q32, y, t, d, d_status, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? EI_OK
+             : EI_EDEVICE;
+}
+
 int ei_silu_lut_build(int32_t* lut, ei_stream stream) {
   if (!lut) return EI_EINVAL;
   return launch_silu_lut(lut, static_cast<hipStream_t>(stream)) == hipSuccess ? EI_OK : EI_EDEVICE;
@@ -628,6 +643,6 @@ const char* ei_status_string(int code) {
   }
 }
 
-int ei_version(void) { return 103; }
+int ei_version(void) { return 104; }
 
 }  // extern "C"

@@ -129,6 +129,10 @@ hipError_t launch_tree_terms(int64_t* terms, int64_t nb, int64_t* y, int64_t t, 
 hipError_t launch_make_perm(int32_t* perm, int64_t n, uint64_t seed, hipStream_t s);
 hipError_t launch_silu_lut(int32_t* lut, hipStream_t s);
 hipError_t launch_topk(const int64_t* scores, int64_t t, int64_t e, int k, int32_t* route, hipStream_t s);
+hipError_t launch_rmsnorm_q16(const int64_t* x, const int32_t* g, int64_t eps, int64_t* y, int64_t t, int64_t d,
+                              int32_t* status, hipStream_t s);
+hipError_t launch_requant(const int64_t* c, int64_t m, int k, int64_t* y, int64_t n, int32_t* status,
+                          hipStream_t s);
 hipError_t launch_shadow(const int8_t* q, const int32_t* s, const int64_t* x, float* y, int64_t n, int64_t k,
                          int64_t t, int schedule, uint64_t seed, hipStream_t st);
 hipError_t launch_silu_mul(const int64_t* g, const int64_t* u, const int32_t* lut, int64_t* h,

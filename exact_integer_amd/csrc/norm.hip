@@ -1,0 +1,107 @@
+// Requantization and integer RMSNorm ("Deterministic, Reproducible Inference
+// in Exact Integer Arithmetic ...", 3.1 arithmetic specification: a scale is
+// an integer mantissa m and a shift k, applied as round(c * m / 2^k) with a
+// 128-bit product and a round-half-away-from-zero shift; 3.2 Normalization:
+// the sum of squares is an exact integer reduction and the per-row
+// inverse-RMS an integer inverse square root folded into the scale).
+//
+// RMSNorm of Q16 codes X with a Q16 weight G and eps in Q32:
+//   inv = floor(sqrt(2^104 d / (sum X^2 + d eps)))      (= 2^52 / rms, exact)
+//   Y_i = round_half_away(X_i * G_i * inv / 2^52)
+// One workgroup per row: the squares are summed in uint64 (|X| <= 2^23 and
+// d <= 2^16 keep the sum below 2^63), one thread forms inv from a float64
+// estimate corrected to the exact floor with 128-bit integer comparisons, and
+// the row is scaled in a second pass.
+#include "ei_internal.h"
+
+namespace ei {
+
+constexpr int kRmsShift = 52;
+constexpr int kNormThreads = 256;
+
+// round_half_away(p / 2^k) for |p| < 2^127, 0 <= k <= 126; false if the
+// result does not fit int64.
+__device__ inline bool shift_half_away(__int128 p, int k, int64_t* out) {
+  if (k == 0) return fit_i64(p, out);
+  const unsigned __int128 a = ((unsigned __int128)(p < 0 ? -p : p) + ((unsigned __int128)1 << (k - 1))) >> k;
+  return fit_i64(p < 0 ? -(__int128)a : (__int128)a, out);
+}
+
+// floor(sqrt(2^104 d / den)) for 1 <= d <= 2^16 and d <= den < 2^63: the
+// quotient n = floor(2^104 d / den) <= 2^104, so its root is at most 2^52 and
+// a float64 estimate is within one of it; the exact floor is then fixed by
+// comparing squares (z^2 <= n  <=>  z <= sqrt(2^104 d / den) for integer z).
+__device__ inline uint64_t rms_inverse(uint64_t ss, int64_t d, int64_t eps) {
+  const uint64_t den = ss + (uint64_t)d * (uint64_t)eps;
+  const unsigned __int128 n = ((unsigned __int128)(uint64_t)d << 104) / den;
+  const double nd = (double)(uint64_t)(n >> 64) * 18446744073709551616.0 + (double)(uint64_t)n;
+  uint64_t z = (uint64_t)sqrt(nd);
+  while (z > 0 && (unsigned __int128)z * z > n) --z;
+  while ((unsigned __int128)(z + 1) * (z + 1) <= n) ++z;
+  return z;
+}
+
+__global__ __launch_bounds__(kNormThreads) void rmsnorm_q16_kernel(const int64_t* __restrict__ x,
+                                                                  const int32_t* __restrict__ g, int64_t eps,
+                                                                  int64_t* __restrict__ y, int64_t d,
+                                                                  int32_t* status) {
+  __shared__ uint64_t part[kNormThreads / 64];
+  __shared__ uint64_t inv_s;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t* row = x + (int64_t)blockIdx.x * d;
+  int64_t* out = y + (int64_t)blockIdx.x * d;
+  uint64_t ss = 0;
+  bool ok = true;
+  for (int64_t i = tid; i < d; i += kNormThreads) {
+    const int64_t v = row[i];
+    const bool in = v >= -((int64_t)1 << 23) && v <= ((int64_t)1 << 23);
+    ok = ok && in;
+    ss += in ? (uint64_t)(v * v) : 0;
+  }
+  if (!ok) flag(status, EI_DEV_LIMB_RANGE);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)ss, o, 64), hi = __shfl_xor((uint32_t)(ss >> 32), o, 64);
+    ss += ((uint64_t)hi << 32) | lo;
+  }
+  if (lane == 0) part[wave] = ss;
+  __syncthreads();
+  if (tid == 0) {
+    uint64_t tot = 0;
+    for (int w = 0; w < kNormThreads / 64; ++w) tot += part[w];
+    inv_s = rms_inverse(tot, d, eps);
+  }
+  __syncthreads();
+  const uint64_t inv = inv_s;
+  for (int64_t i = tid; i < d; i += kNormThreads) {
+    int64_t v;
+    // |X G| <= 2^23 2^31, times inv <= 2^52: below 2^106
+    if (!shift_half_away((__int128)(row[i] * (int64_t)g[i]) * (__int128)inv, kRmsShift, &v))
+      flag(status, EI_DEV_OUT_RANGE);
+    out[i] = v;
+  }
+}
+
+__global__ void requant_kernel(const int64_t* __restrict__ c, int64_t m, int k, int64_t* __restrict__ y, int64_t n,
+                               int32_t* status) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= n) return;
+  int64_t v;
+  if (!shift_half_away((__int128)c[e] * (__int128)m, k, &v)) flag(status, EI_DEV_OUT_RANGE);
+  y[e] = v;
+}
+
+hipError_t launch_rmsnorm_q16(const int64_t* x, const int32_t* g, int64_t eps, int64_t* y, int64_t t, int64_t d,
+                              int32_t* status, hipStream_t s) {
+  hipLaunchKernelGGL(rmsnorm_q16_kernel, dim3((unsigned)t), dim3(kNormThreads), 0, s, x, g, eps, y, d, status);
+  return hipGetLastError();
+}
+
+hipError_t launch_requant(const int64_t* c, int64_t m, int k, int64_t* y, int64_t n, int32_t* status,
+                          hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(requant_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, c, m, k, y, n, status);
+  return hipGetLastError();
+}
+
+}  // namespace ei

@@ -259,6 +259,38 @@ int ei_silu_lut_build(int32_t* lut, ei_stream stream);
 int silu_lut_epilogue(const int64_t* gate, const int64_t* up, const int32_t* lut, int64_t* h,
                       int64_t n, int32_t* d_status, ei_stream stream);
 
+/* ------------------------------------------ requantization and norms */
+
+/*
+ * Fixed-point requantization ([tritify] 3.1, arithmetic specification: a
+ * scale is an integer mantissa and a shift; scaling is a 128-bit product and
+ * a round-half-away-from-zero arithmetic shift):
+ *   y[e] = round_half_away(c[e] * m / 2^k),   0 <= k <= 126.
+ *   c, y     device int64 [n] (may be the same buffer)
+ * EI_EINVAL for null pointers with n > 0, n < 0 or k outside [0, 126]; a
+ * result outside int64 is written as 0 and sets EI_DEV_OUT_RANGE.
+ */
+int ei_requant(const int64_t* c, int64_t m, int k, int64_t* y, int64_t n, int32_t* d_status, ei_stream stream);
+
+/*
+ * Integer RMSNorm of Q16 rows ([tritify] 3.2 Normalization: an exact integer
+ * sum of squares, the inverse-RMS by an integer inverse square root, folded
+ * into an integer scale and applied by one requantization):
+ *   inv = floor(sqrt(2^104 d / (sum_i X_i^2 + d eps_q32)))     (2^52 / rms)
+ *   Y_i = round_half_away(X_i * G_i * inv / 2^52)
+ * i.e. Y = X G / sqrt(mean(X^2) + eps) in Q16 with the float-free scale; inv
+ * is within 2^-29 of 2^52 / rms (relative).
+ *   x        device int64 [t][d], Q16 codes with |X| <= 2^23
+ *   g        device int32 [d], the norm weight in Q16
+ *   eps_q32  eps * 2^32, in [1, 2^32]
+ *   y        device int64 [t][d]
+ * EI_EINVAL for null pointers, t < 1 or d < 1; EI_ERANGE for d > 65536 or
+ * eps_q32 outside [1, 2^32]; |X| > 2^23 sets EI_DEV_LIMB_RANGE (that row's
+ * output is not meaningful).
+ */
+int ei_rmsnorm_q16(const int64_t* x, const int32_t* g, int64_t eps_q32, int64_t* y, int64_t t, int64_t d,
+                   int32_t* d_status, ei_stream stream);
+
 /* ------------------------------------------------------- routing */
 
 /*

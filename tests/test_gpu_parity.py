@@ -458,6 +458,42 @@ def test_olmoe_grouped_ffn_sampled_pairs(ei, lut):
     assert (host(ei.moe_ffn_q8(wg, wu, wd, xd, rd, dev(lut))) == out).all()
 
 
+# ------------------------------------------- requantization and RMSNorm
+
+def test_requant_matches_oracle(ei):
+    r = np.random.default_rng(51)
+    c = np.concatenate([r.integers(-(2**62), 2**62, 4000), np.arange(-9, 10),
+                        [np.iinfo(np.int64).min + 1, np.iinfo(np.int64).max]]).astype(np.int64)
+    for m, k in ((1, 0), (1, 1), (3, 2), (2**31 - 7, 31), (-(2**40) + 3, 60), (2**63 - 1, 126), (-(2**63), 126)):
+        say("requant", m, k)
+        assert (host(ei.requant(dev(c), m, k)) == oracle.requant(c, m, k)).all(), (m, k)
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1), (3, 7, 42950), (16, 896, 42950), (4, 2048, 2**32),
+                                   (2, 65536, 429497)])
+def test_rmsnorm_q16_matches_oracle(ei, shape):
+    T, D, eps = shape
+    r = np.random.default_rng(T * D)
+    x = synth.q16_acts(r, T, D)
+    g = r.integers(2**15, 2**17, D).astype(np.int32)
+    say("rmsnorm", shape)
+    assert (host(ei.rmsnorm_q16(dev(x), dev(g), eps)) == oracle.rmsnorm_q16(x, g, eps)).all()
+
+
+def test_rmsnorm_q16_extremes_and_range_flag(ei):
+    D = 4096
+    x = np.full((3, D), 2**23, np.int64)
+    x[1] = -(2**23)
+    x[2, ::2] = 0
+    g = np.full(D, 2**31 - 1, np.int32)
+    g[::3] = -(2**31)
+    say("rmsnorm extremes")
+    assert (host(ei.rmsnorm_q16(dev(x), dev(g), 1)) == oracle.rmsnorm_q16(x, g, 1)).all()
+    x[0, 5] = 2**23 + 1
+    with pytest.raises(ei.EIError):
+        ei.rmsnorm_q16(dev(x), dev(g), 1)
+
+
 # ---------------------------------------------------------- top-k routing
 
 @pytest.mark.parametrize("shape", [(1, 1, 1), (37, 5, 3), (100, 64, 8), (50, 100, 7), (20, 300, 20),
