@@ -67,6 +67,7 @@ SIGNATURES = {
     "ei_rmsnorm_q16": (I32, [P, P, I64, P, I64, I64, P, P]),
     "ei_ffn_workspace_bytes": (SZ, [WP, WP, I64]),
     "int_ffn_q8": (I32, [WP, WP, WP, P, P, P, I64, P, SZ, P, P]),
+    "int_ffn_q8_prenorm": (I32, [WP, WP, WP, P, I64, P, P, P, I64, P, SZ, P, P]),
     "ei_moe_ffn_workspace_bytes": (SZ, [WP, WP, I64, I32]),
     "int_moe_ffn_q8": (I32, [WP, WP, WP, P, P, I64, I32, P, P, P, SZ, P, P]),
     "ei_status_string": (ctypes.c_char_p, [I32]),
@@ -284,6 +285,29 @@ def ffn_q8(wg: PackedWeights, wu: PackedWeights, wd: PackedWeights, x: torch.Ten
                             workspace.data_ptr(), workspace.numel(), status.data_ptr(), s), "int_ffn_q8")
     if check:
         _raise_status(status, "int_ffn_q8")
+    return y
+
+
+def ffn_q8_prenorm(wg: PackedWeights, wu: PackedWeights, wd: PackedWeights, g_norm: torch.Tensor, eps_q32: int,
+                   x: torch.Tensor, lut: torch.Tensor, out=None, workspace=None, status=None) -> torch.Tensor:
+    """Pre-norm FFN layer: y = x + Q8(wd, silu_mul(Q8(wg, n), Q8(wu, n))), n = rmsnorm_q16(x, g_norm, eps)."""
+    s = _stream()
+    t, d = x.shape
+    if d != wg.k or wu.k != wg.k or wu.n != wg.n or wd.k != wg.n or wd.n != wg.k or g_norm.numel() != d:
+        raise EIError("int_ffn_q8_prenorm: shapes must be wg, wu [f][d], wd [d][f], g_norm [d], x [t][d]")
+    px, pl, pg = _dev(x, torch.int64, "x"), _dev(lut, torch.int32, "lut"), _dev(g_norm, torch.int32, "g_norm")
+    y = out if out is not None else torch.empty((t, d), dtype=torch.int64, device=x.device)
+    py = _dev(y, torch.int64, "y")
+    if workspace is None:
+        workspace = torch.empty(max(ffn_workspace_bytes(wg, wd, t), 1), dtype=torch.uint8, device=x.device)
+    check = status is None
+    if check:
+        status = torch.zeros(1, dtype=torch.int32, device=x.device)
+    _check(lib().int_ffn_q8_prenorm(ctypes.byref(wg.desc), ctypes.byref(wu.desc), ctypes.byref(wd.desc), pg,
+                                    eps_q32, px, pl, py, t, workspace.data_ptr(), workspace.numel(),
+                                    status.data_ptr(), s), "int_ffn_q8_prenorm")
+    if check:
+        _raise_status(status, "int_ffn_q8_prenorm")
     return y
 
 

@@ -325,7 +325,7 @@ hipError_t launch_grouped_projection(const ei_weights* w, const GroupedLayout& g
 // projections' own workspace.
 struct FfnLayout {
   bool fused;
-  size_t h_off, g_off, u_off, gemm_off, total;
+  size_t h_off, g_off, u_off, n_off, gemm_off, total;
 };
 
 FfnLayout ffn_layout(const ei_weights* wg, const ei_weights* wd, int64_t t) {
@@ -343,6 +343,9 @@ FfnLayout ffn_layout(const ei_weights* wg, const ei_weights* wd, int64_t t) {
     f.u_off = 2 * hb;
     off = 3 * hb;
   }
+  // the normalized input (prenorm form, unfused path)
+  f.n_off = off;
+  if (!f.fused) off += align_up(sizeof(int64_t) * (size_t)t * (size_t)wg->k);
   f.gemm_off = off;
   f.total = off + (lg.total > ld.total ? lg.total : ld.total);
   return f;
@@ -450,23 +453,31 @@ size_t ei_ffn_workspace_bytes(const ei_weights* wg, const ei_weights* wd, int64_
   return ffn_layout(wg, wd, t).total;
 }
 
-int int_ffn_q8(const ei_weights* wg, const ei_weights* wu, const ei_weights* wd, const int64_t* x,
-               const int32_t* lut, int64_t* y, int64_t t, void* workspace, size_t workspace_bytes,
-               int32_t* d_status, ei_stream stream) {
+}  // extern "C"
+
+namespace {
+
+// y = x + FFN(x), or y = x + FFN(rmsnorm(x)) when gnorm is given.
+int ffn_run(const ei_weights* wg, const ei_weights* wu, const ei_weights* wd, const int64_t* x,
+            const int32_t* gnorm, int64_t eps_q32, const int32_t* lut, int64_t* y, int64_t t, void* workspace,
+            size_t workspace_bytes, int32_t* d_status, hipStream_t s) {
   if (!x || !lut || !y || t < 1) return EI_EINVAL;
   const int c = ffn_check(wg, wu, wd);
   if (c != EI_OK) return c;
+  if (gnorm && (wg->k > 65536 || eps_q32 < 1 || eps_q32 > ((int64_t)1 << 32))) return EI_ERANGE;
   const FfnLayout f = ffn_layout(wg, wd, t);
   if (!workspace || workspace_bytes < f.total) return EI_ENOSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   void* gws = ws + f.gemm_off;
   const size_t gws_bytes = workspace_bytes - f.gemm_off;
   if (f.fused) {
-    // gate and up in one pass, the SiLU-gated product in its epilogue
+    // gate and up in one pass, the SiLU-gated product in its epilogue; the
+    // (normalized) input goes straight into limb tiles
     const WsLayout lay = layout_for(wg, t, 3, EI_SCHED_DEFAULT);
     int8_t* limb = static_cast<int8_t*>(gws) + lay.limb_off;
-    if (launch_limb_tiles(x, 0, t, wg->k, 3, limb, lay.t_pad, d_status, s) != hipSuccess) return EI_EDEVICE;
+    const hipError_t e = gnorm ? launch_rmsnorm_limb_tiles(x, gnorm, eps_q32, limb, t, lay.t_pad, wg->k, d_status, s)
+                               : launch_limb_tiles(x, 0, t, wg->k, 3, limb, lay.t_pad, d_status, s);
+    if (e != hipSuccess) return EI_EDEVICE;
     GemmArgs a;
     std::memset(&a, 0, sizeof a);
     const uint8_t* bg = static_cast<const uint8_t*>(wg->packed);
@@ -492,14 +503,39 @@ int int_ffn_q8(const ei_weights* wg, const ei_weights* wu, const ei_weights* wd,
     return run_gemm(wd, nullptr, 0, y, t, 3, EI_SCHED_DEFAULT, 0, gws, gws_bytes, d_status, s, OUT_ROUND_Q24, x,
                     reinterpret_cast<const int8_t*>(ws + f.h_off));
   }
+  const int64_t* xin = x;
+  if (gnorm) {
+    int64_t* n = reinterpret_cast<int64_t*>(ws + f.n_off);
+    if (launch_rmsnorm_q16(x, gnorm, eps_q32, n, t, wg->k, d_status, s) != hipSuccess) return EI_EDEVICE;
+    xin = n;
+  }
   int64_t* h = reinterpret_cast<int64_t*>(ws + f.h_off);
   int64_t* g = reinterpret_cast<int64_t*>(ws + f.g_off);
   int64_t* u = reinterpret_cast<int64_t*>(ws + f.u_off);
-  int r = run_gemm(wg, x, 0, g, t, 3, EI_SCHED_DEFAULT, 0, gws, gws_bytes, d_status, s, OUT_ROUND_Q24);
-  if (r == EI_OK) r = run_gemm(wu, x, 0, u, t, 3, EI_SCHED_DEFAULT, 0, gws, gws_bytes, d_status, s, OUT_ROUND_Q24);
+  int r = run_gemm(wg, xin, 0, g, t, 3, EI_SCHED_DEFAULT, 0, gws, gws_bytes, d_status, s, OUT_ROUND_Q24);
+  if (r == EI_OK) r = run_gemm(wu, xin, 0, u, t, 3, EI_SCHED_DEFAULT, 0, gws, gws_bytes, d_status, s, OUT_ROUND_Q24);
   if (r != EI_OK) return r;
   if (launch_silu_mul(g, u, lut, h, t * wg->n, d_status, s) != hipSuccess) return EI_EDEVICE;
   return run_gemm(wd, h, 0, y, t, 3, EI_SCHED_DEFAULT, 0, gws, gws_bytes, d_status, s, OUT_ROUND_Q24, x);
+}
+
+}  // namespace
+
+extern "C" {
+
+int int_ffn_q8(const ei_weights* wg, const ei_weights* wu, const ei_weights* wd, const int64_t* x,
+               const int32_t* lut, int64_t* y, int64_t t, void* workspace, size_t workspace_bytes,
+               int32_t* d_status, ei_stream stream) {
+  return ffn_run(wg, wu, wd, x, nullptr, 0, lut, y, t, workspace, workspace_bytes, d_status,
+                 static_cast<hipStream_t>(stream));
+}
+
+int int_ffn_q8_prenorm(const ei_weights* wg, const ei_weights* wu, const ei_weights* wd, const int32_t* g_norm,
+                       int64_t eps_q32, const int64_t* x, const int32_t* lut, int64_t* y, int64_t t,
+                       void* workspace, size_t workspace_bytes, int32_t* d_status, ei_stream stream) {
+  if (!g_norm) return EI_EINVAL;
+  return ffn_run(wg, wu, wd, x, g_norm, eps_q32, lut, y, t, workspace, workspace_bytes, d_status,
+                 static_cast<hipStream_t>(stream));
 }
 
 size_t ei_moe_ffn_workspace_bytes(const ei_weights* wg, const ei_weights* wd, int64_t rows, int topk) {
@@ -643,6 +679,6 @@ const char* ei_status_string(int code) {
   }
 }
 
-int ei_version(void) { return 104; }
+int ei_version(void) { return 105; }
 
 }  // extern "C"

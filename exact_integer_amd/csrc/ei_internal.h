@@ -131,6 +131,8 @@ hipError_t launch_silu_lut(int32_t* lut, hipStream_t s);
 hipError_t launch_topk(const int64_t* scores, int64_t t, int64_t e, int k, int32_t* route, hipStream_t s);
 hipError_t launch_rmsnorm_q16(const int64_t* x, const int32_t* g, int64_t eps, int64_t* y, int64_t t, int64_t d,
                               int32_t* status, hipStream_t s);
+hipError_t launch_rmsnorm_limb_tiles(const int64_t* x, const int32_t* g, int64_t eps, int8_t* tiles, int64_t t,
+                                     int64_t t_pad, int64_t d, int32_t* status, hipStream_t s);   // d % 32 == 0
 hipError_t launch_requant(const int64_t* c, int64_t m, int k, int64_t* y, int64_t n, int32_t* status,
                           hipStream_t s);
 hipError_t launch_shadow(const int8_t* q, const int32_t* s, const int64_t* x, float* y, int64_t n, int64_t k,

@@ -41,15 +41,32 @@ __device__ inline uint64_t rms_inverse(uint64_t ss, int64_t d, int64_t eps) {
   return z;
 }
 
+// kTiles: the normalized row goes out as 3-limb activation tiles for the MFMA
+// kernels ([3][t_pad/32][d/32][64 lanes][16 B]; d a multiple of 32), with
+// rows t .. t_pad-1 of the last token tile written as zeros; otherwise as
+// int64 y [t][d].
+template <bool kTiles>
 __global__ __launch_bounds__(kNormThreads) void rmsnorm_q16_kernel(const int64_t* __restrict__ x,
                                                                   const int32_t* __restrict__ g, int64_t eps,
-                                                                  int64_t* __restrict__ y, int64_t d,
+                                                                  int64_t* __restrict__ y, int8_t* __restrict__ tiles,
+                                                                  int64_t t, int64_t t_pad, int64_t d,
                                                                   int32_t* status) {
   __shared__ uint64_t part[kNormThreads / 64];
   __shared__ uint64_t inv_s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t* row = x + (int64_t)blockIdx.x * d;
-  int64_t* out = y + (int64_t)blockIdx.x * d;
+  const int64_t tok = blockIdx.x;
+  if (kTiles && tok >= t) {   // padding token of the last tile: zero limbs
+    const int64_t nb = d / 32, tg = tok / kTile, tgs = t_pad / kTile;
+    const int tl = (int)(tok % kTile);
+    const v4i z = {0, 0, 0, 0};
+    for (int64_t c = tid; c < 2 * nb; c += kNormThreads)
+#pragma unroll
+      for (int l = 0; l < 3; ++l)
+        reinterpret_cast<v4i*>(tiles)[((l * tgs + tg) * nb + c / 2) * 64 + tl + 32 * (c & 1)] = z;
+    return;
+  }
+  const int64_t* row = x + tok * d;
+  int64_t* out = kTiles ? nullptr : y + tok * d;
   uint64_t ss = 0;
   bool ok = true;
   for (int64_t i = tid; i < d; i += kNormThreads) {
@@ -73,12 +90,41 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_q16_kernel(const int64_t
   }
   __syncthreads();
   const uint64_t inv = inv_s;
-  for (int64_t i = tid; i < d; i += kNormThreads) {
-    int64_t v;
-    // |X G| <= 2^23 2^31, times inv <= 2^52: below 2^106
-    if (!shift_half_away((__int128)(row[i] * (int64_t)g[i]) * (__int128)inv, kRmsShift, &v))
-      flag(status, EI_DEV_OUT_RANGE);
-    out[i] = v;
+  // |X G| <= 2^23 2^31, times inv <= 2^52: below 2^106
+  auto scaled = [&](int64_t i, int64_t* v) {
+    return shift_half_away((__int128)(row[i] * (int64_t)g[i]) * (__int128)inv, kRmsShift, v);
+  };
+  if constexpr (!kTiles) {
+    for (int64_t i = tid; i < d; i += kNormThreads) {
+      int64_t v;
+      if (!scaled(i, &v)) flag(status, EI_DEV_OUT_RANGE);
+      out[i] = v;
+    }
+  } else {
+    // one 16-column half block per item: lane tok % 32 + 32 (half) of block c / 2
+    const int64_t nb = d / 32, tg = tok / kTile, tgs = t_pad / kTile;
+    const int tl = (int)(tok % kTile);
+    bool range_ok = true, fit = true;
+    for (int64_t c = tid; c < 2 * nb; c += kNormThreads) {
+      uint32_t words[3][4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        int64_t v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) fit = scaled(16 * c + 4 * q + j, &v[j]) && fit;
+        uint32_t w[3];
+        range_ok = limb_words<3>(v, w) && range_ok;
+#pragma unroll
+        for (int l = 0; l < 3; ++l) words[l][q] = w[l];
+      }
+#pragma unroll
+      for (int l = 0; l < 3; ++l) {
+        const v4i v = {(int)words[l][0], (int)words[l][1], (int)words[l][2], (int)words[l][3]};
+        reinterpret_cast<v4i*>(tiles)[((l * tgs + tg) * nb + c / 2) * 64 + tl + 32 * (c & 1)] = v;
+      }
+    }
+    if (!fit) flag(status, EI_DEV_OUT_RANGE);
+    if (!range_ok) flag(status, EI_DEV_LIMB_RANGE);
   }
 }
 
@@ -93,7 +139,15 @@ __global__ void requant_kernel(const int64_t* __restrict__ c, int64_t m, int k, 
 
 hipError_t launch_rmsnorm_q16(const int64_t* x, const int32_t* g, int64_t eps, int64_t* y, int64_t t, int64_t d,
                               int32_t* status, hipStream_t s) {
-  hipLaunchKernelGGL(rmsnorm_q16_kernel, dim3((unsigned)t), dim3(kNormThreads), 0, s, x, g, eps, y, d, status);
+  hipLaunchKernelGGL(rmsnorm_q16_kernel<false>, dim3((unsigned)t), dim3(kNormThreads), 0, s, x, g, eps, y,
+                     (int8_t*)nullptr, t, t, d, status);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_limb_tiles(const int64_t* x, const int32_t* g, int64_t eps, int8_t* tiles, int64_t t,
+                                     int64_t t_pad, int64_t d, int32_t* status, hipStream_t s) {
+  hipLaunchKernelGGL(rmsnorm_q16_kernel<true>, dim3((unsigned)t_pad), dim3(kNormThreads), 0, s, x, g, eps,
+                     (int64_t*)nullptr, tiles, t, t_pad, d, status);
   return hipGetLastError();
 }
 

@@ -334,6 +334,19 @@ int int_ffn_q8(const ei_weights* wg, const ei_weights* wu, const ei_weights* wd,
                int32_t* d_status, ei_stream stream);
 
 /*
+ * The same layer behind an integer RMSNorm ([tritify] 3.2 Normalization; the
+ * pre-norm residual block): y = x + FFN(ei_rmsnorm_q16(x, g_norm, eps_q32)),
+ * with FFN as int_ffn_q8 and the residual taken from x itself.  On the fused
+ * path the normalized rows go straight into the gate/up limb tiles.
+ *   g_norm   device int32 [d], Q16;  eps_q32 in [1, 2^32];  d <= 65536
+ * Workspace: ei_ffn_workspace_bytes(wg, wd, t).  Errors as int_ffn_q8 and
+ * ei_rmsnorm_q16.
+ */
+int int_ffn_q8_prenorm(const ei_weights* wg, const ei_weights* wu, const ei_weights* wd, const int32_t* g_norm,
+                       int64_t eps_q32, const int64_t* x, const int32_t* lut, int64_t* y, int64_t t,
+                       void* workspace, size_t workspace_bytes, int32_t* d_status, ei_stream stream);
+
+/*
  * The routed (mixture-of-experts) feed-forward layer ([tritify] 3.2
  * "Mixture-of-Experts": each selected expert is an exact-integer MLP; the
  * gate as in [Handshake] C1 and C4): for every pair (r, s), with

@@ -281,6 +281,17 @@ def topk_route(scores: np.ndarray, k: int) -> np.ndarray:
     return out
 
 
+def ffn_layer_prenorm(x: np.ndarray, g_norm: np.ndarray, eps_q32: int, wg, wu, wd, lut: np.ndarray,
+                      threads: int = 1):
+    """The pre-norm residual block: n = rmsnorm_q16(x, g_norm, eps), then
+    ffn_layer's gate, up, SiLU product and down projection on n, and
+    x_next = x + d (the residual from the un-normalized x).  Returns
+    (n, d, x_next)."""
+    n = rmsnorm_q16(x, g_norm, eps_q32)
+    _, _, _, d, _ = ffn_layer(n, wg, wu, wd, lut, threads=threads)
+    return n, d, x + d
+
+
 def moe_pairs(x: np.ndarray, route: np.ndarray, experts, lut: np.ndarray, pairs=None,
               down_rows=None, threads: int = 1) -> np.ndarray:
     """Routed expert FFNs: out[t][k] = Wd_e (silu(Wg_e x_t) * (Wu_e x_t) >> 16)

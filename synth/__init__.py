@@ -186,6 +186,15 @@ def olmoe_x(t: int = OLMOE_T):
     return q16_acts(rng_for("olmoe_grouped", 0, "x"), t, OLMOE_H)
 
 
+QWEN_RMS_EPS_Q32 = 4295   # eps = 1e-6 (the Qwen2.5 family's norm epsilon) in Q32
+
+
+def qwen_norm_weight(layer: int):
+    """The layer's RMSNorm weight in Q16: rint(N(1, 0.1) * 2^16) as int32 [896]."""
+    r = rng_for("qwen05b_ffn", layer, "norm")
+    return np.rint(r.normal(1.0, 0.1, QWEN_D) * 2**16).astype(np.int32)
+
+
 def olmoe_router():
     """The router's Q8 weights [64 experts][2048] (integer router scores)."""
     return q8_matrix("olmoe_grouped", 0, "router", OLMOE_E, OLMOE_H)

@@ -48,6 +48,16 @@ def main(threads: int = 8) -> None:
         print("ffn layer", layer, layers[-1]["x_next"][:16], flush=True)
     out["qwen05b_ffn"] = {"layers": layers}
 
+    x = synth.qwen_ffn_x0()
+    layers = []
+    for layer in range(synth.QWEN_LAYERS):
+        wg, wu, wd = synth.qwen_ffn_layer(layer)
+        _, d, x = oracle.ffn_layer_prenorm(x, synth.qwen_norm_weight(layer), synth.QWEN_RMS_EPS_Q32, wg, wu, wd,
+                                           lut, threads=threads)
+        layers.append({"d": oracle.digest(d), "x_next": oracle.digest(x)})
+        print("prenorm ffn layer", layer, layers[-1]["x_next"][:16], flush=True)
+    out["qwen05b_ffn_prenorm"] = {"eps_q32": synth.QWEN_RMS_EPS_Q32, "layers": layers}
+
     (rc, rs), xo = synth.olmoe_router(), synth.olmoe_x()
     scores = oracle.q8(rc, rs, xo, threads=threads)
     out["olmoe_router"] = {"scores": oracle.digest(scores),

@@ -265,6 +265,39 @@ def test_ffn_q8_matches_the_separate_steps(ei, lut, shape):
     assert (y == xn).all()
 
 
+@pytest.mark.parametrize("shape", [(96, 64, 1), (160, 96, 30), (128, 64, 40), (64, 4096, 30), (4096, 64, 30),
+                                   (96, 160, 70)])
+def test_ffn_q8_prenorm_matches_oracle(ei, lut, shape):
+    # the RMSNorm in front of the layer: fused into the gate/up limb tiles (5..63
+    # tokens), or as its own pass ahead of the GEMV, tiled and unfused paths
+    F, D, T = shape
+    r = np.random.default_rng(F * 3 + D + T)
+    mats = [(synth.q8_codes(r, F, D), synth.q8_scales(r, F, D)), (synth.q8_codes(r, F, D), synth.q8_scales(r, F, D)),
+            (synth.q8_codes(r, D, F), synth.q8_scales(r, D, F))]
+    x = synth.q16_acts(r, T, D)
+    gn = np.rint(r.normal(1.0, 0.2, D) * 2**16).astype(np.int32)
+    eps = int(r.integers(1, 2**20))
+    wg, wu, wd = (ei.pack_q8(dev(c), dev(sc)) for c, sc in mats)
+    say("ffn prenorm", shape)
+    y = host(ei.ffn_q8_prenorm(wg, wu, wd, dev(gn), eps, dev(x), dev(lut)))
+    _, _, xn = oracle.ffn_layer_prenorm(x, gn, eps, mats[0], mats[1], mats[2], lut)
+    assert (y == xn).all()
+
+
+def test_qwen_ffn_24_layers_prenorm(ei):
+    lut = ei.silu_lut()
+    x = dev(synth.qwen_ffn_x0())
+    y = torch.empty_like(x)
+    gold = GOLDEN["qwen05b_ffn_prenorm"]
+    for layer in range(synth.QWEN_LAYERS):
+        (gc, gs), (uc, us), (dc, ds) = synth.qwen_ffn_layer(layer)
+        wg, wu, wd = ei.pack_q8(dev(gc), dev(gs)), ei.pack_q8(dev(uc), dev(us)), ei.pack_q8(dev(dc), dev(ds))
+        say("prenorm ffn layer", layer)
+        ei.ffn_q8_prenorm(wg, wu, wd, dev(synth.qwen_norm_weight(layer)), gold["eps_q32"], x, lut, out=y)
+        x, y = y, x
+        assert ei.digest(x) == gold["layers"][layer]["x_next"], layer
+
+
 def test_qwen_ffn_24_layers_fused(ei):
     lut = ei.silu_lut()
     x = dev(synth.qwen_ffn_x0())
