@@ -270,7 +270,7 @@ def bench_olmoe(args, torch, np, ei, synth, dev) -> int:
     return 0 if ok else 1
 
 
-def bench_qwen_ffn(args, torch, np, ei, synth, dev) -> int:
+def bench_qwen_ffn(args, torch, np, ei, synth, dev, prenorm: bool = False) -> int:
     """The Qwen2.5-0.5B-shaped FFN chain: 24 layers of gate and up (4864x896)
     and down (896x4864) Q8 projections at T=30 with the SiLU-gated product and
     the residual add, fresh weights per layer (353 MB, read once per step)."""
@@ -287,24 +287,33 @@ def bench_qwen_ffn(args, torch, np, ei, synth, dev) -> int:
     lut = ei.silu_lut(dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
 
+    norms = [torch.from_numpy(synth.qwen_norm_weight(i)).to(dev) for i in range(synth.QWEN_LAYERS)]
+
     def step():   # layer l reads x_l and writes x_{l+1}; the first reads x0
         src = x0
         for i, (wg, wu, wd) in enumerate(layers):
             dst = bufs[i % 2]
-            ei.ffn_q8(wg, wu, wd, src, lut, out=dst, workspace=ws, status=status)
+            if prenorm:
+                ei.ffn_q8_prenorm(wg, wu, wd, norms[i], synth.QWEN_RMS_EPS_Q32, src, lut, out=dst, workspace=ws,
+                                  status=status)
+            else:
+                ei.ffn_q8(wg, wu, wd, src, lut, out=dst, workspace=ws, status=status)
             src = dst
 
     ms, wall_ms = _time_graph(torch, step, args.steps, args.warmup)
-    gold = _json.load(open(os.path.join(ROOT, "tests", "golden", "oracle_digests.json")))["qwen05b_ffn"]["layers"]
+    gold = _json.load(open(os.path.join(ROOT, "tests", "golden", "oracle_digests.json")))[
+        "qwen05b_ffn_prenorm" if prenorm else "qwen05b_ffn"]["layers"]
     ok = int(status.item()) == 0 and ei.digest(bufs[(synth.QWEN_LAYERS - 1) % 2]) == gold[-1]["x_next"]
     wbytes = synth.QWEN_LAYERS * 3 * F * D * (1 + 4 / 32)
     gbs = wbytes / (ms * 1e-3) / 1e9
     print(json.dumps({
-        "metric": "24-layer Q8 FFN chain: weight GB/s", "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
+        "metric": ("24-layer pre-norm Q8 FFN chain" if prenorm else "24-layer Q8 FFN chain") + ": weight GB/s",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall_ms, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "int8xint8->int32, int64 accumulate",
         "data": "synthetic (seeded Q8 layers, Q16 activations)",
-        "config": {"workload": "qwen05b_ffn_24_layers", "tokens": T, "hidden": D, "intermediate": F,
+        "config": {"workload": "qwen05b_ffn_24_layers" + ("_prenorm" if prenorm else ""), "tokens": T,
+                   "hidden": D, "intermediate": F,
                    "layers": synth.QWEN_LAYERS, "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "step_ms": round(ms, 4),
@@ -326,10 +335,12 @@ def main() -> int:
                     help="only run a plain device copy of 256 MiB, 5 times (the reference for HBM byte counters)")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="rocprofv3 --pmc output directories -> profiles/traffic.json (no GPU needed)")
-    ap.add_argument("--workload", choices=("dense", "olmoe", "olmoe_router", "qwen_ffn"), default="dense",
+    ap.add_argument("--workload", choices=("dense", "olmoe", "olmoe_router", "qwen_ffn", "qwen_ffn_prenorm"),
+                    default="dense",
                     help="dense: the 14336x4096 decode + prefill step (default); olmoe / qwen_ffn: the routed "
                          "expert FFN or the 24-layer FFN chain, timed the same way; olmoe_router: the routed "
-                         "FFN behind the integer router")
+                         "FFN behind the integer router; qwen_ffn_prenorm: the chain with an integer RMSNorm "
+                         "in front of every layer")
     args = ap.parse_args()
     if args.summarize_counters:
         return summarize_counters(*args.summarize_counters)
@@ -355,8 +366,8 @@ def main() -> int:
         return bench_olmoe(args, torch, np, ei, synth, dev)
     if args.workload == "olmoe_router":
         return bench_olmoe_router(args, torch, np, ei, synth, dev)
-    if args.workload == "qwen_ffn":
-        return bench_qwen_ffn(args, torch, np, ei, synth, dev)
+    if args.workload in ("qwen_ffn", "qwen_ffn_prenorm"):
+        return bench_qwen_ffn(args, torch, np, ei, synth, dev, prenorm=args.workload == "qwen_ffn_prenorm")
 
     def to_dev(a):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)

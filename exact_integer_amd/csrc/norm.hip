@@ -10,7 +10,7 @@
 //   Y_i = round_half_away(X_i * G_i * inv / 2^52)
 // One workgroup per row: the squares are summed in uint64 (|X| <= 2^23 and
 // d <= 2^16 keep the sum below 2^63), one thread forms inv from a float64
-// estimate corrected to the exact floor with 128-bit integer comparisons, and
+// estimate corrected to the exact floor with 128-bit integer products, and
 // the row is scaled in a second pass.
 #include "ei_internal.h"
 
@@ -27,17 +27,18 @@ __device__ inline bool shift_half_away(__int128 p, int k, int64_t* out) {
   return fit_i64(p < 0 ? -(__int128)a : (__int128)a, out);
 }
 
-// floor(sqrt(2^104 d / den)) for 1 <= d <= 2^16 and d <= den < 2^63: the
-// quotient n = floor(2^104 d / den) <= 2^104, so its root is at most 2^52 and
-// a float64 estimate is within one of it; the exact floor is then fixed by
-// comparing squares (z^2 <= n  <=>  z <= sqrt(2^104 d / den) for integer z).
+// floor(sqrt(2^104 d / den)) for 1 <= d <= 2^16 and d <= den < 2^63, i.e.
+// the largest z with z^2 den <= 2^104 d (no division: z^2 den is an integer
+// and 2^104 d / den >= z^2 iff z^2 den <= 2^104 d).  The root is at most 2^52;
+// a float64 estimate is within 2 of it, and near the root z^2 den stays below
+// 2^121, so the two correction loops compare exact 128-bit products.
 __device__ inline uint64_t rms_inverse(uint64_t ss, int64_t d, int64_t eps) {
   const uint64_t den = ss + (uint64_t)d * (uint64_t)eps;
-  const unsigned __int128 n = ((unsigned __int128)(uint64_t)d << 104) / den;
-  const double nd = (double)(uint64_t)(n >> 64) * 18446744073709551616.0 + (double)(uint64_t)n;
-  uint64_t z = (uint64_t)sqrt(nd);
-  while (z > 0 && (unsigned __int128)z * z > n) --z;
-  while ((unsigned __int128)(z + 1) * (z + 1) <= n) ++z;
+  const unsigned __int128 lim = (unsigned __int128)(uint64_t)d << 104;
+  uint64_t z = (uint64_t)(sqrt((double)d / (double)den) * 4503599627370496.0);   // 2^52
+  auto above = [&](uint64_t v) { return (unsigned __int128)v * v * den > lim; };
+  while (z > 0 && above(z)) --z;
+  while (!above(z + 1)) ++z;
   return z;
 }
 
@@ -101,27 +102,21 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_q16_kernel(const int64_t
       out[i] = v;
     }
   } else {
-    // one 16-column half block per item: lane tok % 32 + 32 (half) of block c / 2
+    // item i = four consecutive columns 4i .. 4i+3: word i % 4 of the 16-byte
+    // piece of lane tok % 32 + 32 (half) in block i / 8, half (i / 4) % 2
     const int64_t nb = d / 32, tg = tok / kTile, tgs = t_pad / kTile;
     const int tl = (int)(tok % kTile);
     bool range_ok = true, fit = true;
-    for (int64_t c = tid; c < 2 * nb; c += kNormThreads) {
-      uint32_t words[3][4];
+    for (int64_t i = tid; i < d / 4; i += kNormThreads) {
+      int64_t v[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        int64_t v[4];
+      for (int j = 0; j < 4; ++j) fit = scaled(4 * i + j, &v[j]) && fit;
+      uint32_t w[3];
+      range_ok = limb_words<3>(v, w) && range_ok;
+      const int64_t lane16 = tl + 32 * ((i >> 2) & 1);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) fit = scaled(16 * c + 4 * q + j, &v[j]) && fit;
-        uint32_t w[3];
-        range_ok = limb_words<3>(v, w) && range_ok;
-#pragma unroll
-        for (int l = 0; l < 3; ++l) words[l][q] = w[l];
-      }
-#pragma unroll
-      for (int l = 0; l < 3; ++l) {
-        const v4i v = {(int)words[l][0], (int)words[l][1], (int)words[l][2], (int)words[l][3]};
-        reinterpret_cast<v4i*>(tiles)[((l * tgs + tg) * nb + c / 2) * 64 + tl + 32 * (c & 1)] = v;
-      }
+      for (int l = 0; l < 3; ++l)
+        reinterpret_cast<uint32_t*>(tiles)[(((l * tgs + tg) * nb + (i >> 3)) * 64 + lane16) * 4 + (i & 3)] = w[l];
     }
     if (!fit) flag(status, EI_DEV_OUT_RANGE);
     if (!range_ok) flag(status, EI_DEV_LIMB_RANGE);
