@@ -16,7 +16,7 @@ Sources, cited by page title and section:
 
 Parity status of each function (what pins it is in tests/test_oracle_*.py):
   q8, q4, silu_mul, limb_split, silu_lut, ffn_layer, moe_pairs, topk_route,
-  requant, rms_inverse, rmsnorm_q16 -- pinned;
+  requant, rms_inverse, rmsnorm_q16, wide_gemm -- pinned;
   q8_fp32 (the float negative control) -- canonical and tree_walk orders are
   pinned against numpy float32 sequences; the other orders: parity unpinned.
 """
@@ -259,6 +259,34 @@ def rmsnorm_q16(x: np.ndarray, g: np.ndarray, eps_q32: int) -> np.ndarray:
         row = [int(v) for v in x[t]]
         inv = rms_inverse(sum(v * v for v in row), d, int(eps_q32))
         out[t] = [requant(row[i] * gi[i], inv, RMS_SHIFT) for i in range(d)]
+    return out
+
+
+WIDE_TRITS = 12
+WIDE_CODE_MAX = (3 ** WIDE_TRITS - 1) // 2   # 265,720
+
+
+def wide_gemm(codes: np.ndarray, acts: np.ndarray) -> np.ndarray:
+    """The wide-code linear kernel ([tritify] 3.1 and 3.2 Matmul: weights are
+    integer codes of b = 12 balanced trits, activations int32 codes, the
+    products i32 x i32 accumulated exactly; no rounding):
+        y[t][i] = sum_j codes[i][j] * acts[t][j]
+    codes int32 [N][K], acts int32 [T][K]; returns int64 [T][N].  numpy's
+    int64 matmul is exact when sum_j |c| |a| < 2^63, which is checked first;
+    otherwise Python integers are used (and the result must fit int64)."""
+    c = np.asarray(codes, np.int64)
+    a = np.asarray(acts, np.int64)
+    bound = int(np.abs(c).max(initial=0)) * int(np.abs(a).max(initial=0)) * c.shape[1]
+    if bound < (1 << 63):
+        return a @ c.T
+    out = np.empty((a.shape[0], c.shape[0]), np.int64)
+    cl, al = c.tolist(), a.tolist()
+    for t in range(a.shape[0]):
+        for i in range(c.shape[0]):
+            v = sum(x * y for x, y in zip(cl[i], al[t]))
+            if not -(1 << 63) <= v < (1 << 63):
+                raise OracleError("wide_gemm: result outside int64")
+            out[t, i] = v
     return out
 
 

@@ -186,6 +186,34 @@ def olmoe_x(t: int = OLMOE_T):
     return q16_acts(rng_for("olmoe_grouped", 0, "x"), t, OLMOE_H)
 
 
+WIDE_N, WIDE_K, WIDE_T = 896, 896, 4096   # the wide-code hot kernel: 896x896 weights, 4096 rows
+
+
+def wide_trits(r: np.random.Generator, n: int, k: int) -> np.ndarray:
+    """12 balanced trits per weight, uniform in {-1, 0, 1}: int8 [12][n][k]."""
+    return r.integers(-1, 2, (12, n, k)).astype(np.int8)
+
+
+def wide_codes_from_trits(trits: np.ndarray) -> np.ndarray:
+    """code = sum_i 3^i trit_i (the balanced-ternary value), int32 [n][k]."""
+    w = np.zeros(trits.shape[1:], np.int64)
+    for i in range(trits.shape[0]):
+        w += (3 ** i) * trits[i].astype(np.int64)
+    return w.astype(np.int32)
+
+
+def wide_acts(r: np.random.Generator, t: int, k: int) -> np.ndarray:
+    """Activations quantized per tensor by their own maximum to the
+    interchange level 2^28: rint(v / max|v| * 2^28), v ~ N(0, 1); int32 [t][k]."""
+    v = r.normal(0.0, 1.0, (t, k))
+    return np.rint(v / np.abs(v).max() * 2**28).astype(np.int32)
+
+
+def wide_inputs(t: int = WIDE_T):
+    trits = wide_trits(rng_for("wide_gemm", 0, "w"), WIDE_N, WIDE_K)
+    return wide_codes_from_trits(trits), wide_acts(rng_for("wide_gemm", 0, "x"), t, WIDE_K)
+
+
 QWEN_RMS_EPS_Q32 = 4295   # eps = 1e-6 (the Qwen2.5 family's norm epsilon) in Q32
 
 

@@ -58,6 +58,9 @@ def main(threads: int = 8) -> None:
         print("prenorm ffn layer", layer, layers[-1]["x_next"][:16], flush=True)
     out["qwen05b_ffn_prenorm"] = {"eps_q32": synth.QWEN_RMS_EPS_Q32, "layers": layers}
 
+    c, a = synth.wide_inputs()
+    out["wide_896x896_t4096"] = {"inputs": synth.input_sha256(c, a), "y": oracle.digest(oracle.wide_gemm(c, a))}
+
     (rc, rs), xo = synth.olmoe_router(), synth.olmoe_x()
     scores = oracle.q8(rc, rs, xo, threads=threads)
     out["olmoe_router"] = {"scores": oracle.digest(scores),

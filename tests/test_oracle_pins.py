@@ -495,3 +495,46 @@ def test_rmsnorm_q16_closed_form():
     g = np.full(9, 5 * 2**16, np.int32)
     y = oracle.rmsnorm_q16(x, g, 16)
     assert (y[0] == 3 * 2**16).all() and (y[1] == -3 * 2**16).all()
+
+
+# ------------------------------------------------------- wide-code GEMM
+
+def test_wide_gemm_brute_force():
+    r = np.random.default_rng(61)
+    for n, k, t in ((1, 1, 1), (3, 5, 2), (7, 33, 4)):
+        c = synth.wide_codes_from_trits(synth.wide_trits(r, n, k))
+        a = r.integers(-(2**31), 2**31, (t, k)).astype(np.int32)
+        y = oracle.wide_gemm(c, a)
+        for tt in range(t):
+            for i in range(n):
+                assert int(y[tt, i]) == sum(int(c[i, j]) * int(a[tt, j]) for j in range(k))
+
+
+def test_wide_gemm_trit_planes_and_one_hot():
+    r = np.random.default_rng(62)
+    trits = synth.wide_trits(r, 40, 96)
+    c = synth.wide_codes_from_trits(trits)
+    assert int(np.abs(c).max()) <= oracle.WIDE_CODE_MAX
+    a = synth.wide_acts(r, 6, 96)
+    # a second derivation: one integer matmul per trit plane, weighted by 3^i
+    planes = sum((3 ** i) * (a.astype(np.int64) @ trits[i].astype(np.int64).T) for i in range(12))
+    assert (oracle.wide_gemm(c, a) == planes).all()
+    # one-hot activations pick columns of the codes
+    e = np.zeros((3, 96), np.int32)
+    e[0, 5], e[1, 0], e[2, 95] = 1, -1, 7
+    y = oracle.wide_gemm(c, e)
+    assert (y[0] == c[:, 5]).all() and (y[1] == -c[:, 0]).all() and (y[2] == 7 * c[:, 95].astype(np.int64)).all()
+
+
+def test_wide_gemm_beyond_the_int64_fast_path():
+    # |c| |a| K above 2^63 takes the Python-integer path; one large activation
+    # and alternating +-1 elsewhere keep the exact sums in int64 with a plain
+    # closed form
+    K = 1025
+    c = np.full((2, K), 8355711, np.int32)
+    c[1] = -8355711
+    a = np.ones((1, K), np.int64)
+    a[0, 2::2] = -1
+    a[0, 0] = 2**31 - 1
+    y = oracle.wide_gemm(c, a.astype(np.int32))
+    assert y[0, 0] == 8355711 * (2**31 - 1) and y[0, 1] == -8355711 * (2**31 - 1)
