@@ -63,6 +63,10 @@ SIGNATURES = {
     "output_digest": (I32, [P, SZ, P, P]),
     "ei_sha256_host": (None, [P, SZ, P]),
     "ei_topk_route": (I32, [P, I64, I64, I32, P, P]),
+    "ei_wide_packed_bytes": (SZ, [I64, I64]),
+    "ei_wide_pack": (I32, [P, I64, I64, P, SZ, WP, P]),
+    "ei_wide_workspace_bytes": (SZ, [WP, I64]),
+    "int_gemm_wide": (I32, [WP, P, P, I64, P, SZ, P, P]),
     "ei_requant": (I32, [P, I64, I32, P, I64, P, P]),
     "ei_rmsnorm_q16": (I32, [P, P, I64, P, I64, I64, P, P]),
     "ei_ffn_workspace_bytes": (SZ, [WP, WP, I64]),
@@ -242,6 +246,42 @@ def rmsnorm_q16(x: torch.Tensor, g: torch.Tensor, eps_q32: int, out=None, status
     _check(lib().ei_rmsnorm_q16(px, pg, eps_q32, py, t, d, status.data_ptr(), s), "ei_rmsnorm_q16")
     if check:
         _raise_status(status, "ei_rmsnorm_q16")
+    return y
+
+
+def pack_wide(codes: torch.Tensor) -> PackedWeights:
+    """Repack wide integer codes (int32 [n][k], |c| <= 8,355,711) into digit tiles."""
+    s = _stream()
+    n, k = codes.shape
+    pc = _dev(codes, torch.int32, "codes")
+    nbytes = int(lib().ei_wide_packed_bytes(n, k))
+    if nbytes == 0:
+        raise EIError(f"ei_wide_pack: bad shape {n}x{k}")
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=codes.device)
+    desc = Weights()
+    _check(lib().ei_wide_pack(pc, n, k, buf.data_ptr(), nbytes, ctypes.byref(desc), s), "ei_wide_pack")
+    return PackedWeights(buf, desc)
+
+
+def gemm_wide(w: PackedWeights, x: torch.Tensor, out=None, workspace=None, status=None) -> torch.Tensor:
+    """y = x @ codes^T exactly (int32 [t][k] activations, int64 [t][n] result)."""
+    s = _stream()
+    t, k = x.shape
+    if k != w.k:
+        raise EIError(f"int_gemm_wide: x has k={k}, weights k={w.k}")
+    px = _dev(x, torch.int32, "x")
+    y = out if out is not None else torch.empty((t, w.n), dtype=torch.int64, device=x.device)
+    py = _dev(y, torch.int64, "y")
+    if workspace is None:
+        workspace = torch.empty(int(lib().ei_wide_workspace_bytes(ctypes.byref(w.desc), t)), dtype=torch.uint8,
+                                device=x.device)
+    check = status is None
+    if check:
+        status = torch.zeros(1, dtype=torch.int32, device=x.device)
+    _check(lib().int_gemm_wide(ctypes.byref(w.desc), px, py, t, workspace.data_ptr(), workspace.numel(),
+                               status.data_ptr(), s), "int_gemm_wide")
+    if check:
+        _raise_status(status, "int_gemm_wide")
     return y
 
 

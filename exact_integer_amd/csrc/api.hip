@@ -613,6 +613,71 @@ int ei_topk_route(const int64_t* scores, int64_t t, int64_t e, int k, int32_t* r
   return launch_topk(scores, t, e, k, route, static_cast<hipStream_t>(stream)) == hipSuccess ? EI_OK : EI_EDEVICE;
 }
 
+size_t ei_wide_packed_bytes(int64_t n, int64_t k) {
+  if (n < 1 || k < 32 || k % 32 != 0) return 0;
+  return (size_t)kHeaderBytes + (size_t)round_up(n, kTile) * (size_t)k * 3u;
+}
+
+int ei_wide_pack(const int32_t* codes, int64_t n, int64_t k, void* packed, size_t packed_bytes, ei_weights* out,
+                 ei_stream stream) {
+  if (!codes || !packed || !out || n < 1 || k < 32 || k % 32 != 0) return EI_EINVAL;
+  if (!aligned(packed, 256) || !aligned(codes, 16)) return EI_EINVAL;
+  if (packed_bytes < ei_wide_packed_bytes(n, k)) return EI_ENOSPACE;
+  const int64_t n_pad = round_up(n, kTile);
+  if (n_pad * k * 3 >= ((int64_t)1 << 32)) return EI_ERANGE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  PackedHeader h;
+  std::memset(&h, 0, sizeof h);
+  h.magic = kMagic;
+  h.format = EI_FORMAT_WIDE;
+  h.n = n;
+  h.k = k;
+  h.n_pad = n_pad;
+  h.nb = k / 32;
+  h.codes_off = kHeaderBytes;
+  h.scales_off = 0;
+  PackedHeader* dh = static_cast<PackedHeader*>(packed);
+  if (hipMemcpyAsync(dh, &h, sizeof h, hipMemcpyHostToDevice, s) != hipSuccess) return EI_EDEVICE;
+  // pad0 of the device header collects the range flag of the digit split
+  if (launch_wide_pack(codes, n, k, n_pad, static_cast<int8_t*>(packed) + kHeaderBytes, &dh->pad0, s) != hipSuccess)
+    return EI_EDEVICE;
+  if (hipMemcpyAsync(&h, dh, sizeof h, hipMemcpyDeviceToHost, s) != hipSuccess) return EI_EDEVICE;
+  if (hipStreamSynchronize(s) != hipSuccess) return EI_EDEVICE;
+  if (h.magic != kMagic || h.n != n || h.k != k) return EI_EDEVICE;
+  if (h.pad0 != 0) return EI_ERANGE;
+  out->packed = packed;
+  out->n = n;
+  out->k = k;
+  out->n_pad = n_pad;
+  out->nb = k / 32;
+  out->smax = 0;
+  out->format = EI_FORMAT_WIDE;
+  out->experts = 1;
+  out->expert_stride = (int64_t)align_up(ei_wide_packed_bytes(n, k));
+  return EI_OK;
+}
+
+size_t ei_wide_workspace_bytes(const ei_weights* w, int64_t t) {
+  if (!w || t < 1) return 0;
+  return (size_t)4 * (size_t)round_up(t, kTile) * (size_t)w->k;
+}
+
+int int_gemm_wide(const ei_weights* w, const int32_t* x, int64_t* y, int64_t t, void* workspace,
+                  size_t workspace_bytes, int32_t* d_status, ei_stream stream) {
+  if (!w || !w->packed || w->format != EI_FORMAT_WIDE || !x || !y || t < 1) return EI_EINVAL;
+  if (w->k < 32 || w->k % 32 != 0 || w->nb != w->k / 32 || w->n_pad != round_up(w->n, kTile)) return EI_EINVAL;
+  const int64_t t_pad = round_up(t, kTile);
+  if (w->k > 32768 || 4 * t_pad * w->k >= ((int64_t)1 << 32)) return EI_ERANGE;
+  if (!workspace || workspace_bytes < ei_wide_workspace_bytes(w, t)) return EI_ENOSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int8_t* atiles = static_cast<int8_t*>(workspace);
+  if (launch_limb_tiles(x, 1, t, w->k, 4, atiles, t_pad, d_status, s) != hipSuccess) return EI_EDEVICE;
+  const int8_t* wtiles = static_cast<const int8_t*>(w->packed) + kHeaderBytes;
+  return launch_wide_gemm(wtiles, atiles, y, w->n, t, w->n_pad, t_pad, w->nb, d_status, s) == hipSuccess
+             ? EI_OK
+             : EI_EDEVICE;
+}
+
 int ei_requant(const int64_t* c, int64_t m, int k, int64_t* y, int64_t n, int32_t* d_status, ei_stream stream) {
   if (n < 0 || (n > 0 && (!c || !y)) || k < 0 || k > 126) return EI_EINVAL;
   return launch_requant(c, m, k, y, n, d_status, static_cast<hipStream_t>(stream)) == hipSuccess ? EI_OK
@@ -679,6 +744,6 @@ const char* ei_status_string(int code) {
   }
 }
 
-int ei_version(void) { return 105; }
+int ei_version(void) { return 106; }
 
 }  // extern "C"

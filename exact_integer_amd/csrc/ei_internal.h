@@ -128,6 +128,10 @@ hipError_t launch_tree_terms(int64_t* terms, int64_t nb, int64_t* y, int64_t t, 
                              int limbs, int out_mode, int32_t* status, hipStream_t s);
 hipError_t launch_make_perm(int32_t* perm, int64_t n, uint64_t seed, hipStream_t s);
 hipError_t launch_silu_lut(int32_t* lut, hipStream_t s);
+hipError_t launch_wide_pack(const int32_t* codes, int64_t n, int64_t k, int64_t n_pad, int8_t* tiles, uint32_t* bad,
+                            hipStream_t s);
+hipError_t launch_wide_gemm(const int8_t* wtiles, const int8_t* atiles, int64_t* y, int64_t n, int64_t t,
+                            int64_t n_pad, int64_t t_pad, int64_t nb, int32_t* status, hipStream_t s);
 hipError_t launch_topk(const int64_t* scores, int64_t t, int64_t e, int k, int32_t* route, hipStream_t s);
 hipError_t launch_rmsnorm_q16(const int64_t* x, const int32_t* g, int64_t eps, int64_t* y, int64_t t, int64_t d,
                               int32_t* status, hipStream_t s);
@@ -224,6 +228,23 @@ __device__ inline bool limb_words(const int64_t (&v)[4], uint32_t (&w)[L]) {
 // VGPR.  Word 3 is the gfx9 raw-buffer configuration (32-bit data format).
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// Direct-to-LDS copy of 16 bytes per lane from buffer r at voffset +
+// soffset; lane i writes LDS bytes dst + 16 i .. +15.  (A device function of
+// its own: the host pass of a kernel must not see the LDS address space.)
+__device__ inline void copy16_to_lds(__amdgpu_buffer_rsrc_t r, uint8_t* dst, uint32_t voffset, uint32_t soffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)dst, 16, voffset, soffset, 0, 0);
+}
+
+// Workgroup barrier once at most N of this wave's vector-memory operations
+// (direct-to-LDS copies of later blocks) are outstanding and its LDS reads
+// are done.  __syncthreads would wait for every copy in flight.
+template <int N>
+__device__ inline void barrier_after_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
 __device__ inline void flag(int32_t* status, int bits) {

@@ -27,23 +27,6 @@
 
 namespace ei {
 
-typedef __attribute__((address_space(3))) void* lds_ptr;
-
-// Direct-to-LDS copy of 16 bytes per lane from buffer r at voffset +
-// soffset; lane i writes LDS bytes dst + 16 i .. +15.  (A device function of
-// its own: the host pass of the kernel must not see the LDS address space.)
-__device__ inline void copy16_to_lds(__amdgpu_buffer_rsrc_t r, uint8_t* dst, uint32_t voffset, uint32_t soffset) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)dst, 16, voffset, soffset, 0, 0);
-}
-
-// Workgroup barrier once at most N of this wave's vector-memory operations
-// (here: direct-to-LDS copies of later blocks) are outstanding and its LDS
-// reads are done.  __syncthreads would wait for every copy in flight.
-template <int N>
-__device__ inline void barrier_after_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
-}
-
 // Shape of a tiled launch: each of the 4 waves owns RT x TT MFMA tiles; the
 // waves are arranged WR x (4 / WR) over rows x tokens.
 template <int RT, int TT, int WR>

@@ -87,7 +87,7 @@ enum {
   EI_SCHED_TREE = 5             /* per-block terms summed in a pairwise tree      */
 };
 
-enum { EI_FORMAT_Q8 = 1, EI_FORMAT_Q4 = 2 };
+enum { EI_FORMAT_Q8 = 1, EI_FORMAT_Q4 = 2, EI_FORMAT_WIDE = 3 };
 
 /* Host-side descriptor of a packed weight matrix, filled by ei_q8_pack or
  * ei_q4_pack.  `packed` points into the caller's device buffer. */
@@ -98,7 +98,7 @@ typedef struct ei_weights {
   int64_t n_pad;        /* n rounded up to a multiple of 32                */
   int64_t nb;           /* k / 32 blocks                                   */
   uint32_t smax;        /* max |scale| over all blocks (Q4: max 2^e)       */
-  int32_t format;       /* EI_FORMAT_Q8 or EI_FORMAT_Q4                    */
+  int32_t format;       /* EI_FORMAT_Q8, EI_FORMAT_Q4 or EI_FORMAT_WIDE    */
   int64_t experts;      /* matrices stacked in the buffer (1 unless packed */
                         /* with ei_q8_pack_stacked)                         */
   int64_t expert_stride;/* bytes from one stacked matrix to the next       */
@@ -258,6 +258,39 @@ int ei_silu_lut_build(int32_t* lut, ei_stream stream);
  */
 int silu_lut_epilogue(const int64_t* gate, const int64_t* up, const int32_t* lut, int64_t* h,
                       int64_t n, int32_t* d_status, ei_stream stream);
+
+/* ------------------------------------------------ wide-code GEMM */
+
+/*
+ * Wide integer codes ([tritify] 3.1: weights of 12 balanced trits,
+ * |c| <= 265,720; activations int32 codes; 3.2 Matmul: the products are
+ * accumulated exactly).  The repack splits every code into three balanced
+ * base-256 digits (|c| <= 8,355,711 fits) in MFMA tile order.
+ *   codes    device int32 [n][k], 16-byte aligned; k % 32 == 0
+ *   packed   device, 256-byte aligned, ei_wide_packed_bytes(n, k) bytes
+ * Synchronous (reads the header back).  EI_ERANGE if a code is outside the
+ * three-digit range or n_pad * k * 3 >= 2^32.
+ */
+size_t ei_wide_packed_bytes(int64_t n, int64_t k);
+int ei_wide_pack(const int32_t* codes, int64_t n, int64_t k, void* packed, size_t packed_bytes, ei_weights* out,
+                 ei_stream stream);
+
+/*
+ * y[t][i] = sum_j c[i][j] * x[t][j], exact, int64 (no scale, no rounding):
+ * activations split into 4 balanced digits, 12 digit products per 32x32
+ * tile accumulated across K in the matrix cores' int32 accumulators, one
+ * combination per output.
+ *   w        descriptor from ei_wide_pack
+ *   x        device int32 [t][k] in [-2^31, 2,139,062,143] (four balanced
+ *            digits; larger values set EI_DEV_LIMB_RANGE)
+ *   y        device int64 [t][n]
+ * Workspace: ei_wide_workspace_bytes(w, t).  EI_ERANGE for k > 32768 (the
+ * int32 accumulators' bound) or 4 * t_pad * k >= 2^32; a sum outside int64
+ * sets EI_DEV_OUT_RANGE.
+ */
+size_t ei_wide_workspace_bytes(const ei_weights* w, int64_t t);
+int int_gemm_wide(const ei_weights* w, const int32_t* x, int64_t* y, int64_t t, void* workspace,
+                  size_t workspace_bytes, int32_t* d_status, ei_stream stream);
 
 /* ------------------------------------------ requantization and norms */
 

@@ -491,6 +491,52 @@ def test_olmoe_grouped_ffn_sampled_pairs(ei, lut):
     assert (host(ei.moe_ffn_q8(wg, wu, wd, xd, rd, dev(lut))) == out).all()
 
 
+# ------------------------------------------------------- wide-code GEMM
+
+WIDE_ACT_MAX = 127 * (256**4 - 1) // 255   # 2,139,062,143: four balanced digits reach no higher
+
+@pytest.mark.parametrize("shape", [(32, 32, 1), (37, 64, 5), (100, 96, 70), (64, 1024, 33), (130, 320, 200)])
+def test_wide_gemm_matches_oracle(ei, shape):
+    N, K, T = shape
+    r = np.random.default_rng(N * K + T)
+    c = synth.wide_codes_from_trits(synth.wide_trits(r, N, K))
+    a = r.integers(-(2**31), WIDE_ACT_MAX + 1, (T, K)).astype(np.int32)   # all four-digit int32 values
+    say("wide", shape)
+    w = ei.pack_wide(dev(c))
+    assert (host(ei.gemm_wide(w, dev(a))) == oracle.wide_gemm(c, a)).all()
+
+
+def test_wide_gemm_digit_range_ends_and_max_k(ei):
+    r = np.random.default_rng(71)
+    # codes at the three-digit ends, activations at the int32 ends
+    N, K, T = 40, 96, 9
+    c = r.choice(np.array([8355711, -8421504, 0, 1, -1], np.int32), size=(N, K))
+    a = r.choice(np.array([WIDE_ACT_MAX, -(2**31), 0, 1, -1], np.int64), size=(T, K)).astype(np.int32)
+    say("wide ends")
+    assert (host(ei.gemm_wide(ei.pack_wide(dev(c)), dev(a))) == oracle.wide_gemm(c, a)).all()
+    # K = 32768, the largest the int32 accumulators allow
+    N, K, T = 32, 32768, 40
+    c = synth.wide_codes_from_trits(synth.wide_trits(r, N, K))
+    a = synth.wide_acts(r, T, K)
+    say("wide max K")
+    assert (host(ei.gemm_wide(ei.pack_wide(dev(c)), dev(a))) == oracle.wide_gemm(c, a)).all()
+    # a code outside the three-digit range is refused at pack time
+    c[3, 7] = 8355712
+    with pytest.raises(ei.EIError):
+        ei.pack_wide(dev(c))
+    # an activation above the four-digit range is flagged
+    a[0, 0] = WIDE_ACT_MAX + 1
+    with pytest.raises(ei.EIError):
+        ei.gemm_wide(ei.pack_wide(dev(synth.wide_codes_from_trits(synth.wide_trits(r, 32, K)))), dev(a))
+
+
+def test_wide_hot_kernel_digest(ei):
+    c, a = synth.wide_inputs()
+    say("wide hot kernel 896x896, 4096 rows")
+    y = ei.gemm_wide(ei.pack_wide(dev(c)), dev(a))
+    assert ei.digest(y) == GOLDEN["wide_896x896_t4096"]["y"]
+
+
 # ------------------------------------------- requantization and RMSNorm
 
 def test_requant_matches_oracle(ei):
