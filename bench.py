@@ -19,6 +19,7 @@ prefill rate, both roofline fractions, and the oracle timed on the host cores
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -162,6 +163,42 @@ def _time_graph(torch, fn, steps: int, warmup: int):
     wall = time.perf_counter() - t0
     ms = sorted(a.elapsed_time(b) for a, b in ev)
     return ms[len(ms) // 2], wall / steps * 1e3
+
+
+def bench_wide(args, torch, np, ei, synth, dev) -> int:
+    """The wide-code hot kernel: 12-trit codes 896x896 against 4096 rows of
+    int32 activations, exact int64 output; i8-MFMA bound (12 digit products
+    per tile and block, no per-block epilogue)."""
+    c, a = synth.wide_inputs()
+    w = ei.pack_wide(torch.from_numpy(c).to(dev))
+    xd = torch.from_numpy(a).to(dev)
+    T, N, K = a.shape[0], c.shape[0], c.shape[1]
+    y = torch.empty((T, N), dtype=torch.int64, device=dev)
+    ws = torch.empty(int(ei.lib().ei_wide_workspace_bytes(ctypes.byref(w.desc), T)), dtype=torch.uint8, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def step():
+        ei.gemm_wide(w, xd, out=y, workspace=ws, status=status)
+
+    ms, wall_ms = _time_graph(torch, step, args.steps, args.warmup)
+    gold = json.load(open(os.path.join(ROOT, "tests", "golden", "oracle_digests.json")))["wide_896x896_t4096"]["y"]
+    ok = int(status.item()) == 0 and ei.digest(y) == gold
+    logical = 2.0 * T * N * K
+    digit_ops = 12 * logical
+    tops = digit_ops / (ms * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "wide-code exact GEMM: i8 digit TOPS", "value": round(tops, 1), "unit": "TOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall_ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int8xint8->int32 digits, int64 result",
+        "data": "synthetic (12-trit codes, activations quantized per tensor to 2^28)",
+        "config": {"workload": "wide_896x896_t4096", "rows": T, "n": N, "k": K, "weight_digits": 3,
+                   "act_digits": 4, "parallelism": "single-gpu"},
+        "roofline": {"bound": "mfma", "achieved": round(tops, 1), "peak": I8_PEAK_TOPS, "unit": "TOP/s",
+                     "frac": round(tops / I8_PEAK_TOPS, 4), "traffic": None, "step_ms": round(ms, 4),
+                     "note": "i8 ops = 12 digit products x 2*T*N*K; the step includes the activation digit split"},
+        "logical_tops": round(logical / (ms * 1e-3) / 1e12, 2),
+        "parity": {"digest_equals_oracle": ok}}))
+    return 0 if ok else 1
 
 
 def bench_olmoe_router(args, torch, np, ei, synth, dev) -> int:
@@ -335,12 +372,12 @@ def main() -> int:
                     help="only run a plain device copy of 256 MiB, 5 times (the reference for HBM byte counters)")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="rocprofv3 --pmc output directories -> profiles/traffic.json (no GPU needed)")
-    ap.add_argument("--workload", choices=("dense", "olmoe", "olmoe_router", "qwen_ffn", "qwen_ffn_prenorm"),
+    ap.add_argument("--workload", choices=("dense", "olmoe", "olmoe_router", "qwen_ffn", "qwen_ffn_prenorm", "wide"),
                     default="dense",
                     help="dense: the 14336x4096 decode + prefill step (default); olmoe / qwen_ffn: the routed "
                          "expert FFN or the 24-layer FFN chain, timed the same way; olmoe_router: the routed "
                          "FFN behind the integer router; qwen_ffn_prenorm: the chain with an integer RMSNorm "
-                         "in front of every layer")
+                         "in front of every layer; wide: the 12-trit wide-code GEMM (896x896, 4096 rows)")
     args = ap.parse_args()
     if args.summarize_counters:
         return summarize_counters(*args.summarize_counters)
@@ -364,6 +401,8 @@ def main() -> int:
         return copy_calibration(torch, dev)
     if args.workload == "olmoe":
         return bench_olmoe(args, torch, np, ei, synth, dev)
+    if args.workload == "wide":
+        return bench_wide(args, torch, np, ei, synth, dev)
     if args.workload == "olmoe_router":
         return bench_olmoe_router(args, torch, np, ei, synth, dev)
     if args.workload in ("qwen_ffn", "qwen_ffn_prenorm"):
