@@ -5,8 +5,8 @@
 //     y[t][i] = sum_j c[i][j] * a[t][j]      (int64)
 //
 // On gfx950 both operands enter the int8 matrix cores as balanced base-256
-// digits: c = sum_m 256^m w_m (3 digits hold |c| <= 8,355,711) and
-// a = sum_l 256^l d_l (4 digits hold any int32), so
+// digits: c = sum_m 256^m w_m (3 digits hold -8,421,504 .. 8,355,711) and
+// a = sum_l 256^l d_l (4 digits hold -2^31 .. 2,139,062,143 of int32), so
 //     y = sum_{m,l} 256^(m+l) sum_j w_m[i][j] d_l[t][j].
 // There is no per-block scale, so every digit product accumulates across the
 // whole K inside the MFMA (int32 C = D): the 12 products of a 32x32 tile per
