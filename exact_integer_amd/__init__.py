@@ -63,6 +63,8 @@ SIGNATURES = {
     "output_digest": (I32, [P, SZ, P, P]),
     "ei_sha256_host": (None, [P, SZ, P]),
     "ei_topk_route": (I32, [P, I64, I64, I32, P, P]),
+    "int_gemm_q4_table": (I32, [P, P, P, P, I64, I64, I64, P, P]),
+    "silu_lut_epilogue_radix16": (I32, [P, P, P, P, I64, P, P]),
     "ei_wide_packed_bytes": (SZ, [I64, I64]),
     "ei_wide_pack": (I32, [P, I64, I64, P, SZ, WP, P]),
     "ei_wide_workspace_bytes": (SZ, [WP, I64]),
@@ -247,6 +249,41 @@ def rmsnorm_q16(x: torch.Tensor, g: torch.Tensor, eps_q32: int, out=None, status
     if check:
         _raise_status(status, "ei_rmsnorm_q16")
     return y
+
+
+def gemm_q4_table(nib: torch.Tensor, sme: torch.Tensor, x: torch.Tensor, out=None, status=None) -> torch.Tensor:
+    """The 4-bit projection by table reads, from the export format (int64 [t][n])."""
+    s = _stream()
+    n = nib.shape[0]
+    t, k = x.shape
+    if tuple(nib.shape) != (n, k // 2) or tuple(sme.shape) != (n, k // 32):
+        raise EIError("int_gemm_q4_table: nib [n][k/2], sme [n][k/32], x [t][k]")
+    pn, ps, px = _dev(nib, torch.uint8, "nib"), _dev(sme, torch.uint8, "sme"), _dev(x, torch.int32, "x")
+    y = out if out is not None else torch.empty((t, n), dtype=torch.int64, device=x.device)
+    py = _dev(y, torch.int64, "y")
+    check = status is None
+    if check:
+        status = torch.zeros(1, dtype=torch.int32, device=x.device)
+    _check(lib().int_gemm_q4_table(pn, ps, px, py, n, k, t, status.data_ptr(), s), "int_gemm_q4_table")
+    if check:
+        _raise_status(status, "int_gemm_q4_table")
+    return y
+
+
+def silu_mul_radix16(g: torch.Tensor, u: torch.Tensor, lut: torch.Tensor, out=None, status=None) -> torch.Tensor:
+    """silu_mul with the runtime product by base-16 table reads."""
+    s = _stream()
+    pg, pu, pl = _dev(g, torch.int64, "g"), _dev(u, torch.int64, "u"), _dev(lut, torch.int32, "lut")
+    h = out if out is not None else torch.empty_like(g)
+    ph = _dev(h, torch.int64, "h")
+    check = status is None
+    if check:
+        status = torch.zeros(1, dtype=torch.int32, device=g.device)
+    _check(lib().silu_lut_epilogue_radix16(pg, pu, pl, ph, g.numel(), status.data_ptr(), s),
+           "silu_lut_epilogue_radix16")
+    if check:
+        _raise_status(status, "silu_lut_epilogue_radix16")
+    return h
 
 
 def pack_wide(codes: torch.Tensor) -> PackedWeights:

@@ -693,6 +693,23 @@ int ei_rmsnorm_q16(const int64_t* x, const int32_t* g, int64_t eps_q32, int64_t*
              : EI_EDEVICE;
 }
 
+int int_gemm_q4_table(const uint8_t* nib, const uint8_t* sme, const int32_t* x, int64_t* y, int64_t n, int64_t k,
+                      int64_t t, int32_t* d_status, ei_stream stream) {
+  if (!nib || !sme || !x || !y || n < 1 || t < 1 || k < 32 || k % 32 != 0) return EI_EINVAL;
+  if (t > 65535) return EI_ERANGE;
+  return launch_q4_table(nib, sme, x, y, n, k, t, d_status, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? EI_OK
+             : EI_EDEVICE;
+}
+
+int silu_lut_epilogue_radix16(const int64_t* gate, const int64_t* up, const int32_t* lut, int64_t* h, int64_t n,
+                              int32_t* d_status, ei_stream stream) {
+  if (!gate || !up || !lut || !h || n < 0) return EI_EINVAL;
+  return launch_silu_mul_radix16(gate, up, lut, h, n, d_status, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? EI_OK
+             : EI_EDEVICE;
+}
+
 int ei_silu_lut_build(int32_t* lut, ei_stream stream) {
   if (!lut) return EI_EINVAL;
   return launch_silu_lut(lut, static_cast<hipStream_t>(stream)) == hipSuccess ? EI_OK : EI_EDEVICE;
@@ -744,6 +761,6 @@ const char* ei_status_string(int code) {
   }
 }
 
-int ei_version(void) { return 106; }
+int ei_version(void) { return 107; }
 
 }  // extern "C"

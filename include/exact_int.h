@@ -259,6 +259,33 @@ int ei_silu_lut_build(int32_t* lut, ei_stream stream);
 int silu_lut_epilogue(const int64_t* gate, const int64_t* up, const int32_t* lut, int64_t* h,
                       int64_t n, int32_t* d_status, ei_stream stream);
 
+/* ------------------------------------- second derivations (table reads) */
+
+/*
+ * The 4-bit projection by the table read of [UORLUT01] "One projection
+ * (definition)": per activation a 16-entry table T_j[q] = q x_j filled by
+ * additions, one read per weight, four output rows per table, and the group
+ * scale m 2^e applied by shifts and adds.  Reads the export format directly
+ * and gives the same integers as int_gemm_q4 (a second implementation for
+ * the two to be compared bit for bit; not the fast path).
+ *   nib      device uint8 [n][k/2] (element 2j in the low nibble of byte j)
+ *   sme      device uint8 [n][k/32] (m low nibble, e high nibble)
+ *   x        device int32 [t][k];  y device int64 [t][n]
+ * EI_EINVAL for null pointers, n < 1, t < 1, k % 32 != 0; EI_ERANGE for
+ * t > 65535; a sum outside int64 sets EI_DEV_OUT_RANGE.
+ */
+int int_gemm_q4_table(const uint8_t* nib, const uint8_t* sme, const int32_t* x, int64_t* y, int64_t n, int64_t k,
+                      int64_t t, int32_t* d_status, ei_stream stream);
+
+/*
+ * silu_lut_epilogue with its runtime product lut[idx] * u formed as
+ * [UORLUT01] "Products of two runtime values" does: the sixteen multiples of
+ * the table value by repeated addition, read at each base-16 digit of |u|
+ * and summed with shifts.  Same arguments and results as silu_lut_epilogue.
+ */
+int silu_lut_epilogue_radix16(const int64_t* gate, const int64_t* up, const int32_t* lut, int64_t* h, int64_t n,
+                              int32_t* d_status, ei_stream stream);
+
 /* ------------------------------------------------ wide-code GEMM */
 
 /*

@@ -491,6 +491,41 @@ def test_olmoe_grouped_ffn_sampled_pairs(ei, lut):
     assert (host(ei.moe_ffn_q8(wg, wu, wd, xd, rd, dev(lut))) == out).all()
 
 
+# ------------------------------------- second derivations (table reads)
+
+@pytest.mark.parametrize("shape", [(37, 96, 1), (100, 320, 4), (64, 288, 64), (1030, 512, 3), (33, 2048, 7)])
+def test_q4_table_read_equals_mfma_path_and_oracle(ei, shape):
+    N, K, T = shape
+    r = np.random.default_rng(N * 5 + K + T)
+    nib, sme, x = synth.q4_codes_packed(r, N, K), synth.q4_scale_bytes(r, N, K), synth.i32_acts(r, T, K)
+    say("q4 table read", shape)
+    yt = host(ei.gemm_q4_table(dev(nib), dev(sme), dev(x)))
+    assert (yt == oracle.q4(nib, sme, x)).all()
+    assert (yt == host(ei.gemm_q4(ei.pack_q4(dev(nib), dev(sme)), dev(x)))).all()
+
+
+def test_q4_table_read_full_ranges(ei):
+    # every nibble and scale byte value (m = 0 and code -8 included), int32 ends
+    N, K, T = 64, 512, 5
+    r = np.random.default_rng(81)
+    nib = r.integers(0, 256, (N, K // 2)).astype(np.uint8)
+    sme = r.integers(0, 256, (N, K // 32)).astype(np.uint8)
+    x = r.choice(np.array([2**31 - 1, -(2**31), 0, 1, -1, 12345], np.int64), size=(T, K)).astype(np.int32)
+    say("q4 table read ranges")
+    assert (host(ei.gemm_q4_table(dev(nib), dev(sme), dev(x))) == oracle.q4(nib, sme, x)).all()
+
+
+def test_silu_mul_radix16_equals_silu_mul(ei, lut):
+    r = np.random.default_rng(82)
+    g = np.concatenate([r.integers(-(2**21), 2**21, 50000), r.integers(-(2**40), 2**40, 1000),
+                        [-(2**63), 2**63 - 1, -16, -17, 15, 16, 31, 32, 33]]).astype(np.int64)
+    u = np.concatenate([r.integers(-(2**40), 2**40, g.size - 4), [-(2**63), 2**63 - 1, 0, -1]]).astype(np.int64)
+    say("silu_mul radix16")
+    h = host(ei.silu_mul_radix16(dev(g), dev(u), dev(lut)))
+    assert (h == oracle.silu_mul(g, u, lut)).all()
+    assert (h == host(ei.silu_mul(dev(g), dev(u), dev(lut)))).all()
+
+
 # ------------------------------------------------------- wide-code GEMM
 
 WIDE_ACT_MAX = 127 * (256**4 - 1) // 255   # 2,139,062,143: four balanced digits reach no higher
