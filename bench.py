@@ -165,6 +165,54 @@ def _time_graph(torch, fn, steps: int, warmup: int):
     return ms[len(ms) // 2], wall / steps * 1e3
 
 
+def bench_q4_table(args, torch, np, ei, synth, dev) -> int:
+    """The 4-bit projections of the d512 workload (512x512, 2048x512,
+    512x2048; T=1 and T=64) by the table-read derivation and by the MFMA/GEMV
+    path, each timed as one graph of all six projections; parity: the two agree
+    and match the stored oracle digests."""
+    import json as _json
+    gold = _json.load(open(os.path.join(ROOT, "tests", "golden", "oracle_digests.json")))["q4_d512"]
+    cases = []
+    for name, (n, k) in synth.Q4_SHAPES.items():
+        nib, sme = synth.q4_d512_matrix(name)
+        nd, sd = torch.from_numpy(nib).to(dev), torch.from_numpy(sme).to(dev)
+        w = ei.pack_q4(nd, sd)
+        for t in (1, 64):
+            x = torch.from_numpy(synth.q4_d512_x(k, t)).to(dev)
+            cases.append((f"{name}_t{t}", n, k, t, nd, sd, w, x, torch.empty((t, n), dtype=torch.int64, device=dev),
+                          torch.empty((t, n), dtype=torch.int64, device=dev),
+                          torch.empty(max(ei.workspace_bytes(w, t), 1), dtype=torch.uint8, device=dev)))
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def step_table():
+        for _, n, k, t, nd, sd, w, x, yt, ym, ws in cases:
+            ei.gemm_q4_table(nd, sd, x, out=yt, status=status)
+
+    def step_mfma():
+        for _, n, k, t, nd, sd, w, x, yt, ym, ws in cases:
+            ei.gemm_q4(w, x, out=ym, workspace=ws, status=status)
+
+    ms_t, wall_t = _time_graph(torch, step_table, args.steps, args.warmup)
+    ms_m, _ = _time_graph(torch, step_mfma, args.steps, args.warmup)
+    ok = int(status.item()) == 0 and all(ei.digest(yt) == gold[name] and ei.digest(ym) == gold[name]
+                                         for name, n, k, t, nd, sd, w, x, yt, ym, ws in cases)
+    logical = sum(2.0 * t * n * k for _, n, k, t, *rest in cases)
+    tops = logical / (ms_t * 1e-3) / 1e12
+    alu_peak = 78.6   # int32 VALU lane-ops/s: 256 CUs x 4 SIMDs x 32 lanes x 2 issue x 2.4 GHz (fp32 157.3 TFLOP/s / 2)
+    print(json.dumps({
+        "metric": "4-bit projection by table reads: logical int TOPS", "value": round(tops, 3), "unit": "TOPS",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall_t, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int32 x 4-bit by table reads",
+        "data": "synthetic (seeded 4-bit codes and m*2^e scale bytes, int32 activations)",
+        "config": {"workload": "q4_d512_table_read", "shapes": list(synth.Q4_SHAPES.values()), "tokens": [1, 64],
+                   "parallelism": "single-gpu"},
+        "roofline": {"bound": "alu", "achieved": round(tops, 3), "peak": alu_peak, "unit": "TOP/s",
+                     "frac": round(tops / alu_peak, 4), "traffic": None, "step_ms": round(ms_t, 4)},
+        "mfma_path_step_ms": round(ms_m, 4),
+        "parity": {"table_read_and_mfma_digests_equal_oracle": ok}}))
+    return 0 if ok else 1
+
+
 def bench_wide(args, torch, np, ei, synth, dev) -> int:
     """The wide-code hot kernel: 12-trit codes 896x896 against 4096 rows of
     int32 activations, exact int64 output; i8-MFMA bound (12 digit products
@@ -372,12 +420,14 @@ def main() -> int:
                     help="only run a plain device copy of 256 MiB, 5 times (the reference for HBM byte counters)")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="rocprofv3 --pmc output directories -> profiles/traffic.json (no GPU needed)")
-    ap.add_argument("--workload", choices=("dense", "olmoe", "olmoe_router", "qwen_ffn", "qwen_ffn_prenorm", "wide"),
+    ap.add_argument("--workload", choices=("dense", "olmoe", "olmoe_router", "qwen_ffn", "qwen_ffn_prenorm", "wide",
+                                           "q4_table"),
                     default="dense",
                     help="dense: the 14336x4096 decode + prefill step (default); olmoe / qwen_ffn: the routed "
                          "expert FFN or the 24-layer FFN chain, timed the same way; olmoe_router: the routed "
                          "FFN behind the integer router; qwen_ffn_prenorm: the chain with an integer RMSNorm "
-                         "in front of every layer; wide: the 12-trit wide-code GEMM (896x896, 4096 rows)")
+                         "in front of every layer; wide: the 12-trit wide-code GEMM (896x896, 4096 rows); q4_table: the "
+                         "4-bit projections by table reads against the MFMA path")
     args = ap.parse_args()
     if args.summarize_counters:
         return summarize_counters(*args.summarize_counters)
@@ -401,6 +451,8 @@ def main() -> int:
         return copy_calibration(torch, dev)
     if args.workload == "olmoe":
         return bench_olmoe(args, torch, np, ei, synth, dev)
+    if args.workload == "q4_table":
+        return bench_q4_table(args, torch, np, ei, synth, dev)
     if args.workload == "wide":
         return bench_wide(args, torch, np, ei, synth, dev)
     if args.workload == "olmoe_router":
