@@ -140,36 +140,26 @@ __global__ __launch_bounds__(kMoeSortThreads) void moe_sort_kernel(const int32_t
     const int64_t hi = ei < experts ? ei : experts;
     for (int64_t e = ep + 1; e <= hi; ++e) offsets[e] = i;
   }
-  // Token tiles: sorted position i opens a tile when its expert is valid and
-  // i minus the start of its expert's segment is a multiple of 32.  Segment
-  // starts come from a max-scan of the segment boundaries; tiles are numbered
-  // by a scan of the per-thread counts, so they come out in sorted order.
-  const int64_t i1 = r0 + per < pairs ? r0 + per : pairs;
-  auto expert_at = [&](int64_t i) { return (int64_t)(keys[i] >> 14); };
-  auto boundary = [&](int64_t i) { return i == 0 || expert_at(i) != expert_at(i - 1); };
-  int64_t last = -1;
-  for (int64_t i = r0; i < i1; ++i)
-    if (boundary(i)) last = i;
-  const int64_t carry = block_exclusive_max(last, wave_tot);
-  int64_t seg = carry;
-  int cnt = 0;
-  for (int64_t i = r0; i < i1; ++i) {
-    if (boundary(i)) seg = i;
-    cnt += expert_at(i) < experts && ((i - seg) & (kTile - 1)) == 0;
-  }
-  uint64_t total;
-  int64_t j = (int64_t)block_exclusive_sum((uint64_t)cnt, &total, wave_tot);
-  seg = carry;
-  for (int64_t i = r0; i < i1; ++i) {
-    if (boundary(i)) seg = i;
-    const int64_t e = expert_at(i);
-    if (e >= experts || ((i - seg) & (kTile - 1)) != 0) continue;
-    int rows = 1;
-    while (rows < kTile && i + rows < pairs && expert_at(i + rows) == e) ++rows;
-    tile_expert[j] = (int32_t)e;
-    tile_row0[j] = (int32_t)i;
-    tile_rows[j] = rows;
-    ++j;
+  __syncthreads();   // the offsets are visible to the workgroup
+  // Token tiles: expert e's segment [offsets[e], offsets[e+1]) is cut into
+  // ceil(count / 32) tiles; tiles are numbered by a scan of the per-expert
+  // tile counts (experts in order, 1024 at a time), so they come out in
+  // sorted order.
+  uint64_t total = 0;
+  for (int64_t e0 = 0; e0 < experts; e0 += kMoeSortThreads) {
+    const int64_t e = e0 + tid;
+    const int64_t beg = e < experts ? offsets[e] : 0;
+    const int64_t cnt = e < experts ? offsets[e + 1] - beg : 0;
+    const int64_t nt = (cnt + kTile - 1) / kTile;
+    uint64_t chunk;
+    const int64_t j0 = (int64_t)(total + block_exclusive_sum((uint64_t)nt, &chunk, wave_tot));
+    for (int64_t s = 0; s < nt; ++s) {
+      const int64_t left = cnt - s * kTile;
+      tile_expert[j0 + s] = (int32_t)e;
+      tile_row0[j0 + s] = (int32_t)(beg + s * kTile);
+      tile_rows[j0 + s] = (int32_t)(left < kTile ? left : kTile);
+    }
+    total += chunk;
   }
   if (tid == 0) *ntiles = (int32_t)total;
 }
