@@ -289,9 +289,12 @@ Grouping grouping_at(void* workspace, const GroupedLayout& g) {
 }
 
 // The grouped projection of w over the limb tiles in p (already gathered for
-// the sorted pairs): y[pair][n].
+// the sorted pairs): y[pair][n].  With gate and lut: the up projection of a
+// routed FFN, h = silu(gate, u) written as limb tiles to h_limbs.
 hipError_t launch_grouped_projection(const ei_weights* w, const GroupedLayout& g, const Grouping& p, int64_t* y,
-                                     int32_t* status, hipStream_t s) {
+                                     int32_t* status, hipStream_t s, const int64_t* gate = nullptr,
+                                     const int32_t* lut = nullptr, int8_t* h_limbs = nullptr,
+                                     const int8_t* limbs = nullptr) {
   GemmArgs a;
   std::memset(&a, 0, sizeof a);
   const uint8_t* base = static_cast<const uint8_t*>(w->packed);
@@ -317,6 +320,13 @@ hipError_t launch_grouped_projection(const ei_weights* w, const GroupedLayout& g
   a.ntiles = p.ntiles;
   a.tiles_max = g.tiles_max;
   a.expert_stride = w->expert_stride;
+  if (limbs) a.limb_tiles = limbs;
+  if (gate) {
+    a.resid = gate;
+    a.lut = lut;
+    a.limb_out = h_limbs;
+    return launch_gemm_grouped_silu(a, s);
+  }
   return launch_gemm_grouped(a, s);
 }
 
@@ -360,21 +370,21 @@ int ffn_check(const ei_weights* wg, const ei_weights* wu, const ei_weights* wd) 
   return EI_OK;
 }
 
-// Routed FFN workspace: one grouping (its limb area sized for the wider of
-// the two inputs), then g, u and h [pairs][f].
+// Routed FFN workspace: one grouping (its limb area holds x's limb tiles),
+// then g [pairs][f] and h as the down projection's limb tiles
+// [3][tiles_max][f/32][1 KB].
 struct MoeLayout {
   GroupedLayout g;
-  size_t g_off, u_off, h_off, total;
+  size_t g_off, hl_off, total;
 };
 
 MoeLayout moe_layout(const ei_weights* wg, const ei_weights* wd, int64_t rows, int topk) {
   MoeLayout m;
-  m.g = grouped_layout(wd->k > wg->k ? wd : wg, rows, topk, 3);
-  const size_t hb = align_up(sizeof(int64_t) * (size_t)m.g.pairs * (size_t)wg->n);
+  (void)wd;
+  m.g = grouped_layout(wg, rows, topk, 3);
   m.g_off = m.g.total;
-  m.u_off = m.g_off + hb;
-  m.h_off = m.u_off + hb;
-  m.total = m.h_off + hb;
+  m.hl_off = m.g_off + align_up(sizeof(int64_t) * (size_t)m.g.pairs * (size_t)wg->n);
+  m.total = m.hl_off + align_up((size_t)3 * (size_t)m.g.tiles_max * (size_t)wg->n * kTile);
   return m;
 }
 
@@ -558,23 +568,22 @@ int int_moe_ffn_q8(const ei_weights* wg, const ei_weights* wu, const ei_weights*
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   const Grouping p = grouping_at(workspace, m.g);
   int64_t* g = reinterpret_cast<int64_t*>(ws + m.g_off);
-  int64_t* u = reinterpret_cast<int64_t*>(ws + m.u_off);
-  int64_t* h = reinterpret_cast<int64_t*>(ws + m.h_off);
+  int8_t* hl = reinterpret_cast<int8_t*>(ws + m.hl_off);
   const int64_t pairs = m.g.pairs;
   // one grouping serves all three projections: pair p of the down projection
-  // is row p of h, in the same sorted order
+  // is row p of h, in the same sorted order, so the up projection writes h
+  // straight into the down projection's limb tiles
   hipError_t e = launch_moe_sort(route, pairs, wg->experts, p.sorted, p.offs, p.texp, p.trow0, p.trows, p.ntiles,
                                  d_status, s);
   if (e == hipSuccess)
     e = launch_grouped_limb_tiles(x, wg->k, topk, p.sorted, p.trow0, p.trows, p.ntiles, m.g.tiles_max, p.limb,
                                   d_status, s);
   if (e == hipSuccess) e = launch_grouped_projection(wg, m.g, p, g, d_status, s);
-  if (e == hipSuccess) e = launch_grouped_projection(wu, m.g, p, u, d_status, s);
-  if (e == hipSuccess) e = launch_silu_mul(g, u, lut, h, pairs * wg->n, d_status, s);
-  if (e == hipSuccess)
-    e = launch_grouped_limb_tiles(h, wd->k, 1, p.sorted, p.trow0, p.trows, p.ntiles, m.g.tiles_max, p.limb,
-                                  d_status, s);
-  if (e == hipSuccess) e = launch_grouped_projection(wd, m.g, p, y, d_status, s);
+  if (e == hipSuccess) e = launch_grouped_projection(wu, m.g, p, nullptr, d_status, s, g, lut, hl);
+  if (e == hipSuccess) {
+    GroupedLayout gd = m.g;   // the down projection: same pairs and tiles, its own k
+    e = launch_grouped_projection(wd, gd, p, y, d_status, s, nullptr, nullptr, nullptr, hl);
+  }
   return e == hipSuccess ? EI_OK : EI_EDEVICE;
 }
 

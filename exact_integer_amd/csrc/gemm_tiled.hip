@@ -45,7 +45,10 @@ struct TiledShape {
 // kGrouped: each token tile belongs to one expert, whose packed image and
 // output rows it looks up.  PIPE: the epilogue of block b runs after the
 // MFMAs of block b + 1 are issued.  XMAP: XCD-contiguous tile order.
-template <int RT, int TT, int WR, int NBUF, bool kExact, bool kGrouped, bool PIPE, bool XMAP>
+// kSilu (grouped, one tile per wave): the up projection of a routed FFN; each
+// result u meets the gate's g (a.resid, pair order) in the SiLU-gated product,
+// and h goes out as the down projection's limb tiles (a.limb_out) instead of y.
+template <int RT, int TT, int WR, int NBUF, bool kExact, bool kGrouped, bool PIPE, bool XMAP, bool kSilu = false>
 __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs a) {
   using Sh = TiledShape<RT, TT, WR>;
   extern __shared__ __align__(16) uint8_t lds[];
@@ -205,6 +208,54 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs a) {
     }
   }
 
+  if constexpr (kSilu) {
+    static_assert(kGrouped && RT == 1 && TT == 1 && WR == 4, "the fused SiLU epilogue takes one tile per wave");
+    // The wave's 32 x 32 tile of h (rows x pairs of the tile; zero past the
+    // tile's pairs) goes through LDS and out as limb tile (block 4 rb + wr of
+    // the down projection's K, token tile tb).
+    __syncthreads();   // every wave is done with the copy ring
+    int64_t(*ht)[33] = reinterpret_cast<int64_t(*)[33]>(lds + wave * (32 * 33 * 8));
+    const int64_t rtile = rb * 4 + wr, row = rtile * 32 + (lane & 31);
+    const int rows = a.tile_rows[tb];
+    bool good = true;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int tloc = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      int64_t h = 0;
+      if (row < a.n && tloc < rows) {
+        const int64_t orow = a.sorted_pair[a.tile_row0[tb] + tloc];
+        const __int128 v = (__int128)acc[0][0][0][r] + ((__int128)acc[1][0][0][r] << 8) +
+                           ((__int128)acc[2][0][0][r] << 16);
+        int64_t u;
+        good = finish_output(v, OUT_ROUND_Q24, &u) && good;
+        good = silu_gate(a.resid[orow * a.n + row], u, a.lut, &h) && good;
+      }
+      ht[tloc][lane & 31] = h;
+    }
+    if (!good) flag(a.status, EI_DEV_OUT_RANGE);
+    __builtin_amdgcn_wave_barrier();   // the tile is this wave's own: its LDS writes land before its reads
+    if (rtile >= a.n / kTile) return;
+    const int64_t* src = &ht[lane & 31][16 * (lane >> 5)];   // pair lane % 32, rows 16 (lane / 32) .. + 15
+    uint32_t words[3][4];
+    bool ok = true;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t v4[4] = {src[4 * q], src[4 * q + 1], src[4 * q + 2], src[4 * q + 3]};
+      uint32_t w[3];
+      ok = limb_words<3>(v4, w) && ok;
+#pragma unroll
+      for (int l = 0; l < 3; ++l) words[l][q] = w[l];
+    }
+    if (!ok) flag(a.status, EI_DEV_LIMB_RANGE);
+    const int64_t nb_out = a.n / kTile;
+#pragma unroll
+    for (int l = 0; l < 3; ++l) {
+      const v4i v = {(int)words[l][0], (int)words[l][1], (int)words[l][2], (int)words[l][3]};
+      reinterpret_cast<v4i*>(a.limb_out)[((l * a.tiles_max + tb) * nb_out + rtile) * 64 + lane] = v;
+    }
+    return;
+  }
+
   // ---- store: lane holds row 32 jr + lane % 32 and tokens 32 jt + 8 (r / 4)
   // + 4 (lane / 32) + r % 4 of the workgroup tile
 #pragma unroll
@@ -233,17 +284,21 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs a) {
   }
 }
 
-template <int RT, int TT, int WR, int NBUF, bool kGrouped = false, bool PIPE = false, bool XMAP = false>
+template <int RT, int TT, int WR, int NBUF, bool kGrouped = false, bool PIPE = false, bool XMAP = false,
+          bool kSilu = false>
 hipError_t launch_tiled_shape(const GemmArgs& a, hipStream_t s) {
   using Sh = TiledShape<RT, TT, WR>;
   const int64_t rbs = (a.n_pad + Sh::kRows - 1) / Sh::kRows;
   const int64_t tbs = kGrouped ? a.tiles_max : (a.t_pad + Sh::kToks - 1) / Sh::kToks;
   const dim3 grid((unsigned)(rbs * tbs)), block(256);
-  const size_t lds = (size_t)NBUF * Sh::kBlockBytes;
+  size_t lds = (size_t)NBUF * Sh::kBlockBytes;
+  if (kSilu && lds < 4 * 32 * 33 * 8) lds = 4 * 32 * 33 * 8;   // the h tiles of the fused epilogue
   if (a.out_mode == OUT_EXACT)
-    hipLaunchKernelGGL((gemm_tiled_kernel<RT, TT, WR, NBUF, true, kGrouped, PIPE, XMAP>), grid, block, lds, s, a);
+    hipLaunchKernelGGL((gemm_tiled_kernel<RT, TT, WR, NBUF, true, kGrouped, PIPE, XMAP, kSilu>), grid, block, lds, s,
+                       a);
   else
-    hipLaunchKernelGGL((gemm_tiled_kernel<RT, TT, WR, NBUF, false, kGrouped, PIPE, XMAP>), grid, block, lds, s, a);
+    hipLaunchKernelGGL((gemm_tiled_kernel<RT, TT, WR, NBUF, false, kGrouped, PIPE, XMAP, kSilu>), grid, block, lds,
+                       s, a);
   return hipGetLastError();
 }
 
@@ -253,5 +308,9 @@ hipError_t launch_tiled_shape(const GemmArgs& a, hipStream_t s) {
 hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t s) { return launch_tiled_shape<1, 1, 4, 2>(a, s); }
 
 hipError_t launch_gemm_grouped(const GemmArgs& a, hipStream_t s) { return launch_tiled_shape<1, 1, 4, 2, true>(a, s); }
+
+hipError_t launch_gemm_grouped_silu(const GemmArgs& a, hipStream_t s) {
+  return launch_tiled_shape<1, 1, 4, 2, true, false, false, true>(a, s);
+}
 
 }  // namespace ei
