@@ -104,6 +104,7 @@ int run_gemm(const ei_weights* w, const void* x, int x_is_i32, int64_t* y, int64
   if (limbs < 1 || limbs > 8) return EI_EINVAL;
   if (limbs > kMaxLimbs) return EI_ERANGE;
   if (schedule < EI_SCHED_DEFAULT || schedule > EI_SCHED_TREE) return EI_EINVAL;
+  if (round_up(t, kTile) / kTile > 65535) return EI_ERANGE;   // token tiles index a grid dimension
   const WsLayout lay = layout_for(w, t, limbs, schedule);
   if (lay.total > 0 && (!ws || ws_bytes < lay.total)) return EI_ENOSPACE;
   uint8_t* wsb = static_cast<uint8_t*>(ws);

@@ -192,7 +192,7 @@ size_t ei_gemm_workspace_bytes(const ei_weights* w, int64_t t, int limbs, int sc
  * Exactness: per-limb partial sums are carried in int64 and are exact for
  * any int32 scales while k <= 262144 (each term |S P| < 2^31 2^19 = 2^50);
  * the limbs are combined in int128 and rounded once.  EI_ERANGE if
- * k > 262144.  A y outside int64 sets EI_DEV_OUT_RANGE.
+ * k > 262144 or t > 65535 * 32.  A y outside int64 sets EI_DEV_OUT_RANGE.
  */
 int int_gemm_q8(const ei_weights* w, const int64_t* x, int64_t* y, int64_t t, int limbs,
                 int schedule, uint64_t shuffle_seed, void* workspace, size_t workspace_bytes,
