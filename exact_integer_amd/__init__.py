@@ -74,6 +74,8 @@ SIGNATURES = {
     "ei_ffn_workspace_bytes": (SZ, [WP, WP, I64]),
     "int_ffn_q8": (I32, [WP, WP, WP, P, P, P, I64, P, SZ, P, P]),
     "int_ffn_q8_prenorm": (I32, [WP, WP, WP, P, I64, P, P, P, I64, P, SZ, P, P]),
+    "ei_ffn_chain_workspace_bytes": (SZ, [WP, WP, I64]),
+    "int_ffn_q8_chain": (I32, [ctypes.POINTER(WP), I32, P, P, P, I64, P, SZ, P, P]),
     "ei_moe_ffn_workspace_bytes": (SZ, [WP, WP, I64, I32]),
     "int_moe_ffn_q8": (I32, [WP, WP, WP, P, P, I64, I32, P, P, P, SZ, P, P]),
     "ei_status_string": (ctypes.c_char_p, [I32]),
@@ -362,6 +364,34 @@ def ffn_q8(wg: PackedWeights, wu: PackedWeights, wd: PackedWeights, x: torch.Ten
                             workspace.data_ptr(), workspace.numel(), status.data_ptr(), s), "int_ffn_q8")
     if check:
         _raise_status(status, "int_ffn_q8")
+    return y
+
+
+def ffn_chain_workspace_bytes(wg: PackedWeights, wd: PackedWeights, t: int) -> int:
+    return int(lib().ei_ffn_chain_workspace_bytes(ctypes.byref(wg.desc), ctypes.byref(wd.desc), t))
+
+
+def ffn_q8_chain(layers, x: torch.Tensor, lut: torch.Tensor, out=None, workspace=None, status=None) -> torch.Tensor:
+    """A stack of FFN layers (a list of (gate, up, down) PackedWeights): x_{l+1} = ffn_q8(layer l, x_l)."""
+    s = _stream()
+    t, d = x.shape
+    wg0, _, wd0 = layers[0]
+    for wg, wu, wd in layers:
+        if d != wg.k or wu.k != wg.k or wu.n != wg.n or wd.k != wg.n or wd.n != wg.k or wg.n != wg0.n:
+            raise EIError("int_ffn_q8_chain: every layer must be gate, up [f][d], down [d][f] of one shape")
+    descs = (WP * (3 * len(layers)))(*[ctypes.pointer(w.desc) for layer in layers for w in layer])
+    px, pl = _dev(x, torch.int64, "x"), _dev(lut, torch.int32, "lut")
+    y = out if out is not None else torch.empty_like(x)
+    py = _dev(y, torch.int64, "y")
+    if workspace is None:
+        workspace = torch.empty(max(ffn_chain_workspace_bytes(wg0, wd0, t), 1), dtype=torch.uint8, device=x.device)
+    check = status is None
+    if check:
+        status = torch.zeros(1, dtype=torch.int32, device=x.device)
+    _check(lib().int_ffn_q8_chain(descs, len(layers), px, pl, py, t, workspace.data_ptr(), workspace.numel(),
+                                  status.data_ptr(), s), "int_ffn_q8_chain")
+    if check:
+        _raise_status(status, "int_ffn_q8_chain")
     return y
 
 

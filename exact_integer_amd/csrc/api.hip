@@ -469,9 +469,12 @@ size_t ei_ffn_workspace_bytes(const ei_weights* wg, const ei_weights* wd, int64_
 namespace {
 
 // y = x + FFN(x), or y = x + FFN(rmsnorm(x)) when gnorm is given.
+// in_limbs (fused path only): x's limb tiles are already there; out_limbs:
+// y's limb tiles for the next layer's gate/up pass are written there too.
 int ffn_run(const ei_weights* wg, const ei_weights* wu, const ei_weights* wd, const int64_t* x,
             const int32_t* gnorm, int64_t eps_q32, const int32_t* lut, int64_t* y, int64_t t, void* workspace,
-            size_t workspace_bytes, int32_t* d_status, hipStream_t s) {
+            size_t workspace_bytes, int32_t* d_status, hipStream_t s, const int8_t* in_limbs = nullptr,
+            int8_t* out_limbs = nullptr) {
   if (!x || !lut || !y || t < 1) return EI_EINVAL;
   const int c = ffn_check(wg, wu, wd);
   if (c != EI_OK) return c;
@@ -485,10 +488,14 @@ int ffn_run(const ei_weights* wg, const ei_weights* wu, const ei_weights* wd, co
     // gate and up in one pass, the SiLU-gated product in its epilogue; the
     // (normalized) input goes straight into limb tiles
     const WsLayout lay = layout_for(wg, t, 3, EI_SCHED_DEFAULT);
-    int8_t* limb = static_cast<int8_t*>(gws) + lay.limb_off;
-    const hipError_t e = gnorm ? launch_rmsnorm_limb_tiles(x, gnorm, eps_q32, limb, t, lay.t_pad, wg->k, d_status, s)
-                               : launch_limb_tiles(x, 0, t, wg->k, 3, limb, lay.t_pad, d_status, s);
-    if (e != hipSuccess) return EI_EDEVICE;
+    const int8_t* limb = in_limbs;
+    if (!limb) {
+      int8_t* own = static_cast<int8_t*>(gws) + lay.limb_off;
+      const hipError_t e = gnorm ? launch_rmsnorm_limb_tiles(x, gnorm, eps_q32, own, t, lay.t_pad, wg->k, d_status, s)
+                                 : launch_limb_tiles(x, 0, t, wg->k, 3, own, lay.t_pad, d_status, s);
+      if (e != hipSuccess) return EI_EDEVICE;
+      limb = own;
+    }
     GemmArgs a;
     std::memset(&a, 0, sizeof a);
     const uint8_t* bg = static_cast<const uint8_t*>(wg->packed);
@@ -511,8 +518,37 @@ int ffn_run(const ei_weights* wg, const ei_weights* wu, const ei_weights* wd, co
     a.b1 = wg->nb;
     a.out_mode = OUT_ROUND_Q24;
     if (launch_gemm_skinny_gateup(a, s) != hipSuccess) return EI_EDEVICE;
-    return run_gemm(wd, nullptr, 0, y, t, 3, EI_SCHED_DEFAULT, 0, gws, gws_bytes, d_status, s, OUT_ROUND_Q24, x,
-                    reinterpret_cast<const int8_t*>(ws + f.h_off));
+    const int8_t* h_limbs = reinterpret_cast<const int8_t*>(ws + f.h_off);
+    const WsLayout ld = layout_for(wd, t, 3, EI_SCHED_DEFAULT);
+    if (out_limbs && ld.path == PATH_SKINNY && ld.splits > 1) {
+      // split-K down projection whose combiner also writes the next input's limb tiles
+      GemmArgs b;
+      std::memset(&b, 0, sizeof b);
+      const uint8_t* bd = static_cast<const uint8_t*>(wd->packed);
+      b.codes = reinterpret_cast<const int8_t*>(bd + kHeaderBytes);
+      b.scales = reinterpret_cast<const int32_t*>(bd + kHeaderBytes + wd->n_pad * wd->k);
+      b.limb_tiles = h_limbs;
+      int64_t* part = reinterpret_cast<int64_t*>(static_cast<uint8_t*>(gws) + ld.part_off);
+      b.part = part;
+      b.status = d_status;
+      b.n = wd->n;
+      b.k = wd->k;
+      b.t = t;
+      b.n_pad = wd->n_pad;
+      b.t_pad = ld.t_pad;
+      b.nb = wd->nb;
+      b.b0 = 0;
+      b.b1 = wd->nb;
+      b.out_mode = OUT_PARTIAL;
+      if (launch_gemm_skinny(b, 3, ld.splits, s) != hipSuccess) return EI_EDEVICE;
+      return launch_combine_hr_tiles(part, ld.splits, y, t, wd->n, x, out_limbs, ld.t_pad, d_status, s) == hipSuccess
+                 ? EI_OK
+                 : EI_EDEVICE;
+    }
+    const int r = run_gemm(wd, nullptr, 0, y, t, 3, EI_SCHED_DEFAULT, 0, gws, gws_bytes, d_status, s, OUT_ROUND_Q24,
+                           x, h_limbs);
+    if (r != EI_OK || !out_limbs) return r;
+    return launch_limb_tiles(y, 0, t, wd->n, 3, out_limbs, ld.t_pad, d_status, s) == hipSuccess ? EI_OK : EI_EDEVICE;
   }
   const int64_t* xin = x;
   if (gnorm) {
@@ -539,6 +575,45 @@ int int_ffn_q8(const ei_weights* wg, const ei_weights* wu, const ei_weights* wd,
                int32_t* d_status, ei_stream stream) {
   return ffn_run(wg, wu, wd, x, nullptr, 0, lut, y, t, workspace, workspace_bytes, d_status,
                  static_cast<hipStream_t>(stream));
+}
+
+size_t ei_ffn_chain_workspace_bytes(const ei_weights* wg, const ei_weights* wd, int64_t t) {
+  if (!wg || !wd || t < 1) return 0;
+  return ffn_layout(wg, wd, t).total + align_up(sizeof(int64_t) * (size_t)t * (size_t)wg->k) +
+         align_up((size_t)3 * (size_t)round_up(t, kTile) * (size_t)wg->k);
+}
+
+int int_ffn_q8_chain(const ei_weights* const* layers, int n_layers, const int64_t* x, const int32_t* lut, int64_t* y,
+                     int64_t t, void* workspace, size_t workspace_bytes, int32_t* d_status, ei_stream stream) {
+  if (!layers || n_layers < 1 || !x || !lut || !y || t < 1) return EI_EINVAL;
+  for (int l = 0; l < n_layers; ++l) {
+    const ei_weights *wg = layers[3 * l], *wu = layers[3 * l + 1], *wd = layers[3 * l + 2];
+    const int c = ffn_check(wg, wu, wd);
+    if (c != EI_OK) return c;
+    if (wg->n != layers[0]->n || wg->k != layers[0]->k) return EI_EINVAL;   // one shape for the whole chain
+  }
+  const ei_weights *g0 = layers[0], *d0 = layers[2];
+  const FfnLayout f = ffn_layout(g0, d0, t);
+  if (!workspace || workspace_bytes < ei_ffn_chain_workspace_bytes(g0, d0, t)) return EI_ENOSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  int64_t* xbuf = reinterpret_cast<int64_t*>(ws + f.total);
+  int8_t* limbs = reinterpret_cast<int8_t*>(ws + f.total + align_up(sizeof(int64_t) * (size_t)t * (size_t)g0->k));
+  const int64_t t_pad = round_up(t, kTile);
+  // layer l writes y when n_layers - 1 - l is even, else xbuf, so the last
+  // layer lands in y; on the fused path each layer's combiner leaves the next
+  // layer's input limbs in `limbs` (the first layer's are split here)
+  if (f.fused && launch_limb_tiles(x, 0, t, g0->k, 3, limbs, t_pad, d_status, s) != hipSuccess) return EI_EDEVICE;
+  const int64_t* in = x;
+  for (int l = 0; l < n_layers; ++l) {
+    int64_t* out = ((n_layers - 1 - l) % 2 == 0) ? y : xbuf;
+    const bool last = l == n_layers - 1;
+    const int r = ffn_run(layers[3 * l], layers[3 * l + 1], layers[3 * l + 2], in, nullptr, 0, lut, out, t, workspace,
+                          f.total, d_status, s, f.fused ? limbs : nullptr, f.fused && !last ? limbs : nullptr);
+    if (r != EI_OK) return r;
+    in = out;
+  }
+  return EI_OK;
 }
 
 int int_ffn_q8_prenorm(const ei_weights* wg, const ei_weights* wu, const ei_weights* wd, const int32_t* g_norm,
@@ -771,6 +846,6 @@ const char* ei_status_string(int code) {
   }
 }
 
-int ei_version(void) { return 107; }
+int ei_version(void) { return 108; }
 
 }  // extern "C"

@@ -126,6 +126,9 @@ hipError_t launch_combine_partials(const int64_t* part, int nparts, int64_t* y, 
                                    int limbs, int out_mode, const int64_t* resid, int32_t* status, hipStream_t s);
 hipError_t launch_combine_hr(const int64_t* part, int nparts, int64_t* y, int64_t t, int64_t n, int out_mode,
                              const int64_t* resid, int32_t* status, hipStream_t s);   // (h, r) partials
+hipError_t launch_combine_hr_tiles(const int64_t* part, int nparts, int64_t* y, int64_t t, int64_t n,
+                                   const int64_t* resid, int8_t* tiles, int64_t t_pad, int32_t* status,
+                                   hipStream_t s);   // Q8 rounding; n % 32 == 0
 hipError_t launch_add_residual(int64_t* y, const int64_t* resid, int64_t n, int32_t* status, hipStream_t s);
 hipError_t launch_gemm_skinny_gateup(const GemmArgs& a, hipStream_t s);   // 3 limbs, one split
 hipError_t launch_tree_terms(int64_t* terms, int64_t nb, int64_t* y, int64_t t, int64_t n,

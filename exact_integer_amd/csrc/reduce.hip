@@ -75,6 +75,46 @@ __global__ void combine_hr_kernel(const int64_t* __restrict__ part, int nparts, 
   y[e] = out;
 }
 
+// combine_hr_kernel whose outputs also go out as 3-limb activation tiles for
+// the next projection ([3][t_pad/32][n/32][64 lanes][16 B]; n a multiple of
+// 32): the residual stream's next input, split where it is formed.  One
+// output per thread; its three digits are single-byte stores.
+__global__ void combine_hr_tiles_kernel(const int64_t* __restrict__ part, int nparts, int64_t* __restrict__ y,
+                                        int64_t t, int64_t n, const int64_t* __restrict__ resid,
+                                        int8_t* __restrict__ tiles, int64_t t_pad, int32_t* status) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= t * n) return;
+  const int64_t tn = t * n, tok = e / n, c = e % n;
+  int64_t h = 0, r = 0;
+  for (int p0 = 0; p0 < nparts; p0 += 8) {   // eight partials' loads in flight
+    int64_t vh[8], vr[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const bool in = p0 + q < nparts;
+      vh[q] = in ? part[(int64_t)(p0 + q) * 2 * tn + e] : 0;
+      vr[q] = in ? part[((int64_t)(p0 + q) * 2 + 1) * tn + e] : 0;
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      h += vh[q];
+      r += vr[q];
+    }
+  }
+  int64_t out;
+  bool ok = finish_hr(h, r, OUT_ROUND_Q24, &out);
+  if (resid) ok = fit_i64((__int128)resid[e] + out, &out) && ok;
+  if (!ok) flag(status, EI_DEV_OUT_RANGE);
+  y[e] = out;
+  // balanced digits: the bytes of out + 0x808080, each less 0x80
+  const uint64_t u = (uint64_t)out + 0x808080u;
+  if (u >> 24) flag(status, EI_DEV_LIMB_RANGE);
+  const int64_t nb = n / 32, tg = tok / 32, tgs = t_pad / 32;
+  const int64_t lane16 = (tok % 32) + 32 * ((c % 32) / 16);
+#pragma unroll
+  for (int l = 0; l < 3; ++l)
+    tiles[(((l * tgs + tg) * nb + c / 32) * 64 + lane16) * 16 + (c % 16)] = (int8_t)(((u >> (8 * l)) & 0xFF) ^ 0x80);
+}
+
 // y += resid, checked to fit int64.
 __global__ void add_residual_kernel(int64_t* __restrict__ y, const int64_t* __restrict__ resid, int64_t n,
                                     int32_t* status) {
@@ -142,6 +182,15 @@ hipError_t launch_combine_hr(const int64_t* part, int nparts, int64_t* y, int64_
   const int64_t total = t * n;
   hipLaunchKernelGGL(combine_hr_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, part, nparts, y, t, n,
                      out_mode, resid, status);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_hr_tiles(const int64_t* part, int nparts, int64_t* y, int64_t t, int64_t n,
+                                   const int64_t* resid, int8_t* tiles, int64_t t_pad, int32_t* status,
+                                   hipStream_t s) {
+  const int64_t total = t * n;
+  hipLaunchKernelGGL(combine_hr_tiles_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, part, nparts, y,
+                     t, n, resid, tiles, t_pad, status);
   return hipGetLastError();
 }
 

@@ -394,6 +394,21 @@ int int_ffn_q8(const ei_weights* wg, const ei_weights* wu, const ei_weights* wd,
                int32_t* d_status, ei_stream stream);
 
 /*
+ * A stack of such layers in one call: x_{l+1} = int_ffn_q8(layer l, x_l) for
+ * l = 0 .. n_layers - 1, y = x_{n_layers}.  Where the fused gate/up pass and
+ * a split-K down projection apply, each layer's partial combiner also writes
+ * the next layer's activation limb tiles, so no layer after the first splits
+ * its input again.  Results equal n_layers calls of int_ffn_q8.
+ *   layers   host array of 3 * n_layers descriptors: gate, up, down of each
+ *            layer, all layers of one shape ([f][d], [f][d], [d][f])
+ *   x, y     device int64 [t][d]; y must not overlap x
+ * Workspace: ei_ffn_chain_workspace_bytes(gate, down, t) (any layer's).
+ */
+size_t ei_ffn_chain_workspace_bytes(const ei_weights* wg, const ei_weights* wd, int64_t t);
+int int_ffn_q8_chain(const ei_weights* const* layers, int n_layers, const int64_t* x, const int32_t* lut, int64_t* y,
+                     int64_t t, void* workspace, size_t workspace_bytes, int32_t* d_status, ei_stream stream);
+
+/*
  * The same layer behind an integer RMSNorm ([tritify] 3.2 Normalization; the
  * pre-norm residual block): y = x + FFN(ei_rmsnorm_q16(x, g_norm, eps_q32)),
  * with FFN as int_ffn_q8 and the residual taken from x itself.  On the fused

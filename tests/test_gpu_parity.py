@@ -284,6 +284,35 @@ def test_ffn_q8_prenorm_matches_oracle(ei, lut, shape):
     assert (y == xn).all()
 
 
+@pytest.mark.parametrize("shape", [(96, 64, 3), (160, 96, 30), (64, 4096, 30), (4096, 64, 30), (96, 160, 70)])
+def test_ffn_q8_chain_matches_oracle(ei, lut, shape):
+    # three layers in one call: the fused path hands limb tiles from each
+    # layer's combiner to the next; other token counts take the plain path
+    F, D, T = shape
+    r = np.random.default_rng(F * 7 + D + T)
+    layers = [[(synth.q8_codes(r, F, D), synth.q8_scales(r, F, D)), (synth.q8_codes(r, F, D), synth.q8_scales(r, F, D)),
+               (synth.q8_codes(r, D, F), synth.q8_scales(r, D, F))] for _ in range(3)]
+    x = synth.q16_acts(r, T, D)
+    packed = [tuple(ei.pack_q8(dev(c), dev(sc)) for c, sc in layer) for layer in layers]
+    say("ffn chain", shape)
+    y = host(ei.ffn_q8_chain(packed, dev(x), dev(lut)))
+    ref = x
+    for wg, wu, wd in layers:
+        *_, ref = oracle.ffn_layer(ref, wg, wu, wd, lut)
+    assert (y == ref).all()
+
+
+def test_qwen_ffn_24_layers_chain(ei):
+    lut = ei.silu_lut()
+    packed = []
+    for layer in range(synth.QWEN_LAYERS):
+        (gc, gs), (uc, us), (dc, ds) = synth.qwen_ffn_layer(layer)
+        packed.append((ei.pack_q8(dev(gc), dev(gs)), ei.pack_q8(dev(uc), dev(us)), ei.pack_q8(dev(dc), dev(ds))))
+    say("ffn chain 24 layers")
+    y = ei.ffn_q8_chain(packed, dev(synth.qwen_ffn_x0()), lut)
+    assert ei.digest(y) == GOLDEN["qwen05b_ffn"]["layers"][-1]["x_next"]
+
+
 def test_qwen_ffn_24_layers_prenorm(ei):
     lut = ei.silu_lut()
     x = dev(synth.qwen_ffn_x0())
