@@ -290,10 +290,11 @@ Grouping grouping_at(void* workspace, const GroupedLayout& g) {
 }
 
 // The grouped projection of w over the limb tiles in p (already gathered for
-// the sorted pairs): y[pair][n].  With gate and lut: the up projection of a
-// routed FFN, h = silu(gate, u) written as limb tiles to h_limbs.
+// the sorted pairs): y[pair][n].  With up, lut and h_limbs: w is the gate
+// matrix of a routed FFN and one pass computes gate and up and writes
+// h = silu(g, u) as limb tiles to h_limbs.
 hipError_t launch_grouped_projection(const ei_weights* w, const GroupedLayout& g, const Grouping& p, int64_t* y,
-                                     int32_t* status, hipStream_t s, const int64_t* gate = nullptr,
+                                     int32_t* status, hipStream_t s, const ei_weights* up = nullptr,
                                      const int32_t* lut = nullptr, int8_t* h_limbs = nullptr,
                                      const int8_t* limbs = nullptr) {
   GemmArgs a;
@@ -322,11 +323,13 @@ hipError_t launch_grouped_projection(const ei_weights* w, const GroupedLayout& g
   a.tiles_max = g.tiles_max;
   a.expert_stride = w->expert_stride;
   if (limbs) a.limb_tiles = limbs;
-  if (gate) {
-    a.resid = gate;
+  if (up) {
+    const uint8_t* ubase = static_cast<const uint8_t*>(up->packed);
+    a.codes2 = reinterpret_cast<const int8_t*>(ubase + kHeaderBytes);
+    a.scales2 = reinterpret_cast<const int32_t*>(ubase + kHeaderBytes + up->n_pad * up->k);
     a.lut = lut;
     a.limb_out = h_limbs;
-    return launch_gemm_grouped_silu(a, s);
+    return launch_gemm_grouped_gateup(a, s);
   }
   return launch_gemm_grouped(a, s);
 }
@@ -372,19 +375,17 @@ int ffn_check(const ei_weights* wg, const ei_weights* wu, const ei_weights* wd) 
 }
 
 // Routed FFN workspace: one grouping (its limb area holds x's limb tiles),
-// then g [pairs][f] and h as the down projection's limb tiles
-// [3][tiles_max][f/32][1 KB].
+// then h as the down projection's limb tiles [3][tiles_max][f/32][1 KB].
 struct MoeLayout {
   GroupedLayout g;
-  size_t g_off, hl_off, total;
+  size_t hl_off, total;
 };
 
 MoeLayout moe_layout(const ei_weights* wg, const ei_weights* wd, int64_t rows, int topk) {
   MoeLayout m;
   (void)wd;
   m.g = grouped_layout(wg, rows, topk, 3);
-  m.g_off = m.g.total;
-  m.hl_off = m.g_off + align_up(sizeof(int64_t) * (size_t)m.g.pairs * (size_t)wg->n);
+  m.hl_off = m.g.total;
   m.total = m.hl_off + align_up((size_t)3 * (size_t)m.g.tiles_max * (size_t)wg->n * kTile);
   return m;
 }
@@ -637,25 +638,24 @@ int int_moe_ffn_q8(const ei_weights* wg, const ei_weights* wu, const ei_weights*
   if (c == EI_OK) c = grouped_check(wg, rows, topk, 3);
   if (c == EI_OK) c = grouped_check(wd, rows * topk, 1, 3);
   if (c != EI_OK) return c;
-  if (wu->experts != wg->experts || wd->experts != wg->experts) return EI_EINVAL;
+  if (wu->experts != wg->experts || wd->experts != wg->experts || wu->expert_stride != wg->expert_stride)
+    return EI_EINVAL;
   const MoeLayout m = moe_layout(wg, wd, rows, topk);
   if (!workspace || workspace_bytes < m.total) return EI_ENOSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   const Grouping p = grouping_at(workspace, m.g);
-  int64_t* g = reinterpret_cast<int64_t*>(ws + m.g_off);
   int8_t* hl = reinterpret_cast<int8_t*>(ws + m.hl_off);
   const int64_t pairs = m.g.pairs;
   // one grouping serves all three projections: pair p of the down projection
-  // is row p of h, in the same sorted order, so the up projection writes h
+  // is row p of h, in the same sorted order, so the gate/up pass writes h
   // straight into the down projection's limb tiles
   hipError_t e = launch_moe_sort(route, pairs, wg->experts, p.sorted, p.offs, p.texp, p.trow0, p.trows, p.ntiles,
                                  d_status, s);
   if (e == hipSuccess)
     e = launch_grouped_limb_tiles(x, wg->k, topk, p.sorted, p.trow0, p.trows, p.ntiles, m.g.tiles_max, p.limb,
                                   d_status, s);
-  if (e == hipSuccess) e = launch_grouped_projection(wg, m.g, p, g, d_status, s);
-  if (e == hipSuccess) e = launch_grouped_projection(wu, m.g, p, nullptr, d_status, s, g, lut, hl);
+  if (e == hipSuccess) e = launch_grouped_projection(wg, m.g, p, nullptr, d_status, s, wu, lut, hl);
   if (e == hipSuccess) {
     GroupedLayout gd = m.g;   // the down projection: same pairs and tiles, its own k
     e = launch_grouped_projection(wd, gd, p, y, d_status, s, nullptr, nullptr, nullptr, hl);

@@ -108,10 +108,10 @@ hipError_t launch_gemv(const GemmArgs& a, int limbs, hipStream_t s);
 hipError_t launch_gemm_mfma(const GemmArgs& a, int limbs, hipStream_t s);
 hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t s);    // 3 limbs, see tiled_ok()
 hipError_t launch_gemm_grouped(const GemmArgs& a, hipStream_t s);  // 3 limbs
-// grouped up projection with the SiLU gate in its epilogue: reads g (a.resid,
-// [pairs][n]), writes h as limb tiles [3][tiles_max][n/32][1 KB] (a.limb_out);
-// n % 32 == 0
-hipError_t launch_gemm_grouped_silu(const GemmArgs& a, hipStream_t s);
+// grouped gate (a.codes, a.scales) and up (a.codes2, a.scales2, same shape and
+// expert stride) projections in one pass; writes h = SiLU-gated product as
+// limb tiles [3][tiles_max][n/32][1 KB] (a.limb_out); n % 32 == 0
+hipError_t launch_gemm_grouped_gateup(const GemmArgs& a, hipStream_t s);
 int skinny_splits(int64_t n_pad, int64_t t_pad, int64_t nb);       // workgroup K splits of the skinny kernel
 // a.part when splits > 1: (h, r) partials [splits][2][t][n] for up to three
 // limbs, per-limb partials [splits][limbs][t][n] for four

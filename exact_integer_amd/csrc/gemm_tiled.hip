@@ -45,10 +45,7 @@ struct TiledShape {
 // kGrouped: each token tile belongs to one expert, whose packed image and
 // output rows it looks up.  PIPE: the epilogue of block b runs after the
 // MFMAs of block b + 1 are issued.  XMAP: XCD-contiguous tile order.
-// kSilu (grouped, one tile per wave): the up projection of a routed FFN; each
-// result u meets the gate's g (a.resid, pair order) in the SiLU-gated product,
-// and h goes out as the down projection's limb tiles (a.limb_out) instead of y.
-template <int RT, int TT, int WR, int NBUF, bool kExact, bool kGrouped, bool PIPE, bool XMAP, bool kSilu = false>
+template <int RT, int TT, int WR, int NBUF, bool kExact, bool kGrouped, bool PIPE, bool XMAP>
 __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs a) {
   using Sh = TiledShape<RT, TT, WR>;
   extern __shared__ __align__(16) uint8_t lds[];
@@ -208,54 +205,6 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs a) {
     }
   }
 
-  if constexpr (kSilu) {
-    static_assert(kGrouped && RT == 1 && TT == 1 && WR == 4, "the fused SiLU epilogue takes one tile per wave");
-    // The wave's 32 x 32 tile of h (rows x pairs of the tile; zero past the
-    // tile's pairs) goes through LDS and out as limb tile (block 4 rb + wr of
-    // the down projection's K, token tile tb).
-    __syncthreads();   // every wave is done with the copy ring
-    int64_t(*ht)[33] = reinterpret_cast<int64_t(*)[33]>(lds + wave * (32 * 33 * 8));
-    const int64_t rtile = rb * 4 + wr, row = rtile * 32 + (lane & 31);
-    const int rows = a.tile_rows[tb];
-    bool good = true;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int tloc = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      int64_t h = 0;
-      if (row < a.n && tloc < rows) {
-        const int64_t orow = a.sorted_pair[a.tile_row0[tb] + tloc];
-        const __int128 v = (__int128)acc[0][0][0][r] + ((__int128)acc[1][0][0][r] << 8) +
-                           ((__int128)acc[2][0][0][r] << 16);
-        int64_t u;
-        good = finish_output(v, OUT_ROUND_Q24, &u) && good;
-        good = silu_gate(a.resid[orow * a.n + row], u, a.lut, &h) && good;
-      }
-      ht[tloc][lane & 31] = h;
-    }
-    if (!good) flag(a.status, EI_DEV_OUT_RANGE);
-    __builtin_amdgcn_wave_barrier();   // the tile is this wave's own: its LDS writes land before its reads
-    if (rtile >= a.n / kTile) return;
-    const int64_t* src = &ht[lane & 31][16 * (lane >> 5)];   // pair lane % 32, rows 16 (lane / 32) .. + 15
-    uint32_t words[3][4];
-    bool ok = true;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t v4[4] = {src[4 * q], src[4 * q + 1], src[4 * q + 2], src[4 * q + 3]};
-      uint32_t w[3];
-      ok = limb_words<3>(v4, w) && ok;
-#pragma unroll
-      for (int l = 0; l < 3; ++l) words[l][q] = w[l];
-    }
-    if (!ok) flag(a.status, EI_DEV_LIMB_RANGE);
-    const int64_t nb_out = a.n / kTile;
-#pragma unroll
-    for (int l = 0; l < 3; ++l) {
-      const v4i v = {(int)words[l][0], (int)words[l][1], (int)words[l][2], (int)words[l][3]};
-      reinterpret_cast<v4i*>(a.limb_out)[((l * a.tiles_max + tb) * nb_out + rtile) * 64 + lane] = v;
-    }
-    return;
-  }
-
   // ---- store: lane holds row 32 jr + lane % 32 and tokens 32 jt + 8 (r / 4)
   // + 4 (lane / 32) + r % 4 of the workgroup tile
 #pragma unroll
@@ -284,20 +233,18 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs a) {
   }
 }
 
-template <int RT, int TT, int WR, int NBUF, bool kGrouped = false, bool PIPE = false, bool XMAP = false,
-          bool kSilu = false>
+template <int RT, int TT, int WR, int NBUF, bool kGrouped = false, bool PIPE = false, bool XMAP = false>
 hipError_t launch_tiled_shape(const GemmArgs& a, hipStream_t s) {
   using Sh = TiledShape<RT, TT, WR>;
   const int64_t rbs = (a.n_pad + Sh::kRows - 1) / Sh::kRows;
   const int64_t tbs = kGrouped ? a.tiles_max : (a.t_pad + Sh::kToks - 1) / Sh::kToks;
   const dim3 grid((unsigned)(rbs * tbs)), block(256);
-  size_t lds = (size_t)NBUF * Sh::kBlockBytes;
-  if (kSilu && lds < 4 * 32 * 33 * 8) lds = 4 * 32 * 33 * 8;   // the h tiles of the fused epilogue
+  const size_t lds = (size_t)NBUF * Sh::kBlockBytes;
   if (a.out_mode == OUT_EXACT)
-    hipLaunchKernelGGL((gemm_tiled_kernel<RT, TT, WR, NBUF, true, kGrouped, PIPE, XMAP, kSilu>), grid, block, lds, s,
+    hipLaunchKernelGGL((gemm_tiled_kernel<RT, TT, WR, NBUF, true, kGrouped, PIPE, XMAP>), grid, block, lds, s,
                        a);
   else
-    hipLaunchKernelGGL((gemm_tiled_kernel<RT, TT, WR, NBUF, false, kGrouped, PIPE, XMAP, kSilu>), grid, block, lds,
+    hipLaunchKernelGGL((gemm_tiled_kernel<RT, TT, WR, NBUF, false, kGrouped, PIPE, XMAP>), grid, block, lds,
                        s, a);
   return hipGetLastError();
 }
@@ -309,8 +256,166 @@ hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t s) { return launch_t
 
 hipError_t launch_gemm_grouped(const GemmArgs& a, hipStream_t s) { return launch_tiled_shape<1, 1, 4, 2, true>(a, s); }
 
-hipError_t launch_gemm_grouped_silu(const GemmArgs& a, hipStream_t s) {
-  return launch_tiled_shape<1, 1, 4, 2, true, false, false, true>(a, s);
+// ================================================================ routed FFN gate + up
+// The gate and up projections of a routed FFN in one pass over each token
+// tile's activation limbs.  A workgroup of 8 waves owns 128 rows of both
+// matrices for one token tile (one expert): waves 0-3 the four row tiles of
+// the gate matrix, waves 4-7 the same row tiles of the up matrix, all reading
+// the tile's three limb tiles from one LDS ring (per block: 8 code tiles, 3
+// limb tiles, 8 x 128 B of scales; every wave copies its own row tile's
+// scales).  The accumulation is the tiled kernel's (per-limb int64, exact for
+// any int32 scale).  At the end the up waves put their rounded results u in
+// LDS; each gate wave forms h = SiLU-gated product of its own g and the u of
+// the same elements in place, and writes its 32 x 32 tile of h (rows of the
+// tile x pairs) out as limb tile (block 4 rb + wave, token tile tb) of the
+// down projection's input, zero for pairs past the tile.  g and u never reach
+// HBM.
+constexpr int kGuWaves = 8;
+constexpr int kGuLimbOff = 8 * 1024;               // after the 8 code tiles
+constexpr int kGuScaleOff = kGuLimbOff + 3 * 1024;
+constexpr int kGuBlockBytes = kGuScaleOff + 8 * 128;
+constexpr int kGuNbuf = 2;
+constexpr int kGuTileBytes = 32 * 33 * 8;          // one wave's 32 x 32 int64 exchange tile (padded rows)
+
+__global__ __launch_bounds__(kGuWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void gemm_grouped_gateup_kernel(GemmArgs a) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wave & 3;              // row tile within the workgroup's 128 rows
+  const bool is_up = wave >= 4;
+  const int64_t tgs = a.tiles_max, rgs = a.n_pad / kTile;
+  const int64_t rb = blockIdx.x / tgs, tb = blockIdx.x % tgs;
+  if (tb >= *a.ntiles) return;          // the whole workgroup: no tile here
+  const int64_t ex = a.tile_expert[tb];
+  const int8_t* codes[2] = {a.codes + ex * a.expert_stride, a.codes2 + ex * a.expert_stride};
+  const int32_t* scales[2] = {
+      reinterpret_cast<const int32_t*>(reinterpret_cast<const int8_t*>(a.scales) + ex * a.expert_stride),
+      reinterpret_cast<const int32_t*>(reinterpret_cast<const int8_t*>(a.scales2) + ex * a.expert_stride)};
+  const int64_t nb = a.nb;
+  const __amdgpu_buffer_rsrc_t rlimb = make_rsrc(a.limb_tiles, (uint32_t)(3 * tgs * nb * 1024));
+  // copies j = wave and j = wave + 8 (< 11): j < 8 code tile (matrix j / 4,
+  // row tile j % 4), else limb tile j - 8.  Row tiles past the matrix re-read
+  // the last one (results unused).
+  constexpr int kCopies = 11;
+  __amdgpu_buffer_rsrc_t rsrc[2];
+  uint32_t soff[2];
+  int dst[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int j = wave + kGuWaves * i;
+    if (j < 8) {
+      int64_t rg = 4 * rb + (j & 3);
+      rg = rg < rgs ? rg : rgs - 1;
+      rsrc[i] = make_rsrc(codes[j >> 2], (uint32_t)(a.n_pad * nb * 1024));
+      soff[i] = (uint32_t)(rg * nb * 1024);
+      dst[i] = j * 1024;
+    } else {   // j < kCopies is checked where the copy is issued
+      rsrc[i] = rlimb;
+      soff[i] = (uint32_t)(((int64_t)(j - 8) * tgs + tb) * nb * 1024);
+      dst[i] = kGuLimbOff + (j - 8) * 1024;
+    }
+  }
+  const __amdgpu_buffer_rsrc_t rscal = make_rsrc(scales[is_up ? 1 : 0], (uint32_t)(a.n_pad * nb * 4));
+  uint32_t svoff;
+  {
+    int64_t rg = 4 * rb + wr;
+    rg = rg < rgs ? rg : rgs - 1;
+    svoff = (uint32_t)(rg * nb * 128) + (lane & 7) * 16;
+  }
+  const bool second = wave + kGuWaves < kCopies;   // waves 0-2 copy a limb tile too
+  auto issue = [&](int64_t b) {
+    uint8_t* blk = lds + (int)(b % kGuNbuf) * kGuBlockBytes;
+    copy16_to_lds(rsrc[0], blk + dst[0], lane * 16, soff[0] + (uint32_t)b * 1024u);
+    if (second) copy16_to_lds(rsrc[1], blk + dst[1], lane * 16, soff[1] + (uint32_t)b * 1024u);
+    if (lane < 8) copy16_to_lds(rscal, blk + kGuScaleOff + wave * 128, svoff, (uint32_t)b * 128u);
+  };
+
+  int64_t acc[3][16];
+#pragma unroll
+  for (int l = 0; l < 3; ++l)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[l][r] = 0;
+  const v16i zero = {};
+  if (nb > 0) issue(0);
+  for (int64_t b = 0; b < nb; ++b) {
+    barrier_after_vmcnt<0>();   // block b has landed for every wave; block b - 1's buffer is free
+    if (b + 1 < nb) issue(b + 1);
+    const uint8_t* blk = lds + (int)(b % kGuNbuf) * kGuBlockBytes;
+    const v4i q = *reinterpret_cast<const v4i*>(blk + wave * 1024 + lane * 16);
+    const int32_t S = *reinterpret_cast<const int32_t*>(blk + kGuScaleOff + (wave * 32 + (lane & 31)) * 4);
+#pragma unroll
+    for (int l = 0; l < 3; ++l) {
+      const v4i d = *reinterpret_cast<const v4i*>(blk + kGuLimbOff + l * 1024 + lane * 16);
+      const v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(d, q, zero, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[l][r] += (int64_t)S * D[r];
+    }
+  }
+
+  // ---- u through LDS, h in place, h out as limb tiles
+  __syncthreads();   // every wave is done with the ring
+  int64_t(*xt)[33] = reinterpret_cast<int64_t(*)[33]>(lds + wr * kGuTileBytes);   // [pair][row]
+  const int64_t rtile = rb * 4 + wr, row = rtile * kTile + (lane & 31);
+  const int rows = a.tile_rows[tb];
+  bool good = true;
+  if (is_up) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int tloc = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      int64_t u = 0;
+      if (row < a.n && tloc < rows) {
+        const __int128 v = (__int128)acc[0][r] + ((__int128)acc[1][r] << 8) + ((__int128)acc[2][r] << 16);
+        good = finish_output(v, OUT_ROUND_Q24, &u) && good;
+      }
+      xt[tloc][lane & 31] = u;
+    }
+  }
+  __syncthreads();   // u is in place for the gate waves
+  if (is_up) {
+    if (!good) flag(a.status, EI_DEV_OUT_RANGE);
+    return;
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int tloc = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+    int64_t h = 0;
+    if (row < a.n && tloc < rows) {
+      const __int128 v = (__int128)acc[0][r] + ((__int128)acc[1][r] << 8) + ((__int128)acc[2][r] << 16);
+      int64_t g;
+      good = finish_output(v, OUT_ROUND_Q24, &g) && good;
+      good = silu_gate(g, xt[tloc][lane & 31], a.lut, &h) && good;
+    }
+    xt[tloc][lane & 31] = h;   // the element this lane read: no other lane touches it
+  }
+  if (!good) flag(a.status, EI_DEV_OUT_RANGE);
+  __builtin_amdgcn_wave_barrier();   // this wave's LDS writes land before its reads
+  if (rtile >= a.n / kTile) return;
+  const int64_t* src = &xt[lane & 31][16 * (lane >> 5)];   // pair lane % 32, rows 16 (lane / 32) .. + 15
+  uint32_t words[3][4];
+  bool ok = true;
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    const int64_t v4[4] = {src[4 * q4], src[4 * q4 + 1], src[4 * q4 + 2], src[4 * q4 + 3]};
+    uint32_t w[3];
+    ok = limb_words<3>(v4, w) && ok;
+#pragma unroll
+    for (int l = 0; l < 3; ++l) words[l][q4] = w[l];
+  }
+  if (!ok) flag(a.status, EI_DEV_LIMB_RANGE);
+  const int64_t nb_out = a.n / kTile;
+#pragma unroll
+  for (int l = 0; l < 3; ++l) {
+    const v4i v = {(int)words[l][0], (int)words[l][1], (int)words[l][2], (int)words[l][3]};
+    reinterpret_cast<v4i*>(a.limb_out)[((l * tgs + tb) * nb_out + rtile) * 64 + lane] = v;
+  }
+}
+
+hipError_t launch_gemm_grouped_gateup(const GemmArgs& a, hipStream_t s) {
+  const int64_t rbs = (a.n_pad + 4 * kTile - 1) / (4 * kTile);
+  const size_t ring = (size_t)kGuNbuf * kGuBlockBytes, xch = (size_t)4 * kGuTileBytes;
+  hipLaunchKernelGGL(gemm_grouped_gateup_kernel, dim3((unsigned)(rbs * a.tiles_max)), dim3(kGuWaves * 64),
+                     ring > xch ? ring : xch, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace ei

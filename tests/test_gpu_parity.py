@@ -340,7 +340,7 @@ def test_qwen_ffn_24_layers_fused(ei):
         assert ei.digest(x) == GOLDEN["qwen05b_ffn"]["layers"][layer]["x_next"], layer
 
 
-@pytest.mark.parametrize("shape", [(5, 37, 3, 64, 96), (9, 12, 4, 32, 288), (100, 600, 2, 32, 64)])
+@pytest.mark.parametrize("shape", [(5, 37, 3, 64, 96), (9, 12, 4, 32, 288), (100, 600, 2, 32, 64), (7, 50, 2, 160, 64)])
 def test_moe_ffn_q8_small(ei, lut, shape):
     E, rows, topk, F, D = shape
     r = np.random.default_rng(E * 7 + rows)
