@@ -141,7 +141,7 @@ int run_gemm(const ei_weights* w, const void* x, int x_is_i32, int64_t* y, int64
     return EI_EINVAL;
   }
   auto launch = [&](const GemmArgs& args) {
-    if (lay.path == PATH_TILED) return launch_gemm_tiled(args, s);
+    if (lay.path == PATH_TILED) return launch_gemm_tiled(args, narrow_scales(w->smax, w->nb), s);
     return lay.mfma ? launch_gemm_mfma(args, limbs, s) : launch_gemv(args, limbs, s);
   };
 
@@ -329,9 +329,9 @@ hipError_t launch_grouped_projection(const ei_weights* w, const GroupedLayout& g
     a.scales2 = reinterpret_cast<const int32_t*>(ubase + kHeaderBytes + up->n_pad * up->k);
     a.lut = lut;
     a.limb_out = h_limbs;
-    return launch_gemm_grouped_gateup(a, s);
+    return launch_gemm_grouped_gateup(a, narrow_scales(w->smax, w->nb) && narrow_scales(up->smax, up->nb), s);
   }
-  return launch_gemm_grouped(a, s);
+  return launch_gemm_grouped(a, narrow_scales(w->smax, w->nb), s);
 }
 
 // FFN workspace: fused gate/up, h as the down projection's limb tiles

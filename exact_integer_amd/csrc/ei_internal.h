@@ -34,6 +34,16 @@ static_assert(sizeof(PackedHeader) <= kHeaderBytes, "header too large");
 
 inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
+// Three-limb accumulation in two int64 chains per output instead of one per
+// limb: S (P_0 + 2^8 P_1) and (2^16 S) P_2, each multiply-add on 32-bit
+// operands.  With |P_l| <= 32 * 128 * 128 = 2^19 a block adds at most
+// |S| (2^27 + 2^19) to the first chain and |S| 2^35 to the second, so both
+// chains and their sum stay below 2^62.01 (and 2^16 S fits int32) whenever
+// max|S| < 2^15 and nb * max|S| <= 2^27.
+inline bool narrow_scales(uint32_t smax, int64_t nb) {
+  return smax < 32768u && (uint64_t)smax * (uint64_t)nb <= ((uint64_t)1 << 27);
+}
+
 inline size_t packed_bytes(int64_t n, int64_t k) {
   int64_t n_pad = round_up(n, kTile);
   return (size_t)kHeaderBytes + (size_t)n_pad * (size_t)k + (size_t)n_pad * (size_t)(k / 32) * 4u;
@@ -106,12 +116,14 @@ hipError_t launch_limb_tiles(const void* x, int x_is_i32, int64_t t, int64_t k, 
                              int8_t* tiles, int64_t t_pad, int32_t* status, hipStream_t s);
 hipError_t launch_gemv(const GemmArgs& a, int limbs, hipStream_t s);
 hipError_t launch_gemm_mfma(const GemmArgs& a, int limbs, hipStream_t s);
-hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t s);    // 3 limbs, see tiled_ok()
-hipError_t launch_gemm_grouped(const GemmArgs& a, hipStream_t s);  // 3 limbs
+// narrow: the scales allow two int64 accumulators per output (narrow_scales);
+// otherwise one per limb
+hipError_t launch_gemm_tiled(const GemmArgs& a, bool narrow, hipStream_t s);    // 3 limbs, see tiled_ok()
+hipError_t launch_gemm_grouped(const GemmArgs& a, bool narrow, hipStream_t s);  // 3 limbs
 // grouped gate (a.codes, a.scales) and up (a.codes2, a.scales2, same shape and
 // expert stride) projections in one pass; writes h = SiLU-gated product as
 // limb tiles [3][tiles_max][n/32][1 KB] (a.limb_out); n % 32 == 0
-hipError_t launch_gemm_grouped_gateup(const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm_grouped_gateup(const GemmArgs& a, bool narrow, hipStream_t s);
 int skinny_splits(int64_t n_pad, int64_t t_pad, int64_t nb);       // workgroup K splits of the skinny kernel
 // a.part when splits > 1: (h, r) partials [splits][2][t][n] for up to three
 // limbs, per-limb partials [splits][limbs][t][n] for four

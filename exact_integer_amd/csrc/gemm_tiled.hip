@@ -8,10 +8,14 @@
 // blocks is exact for any int32 scale), then acc = A_0 + 2^8 A_1 + 2^16 A_2
 // in int128 and y = floor((acc + 2^23) / 2^24) (or acc).  Every step is exact
 // integer arithmetic, so the result is the same bits as any other
-// evaluation order.  (One shared int64 accumulator, with P_0 + 2^8 P_1 formed
-// in int32, needs one VALU op less per element but measured slower on
-// MI355X: its two dependent 64-bit multiply-adds per element stall where
-// three independent ones do not.)
+// evaluation order.
+// When the matrix's scales are narrow (max|S| < 2^15 and nb max|S| <= 2^27,
+// checked on the host from the packed header) the narrow form keeps two
+// chains per output instead: S (P_0 + 2^8 P_1), with P_0 + 2^8 P_1 formed in
+// int32, and (2^16 S) P_2 -- one 32-bit shift-add and two multiply-adds per
+// element instead of three multiply-adds, both chains below 2^62.01.  (One
+// shared chain would save registers, but the compiler then re-associates the
+// two dependent multiply-adds into three operations.)
 //
 // Work split.  A workgroup of 4 waves owns a tile of 32 RT WR rows x
 // 32 TT (4 / WR) tokens; each wave owns RT x TT 32x32 MFMA tiles.  Per
@@ -21,8 +25,8 @@
 // buffer loads (no VGPR round trip, scalar block offsets) into a ring of
 // NBUF one-block buffers, NBUF - 1 blocks ahead of use.  Per block a wave
 // issues 3 RT TT v_mfma_i32_32x32x32_i8 and, per output element, three
-// v_mad_i64_i32: this VALU epilogue, which the matrix cores only partly
-// overlap, is the critical resource.
+// v_mad_i64_i32 (narrow: two and a shift-add): this VALU epilogue, which the
+// matrix cores only partly overlap, is the critical resource.
 #include "ei_internal.h"
 
 namespace ei {
@@ -45,7 +49,8 @@ struct TiledShape {
 // kGrouped: each token tile belongs to one expert, whose packed image and
 // output rows it looks up.  PIPE: the epilogue of block b runs after the
 // MFMAs of block b + 1 are issued.  XMAP: XCD-contiguous tile order.
-template <int RT, int TT, int WR, int NBUF, bool kExact, bool kGrouped, bool PIPE, bool XMAP>
+// NARROW: two int64 accumulators per output (see narrow_scales), else one per limb.
+template <int RT, int TT, int WR, int NBUF, bool kExact, bool kGrouped, bool PIPE, bool XMAP, bool NARROW>
 __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs a) {
   using Sh = TiledShape<RT, TT, WR>;
   extern __shared__ __align__(16) uint8_t lds[];
@@ -129,9 +134,10 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs a) {
       copy16_to_lds(rscal, blk + sdst, svoff, (uint32_t)b * 128u);
   };
 
-  int64_t acc[3][RT][TT][16];
+  constexpr int NACC = NARROW ? 2 : 3;
+  int64_t acc[NACC][RT][TT][16];
 #pragma unroll
-  for (int c = 0; c < 3; ++c)
+  for (int c = 0; c < NACC; ++c)
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -176,13 +182,25 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs a) {
   };
   auto epilogue = [&](const Dset& D, const int32_t (&S)[RT]) {
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+    for (int rt = 0; rt < RT; ++rt) {
+      // NARROW: S P_0 + S 2^8 P_1 + S 2^16 P_2 as S (P_0 + 2^8 P_1) + (2^16 S) P_2;
+      // |P_0 + 2^8 P_1| < 2^28 and |2^16 S| < 2^31, so both multiply-adds
+      // take 32-bit operands (wraparound arithmetic, exact results)
+      const int32_t S16 = (int32_t)((uint32_t)S[rt] << 16);
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
+        for (int r = 0; r < 16; ++r) {
+          if constexpr (NARROW) {   // two independent chains: one multiply-add each
+            const int32_t p01 = (int32_t)(((uint32_t)D[rt][tt][1][r] << 8) + (uint32_t)D[rt][tt][0][r]);
+            acc[0][rt][tt][r] += (int64_t)S[rt] * p01;
+            acc[1][rt][tt][r] += (int64_t)S16 * D[rt][tt][2][r];
+          } else {
 #pragma unroll
-          for (int l = 0; l < 3; ++l) acc[l][rt][tt][r] += (int64_t)S[rt] * D[rt][tt][l][r];
+            for (int l = 0; l < NACC; ++l) acc[l][rt][tt][r] += (int64_t)S[rt] * D[rt][tt][l][r];
+          }
+        }
+    }
   };
 
   for (int64_t b = 0; b < NBUF - 1 && b < nb; ++b) issue(b);
@@ -224,16 +242,22 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs a) {
           orow = tb * Sh::kToks + tloc;
           if (orow >= a.t) continue;
         }
-        const __int128 v = (__int128)acc[0][rt][tt][r] + ((__int128)acc[1][rt][tt][r] << 8) +
-                           ((__int128)acc[2][rt][tt][r] << 16);
         int64_t out;
-        if (!finish_output(v, kExact ? OUT_EXACT : OUT_ROUND_Q24, &out)) flag(a.status, EI_DEV_OUT_RANGE);
+        if constexpr (NARROW) {   // |acc| < 2^62.01: the rounding add cannot overflow
+          const int64_t v = acc[0][rt][tt][r] + acc[1][rt][tt][r];
+          out = kExact ? v : (v + ((int64_t)1 << 23)) >> 24;
+        } else {
+          const __int128 v = (__int128)acc[0][rt][tt][r] + ((__int128)acc[NACC - 2][rt][tt][r] << 8) +
+                             ((__int128)acc[NACC - 1][rt][tt][r] << 16);
+          if (!finish_output(v, kExact ? OUT_EXACT : OUT_ROUND_Q24, &out)) flag(a.status, EI_DEV_OUT_RANGE);
+        }
         a.y[orow * a.n + row] = out;
       }
   }
 }
 
-template <int RT, int TT, int WR, int NBUF, bool kGrouped = false, bool PIPE = false, bool XMAP = false>
+template <int RT, int TT, int WR, int NBUF, bool kGrouped = false, bool PIPE = false, bool XMAP = false,
+          bool NARROW = false>
 hipError_t launch_tiled_shape(const GemmArgs& a, hipStream_t s) {
   using Sh = TiledShape<RT, TT, WR>;
   const int64_t rbs = (a.n_pad + Sh::kRows - 1) / Sh::kRows;
@@ -241,20 +265,27 @@ hipError_t launch_tiled_shape(const GemmArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)(rbs * tbs)), block(256);
   const size_t lds = (size_t)NBUF * Sh::kBlockBytes;
   if (a.out_mode == OUT_EXACT)
-    hipLaunchKernelGGL((gemm_tiled_kernel<RT, TT, WR, NBUF, true, kGrouped, PIPE, XMAP>), grid, block, lds, s,
+    hipLaunchKernelGGL((gemm_tiled_kernel<RT, TT, WR, NBUF, true, kGrouped, PIPE, XMAP, NARROW>), grid, block, lds, s,
                        a);
   else
-    hipLaunchKernelGGL((gemm_tiled_kernel<RT, TT, WR, NBUF, false, kGrouped, PIPE, XMAP>), grid, block, lds,
+    hipLaunchKernelGGL((gemm_tiled_kernel<RT, TT, WR, NBUF, false, kGrouped, PIPE, XMAP, NARROW>), grid, block, lds,
                        s, a);
   return hipGetLastError();
 }
 
 // Launch shape: one 32x32 tile per wave, 128 rows x 32 tokens per workgroup,
-// copies one block ahead, no software pipelining, natural tile order (the
-// fastest of the variants measured on MI355X).
-hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t s) { return launch_tiled_shape<1, 1, 4, 2>(a, s); }
+// copies one block ahead, no software pipelining (the fastest of the
+// variants measured on MI355X; larger wave tiles, deeper rings and a
+// pipelined epilogue were all slower).  The narrow-scale form runs in the
+// XCD-contiguous tile order, which measured a few per cent faster for it.
+hipError_t launch_gemm_tiled(const GemmArgs& a, bool narrow, hipStream_t s) {
+  return narrow ? launch_tiled_shape<1, 1, 4, 2, false, false, true, true>(a, s) : launch_tiled_shape<1, 1, 4, 2>(a, s);
+}
 
-hipError_t launch_gemm_grouped(const GemmArgs& a, hipStream_t s) { return launch_tiled_shape<1, 1, 4, 2, true>(a, s); }
+hipError_t launch_gemm_grouped(const GemmArgs& a, bool narrow, hipStream_t s) {
+  return narrow ? launch_tiled_shape<1, 1, 4, 2, true, false, false, true>(a, s)
+                : launch_tiled_shape<1, 1, 4, 2, true>(a, s);
+}
 
 // ================================================================ routed FFN gate + up
 // The gate and up projections of a routed FFN in one pass over each token
@@ -277,6 +308,8 @@ constexpr int kGuBlockBytes = kGuScaleOff + 8 * 128;
 constexpr int kGuNbuf = 2;
 constexpr int kGuTileBytes = 32 * 33 * 8;          // one wave's 32 x 32 int64 exchange tile (padded rows)
 
+// NARROW: two int64 accumulators per output, as in the tiled kernel.
+template <bool NARROW>
 __global__ __launch_bounds__(kGuWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void gemm_grouped_gateup_kernel(GemmArgs a) {
   extern __shared__ __align__(16) uint8_t lds[];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -330,9 +363,10 @@ __global__ __launch_bounds__(kGuWaves * 64) __attribute__((amdgpu_waves_per_eu(4
     if (lane < 8) copy16_to_lds(rscal, blk + kGuScaleOff + wave * 128, svoff, (uint32_t)b * 128u);
   };
 
-  int64_t acc[3][16];
+  constexpr int NACC = NARROW ? 2 : 3;
+  int64_t acc[NACC][16];
 #pragma unroll
-  for (int l = 0; l < 3; ++l)
+  for (int l = 0; l < NACC; ++l)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[l][r] = 0;
   const v16i zero = {};
@@ -343,14 +377,35 @@ __global__ __launch_bounds__(kGuWaves * 64) __attribute__((amdgpu_waves_per_eu(4
     const uint8_t* blk = lds + (int)(b % kGuNbuf) * kGuBlockBytes;
     const v4i q = *reinterpret_cast<const v4i*>(blk + wave * 1024 + lane * 16);
     const int32_t S = *reinterpret_cast<const int32_t*>(blk + kGuScaleOff + (wave * 32 + (lane & 31)) * 4);
+    if constexpr (NARROW) {
+      v16i D[3];
 #pragma unroll
-    for (int l = 0; l < 3; ++l) {
-      const v4i d = *reinterpret_cast<const v4i*>(blk + kGuLimbOff + l * 1024 + lane * 16);
-      const v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(d, q, zero, 0, 0, 0);
+      for (int l = 0; l < 3; ++l) {
+        const v4i d = *reinterpret_cast<const v4i*>(blk + kGuLimbOff + l * 1024 + lane * 16);
+        D[l] = __builtin_amdgcn_mfma_i32_32x32x32_i8(d, q, zero, 0, 0, 0);
+      }
+      const int32_t S16 = (int32_t)((uint32_t)S << 16);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[l][r] += (int64_t)S * D[r];
+      for (int r = 0; r < 16; ++r) {
+        const int32_t p01 = (int32_t)(((uint32_t)D[1][r] << 8) + (uint32_t)D[0][r]);
+        acc[0][r] += (int64_t)S * p01;
+        acc[1][r] += (int64_t)S16 * D[2][r];
+      }
+    } else {
+#pragma unroll
+      for (int l = 0; l < 3; ++l) {
+        const v4i d = *reinterpret_cast<const v4i*>(blk + kGuLimbOff + l * 1024 + lane * 16);
+        const v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(d, q, zero, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[l][r] += (int64_t)S * D[r];
+      }
     }
   }
+  // the output before rounding, from the accumulators of element r
+  auto total = [&](int r) -> __int128 {
+    if constexpr (NARROW) return (__int128)(acc[0][r] + acc[1][r]);   // |sum| < 2^62.01
+    else return (__int128)acc[0][r] + ((__int128)acc[NACC - 2][r] << 8) + ((__int128)acc[NACC - 1][r] << 16);
+  };
 
   // ---- u through LDS, h in place, h out as limb tiles
   __syncthreads();   // every wave is done with the ring
@@ -364,7 +419,7 @@ __global__ __launch_bounds__(kGuWaves * 64) __attribute__((amdgpu_waves_per_eu(4
       const int tloc = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
       int64_t u = 0;
       if (row < a.n && tloc < rows) {
-        const __int128 v = (__int128)acc[0][r] + ((__int128)acc[1][r] << 8) + ((__int128)acc[2][r] << 16);
+        const __int128 v = total(r);
         good = finish_output(v, OUT_ROUND_Q24, &u) && good;
       }
       xt[tloc][lane & 31] = u;
@@ -380,7 +435,7 @@ __global__ __launch_bounds__(kGuWaves * 64) __attribute__((amdgpu_waves_per_eu(4
     const int tloc = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
     int64_t h = 0;
     if (row < a.n && tloc < rows) {
-      const __int128 v = (__int128)acc[0][r] + ((__int128)acc[1][r] << 8) + ((__int128)acc[2][r] << 16);
+      const __int128 v = total(r);
       int64_t g;
       good = finish_output(v, OUT_ROUND_Q24, &g) && good;
       good = silu_gate(g, xt[tloc][lane & 31], a.lut, &h) && good;
@@ -410,11 +465,14 @@ __global__ __launch_bounds__(kGuWaves * 64) __attribute__((amdgpu_waves_per_eu(4
   }
 }
 
-hipError_t launch_gemm_grouped_gateup(const GemmArgs& a, hipStream_t s) {
+hipError_t launch_gemm_grouped_gateup(const GemmArgs& a, bool narrow, hipStream_t s) {
   const int64_t rbs = (a.n_pad + 4 * kTile - 1) / (4 * kTile);
   const size_t ring = (size_t)kGuNbuf * kGuBlockBytes, xch = (size_t)4 * kGuTileBytes;
-  hipLaunchKernelGGL(gemm_grouped_gateup_kernel, dim3((unsigned)(rbs * a.tiles_max)), dim3(kGuWaves * 64),
-                     ring > xch ? ring : xch, s, a);
+  const dim3 grid((unsigned)(rbs * a.tiles_max)), block(kGuWaves * 64);
+  if (narrow)
+    hipLaunchKernelGGL(gemm_grouped_gateup_kernel<true>, grid, block, ring > xch ? ring : xch, s, a);
+  else
+    hipLaunchKernelGGL(gemm_grouped_gateup_kernel<false>, grid, block, ring > xch ? ring : xch, s, a);
   return hipGetLastError();
 }
 

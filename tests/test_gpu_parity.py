@@ -348,6 +348,8 @@ def test_moe_ffn_q8_small(ei, lut, shape):
              (synth.q8_codes(r, D, F), synth.q8_scales(r, D, F))] for _ in range(E)]
     x = synth.q16_acts(r, rows, D)
     route = (r.integers(0, E, (rows, topk)) ** 2 % E).astype(np.int32)
+    if E == 9:   # one gate scale of 2^15 sends the fused gate/up pass to its per-limb accumulators
+        mats[0][0][1][0, 0] = 32768
 
     def stack(m):
         return (dev(np.stack([mm[m][0] for mm in mats])), dev(np.stack([mm[m][1] for mm in mats])))
@@ -406,6 +408,38 @@ def test_q8_tiled_per_limb_accumulators_extreme_scales(ei):
     say("tiled per-limb accumulators")
     w = ei.pack_q8(dev(q), dev(s))
     assert (host(ei.gemm_q8(w, dev(x))) == oracle.q8(q, s, x)).all()
+
+
+def test_q8_tiled_narrow_scales_at_the_edge(ei):
+    # max|S| = 2^15 - 1: the tiled kernel's two-chain accumulation (S (P_0 +
+    # 2^8 P_1) and 2^16 S P_2), with codes and activations at their ends
+    N, K, T = 1000, 256, 520
+    r = np.random.default_rng(13)
+    q = r.choice(np.array([-128, 127, -127, 3, 0], np.int8), size=(N, K))
+    s = r.choice(np.array([-32767, 32767, 1, -1, 0, 12345], np.int64), size=(N, K // 32)).astype(np.int32)
+    x = r.choice(np.array([8355711, -8421504, 0, 1, -1, 2**22], np.int64), size=(T, K))
+    say("tiled narrow scales")
+    w = ei.pack_q8(dev(q), dev(s))
+    assert w.desc.smax == 32767
+    assert (host(ei.gemm_q8(w, dev(x))) == oracle.q8(q, s, x)).all()
+
+
+@pytest.mark.parametrize("scale", [-32767, -32768])
+def test_q8_grouped_accumulators_at_the_narrow_bound(ei, scale):
+    # K = 131072 (4096 blocks) with every term at its extreme: at |S| = 2^15 - 1
+    # the two-chain accumulation reaches nb * max|S| = 2^27 - 4096, its bound
+    # (sums near 2^62); at |S| = 2^15 the per-limb accumulators take over
+    E, rows, topk, N, K = 2, 40, 1, 32, 131072
+    codes = np.full((E, N, K), -128, np.int8)
+    codes[1, ::3] = 127
+    scales = np.full((E, N, K // 32), scale, np.int32)
+    x = np.full((rows, K), -8421504, np.int64)
+    x[::4] = 8355711
+    route = (np.arange(rows) % E).astype(np.int32)[:, None]
+    say("grouped narrow bound", scale)
+    w = ei.pack_q8_stacked(dev(codes), dev(scales))
+    y = host(ei.gemm_q8_grouped(w, dev(x), dev(route)))
+    assert (y == _grouped_reference(codes, scales, x, route)).all()
 
 
 # ------------------------------------------------------------- routed (MoE)
