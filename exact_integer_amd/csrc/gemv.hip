@@ -23,14 +23,20 @@
 // operations complete in order.  Large K is staged in chunks of `a.chunk`
 // blocks per wave.
 //
-// Per block a lane issues one 16-byte code load and one scale load, L*T
-// 16-byte LDS reads, 4*L*T dot4 and L*T int64 multiply-adds.  The two halves
-// of every row are added with a cross-lane swap, the W waves through LDS.
+// Scales.  In the ascending order a wave's blocks are contiguous, so the
+// scales of a chunk (128 B per block) arrive in at most four 1 KB wave loads
+// and wait in LDS next to the limbs; the other orders load 128 B per block.
+//
+// Per block a lane issues one 16-byte code load, L*T 16-byte LDS reads and
+// one 4-byte scale read, 4*L*T dot4 and L*T int64 multiply-adds.  The two
+// halves of every row are added with a cross-lane swap, the W waves through
+// LDS.
 #include "ei_internal.h"
 
 namespace ei {
 
 constexpr int kGemvLdsPerWave = 8192;   // bytes of limb staging per wave (upper bound)
+constexpr int kGemvScaleLoads = 4;       // 1 KB scale loads per chunk: at most 32 blocks per chunk
 
 // Block visited at position pos: the plain ascending order unless the launch
 // is one of the schedule variants (kGeneric).
@@ -73,6 +79,8 @@ __global__ __launch_bounds__(W * 64) void gemv_kernel(GemmArgs a) {
   const int64_t p0 = wave * nblk / W, cnt = (wave + 1) * nblk / W - p0;   // this wave's block positions
   const int chunk = a.chunk;   // a multiple of 2D
   uint8_t* my = lds + (size_t)wave * chunk * kSlot;
+  // ascending order: the scales of a chunk's blocks, [slot][32] int32
+  uint8_t* mysc = lds + (size_t)W * chunk * kSlot + (size_t)wave * chunk * 128;
   // this row group's code tiles (nb x 1 KB) and scales (nb x 128 B)
   const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.codes + rg * a.nb * 1024, (uint32_t)(a.nb * 1024));
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scales + rg * a.nb * 32, (uint32_t)(a.nb * 128));
@@ -97,7 +105,7 @@ __global__ __launch_bounds__(W * 64) void gemv_kernel(GemmArgs a) {
       const int64_t m = m0 + u < cnt ? m0 + u : cnt - 1;
       const int b = (int)visit<kGeneric>(a, p0 + m);
       q[u] = __builtin_amdgcn_raw_buffer_load_b128(rc, vo_code, b * 1024, 0);
-      S[u] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo_scale, b * 128, 0);
+      if constexpr (kGeneric) S[u] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo_scale, b * 128, 0);
     }
   };
   auto consume = [&](const v4i (&q)[D], const int32_t (&S)[D], int64_t m0, int64_t c0) {
@@ -131,7 +139,10 @@ __global__ __launch_bounds__(W * 64) void gemv_kernel(GemmArgs a) {
             }
         }
       } else {
-        const int32_t Su = m0 + u < cnt ? S[u] : 0;   // a clamped reload past the end counts zero
+        int32_t Sb;
+        if constexpr (kGeneric) Sb = S[u];
+        else Sb = *reinterpret_cast<const int32_t*>(mysc + (s * 32 + (lane & 31)) * 4);
+        const int32_t Su = m0 + u < cnt ? Sb : 0;   // a clamped reload past the end counts zero
 #pragma unroll
         for (int t = 0; t < T; ++t)
 #pragma unroll
@@ -150,7 +161,18 @@ __global__ __launch_bounds__(W * 64) void gemv_kernel(GemmArgs a) {
   }
   for (int64_t c0 = 0; c0 < cnt; c0 += chunk) {
     const int cb = (int)(cnt - c0 < chunk ? cnt - c0 : chunk);
+    // ascending order: the chunk's scales are cb x 128 contiguous bytes,
+    // fetched with at most four 1 KB wave loads and parked in LDS (one
+    // 128-byte request per block measured slower)
+    v4i sc[kGemvScaleLoads];
+    const int nsl = kGeneric ? 0 : (cb * 128 + 1023) / 1024;
+#pragma unroll
+    for (int i = 0; i < kGemvScaleLoads; ++i)
+      if (i < nsl) sc[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16, (int)(a.b0 + p0 + c0) * 128 + i * 1024, 0);
     ok &= stage_limbs<L, T, XT, kGeneric>(a, p0, c0, cb, my, lane);
+#pragma unroll
+    for (int i = 0; i < kGemvScaleLoads; ++i)
+      if (i < nsl && lane * 16 + i * 1024 < cb * 128) *reinterpret_cast<v4i*>(mysc + lane * 16 + i * 1024) = sc[i];
     __builtin_amdgcn_wave_barrier();
     for (int64_t m = c0; m < c0 + cb; m += 2 * D) {
       consume(qa, Sa, m, c0);
@@ -214,11 +236,14 @@ static hipError_t gemv_launch(GemmArgs a, hipStream_t s) {
   const int64_t nblk = a.b1 - a.b0;
   const int64_t per_wave = ((nblk + W - 1) / W + 2 * D - 1) / (2 * D) * (2 * D);   // up to a multiple of 2D
   int64_t chunk = kGemvLdsPerWave / kSlot / (2 * D) * (2 * D);                      // down to a multiple of 2D
+  constexpr int kMaxScaleChunk = kGemvScaleLoads * 1024 / 128 / (2 * D) * (2 * D);
+  static_assert(kMaxScaleChunk >= 2 * D, "scale staging holds at least two batches");
+  if (chunk > kMaxScaleChunk) chunk = kMaxScaleChunk;
   if (chunk < 2 * D) chunk = 2 * D;
   if (chunk > per_wave) chunk = per_wave;
   a.chunk = (int)chunk;
   const size_t red = (size_t)W * 32 * T * L * 8;
-  size_t lds = (size_t)W * chunk * kSlot;
+  size_t lds = (size_t)W * chunk * (kSlot + 128);   // limbs, then the scales
   if (lds < red) lds = red;
   const dim3 grid((unsigned)(a.n_pad / kTile)), block(W * 64);
   const bool generic = a.order != ORDER_ASC || a.out_mode == OUT_TERMS;
