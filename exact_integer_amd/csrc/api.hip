@@ -153,13 +153,13 @@ int run_gemm(const ei_weights* w, const void* x, int x_is_i32, int64_t* y, int64
           int64_t* part = reinterpret_cast<int64_t*>(wsb + lay.part_off);
           a.part = part;
           a.out_mode = OUT_PARTIAL;
-          e = launch_gemm_skinny(a, limbs, lay.splits, s);
+          e = launch_gemm_skinny(a, limbs, lay.splits, limbs == 3 && narrow_scales(w->smax, w->nb), s);
           if (e == hipSuccess)
             e = limbs <= 3 ? launch_combine_hr(part, lay.splits, y, t, w->n, out_mode, resid, status, s)
                            : launch_combine_partials(part, lay.splits, y, t, w->n, limbs, out_mode, resid, status, s);
         } else {
           a.resid = resid;
-          e = launch_gemm_skinny(a, limbs, 1, s);
+          e = launch_gemm_skinny(a, limbs, 1, limbs == 3 && narrow_scales(w->smax, w->nb), s);
         }
         return e == hipSuccess ? EI_OK : EI_EDEVICE;
       }
@@ -518,7 +518,9 @@ int ffn_run(const ei_weights* wg, const ei_weights* wu, const ei_weights* wd, co
     a.b0 = 0;
     a.b1 = wg->nb;
     a.out_mode = OUT_ROUND_Q24;
-    if (launch_gemm_skinny_gateup(a, s) != hipSuccess) return EI_EDEVICE;
+    if (launch_gemm_skinny_gateup(a, narrow_scales(wg->smax, wg->nb) && narrow_scales(wu->smax, wu->nb), s) !=
+        hipSuccess)
+      return EI_EDEVICE;
     const int8_t* h_limbs = reinterpret_cast<const int8_t*>(ws + f.h_off);
     const WsLayout ld = layout_for(wd, t, 3, EI_SCHED_DEFAULT);
     if (out_limbs && ld.path == PATH_SKINNY && ld.splits > 1) {
@@ -541,7 +543,7 @@ int ffn_run(const ei_weights* wg, const ei_weights* wu, const ei_weights* wd, co
       b.b0 = 0;
       b.b1 = wd->nb;
       b.out_mode = OUT_PARTIAL;
-      if (launch_gemm_skinny(b, 3, ld.splits, s) != hipSuccess) return EI_EDEVICE;
+      if (launch_gemm_skinny(b, 3, ld.splits, narrow_scales(wd->smax, wd->nb), s) != hipSuccess) return EI_EDEVICE;
       return launch_combine_hr_tiles(part, ld.splits, y, t, wd->n, x, out_limbs, ld.t_pad, d_status, s) == hipSuccess
                  ? EI_OK
                  : EI_EDEVICE;

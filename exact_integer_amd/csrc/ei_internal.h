@@ -127,7 +127,7 @@ hipError_t launch_gemm_grouped_gateup(const GemmArgs& a, bool narrow, hipStream_
 int skinny_splits(int64_t n_pad, int64_t t_pad, int64_t nb);       // workgroup K splits of the skinny kernel
 // a.part when splits > 1: (h, r) partials [splits][2][t][n] for up to three
 // limbs, per-limb partials [splits][limbs][t][n] for four
-hipError_t launch_gemm_skinny(const GemmArgs& a, int limbs, int splits, hipStream_t s);
+hipError_t launch_gemm_skinny(const GemmArgs& a, int limbs, int splits, bool narrow, hipStream_t s);   // narrow: 3 limbs
 hipError_t launch_moe_sort(const int32_t* route, int64_t pairs, int64_t experts, int32_t* sorted_pair,
                            int32_t* offsets, int32_t* tile_expert, int32_t* tile_row0, int32_t* tile_rows,
                            int32_t* ntiles, int32_t* status, hipStream_t s);
@@ -142,7 +142,7 @@ hipError_t launch_combine_hr_tiles(const int64_t* part, int nparts, int64_t* y, 
                                    const int64_t* resid, int8_t* tiles, int64_t t_pad, int32_t* status,
                                    hipStream_t s);   // Q8 rounding; n % 32 == 0
 hipError_t launch_add_residual(int64_t* y, const int64_t* resid, int64_t n, int32_t* status, hipStream_t s);
-hipError_t launch_gemm_skinny_gateup(const GemmArgs& a, hipStream_t s);   // 3 limbs, one split
+hipError_t launch_gemm_skinny_gateup(const GemmArgs& a, bool narrow, hipStream_t s);   // 3 limbs, one split
 hipError_t launch_tree_terms(int64_t* terms, int64_t nb, int64_t* y, int64_t t, int64_t n,
                              int limbs, int out_mode, int32_t* status, hipStream_t s);
 hipError_t launch_make_perm(int32_t* perm, int64_t n, uint64_t seed, hipStream_t s);

@@ -34,8 +34,12 @@ struct SkinnyBatch {
 // FFN layer, W waves each, meet in the epilogue: h, the SiLU-gated product of
 // the two rounded results, goes out as the down projection's activation limb
 // tiles (limb_out; one workgroup split only, n a multiple of 32).
-template <int L, int W, int D, int G>
+// NARROW (three limbs only): two int64 chains per output, S (P_0 + 2^8 P_1)
+// and (2^16 S) P_2, whose sum is the exact total (see narrow_scales).
+template <int L, int W, int D, int G, bool NARROW>
 __global__ __launch_bounds__(64 * W * G) void gemm_skinny_kernel(GemmArgs a) {
+  static_assert(!NARROW || L == 3, "the narrow form takes three limbs");
+  constexpr int NACC = NARROW ? 2 : L;
   const int lane = threadIdx.x & 63;
   const int wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int m = wave_all / W, wave = wave_all % W;   // matrix, wave within it
@@ -50,9 +54,9 @@ __global__ __launch_bounds__(64 * W * G) void gemm_skinny_kernel(GemmArgs a) {
   const v4i* lbase = reinterpret_cast<const v4i*>(a.limb_tiles) + tg * a.nb * 64 + lane;
   const int64_t lstride = tgs * a.nb * 64;   // between limbs
 
-  int64_t acc[L][16];
+  int64_t acc[NACC][16];
 #pragma unroll
-  for (int l = 0; l < L; ++l)
+  for (int l = 0; l < NACC; ++l)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[l][r] = 0;
 
@@ -71,12 +75,25 @@ __global__ __launch_bounds__(64 * W * G) void gemm_skinny_kernel(GemmArgs a) {
     auto compute = [&](const SkinnyBatch<L, D>& bt, int64_t pos0) {
 #pragma unroll
       for (int u = 0; u < D; ++u) {
-        const int64_t S = pos0 + u < w1 ? (int64_t)bt.s[u] : 0;
+        const int32_t S = pos0 + u < w1 ? bt.s[u] : 0;
+        if constexpr (NARROW) {
+          v16i P[3];
 #pragma unroll
-        for (int l = 0; l < L; ++l) {
-          const v16i P = __builtin_amdgcn_mfma_i32_32x32x32_i8(bt.d[u][l], bt.q[u], zero, 0, 0, 0);
+          for (int l = 0; l < 3; ++l) P[l] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bt.d[u][l], bt.q[u], zero, 0, 0, 0);
+          const int32_t S16 = (int32_t)((uint32_t)S << 16);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[l][r] += S * (int64_t)P[r];
+          for (int r = 0; r < 16; ++r) {
+            const int32_t p01 = (int32_t)(((uint32_t)P[1][r] << 8) + (uint32_t)P[0][r]);
+            acc[0][r] += (int64_t)S * p01;
+            acc[NACC - 1][r] += (int64_t)S16 * P[2][r];
+          }
+        } else {
+#pragma unroll
+          for (int l = 0; l < L; ++l) {
+            const v16i P = __builtin_amdgcn_mfma_i32_32x32x32_i8(bt.d[u][l], bt.q[u], zero, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[l][r] += (int64_t)S * P[r];
+          }
         }
       }
     };
@@ -114,7 +131,10 @@ __global__ __launch_bounds__(64 * W * G) void gemm_skinny_kernel(GemmArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           int64_t h, rr;
-          split_hr(acc[0][r], L > 1 ? acc[L > 1 ? 1 : 0][r] : 0, L > 2 ? acc[L > 2 ? 2 : 0][r] : 0, &h, &rr);
+          if constexpr (NARROW)   // the exact total, |.| < 2^62.01
+            split_hr(acc[0][r] + acc[NACC - 1][r], 0, 0, &h, &rr);
+          else
+            split_hr(acc[0][r], L > 1 ? acc[L > 1 ? 1 : 0][r] : 0, L > 2 ? acc[L > 2 ? 2 : 0][r] : 0, &h, &rr);
           xh[wave][r][lane] = h;
           xr[wave][r][lane] = (int32_t)rr;   // < 3 * 2^24
         }
@@ -264,22 +284,37 @@ int skinny_splits(int64_t n_pad, int64_t t_pad, int64_t nb) {
   return ks < 1 ? 1 : (int)ks;
 }
 
-hipError_t launch_gemm_skinny(const GemmArgs& a, int limbs, int splits, hipStream_t s) {
+hipError_t launch_gemm_skinny(const GemmArgs& a, int limbs, int splits, bool narrow, hipStream_t s) {
   const dim3 grid((unsigned)(a.n_pad / kTile), (unsigned)splits, (unsigned)(a.t_pad / kTile));
   const dim3 block(64 * kSkinnyWaves);
   switch (limbs) {
-    case 1: hipLaunchKernelGGL((gemm_skinny_kernel<1, kSkinnyWaves, kSkinnyDepth, 1>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((gemm_skinny_kernel<2, kSkinnyWaves, kSkinnyDepth, 1>), grid, block, 0, s, a); break;
-    case 3: hipLaunchKernelGGL((gemm_skinny_kernel<3, kSkinnyWaves, kSkinnyDepth, 1>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((gemm_skinny_kernel<4, kSkinnyWaves, kSkinnyDepth, 1>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((gemm_skinny_kernel<1, kSkinnyWaves, kSkinnyDepth, 1, false>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((gemm_skinny_kernel<2, kSkinnyWaves, kSkinnyDepth, 1, false>), grid, block, 0, s, a); break;
+    case 3:
+      if (narrow)
+        hipLaunchKernelGGL((gemm_skinny_kernel<3, kSkinnyWaves, kSkinnyDepth, 1, true>), grid, block, 0, s, a);
+      else
+        hipLaunchKernelGGL((gemm_skinny_kernel<3, kSkinnyWaves, kSkinnyDepth, 1, false>), grid, block, 0, s, a);
+      break;
+    default: hipLaunchKernelGGL((gemm_skinny_kernel<4, kSkinnyWaves, kSkinnyDepth, 1, false>), grid, block, 0, s, a); break;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_skinny_gateup(const GemmArgs& a, hipStream_t s) {
+// The fused gate/up pass runs one workgroup split, so a wave owns a quarter
+// of all the blocks (7 at K = 896): four blocks per batch keep them all in
+// flight at once (two batches of two took two round trips to memory).  The
+// per-limb form keeps two blocks per batch (more would spill registers).
+constexpr int kGateUpDepth = 3;
+
+hipError_t launch_gemm_skinny_gateup(const GemmArgs& a, bool narrow, hipStream_t s) {
   const dim3 grid((unsigned)(a.n_pad / kTile), 1, (unsigned)(a.t_pad / kTile));
-  hipLaunchKernelGGL((gemm_skinny_kernel<3, kSkinnyWaves, kSkinnyDepth, 2>), grid, dim3(64 * kSkinnyWaves * 2), 0, s,
-                     a);
+  if (narrow)
+    hipLaunchKernelGGL((gemm_skinny_kernel<3, kSkinnyWaves, kGateUpDepth, 2, true>), grid, dim3(64 * kSkinnyWaves * 2),
+                       0, s, a);
+  else
+    hipLaunchKernelGGL((gemm_skinny_kernel<3, kSkinnyWaves, kSkinnyDepth, 2, false>), grid, dim3(64 * kSkinnyWaves * 2),
+                       0, s, a);
   return hipGetLastError();
 }
 

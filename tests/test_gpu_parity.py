@@ -424,6 +424,25 @@ def test_q8_tiled_narrow_scales_at_the_edge(ei):
     assert (host(ei.gemm_q8(w, dev(x))) == oracle.q8(q, s, x)).all()
 
 
+@pytest.mark.parametrize("shape", [(200, 512, 40), (70, 131072, 8), (96, 1024, 63)])
+@pytest.mark.parametrize("scale", [32767, -32768])
+def test_q8_skinny_accumulators_at_the_narrow_bound(ei, shape, scale):
+    # the skinny kernel (5 <= T < 64, K split over workgroups) with every term
+    # at its extreme: |S| = 2^15 - 1 takes the two-chain accumulation (at
+    # K = 131072 its sums reach about 2^62), |S| = 2^15 the per-limb one
+    N, K, T = shape
+    r = np.random.default_rng(N + K + T)
+    q = r.choice(np.array([-128, 127], np.int8), size=(N, K))
+    s = np.full((N, K // 32), scale, np.int32)
+    s[::5] = -scale
+    x = r.choice(np.array([8355711, -8421504], np.int64), size=(T, K))
+    x[0] = -8421504
+    q[0] = -128
+    say("skinny narrow bound", shape, scale)
+    w = ei.pack_q8(dev(q), dev(s))
+    assert (host(ei.gemm_q8(w, dev(x))) == oracle.q8(q, s, x)).all()
+
+
 @pytest.mark.parametrize("scale", [-32767, -32768])
 def test_q8_grouped_accumulators_at_the_narrow_bound(ei, scale):
     # K = 131072 (4096 blocks) with every term at its extreme: at |S| = 2^15 - 1
