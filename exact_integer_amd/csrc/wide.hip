@@ -21,14 +21,16 @@
 // operand lane order (lane l: row l % 32, columns 16 (l / 32) .. + 15).
 // Workgroup: 4 waves as 2 row tiles x 2 token tiles (64 rows x 64 tokens);
 // per block the 6 weight-digit and 8 activation-digit tiles are copied to
-// LDS with direct-to-LDS loads, NBUF blocks ahead.
+// LDS with direct-to-LDS loads, one block ahead.  (Wave tiles of 2 x 1, 1 x 2
+// and 2 x 2 MFMA tiles, which read less LDS per MFMA, measured the same time
+// on the 896 x 896, 4096-row shape: LDS traffic is not what bounds it.)
 #include "ei_internal.h"
 
 namespace ei {
 
 constexpr int kWideDigits = 3, kWideActLimbs = 4;
 constexpr int kWideBlockBytes = 16 * 1024;   // 6 + 8 tiles of 1 KB, 2 KB of padding copies
-constexpr int kWideNbuf = 3;
+constexpr int kWideNbuf = 2;                 // one block ahead: measured faster than two (44 vs 47 us)
 constexpr int kWideCopiesPerWave = 4;        // 16 copies of 1 KB per block, 4 per wave
 
 // One thread per (row tile, block, lane): 16 codes -> 3 digit words x 4.
