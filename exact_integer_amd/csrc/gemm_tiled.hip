@@ -282,9 +282,11 @@ hipError_t launch_gemm_tiled(const GemmArgs& a, bool narrow, hipStream_t s) {
   return narrow ? launch_tiled_shape<1, 1, 4, 2, false, false, true, true>(a, s) : launch_tiled_shape<1, 1, 4, 2>(a, s);
 }
 
+// Grouped: XCD-contiguous order, so that the token tiles of one expert
+// share an XCD's L2 (see the gate/up kernel).
 hipError_t launch_gemm_grouped(const GemmArgs& a, bool narrow, hipStream_t s) {
-  return narrow ? launch_tiled_shape<1, 1, 4, 2, true, false, false, true>(a, s)
-                : launch_tiled_shape<1, 1, 4, 2, true>(a, s);
+  return narrow ? launch_tiled_shape<1, 1, 4, 2, true, false, true, true>(a, s)
+                : launch_tiled_shape<1, 1, 4, 2, true, false, true>(a, s);
 }
 
 // ================================================================ routed FFN gate + up
@@ -317,7 +319,14 @@ __global__ __launch_bounds__(kGuWaves * 64) __attribute__((amdgpu_waves_per_eu(4
   const int wr = wave & 3;              // row tile within the workgroup's 128 rows
   const bool is_up = wave >= 4;
   const int64_t tgs = a.tiles_max, rgs = a.n_pad / kTile;
-  const int64_t rb = blockIdx.x / tgs, tb = blockIdx.x % tgs;
+  // XCD-contiguous order (workgroup g runs on XCD g % 8): each XCD takes a
+  // contiguous run of (row block, token tile) pairs, token tiles fastest, so
+  // the token tiles of one expert, which read the same weight rows, share
+  // that XCD's L2 instead of fetching the rows once per XCD
+  const int64_t nwg = ((a.n_pad + 4 * kTile - 1) / (4 * kTile)) * tgs;
+  int64_t g = blockIdx.x;
+  if (nwg % 8 == 0) g = (g % 8) * (nwg / 8) + g / 8;
+  const int64_t rb = g / tgs, tb = g % tgs;
   if (tb >= *a.ntiles) return;          // the whole workgroup: no tile here
   const int64_t ex = a.tile_expert[tb];
   const int8_t* codes[2] = {a.codes + ex * a.expert_stride, a.codes2 + ex * a.expert_stride};
