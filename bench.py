@@ -37,7 +37,7 @@ N, K = 14336, 4096
 LIMBS = 3                      # Q16 activations with |x| <= 2^22 need 3 balanced base-256 limbs
 W_BYTES = N * K + N * (K // 32) * 4          # canonical Q8: 1 B/code + 4 B/32-block scale
 GEMV_KERNEL = "gemv_kernel"
-GEMM_KERNEL = "gemm_tiled_kernel"
+GEMM_KERNEL = "gemm_tiled_qreg_kernel"   # the T=512 kernel for narrow scales (the synthetic Q24 ones)
 # the source file each timed kernel is built from: a stored HBM-traffic figure
 # is used only while that file is unchanged
 KERNEL_SOURCES = {GEMV_KERNEL: "gemv.hip", GEMM_KERNEL: "gemm_tiled.hip"}

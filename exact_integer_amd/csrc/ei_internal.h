@@ -120,6 +120,8 @@ hipError_t launch_gemm_mfma(const GemmArgs& a, int limbs, hipStream_t s);
 // otherwise one per limb
 hipError_t launch_gemm_tiled(const GemmArgs& a, bool narrow, hipStream_t s);    // 3 limbs, see tiled_ok()
 hipError_t launch_gemm_grouped(const GemmArgs& a, bool narrow, hipStream_t s);  // 3 limbs
+// narrow scales only (the register-fed tiled kernel), dense or grouped
+hipError_t launch_gemm_tiled_qreg(const GemmArgs& a, bool grouped, hipStream_t s);
 // grouped gate (a.codes, a.scales) and up (a.codes2, a.scales2, same shape and
 // expert stride) projections in one pass; writes h = SiLU-gated product as
 // limb tiles [3][tiles_max][n/32][1 KB] (a.limb_out); n % 32 == 0

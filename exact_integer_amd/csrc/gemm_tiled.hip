@@ -10,10 +10,9 @@
 // integer arithmetic, so the result is the same bits as any other
 // evaluation order.
 // When the matrix's scales are narrow (max|S| < 2^15 and nb max|S| <= 2^27,
-// checked on the host from the packed header) the narrow form keeps two
-// chains per output instead: S (P_0 + 2^8 P_1), with P_0 + 2^8 P_1 formed in
-// int32, and (2^16 S) P_2 -- one 32-bit shift-add and two multiply-adds per
-// element instead of three multiply-adds, both chains below 2^62.01.  (One
+// checked on the host from the packed header) the register-fed kernel keeps
+// two chains per output instead: S (P_0 + 2^8 P_1) and (2^16 S) P_2, both
+// below 2^62.01 -- two multiply-adds per element instead of three.  (One
 // shared chain would save registers, but the compiler then re-associates the
 // two dependent multiply-adds into three operations.)
 //
@@ -49,8 +48,7 @@ struct TiledShape {
 // kGrouped: each token tile belongs to one expert, whose packed image and
 // output rows it looks up.  PIPE: the epilogue of block b runs after the
 // MFMAs of block b + 1 are issued.  XMAP: XCD-contiguous tile order.
-// NARROW: two int64 accumulators per output (see narrow_scales), else one per limb.
-template <int RT, int TT, int WR, int NBUF, bool kExact, bool kGrouped, bool PIPE, bool XMAP, bool NARROW>
+template <int RT, int TT, int WR, int NBUF, bool kExact, bool kGrouped, bool PIPE, bool XMAP>
 __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs a) {
   using Sh = TiledShape<RT, TT, WR>;
   extern __shared__ __align__(16) uint8_t lds[];
@@ -134,10 +132,9 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs a) {
       copy16_to_lds(rscal, blk + sdst, svoff, (uint32_t)b * 128u);
   };
 
-  constexpr int NACC = NARROW ? 2 : 3;
-  int64_t acc[NACC][RT][TT][16];
+  int64_t acc[3][RT][TT][16];
 #pragma unroll
-  for (int c = 0; c < NACC; ++c)
+  for (int c = 0; c < 3; ++c)
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -182,25 +179,13 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs a) {
   };
   auto epilogue = [&](const Dset& D, const int32_t (&S)[RT]) {
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      // NARROW: S P_0 + S 2^8 P_1 + S 2^16 P_2 as S (P_0 + 2^8 P_1) + (2^16 S) P_2;
-      // |P_0 + 2^8 P_1| < 2^28 and |2^16 S| < 2^31, so both multiply-adds
-      // take 32-bit operands (wraparound arithmetic, exact results)
-      const int32_t S16 = (int32_t)((uint32_t)S[rt] << 16);
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if constexpr (NARROW) {   // two independent chains: one multiply-add each
-            const int32_t p01 = (int32_t)(((uint32_t)D[rt][tt][1][r] << 8) + (uint32_t)D[rt][tt][0][r]);
-            acc[0][rt][tt][r] += (int64_t)S[rt] * p01;
-            acc[1][rt][tt][r] += (int64_t)S16 * D[rt][tt][2][r];
-          } else {
+        for (int r = 0; r < 16; ++r)
 #pragma unroll
-            for (int l = 0; l < NACC; ++l) acc[l][rt][tt][r] += (int64_t)S[rt] * D[rt][tt][l][r];
-          }
-        }
-    }
+          for (int l = 0; l < 3; ++l) acc[l][rt][tt][r] += (int64_t)S[rt] * D[rt][tt][l][r];
   };
 
   for (int64_t b = 0; b < NBUF - 1 && b < nb; ++b) issue(b);
@@ -242,22 +227,16 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs a) {
           orow = tb * Sh::kToks + tloc;
           if (orow >= a.t) continue;
         }
+        const __int128 v = (__int128)acc[0][rt][tt][r] + ((__int128)acc[1][rt][tt][r] << 8) +
+                           ((__int128)acc[2][rt][tt][r] << 16);
         int64_t out;
-        if constexpr (NARROW) {   // |acc| < 2^62.01: the rounding add cannot overflow
-          const int64_t v = acc[0][rt][tt][r] + acc[1][rt][tt][r];
-          out = kExact ? v : (v + ((int64_t)1 << 23)) >> 24;
-        } else {
-          const __int128 v = (__int128)acc[0][rt][tt][r] + ((__int128)acc[NACC - 2][rt][tt][r] << 8) +
-                             ((__int128)acc[NACC - 1][rt][tt][r] << 16);
-          if (!finish_output(v, kExact ? OUT_EXACT : OUT_ROUND_Q24, &out)) flag(a.status, EI_DEV_OUT_RANGE);
-        }
+        if (!finish_output(v, kExact ? OUT_EXACT : OUT_ROUND_Q24, &out)) flag(a.status, EI_DEV_OUT_RANGE);
         a.y[orow * a.n + row] = out;
       }
   }
 }
 
-template <int RT, int TT, int WR, int NBUF, bool kGrouped = false, bool PIPE = false, bool XMAP = false,
-          bool NARROW = false>
+template <int RT, int TT, int WR, int NBUF, bool kGrouped = false, bool PIPE = false, bool XMAP = false>
 hipError_t launch_tiled_shape(const GemmArgs& a, hipStream_t s) {
   using Sh = TiledShape<RT, TT, WR>;
   const int64_t rbs = (a.n_pad + Sh::kRows - 1) / Sh::kRows;
@@ -265,28 +244,149 @@ hipError_t launch_tiled_shape(const GemmArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)(rbs * tbs)), block(256);
   const size_t lds = (size_t)NBUF * Sh::kBlockBytes;
   if (a.out_mode == OUT_EXACT)
-    hipLaunchKernelGGL((gemm_tiled_kernel<RT, TT, WR, NBUF, true, kGrouped, PIPE, XMAP, NARROW>), grid, block, lds, s,
+    hipLaunchKernelGGL((gemm_tiled_kernel<RT, TT, WR, NBUF, true, kGrouped, PIPE, XMAP>), grid, block, lds, s,
                        a);
   else
-    hipLaunchKernelGGL((gemm_tiled_kernel<RT, TT, WR, NBUF, false, kGrouped, PIPE, XMAP, NARROW>), grid, block, lds,
+    hipLaunchKernelGGL((gemm_tiled_kernel<RT, TT, WR, NBUF, false, kGrouped, PIPE, XMAP>), grid, block, lds,
                        s, a);
   return hipGetLastError();
 }
 
-// Launch shape: one 32x32 tile per wave, 128 rows x 32 tokens per workgroup,
-// copies one block ahead, no software pipelining (the fastest of the
-// variants measured on MI355X; larger wave tiles, deeper rings and a
-// pipelined epilogue were all slower).  The narrow-scale form runs in the
-// XCD-contiguous tile order, which measured a few per cent faster for it.
+// ================================================================ register-fed form
+// The narrow-scale tiled projection: the same 128-row x 32-token workgroup
+// tiles (XCD-contiguous order), one 32x32 tile per wave, but each wave's code
+// tile and scales are loaded straight into its registers (a wave is the only
+// reader of its row tile), so only the three activation limb tiles of a
+// block, which all four waves read, pass through LDS (measured 7 % faster
+// than staging the code tiles in LDS too).  P_0 + 2^8 P_1 comes out of the
+// matrix core: the limb-1 result, shifted left by 8 bits, is the accumulator
+// input of the limb-0 product (every partial sum stays below 2^28 in
+// magnitude).  Then two int64 chains per output, S (P_0 + 2^8 P_1) and
+// (2^16 S) P_2, exact for narrow scales (narrow_scales).
+template <bool kExact, bool kGrouped>
+__global__ __launch_bounds__(256) void gemm_tiled_qreg_kernel(GemmArgs a) {
+  constexpr int kBuf = 4 * 1024;   // per block: 3 limb tiles + 1 KB for the fourth wave's dummy copy
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // ---- tile of this workgroup: 128 rows x 32 tokens, XCD-contiguous order
+  const int64_t tbs = kGrouped ? a.tiles_max : a.t_pad / kTile;
+  const int64_t rbs = (a.n_pad + 127) / 128, ntiles = rbs * tbs;
+  int64_t g = blockIdx.x;
+  if (ntiles % 8 == 0) g = (g % 8) * (ntiles / 8) + g / 8;
+  const int64_t rb = g / tbs, tb = g % tbs;
+  const int64_t rgs = a.n_pad / kTile, tgs = kGrouped ? a.tiles_max : a.t_pad / kTile;
+  const int8_t* codes = a.codes;
+  const int32_t* scales = a.scales;
+  if (kGrouped) {
+    if (tb >= *a.ntiles) return;   // the whole workgroup: no tile here
+    const int64_t e = a.tile_expert[tb];
+    codes += e * a.expert_stride;
+    scales = reinterpret_cast<const int32_t*>(reinterpret_cast<const int8_t*>(scales) + e * a.expert_stride);
+  }
+  int64_t rg = 4 * rb + wave;     // this wave's row tile (past the matrix: the last one, results unused)
+  rg = rg < rgs ? rg : rgs - 1;
+  const __amdgpu_buffer_rsrc_t rcode = make_rsrc(codes + rg * a.nb * 1024, (uint32_t)(a.nb * 1024));
+  const __amdgpu_buffer_rsrc_t rscal = make_rsrc(scales + rg * a.nb * 32, (uint32_t)(a.nb * 128));
+  const __amdgpu_buffer_rsrc_t rlimb = make_rsrc(a.limb_tiles, (uint32_t)(3 * tgs * a.nb * 1024));
+  // limb copy of this wave: waves 0-2 limb tile `wave`, wave 3 limb tile 0
+  // again into the spare kilobyte (every wave issues one copy per block)
+  const int64_t tg = tb < tgs ? tb : tgs - 1;
+  const uint32_t lsoff = (uint32_t)(((int64_t)(wave < 3 ? wave : 0) * tgs + tg) * a.nb * 1024);
+  const int ldst = wave * 1024;
+  auto issue = [&](int64_t b) {
+    copy16_to_lds(rlimb, lds + (int)(b & 1) * kBuf + ldst, lane * 16, lsoff + (uint32_t)b * 1024u);
+  };
+
+  int64_t acc0[16], acc1[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc0[r] = acc1[r] = 0;
+  const v16i zero = {};
+  const int64_t nb = a.nb;
+  v4i qn = {};
+  int32_t Sn = 0;
+  if (nb > 0) {
+    issue(0);
+    qn = __builtin_amdgcn_raw_buffer_load_b128(rcode, lane * 16, 0, 0);
+    Sn = __builtin_amdgcn_raw_buffer_load_b32(rscal, (lane & 31) * 4, 0, 0);
+  }
+  for (int64_t b = 0; b < nb; ++b) {
+    barrier_after_vmcnt<0>();   // block b: limb tiles in LDS (every wave), code tile and scales in registers
+    const v4i q = qn;
+    const int32_t S = Sn;
+    if (b + 1 < nb) {
+      issue(b + 1);             // into the buffer block b - 1 used: every wave is past it
+      qn = __builtin_amdgcn_raw_buffer_load_b128(rcode, lane * 16, (int)(b + 1) * 1024, 0);
+      Sn = __builtin_amdgcn_raw_buffer_load_b32(rscal, (lane & 31) * 4, (int)(b + 1) * 128, 0);
+    }
+    const uint8_t* blk = lds + (int)(b & 1) * kBuf;
+    const v4i d0 = *reinterpret_cast<const v4i*>(blk + 0 * 1024 + lane * 16);
+    const v4i d1 = *reinterpret_cast<const v4i*>(blk + 1 * 1024 + lane * 16);
+    const v4i d2 = *reinterpret_cast<const v4i*>(blk + 2 * 1024 + lane * 16);
+    v16i c = __builtin_amdgcn_mfma_i32_32x32x32_i8(d1, q, zero, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) c[r] = (int)((uint32_t)c[r] << 8);
+    const v16i P01 = __builtin_amdgcn_mfma_i32_32x32x32_i8(d0, q, c, 0, 0, 0);   // P_0 + 2^8 P_1
+    const v16i P2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(d2, q, zero, 0, 0, 0);
+    const int32_t S16 = (int32_t)((uint32_t)S << 16);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      acc0[r] += (int64_t)S * P01[r];
+      acc1[r] += (int64_t)S16 * P2[r];
+    }
+  }
+
+  // ---- store: lane holds row 32 (4 rb + wave) + lane % 32 and tokens
+  // 8 (r / 4) + 4 (lane / 32) + r % 4 of the token tile
+  const int64_t row = (4 * rb + wave) * 32 + (lane & 31);
+  if (row >= a.n) return;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int tloc = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+    int64_t orow;
+    if (kGrouped) {
+      if (tloc >= a.tile_rows[tb]) continue;
+      orow = a.sorted_pair[a.tile_row0[tb] + tloc];
+    } else {
+      orow = tb * kTile + tloc;
+      if (orow >= a.t) continue;
+    }
+    const int64_t v = acc0[r] + acc1[r];   // |v| < 2^62.01: the rounding add cannot overflow
+    a.y[orow * a.n + row] = kExact ? v : (v + ((int64_t)1 << 23)) >> 24;
+  }
+}
+
+hipError_t launch_gemm_tiled_qreg(const GemmArgs& a, bool grouped, hipStream_t s) {
+  const int64_t rbs = (a.n_pad + 127) / 128;
+  const int64_t tbs = grouped ? a.tiles_max : a.t_pad / kTile;
+  const dim3 grid((unsigned)(rbs * tbs)), block(256);
+  const bool exact = a.out_mode == OUT_EXACT;
+  const size_t lds = 2 * 4 * 1024;
+  if (grouped && exact)
+    hipLaunchKernelGGL((gemm_tiled_qreg_kernel<true, true>), grid, block, lds, s, a);
+  else if (grouped)
+    hipLaunchKernelGGL((gemm_tiled_qreg_kernel<false, true>), grid, block, lds, s, a);
+  else if (exact)
+    hipLaunchKernelGGL((gemm_tiled_qreg_kernel<true, false>), grid, block, lds, s, a);
+  else
+    hipLaunchKernelGGL((gemm_tiled_qreg_kernel<false, false>), grid, block, lds, s, a);
+  return hipGetLastError();
+}
+
+// Launch shape of the per-limb form: one 32x32 tile per wave, 128 rows x 32
+// tokens per workgroup, copies one block ahead, no software pipelining (the
+// fastest of the variants measured on MI355X; larger wave tiles, deeper rings
+// and a pipelined epilogue were all slower).  Narrow scales take the
+// register-fed kernel above.
 hipError_t launch_gemm_tiled(const GemmArgs& a, bool narrow, hipStream_t s) {
-  return narrow ? launch_tiled_shape<1, 1, 4, 2, false, false, true, true>(a, s) : launch_tiled_shape<1, 1, 4, 2>(a, s);
+  return narrow ? launch_gemm_tiled_qreg(a, false, s) : launch_tiled_shape<1, 1, 4, 2>(a, s);
 }
 
 // Grouped: XCD-contiguous order, so that the token tiles of one expert
 // share an XCD's L2 (see the gate/up kernel).
 hipError_t launch_gemm_grouped(const GemmArgs& a, bool narrow, hipStream_t s) {
-  return narrow ? launch_tiled_shape<1, 1, 4, 2, true, false, true, true>(a, s)
-                : launch_tiled_shape<1, 1, 4, 2, true, false, true>(a, s);
+  return narrow ? launch_gemm_tiled_qreg(a, true, s) : launch_tiled_shape<1, 1, 4, 2, true, false, true>(a, s);
 }
 
 // ================================================================ routed FFN gate + up
@@ -310,7 +410,7 @@ constexpr int kGuBlockBytes = kGuScaleOff + 8 * 128;
 constexpr int kGuNbuf = 2;
 constexpr int kGuTileBytes = 32 * 33 * 8;          // one wave's 32 x 32 int64 exchange tile (padded rows)
 
-// NARROW: two int64 accumulators per output, as in the tiled kernel.
+// NARROW: two int64 accumulators per output, as in the register-fed tiled kernel.
 template <bool NARROW>
 __global__ __launch_bounds__(kGuWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void gemm_grouped_gateup_kernel(GemmArgs a) {
   extern __shared__ __align__(16) uint8_t lds[];
@@ -379,28 +479,58 @@ __global__ __launch_bounds__(kGuWaves * 64) __attribute__((amdgpu_waves_per_eu(4
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[l][r] = 0;
   const v16i zero = {};
-  if (nb > 0) issue(0);
-  for (int64_t b = 0; b < nb; ++b) {
-    barrier_after_vmcnt<0>();   // block b has landed for every wave; block b - 1's buffer is free
-    if (b + 1 < nb) issue(b + 1);
-    const uint8_t* blk = lds + (int)(b % kGuNbuf) * kGuBlockBytes;
-    const v4i q = *reinterpret_cast<const v4i*>(blk + wave * 1024 + lane * 16);
-    const int32_t S = *reinterpret_cast<const int32_t*>(blk + kGuScaleOff + (wave * 32 + (lane & 31)) * 4);
-    if constexpr (NARROW) {
-      v16i D[3];
-#pragma unroll
-      for (int l = 0; l < 3; ++l) {
-        const v4i d = *reinterpret_cast<const v4i*>(blk + kGuLimbOff + l * 1024 + lane * 16);
-        D[l] = __builtin_amdgcn_mfma_i32_32x32x32_i8(d, q, zero, 0, 0, 0);
+  if constexpr (NARROW) {
+    // register-fed, as in gemm_tiled_qreg_kernel: each wave loads its own
+    // code tile and scales into registers one block ahead; only the three
+    // limb tiles (copied by waves 0-2) pass through LDS
+    int64_t rg = 4 * rb + wr;
+    rg = rg < rgs ? rg : rgs - 1;
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(codes[is_up ? 1 : 0] + rg * nb * 1024, (uint32_t)(nb * 1024));
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(scales[is_up ? 1 : 0] + rg * nb * 32, (uint32_t)(nb * 128));
+    const uint32_t lsoff = (uint32_t)(((int64_t)(wave < 3 ? wave : 0) * tgs + tb) * nb * 1024);
+    auto issue_limb = [&](int64_t b) {
+      if (wave < 3) copy16_to_lds(rlimb, lds + (int)(b & 1) * 3072 + wave * 1024, lane * 16, lsoff + (uint32_t)b * 1024u);
+    };
+    v4i qn = {};
+    int32_t Sn = 0;
+    if (nb > 0) {
+      issue_limb(0);
+      qn = __builtin_amdgcn_raw_buffer_load_b128(rc, lane * 16, 0, 0);
+      Sn = __builtin_amdgcn_raw_buffer_load_b32(rs, (lane & 31) * 4, 0, 0);
+    }
+    for (int64_t b = 0; b < nb; ++b) {
+      barrier_after_vmcnt<0>();   // block b: limb tiles in LDS, code tile and scales in registers
+      const v4i q = qn;
+      const int32_t S = Sn;
+      if (b + 1 < nb) {
+        issue_limb(b + 1);        // into the buffer block b - 1 used: every wave is past it
+        qn = __builtin_amdgcn_raw_buffer_load_b128(rc, lane * 16, (int)(b + 1) * 1024, 0);
+        Sn = __builtin_amdgcn_raw_buffer_load_b32(rs, (lane & 31) * 4, (int)(b + 1) * 128, 0);
       }
+      const uint8_t* blk = lds + (int)(b & 1) * 3072;
+      const v4i d0 = *reinterpret_cast<const v4i*>(blk + lane * 16);
+      const v4i d1 = *reinterpret_cast<const v4i*>(blk + 1024 + lane * 16);
+      const v4i d2 = *reinterpret_cast<const v4i*>(blk + 2048 + lane * 16);
+      v16i c = __builtin_amdgcn_mfma_i32_32x32x32_i8(d1, q, zero, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) c[r] = (int)((uint32_t)c[r] << 8);
+      const v16i P01 = __builtin_amdgcn_mfma_i32_32x32x32_i8(d0, q, c, 0, 0, 0);   // P_0 + 2^8 P_1
+      const v16i P2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(d2, q, zero, 0, 0, 0);
       const int32_t S16 = (int32_t)((uint32_t)S << 16);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int32_t p01 = (int32_t)(((uint32_t)D[1][r] << 8) + (uint32_t)D[0][r]);
-        acc[0][r] += (int64_t)S * p01;
-        acc[1][r] += (int64_t)S16 * D[2][r];
+        acc[0][r] += (int64_t)S * P01[r];
+        acc[NACC - 1][r] += (int64_t)S16 * P2[r];
       }
-    } else {
+    }
+  } else {
+    if (nb > 0) issue(0);
+    for (int64_t b = 0; b < nb; ++b) {
+      barrier_after_vmcnt<0>();   // block b has landed for every wave; block b - 1's buffer is free
+      if (b + 1 < nb) issue(b + 1);
+      const uint8_t* blk = lds + (int)(b % kGuNbuf) * kGuBlockBytes;
+      const v4i q = *reinterpret_cast<const v4i*>(blk + wave * 1024 + lane * 16);
+      const int32_t S = *reinterpret_cast<const int32_t*>(blk + kGuScaleOff + (wave * 32 + (lane & 31)) * 4);
 #pragma unroll
       for (int l = 0; l < 3; ++l) {
         const v4i d = *reinterpret_cast<const v4i*>(blk + kGuLimbOff + l * 1024 + lane * 16);
