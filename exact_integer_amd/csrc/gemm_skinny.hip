@@ -36,9 +36,15 @@ struct SkinnyBatch {
 // tiles (limb_out; one workgroup split only, n a multiple of 32).
 // NARROW (three limbs only): two int64 chains per output, S (P_0 + 2^8 P_1)
 // and (2^16 S) P_2, whose sum is the exact total (see narrow_scales).
-template <int L, int W, int D, int G, bool NARROW>
+// STAGE > 0 (the fused gate/up pass with narrow scales, one split, at most
+// STAGE blocks per wave): the token tile's limb tiles for the whole K are
+// staged in LDS once (the gate waves copy them, one barrier), and every wave
+// issues the loads of all its code tiles and scales at once, so each wave
+// waits for memory once instead of once per batch.
+template <int L, int W, int D, int G, bool NARROW, int STAGE = 0>
 __global__ __launch_bounds__(64 * W * G) void gemm_skinny_kernel(GemmArgs a) {
   static_assert(!NARROW || L == 3, "the narrow form takes three limbs");
+  static_assert(STAGE == 0 || (G == 2 && NARROW), "staged limbs: the fused narrow gate/up pass");
   constexpr int NACC = NARROW ? 2 : L;
   const int lane = threadIdx.x & 63;
   const int wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -60,7 +66,49 @@ __global__ __launch_bounds__(64 * W * G) void gemm_skinny_kernel(GemmArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[l][r] = 0;
 
-  if (w1 > w0) {
+  if constexpr (STAGE > 0) {
+    extern __shared__ __align__(16) uint8_t stage[];   // limb tile (b, l) at (3 b + l) KB
+    const v16i zero = {};
+    if (m == 0) {   // the gate waves copy the limb tiles of their blocks
+      const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.limb_tiles, (uint32_t)(3 * tgs * a.nb * 1024));
+      for (int64_t b = w0; b < w1; ++b)
+#pragma unroll
+        for (int l = 0; l < 3; ++l)
+          copy16_to_lds(rl, stage + (3 * b + l) * 1024, lane * 16, (uint32_t)(((l * tgs + tg) * a.nb + b) * 1024));
+    }
+    // then every wave's code tiles and scales, positions past w1 repeating its last block
+    v4i q[STAGE];
+    int32_t sc[STAGE];
+    const int64_t bl = w1 > w0 ? w1 - 1 : 0;   // a wave without blocks loads block 0 (unused)
+#pragma unroll
+    for (int u = 0; u < STAGE; ++u) {
+      const int64_t b = w0 + u < w1 ? w0 + u : bl;
+      q[u] = cbase[b * 64];
+      sc[u] = sbase[b * 32];
+    }
+    // the copies were issued first: waiting until at most the 2 STAGE code
+    // and scale loads are outstanding leaves only those in flight
+    barrier_after_vmcnt<2 * STAGE>();
+#pragma unroll
+    for (int u = 0; u < STAGE; ++u) {
+      if (w0 + u >= w1) break;
+      const int64_t b = w0 + u;
+      const v4i d0 = *reinterpret_cast<const v4i*>(stage + (3 * b + 0) * 1024 + lane * 16);
+      const v4i d1 = *reinterpret_cast<const v4i*>(stage + (3 * b + 1) * 1024 + lane * 16);
+      const v4i d2 = *reinterpret_cast<const v4i*>(stage + (3 * b + 2) * 1024 + lane * 16);
+      v16i c = __builtin_amdgcn_mfma_i32_32x32x32_i8(d1, q[u], zero, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) c[r] = (int)((uint32_t)c[r] << 8);
+      const v16i P01 = __builtin_amdgcn_mfma_i32_32x32x32_i8(d0, q[u], c, 0, 0, 0);   // P_0 + 2^8 P_1
+      const v16i P2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(d2, q[u], zero, 0, 0, 0);
+      const int32_t S16 = (int32_t)((uint32_t)sc[u] << 16);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        acc[0][r] += (int64_t)sc[u] * P01[r];
+        acc[NACC - 1][r] += (int64_t)S16 * P2[r];
+      }
+    }
+  } else if (w1 > w0) {
     const v16i zero = {};
     auto load = [&](SkinnyBatch<L, D>& bt, int64_t pos0) {
 #pragma unroll
@@ -309,10 +357,14 @@ hipError_t launch_gemm_skinny(const GemmArgs& a, int limbs, int splits, bool nar
 // flight at once (two batches of two took two round trips to memory).  The
 // per-limb form keeps two blocks per batch (more would spill registers).
 constexpr int kGateUpDepth = 3;
+constexpr int kGateUpStage = 8;   // blocks per wave with the limb tiles staged in LDS (K <= 1024)
 
 hipError_t launch_gemm_skinny_gateup(const GemmArgs& a, bool narrow, hipStream_t s) {
   const dim3 grid((unsigned)(a.n_pad / kTile), 1, (unsigned)(a.t_pad / kTile));
-  if (narrow)
+  if (narrow && a.nb <= kSkinnyWaves * kGateUpStage)
+    hipLaunchKernelGGL((gemm_skinny_kernel<3, kSkinnyWaves, kGateUpDepth, 2, true, kGateUpStage>), grid,
+                       dim3(64 * kSkinnyWaves * 2), (size_t)a.nb * 3 * 1024, s, a);
+  else if (narrow)
     hipLaunchKernelGGL((gemm_skinny_kernel<3, kSkinnyWaves, kGateUpDepth, 2, true>), grid, dim3(64 * kSkinnyWaves * 2),
                        0, s, a);
   else
