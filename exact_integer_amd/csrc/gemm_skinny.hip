@@ -353,9 +353,11 @@ hipError_t launch_gemm_skinny(const GemmArgs& a, int limbs, int splits, bool nar
 }
 
 // The fused gate/up pass runs one workgroup split, so a wave owns a quarter
-// of all the blocks (7 at K = 896): four blocks per batch keep them all in
-// flight at once (two batches of two took two round trips to memory).  The
-// per-limb form keeps two blocks per batch (more would spill registers).
+// of all the blocks (7 at K = 896).  With narrow scales and K <= 1024 the
+// staged form holds the whole K's limb tiles in LDS and all of a wave's code
+// tiles in flight at once (11.7 -> 10.8 us per Qwen layer); otherwise the
+// narrow form keeps three blocks per batch (four spill registers) and the
+// per-limb form two.
 constexpr int kGateUpDepth = 3;
 constexpr int kGateUpStage = 8;   // blocks per wave with the limb tiles staged in LDS (K <= 1024)
 
