@@ -424,6 +424,26 @@ def test_q8_tiled_narrow_scales_at_the_edge(ei):
     assert (host(ei.gemm_q8(w, dev(x))) == oracle.q8(q, s, x)).all()
 
 
+@pytest.mark.parametrize("emax", [14, 15])
+def test_q4_tiled_exact_output(ei, emax):
+    # the tiled prefill path (128 workgroups of 128 rows x 32 tokens) with the
+    # exact, unrounded output of the 4-bit format: scales 2^e with e <= 14 take
+    # the register-fed narrow kernel, one e = 15 (max|S| = 2^15) the per-limb one
+    N, K, T = 2048, 128, 256
+    r = np.random.default_rng(31 + emax)
+    nib = synth.q4_codes_packed(r, N, K)
+    m = r.integers(1, 16, (N, K // 32))
+    e = r.integers(0, emax + 1, (N, K // 32))
+    e[5, 1] = emax
+    sme = (m | (e << 4)).astype(np.uint8)
+    x = r.integers(-(2**15), 2**15, (T, K), dtype=np.int64).astype(np.int32)
+    x[3] = -(2**15)
+    say("q4 tiled exact", emax)
+    w = ei.pack_q4(dev(nib), dev(sme))
+    assert w.desc.smax == 2**emax
+    assert (host(ei.gemm_q4(w, dev(x))) == oracle.q4(nib, sme, x)).all()
+
+
 @pytest.mark.parametrize("shape", [(200, 512, 40), (70, 131072, 8), (96, 1024, 63)])
 @pytest.mark.parametrize("scale", [32767, -32768])
 def test_q8_skinny_accumulators_at_the_narrow_bound(ei, shape, scale):
