@@ -90,7 +90,11 @@ enum {
 enum { EI_FORMAT_Q8 = 1, EI_FORMAT_Q4 = 2, EI_FORMAT_WIDE = 3 };
 
 /* Host-side descriptor of a packed weight matrix, filled by ei_q8_pack or
- * ei_q4_pack.  `packed` points into the caller's device buffer. */
+ * ei_q4_pack.  `packed` points into the caller's device buffer.  The fields
+ * are read as the pack call wrote them; in particular `smax` selects the
+ * accumulation form of the MFMA kernels (two int64 chains per output when
+ * smax < 2^15 and nb * smax <= 2^27, else one per activation limb), so a
+ * descriptor whose smax understates the packed scales voids exactness. */
 typedef struct ei_weights {
   const void* packed;   /* device: packed tiles, see ei_q8_pack            */
   int64_t n;            /* output rows                                     */
@@ -191,8 +195,11 @@ size_t ei_gemm_workspace_bytes(const ei_weights* w, int64_t t, int limbs, int sc
  *   schedule EI_SCHED_*; shuffle_seed seeds EI_SCHED_TILED_SHUFFLED
  * Exactness: per-limb partial sums are carried in int64 and are exact for
  * any int32 scales while k <= 262144 (each term |S P| < 2^31 2^19 = 2^50);
- * the limbs are combined in int128 and rounded once.  EI_ERANGE if
- * k > 262144 or t > 65535 * 32.  A y outside int64 sets EI_DEV_OUT_RANGE.
+ * the limbs are combined in int128 and rounded once.  With 3 limbs and
+ * narrow scales (w->smax < 2^15 and nb * smax <= 2^27) the MFMA kernels
+ * carry S (P_0 + 2^8 P_1) and 2^16 S P_2 instead, both below 2^62.01: the
+ * same exact sum.  EI_ERANGE if k > 262144 or t > 65535 * 32.  A y outside
+ * int64 sets EI_DEV_OUT_RANGE.
  */
 int int_gemm_q8(const ei_weights* w, const int64_t* x, int64_t* y, int64_t t, int limbs,
                 int schedule, uint64_t shuffle_seed, void* workspace, size_t workspace_bytes,
