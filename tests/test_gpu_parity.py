@@ -410,11 +410,14 @@ def test_q8_tiled_per_limb_accumulators_extreme_scales(ei):
     assert (host(ei.gemm_q8(w, dev(x))) == oracle.q8(q, s, x)).all()
 
 
-def test_q8_tiled_narrow_scales_at_the_edge(ei):
+@pytest.mark.parametrize("N", [1000, 1100])
+def test_q8_tiled_narrow_scales_at_the_edge(ei, N):
     # max|S| = 2^15 - 1: the tiled kernel's two-chain accumulation (S (P_0 +
-    # 2^8 P_1) and 2^16 S P_2), with codes and activations at their ends
-    N, K, T = 1000, 256, 520
-    r = np.random.default_rng(13)
+    # 2^8 P_1) and 2^16 S P_2), with codes and activations at their ends;
+    # 8 x 17 = 136 workgroups take the XCD-contiguous order, 9 x 17 = 153 the
+    # launch order
+    K, T = 256, 520
+    r = np.random.default_rng(13 + N)
     q = r.choice(np.array([-128, 127, -127, 3, 0], np.int8), size=(N, K))
     s = r.choice(np.array([-32767, 32767, 1, -1, 0, 12345], np.int64), size=(N, K // 32)).astype(np.int32)
     x = r.choice(np.array([8355711, -8421504, 0, 1, -1, 2**22], np.int64), size=(T, K))
