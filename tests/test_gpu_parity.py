@@ -246,13 +246,14 @@ def test_qwen_ffn_24_layers(ei):
 
 
 @pytest.mark.parametrize("shape", [(96, 64, 1), (96, 64, 3), (160, 96, 30), (128, 64, 40), (64, 4096, 30),
-                                   (4096, 64, 30), (96, 160, 70), (32, 320, 5)])
+                                   (4096, 64, 30), (96, 160, 70), (32, 320, 5), (4096, 1024, 30), (4096, 1056, 30)])
 def test_ffn_q8_matches_the_separate_steps(ei, lut, shape):
     # one layer through int_ffn_q8 against the oracle's gate, up, SiLU
     # product, down projection and residual: the fused gate/up pass (5..63
     # tokens with one workgroup split), the GEMV path, the tiled path, the
     # unfused path, and split-K partials (with the residual) on the down
-    # projection
+    # projection; K = 1024 is the largest the fused pass stages in LDS
+    # (152 KB with its exchange buffers), K = 1056 the smallest it does not
     F, D, T = shape
     r = np.random.default_rng(F + D + T)
     mats = [(synth.q8_codes(r, F, D), synth.q8_scales(r, F, D)), (synth.q8_codes(r, F, D), synth.q8_scales(r, F, D)),
