@@ -516,6 +516,22 @@ def main() -> int:
         print(f"bench.py: device status {int(status.item())}", file=sys.stderr)
         return 1
 
+    # ---- the same decode pass as batched launches (int_gemm_q8_multi, up to
+    # 16 matrices sharing x per launch): reported beside `value`, not in it
+    yb = [torch.empty((1, N), dtype=torch.int64, device=dev) for _ in copies]
+    batched = {}
+    for group in (2, 16):   # 2: gate and up of one FFN layer; 16: the largest batch
+        def decode_batched():
+            for i in range(0, len(copies), group):
+                ei.gemm_q8_multi(copies[i:i + group], x1d, LIMBS, outs=yb[i:i + group], status=status)
+
+        batched[group], _ = _time_graph(torch, decode_batched, args.steps, args.warmup)
+        if {ei.digest(y) for y in yb} != {json.load(open(os.path.join(ROOT, "tests", "golden", "oracle_digests.json")))[
+                "dense_14336x4096"]["t1_y"]}:
+            print(json.dumps({"error": "parity failure (batched decode)", "group": group}))
+            return 1
+        yb = [torch.empty((1, N), dtype=torch.int64, device=dev) for _ in copies]
+
     # ---- parity of what was timed
     import oracle
     gold = json.load(open(os.path.join(ROOT, "tests", "golden", "oracle_digests.json")))["dense_14336x4096"]["t1_y"]
@@ -524,7 +540,7 @@ def main() -> int:
     ref = oracle.q8(q[rows], s[rows], x512, threads=min(os.cpu_count() or 1, 16))
     ok512 = bool((y512.cpu().numpy()[:, rows] == ref).all())
     parity = {"t1_digest_equals_oracle": dig == {gold}, "t512_sampled_rows_equal_oracle": ok512,
-              "t512_rows_checked": int(rows.size)}
+              "t512_rows_checked": int(rows.size), "t1_batched_digests_equal_oracle": True}
     if not (parity["t1_digest_equals_oracle"] and ok512):
         print(json.dumps({"error": "parity failure", "parity": parity}))
         return 1
@@ -547,6 +563,14 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": round(ach_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(ach_gbs / HBM_PEAK_GBS, 4), "traffic": tr_dec, "kernel": GEMV_KERNEL,
                      "launch_us": round(per_gemv_ms * 1e3, 3), "algorithmic_bytes": algo_bytes},
+        "decode_batched": {
+            f"{g}_per_launch": {
+                "launches": (args.copies + g - 1) // g, "us_per_matrix": round(ms * 1e3 / args.copies, 3),
+                "weight_gbs": round(W_BYTES * args.copies / (ms * 1e-3) / 1e9, 1),
+                "frac_of_hbm_peak": round(W_BYTES * args.copies / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            for g, ms in batched.items()} | {
+            "note": "the same T=1 projections in launches of up to 2 (gate and up of a layer) or 16 matrices "
+                    "sharing x (int_gemm_q8_multi); `value` times one launch per matrix"},
         "prefill_t512": {
             "ms": round(pre_med, 4), "useful_tops": round(pre_tops, 2),
             "logical_tops": round(pre_tops / LIMBS, 2),

@@ -56,6 +56,7 @@ SIGNATURES = {
     "ei_limb_split": (I32, [P, P, I64, I32, P, P]),
     "ei_gemm_workspace_bytes": (SZ, [WP, I64, I32, I32]),
     "int_gemm_q8": (I32, [WP, P, P, I64, I32, I32, U64, P, SZ, P, P]),
+    "int_gemm_q8_multi": (I32, [P, I32, P, P, I64, I32, P, P]),
     "int_gemm_q4": (I32, [WP, P, P, I64, I32, I32, U64, P, SZ, P, P]),
     "ei_silu_lut_build": (I32, [P, P]),
     "silu_lut_epilogue": (I32, [P, P, P, P, I64, P, P]),
@@ -485,6 +486,31 @@ def gemm_q8(w: PackedWeights, x: torch.Tensor, limbs: int = 3, schedule: str = "
             out=None, workspace=None, status=None) -> torch.Tensor:
     """y = (sum_b S sum_j q x + 2^23) >> 24 for Q16 int64 activations x [t][k]."""
     return _gemm("int_gemm_q8", w, x, torch.int64, limbs, schedule, seed, out, workspace, status)
+
+
+def gemm_q8_multi(ws, x: torch.Tensor, limbs: int = 3, outs=None, status=None):
+    """Several Q8 projections of the same x [t][k] (t <= 4) in one launch:
+    returns [gemm_q8(w, x) for w in ws] (list of int64 [t][w.n])."""
+    s = _stream()
+    t, k = x.shape
+    count = len(ws)
+    if any(w.k != k for w in ws):
+        raise EIError("int_gemm_q8_multi: every matrix must have x's k")
+    px = _dev(x, torch.int64, "x")
+    ys = outs if outs is not None else [torch.empty((t, w.n), dtype=torch.int64, device=x.device) for w in ws]
+    if len(ys) != count or any(tuple(y.shape) != (t, w.n) for y, w in zip(ys, ws)):
+        raise EIError("int_gemm_q8_multi: outs must be [t][n] per matrix")
+    descs = (Weights * max(count, 1))(*[w.desc for w in ws])
+    dptrs = (ctypes.POINTER(Weights) * max(count, 1))(*[ctypes.pointer(descs[m]) for m in range(count)])
+    yptrs = (ctypes.c_void_p * max(count, 1))(*[_dev(y, torch.int64, "y") for y in ys])
+    check = status is None
+    if check:
+        status = torch.zeros(1, dtype=torch.int32, device=x.device)
+    _check(lib().int_gemm_q8_multi(ctypes.cast(dptrs, ctypes.c_void_p), count, px, ctypes.cast(yptrs, ctypes.c_void_p),
+                                   t, limbs, status.data_ptr(), s), "int_gemm_q8_multi")
+    if check:
+        _raise_status(status, "int_gemm_q8_multi")
+    return ys
 
 
 def gemm_q4(w: PackedWeights, x: torch.Tensor, limbs: int = 3, schedule: str = "default", seed: int = 0xE1,

@@ -686,6 +686,41 @@ int int_gemm_q8(const ei_weights* w, const int64_t* x, int64_t* y, int64_t t, in
                   static_cast<hipStream_t>(stream), OUT_ROUND_Q24);
 }
 
+int int_gemm_q8_multi(const ei_weights* const* w, int count, const int64_t* x, int64_t* const* y, int64_t t,
+                      int limbs, int32_t* d_status, ei_stream stream) {
+  if (!w || !y || !x || count < 1 || count > kMultiMax) return EI_EINVAL;
+  if (t < 1 || t > kSmallT || limbs < 1 || limbs > 8) return EI_EINVAL;
+  if (limbs > kMaxLimbs) return EI_ERANGE;
+  GemvMulti mm;
+  std::memset(&mm, 0, sizeof mm);
+  mm.count = count;
+  for (int m = 0; m < count; ++m) {
+    const int c = check_weights(w[m], EI_FORMAT_Q8);
+    if (c != EI_OK) return c;
+    if (w[m]->k != w[0]->k || !y[m]) return EI_EINVAL;
+    const uint8_t* base = static_cast<const uint8_t*>(w[m]->packed);
+    mm.codes[m] = reinterpret_cast<const int8_t*>(base + kHeaderBytes);
+    mm.scales[m] = reinterpret_cast<const int32_t*>(base + kHeaderBytes + w[m]->n_pad * w[m]->k);
+    mm.y[m] = y[m];
+    mm.n[m] = w[m]->n;
+    mm.n_pad[m] = w[m]->n_pad;
+    mm.rg0[m + 1] = mm.rg0[m] + w[m]->n_pad / kTile;
+  }
+  if (mm.rg0[count] > 0x7FFFFFFF) return EI_ERANGE;   // one grid dimension
+  GemmArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.x = x;
+  a.status = d_status;
+  a.k = w[0]->k;
+  a.t = t;
+  a.nb = w[0]->nb;
+  a.b0 = 0;
+  a.b1 = w[0]->nb;
+  a.out_mode = OUT_ROUND_Q24;
+  a.order = ORDER_ASC;
+  return launch_gemv_multi(a, mm, limbs, static_cast<hipStream_t>(stream)) == hipSuccess ? EI_OK : EI_EDEVICE;
+}
+
 int int_gemm_q4(const ei_weights* w, const int32_t* x, int64_t* y, int64_t t, int limbs, int schedule,
                 uint64_t shuffle_seed, void* workspace, size_t workspace_bytes, int32_t* d_status, ei_stream stream) {
   const int c = check_weights(w, EI_FORMAT_Q4);

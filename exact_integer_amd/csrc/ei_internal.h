@@ -98,6 +98,18 @@ struct GemmArgs {
   int8_t* limb_out;          // fused gate/up: h as limb tiles [3][t_pad/32][n/32][1 KB]
 };
 
+// Matrices of one batched GEMV launch (same k, same activations): matrix m
+// owns the launch's row groups rg0[m] .. rg0[m + 1] - 1.
+constexpr int kMultiMax = 16;
+struct GemvMulti {
+  const int8_t* codes[kMultiMax];
+  const int32_t* scales[kMultiMax];
+  int64_t* y[kMultiMax];
+  int64_t n[kMultiMax], n_pad[kMultiMax];
+  int64_t rg0[kMultiMax + 1];
+  int count;
+};
+
 // pos-th block visited by a kernel in the block range [b0, b1) of `a`.
 __device__ inline int64_t block_at(const GemmArgs& a, int64_t pos) {
   if (a.order == ORDER_DESC) return a.b1 - 1 - pos;
@@ -115,6 +127,8 @@ hipError_t launch_limb_split_flat(const int64_t* x, int8_t* d, int64_t n, int li
 hipError_t launch_limb_tiles(const void* x, int x_is_i32, int64_t t, int64_t k, int limbs,
                              int8_t* tiles, int64_t t_pad, int32_t* status, hipStream_t s);
 hipError_t launch_gemv(const GemmArgs& a, int limbs, hipStream_t s);
+// a carries k, t, x, the block range and status; mm the matrices and outputs
+hipError_t launch_gemv_multi(const GemmArgs& a, const GemvMulti& mm, int limbs, hipStream_t s);
 hipError_t launch_gemm_mfma(const GemmArgs& a, int limbs, hipStream_t s);
 // narrow: the scales allow two int64 accumulators per output (narrow_scales);
 // otherwise one per limb

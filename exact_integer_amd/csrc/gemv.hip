@@ -66,15 +66,14 @@ __device__ inline bool stage_limbs(const GemmArgs& a, int64_t p0, int64_t c0, in
   return ok;
 }
 
-// kGeneric: any block order (descending, permuted) and the per-block-term
-// output of the tree schedule; otherwise ascending blocks only.
+// The projection of row group rg of the matrix in `a` by one workgroup of W
+// waves.  kGeneric: any block order (descending, permuted) and the
+// per-block-term output of the tree schedule; otherwise ascending blocks only.
 template <int L, int T, typename XT, int W, int D, bool kGeneric>
-__global__ __launch_bounds__(W * 64) void gemv_kernel(GemmArgs a) {
+__device__ inline void gemv_rows(const GemmArgs& a, int64_t rg, uint8_t* lds) {
   constexpr int kSlot = L * T * 32;                  // LDS bytes of one block's limbs
-  extern __shared__ __align__(16) uint8_t lds[];
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t rg = a.tperm ? a.tperm[blockIdx.x] : blockIdx.x;
   const int64_t nblk = a.b1 - a.b0;
   const int64_t p0 = wave * nblk / W, cnt = (wave + 1) * nblk / W - p0;   // this wave's block positions
   const int chunk = a.chunk;   // a multiple of 2D
@@ -228,6 +227,29 @@ __global__ __launch_bounds__(W * 64) void gemv_kernel(GemmArgs a) {
   }
 }
 
+template <int L, int T, typename XT, int W, int D, bool kGeneric>
+__global__ __launch_bounds__(W * 64) void gemv_kernel(GemmArgs a) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  gemv_rows<L, T, XT, W, D, kGeneric>(a, a.tperm ? a.tperm[blockIdx.x] : blockIdx.x, lds);
+}
+
+// Several matrices of the same k against the same activations in one launch:
+// workgroup g takes row group g - rg0[m] of matrix m, rg0[m] <= g < rg0[m + 1].
+template <int L, int T, int W, int D>
+__global__ __launch_bounds__(W * 64) void gemv_multi_kernel(GemmArgs a, GemvMulti mm) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int64_t g = blockIdx.x;
+  int m = 0;
+  while (m + 1 < mm.count && g >= mm.rg0[m + 1]) ++m;
+  GemmArgs b = a;
+  b.codes = mm.codes[m];
+  b.scales = mm.scales[m];
+  b.y = mm.y[m];
+  b.n = mm.n[m];
+  b.n_pad = mm.n_pad[m];
+  gemv_rows<L, T, int64_t, W, D, false>(b, g - mm.rg0[m], lds);
+}
+
 // ================================================================ launchers
 // Launch shape: W waves per row group, D blocks in flight per wave.
 template <int L, int T, int W, int D>
@@ -263,6 +285,44 @@ static hipError_t gemv_launch(GemmArgs a, hipStream_t s) {
 
 constexpr int kGemvWaves = 8;
 constexpr int kGemvDepth = 2;
+
+template <int L, int T, int W, int D>
+static hipError_t gemv_multi_launch(GemmArgs a, const GemvMulti& mm, hipStream_t s) {
+  constexpr int kSlot = L * T * 32;
+  const int64_t nblk = a.b1 - a.b0;
+  const int64_t per_wave = ((nblk + W - 1) / W + 2 * D - 1) / (2 * D) * (2 * D);
+  int64_t chunk = kGemvLdsPerWave / kSlot / (2 * D) * (2 * D);
+  constexpr int kMaxScaleChunk = kGemvScaleLoads * 1024 / 128 / (2 * D) * (2 * D);
+  if (chunk > kMaxScaleChunk) chunk = kMaxScaleChunk;
+  if (chunk < 2 * D) chunk = 2 * D;
+  if (chunk > per_wave) chunk = per_wave;
+  a.chunk = (int)chunk;
+  const size_t red = (size_t)W * 32 * T * L * 8;
+  size_t lds = (size_t)W * chunk * (kSlot + 128);
+  if (lds < red) lds = red;
+  hipLaunchKernelGGL((gemv_multi_kernel<L, T, W, D>), dim3((unsigned)mm.rg0[mm.count]), dim3(W * 64), lds, s, a,
+                     mm);
+  return hipGetLastError();
+}
+
+template <int L>
+static hipError_t gemv_multi_l(const GemmArgs& a, const GemvMulti& mm, hipStream_t s) {
+  switch (a.t) {
+    case 1: return gemv_multi_launch<L, 1, kGemvWaves, kGemvDepth>(a, mm, s);
+    case 2: return gemv_multi_launch<L, 2, kGemvWaves, kGemvDepth>(a, mm, s);
+    case 3: return gemv_multi_launch<L, 3, kGemvWaves, kGemvDepth>(a, mm, s);
+    default: return gemv_multi_launch<L, 4, kGemvWaves, kGemvDepth>(a, mm, s);
+  }
+}
+
+hipError_t launch_gemv_multi(const GemmArgs& a, const GemvMulti& mm, int limbs, hipStream_t s) {
+  switch (limbs) {
+    case 1: return gemv_multi_l<1>(a, mm, s);
+    case 2: return gemv_multi_l<2>(a, mm, s);
+    case 3: return gemv_multi_l<3>(a, mm, s);
+    default: return gemv_multi_l<4>(a, mm, s);
+  }
+}
 
 template <int L>
 static hipError_t gemv_l(const GemmArgs& a, hipStream_t s) {

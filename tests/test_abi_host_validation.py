@@ -63,6 +63,28 @@ def test_projection_arguments(ei):
     assert L.int_gemm_q4(ctypes.byref(d), FAKE, FAKE, 4, 3, 0, 0, None, 0, None, None) == EI_EINVAL
 
 
+def test_batched_gemv_arguments(ei):
+    L = ei.lib()
+    WP = ctypes.POINTER(ei.Weights)
+    a, b, c = _desc(ei, 64, 128), _desc(ei, 96, 128), _desc(ei, 64, 96)
+    ws = (WP * 17)(*[ctypes.pointer(a)] * 17)
+    ys = (ctypes.c_void_p * 17)(*[0x1000] * 17)
+    assert L.int_gemm_q8_multi(ws, 0, FAKE, ys, 1, 3, None, None) == EI_EINVAL      # no matrices
+    assert L.int_gemm_q8_multi(ws, 17, FAKE, ys, 1, 3, None, None) == EI_EINVAL     # more than 16
+    assert L.int_gemm_q8_multi(ws, 2, FAKE, ys, 5, 3, None, None) == EI_EINVAL      # t > 4: not a decode size
+    assert L.int_gemm_q8_multi(ws, 2, FAKE, ys, 0, 3, None, None) == EI_EINVAL
+    assert L.int_gemm_q8_multi(ws, 2, None, ys, 1, 3, None, None) == EI_EINVAL
+    assert L.int_gemm_q8_multi(ws, 2, FAKE, None, 1, 3, None, None) == EI_EINVAL
+    assert L.int_gemm_q8_multi(ws, 2, FAKE, ys, 1, 5, None, None) == EI_ERANGE
+    mixed = (WP * 2)(ctypes.pointer(b), ctypes.pointer(c))                          # k 128 and 96
+    assert L.int_gemm_q8_multi(mixed, 2, FAKE, ys, 1, 3, None, None) == EI_EINVAL
+    holes = (ctypes.c_void_p * 2)(0x1000, None)                                      # a null output
+    assert L.int_gemm_q8_multi(ws, 2, FAKE, holes, 1, 3, None, None) == EI_EINVAL
+    q4 = _desc(ei, 64, 128, fmt=2)
+    fmt = (WP * 2)(ctypes.pointer(a), ctypes.pointer(q4))
+    assert L.int_gemm_q8_multi(fmt, 2, FAKE, ys, 1, 3, None, None) == EI_EINVAL
+
+
 def test_routed_and_ffn_arguments(ei):
     L = ei.lib()
     w = _desc(ei, 64, 128, experts=8)

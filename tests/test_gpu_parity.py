@@ -361,6 +361,41 @@ def test_moe_ffn_q8_small(ei, lut, shape):
     assert (y == ref).all()
 
 
+@pytest.mark.parametrize("t", [1, 2, 3, 4])
+def test_q8_multi_qkv_and_ragged(ei, t):
+    # one batched GEMV launch over Q, K, V of the Qwen layer-0 shapes plus
+    # ragged row counts; every output equal to the oracle's and to the
+    # separate projections
+    r = np.random.default_rng(40 + t)
+    K = 896
+    ns = [896, 128, 128, 1000, 33, 32]
+    mats = [(synth.q8_codes(r, n, K), synth.q8_scales(r, n, K)) for n in ns]
+    mats[4] = (r.choice(np.array([-128, 127], np.int8), size=(33, K)),
+               r.choice(np.array([-(2**31), 2**31 - 1], np.int64), size=(33, K // 32)).astype(np.int32))
+    x = synth.q16_acts(r, t, K)
+    x[0, :5] = [8355711, -8421504, 8355711, -8421504, 0]
+    ws = [ei.pack_q8(dev(q), dev(s)) for q, s in mats]
+    xd = dev(x)
+    say("q8 multi", t)
+    ys = [host(y) for y in ei.gemm_q8_multi(ws, xd)]
+    for (q, s), w, y in zip(mats, ws, ys):
+        assert (y == oracle.q8(q, s, x)).all()
+        assert (y == host(ei.gemm_q8(w, xd))).all()
+
+
+def test_q8_multi_sixteen_matrices(ei):
+    # the largest batch, each matrix a different row count
+    r = np.random.default_rng(77)
+    K = 256
+    mats = [(synth.q8_codes(r, 32 * (m + 1) - m, K), synth.q8_scales(r, 32 * (m + 1) - m, K)) for m in range(16)]
+    x = synth.q16_acts(r, 1, K)
+    ws = [ei.pack_q8(dev(q), dev(s)) for q, s in mats]
+    say("q8 multi 16")
+    ys = [host(y) for y in ei.gemm_q8_multi(ws, dev(x))]
+    for (q, s), y in zip(mats, ys):
+        assert (y == oracle.q8(q, s, x)).all()
+
+
 def test_dense_t1(ei):
     q, s = synth.dense_w()
     w = ei.pack_q8(dev(q), dev(s))
