@@ -562,8 +562,15 @@ int ffn_run(const ei_weights* wg, const ei_weights* wu, const ei_weights* wd, co
   int64_t* h = reinterpret_cast<int64_t*>(ws + f.h_off);
   int64_t* g = reinterpret_cast<int64_t*>(ws + f.g_off);
   int64_t* u = reinterpret_cast<int64_t*>(ws + f.u_off);
-  int r = run_gemm(wg, xin, 0, g, t, 3, EI_SCHED_DEFAULT, 0, gws, gws_bytes, d_status, s, OUT_ROUND_Q24);
-  if (r == EI_OK) r = run_gemm(wu, xin, 0, u, t, 3, EI_SCHED_DEFAULT, 0, gws, gws_bytes, d_status, s, OUT_ROUND_Q24);
+  int r = EI_OK;
+  if (t <= kSmallT) {   // decode sizes: gate and up share x, one batched GEMV launch
+    const ei_weights* pair[2] = {wg, wu};
+    int64_t* outs[2] = {g, u};
+    r = int_gemm_q8_multi(pair, 2, xin, outs, t, 3, d_status, s);
+  } else {
+    r = run_gemm(wg, xin, 0, g, t, 3, EI_SCHED_DEFAULT, 0, gws, gws_bytes, d_status, s, OUT_ROUND_Q24);
+    if (r == EI_OK) r = run_gemm(wu, xin, 0, u, t, 3, EI_SCHED_DEFAULT, 0, gws, gws_bytes, d_status, s, OUT_ROUND_Q24);
+  }
   if (r != EI_OK) return r;
   if (launch_silu_mul(g, u, lut, h, t * wg->n, d_status, s) != hipSuccess) return EI_EDEVICE;
   return run_gemm(wd, h, 0, y, t, 3, EI_SCHED_DEFAULT, 0, gws, gws_bytes, d_status, s, OUT_ROUND_Q24, x);
