@@ -184,6 +184,23 @@ def test_q8_limb_range_is_flagged(ei):
         ei.gemm_q8(w, dev(x), 4)   # four limbs hold it
 
 
+def test_q8_multi_limb_range_is_flagged(ei):
+    # the batched GEMV splits x into limbs once per row group of every
+    # matrix: an activation past the 3-limb range is flagged there too
+    r = np.random.default_rng(8)
+    mats = [(synth.q8_codes(r, n, 64), synth.q8_scales(r, n, 64)) for n in (32, 40)]
+    ws = [ei.pack_q8(dev(q), dev(s)) for q, s in mats]
+    for T in (1, 4):
+        x = np.zeros((T, 64), np.int64)
+        x[T - 1, 63] = -8421505      # one past the 3-limb range, below
+        say("multi range flag", T)
+        with pytest.raises(ei.EIError):
+            ei.gemm_q8_multi(ws, dev(x), 3)
+        ys = [host(y) for y in ei.gemm_q8_multi(ws, dev(x), 4)]
+        for (q, s), y in zip(mats, ys):
+            assert (y == oracle.q8(q, s, x)).all()
+
+
 @pytest.mark.parametrize("shape", [(37, 96, 1), (100, 320, 4), (64, 288, 64), (33, 512, 7)])
 def test_q4_small_all_schedules(ei, shape):
     N, K, T = shape
