@@ -302,10 +302,13 @@ def test_ffn_q8_prenorm_matches_oracle(ei, lut, shape):
     assert (y == xn).all()
 
 
-@pytest.mark.parametrize("shape", [(96, 64, 3), (160, 96, 30), (64, 4096, 30), (4096, 64, 30), (96, 160, 70)])
+@pytest.mark.parametrize("shape", [(96, 64, 3), (160, 96, 30), (64, 4096, 30), (4096, 64, 30), (4096, 64, 50),
+                                   (2048, 96, 33), (96, 160, 70)])
 def test_ffn_q8_chain_matches_oracle(ei, lut, shape):
     # three layers in one call: the fused path hands limb tiles from each
-    # layer's combiner to the next; other token counts take the plain path
+    # layer's combiner to the next (K-split down projections: 4096 x 64 with
+    # one and two token tiles, 2048 x 96 with a one-token second tile); other
+    # token counts take the plain path
     F, D, T = shape
     r = np.random.default_rng(F * 7 + D + T)
     layers = [[(synth.q8_codes(r, F, D), synth.q8_scales(r, F, D)), (synth.q8_codes(r, F, D), synth.q8_scales(r, F, D)),
