@@ -165,7 +165,63 @@ __global__ __launch_bounds__(64 * W * G) void gemm_skinny_kernel(GemmArgs a) {
   const int64_t row = rg * kTile + (lane & 31);
   auto token = [&](int r) { return tg * kTile + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); };
 
-  if constexpr (L <= 3) {
+  if constexpr (G == 2 && NARROW) {
+    // Narrow scales: a wave's two chains sum exactly in int64, and so does any
+    // sum of them over waves (every partial total is a sum over a subset of
+    // blocks, below 2^62.01).  The gate and up waves put their totals in LDS
+    // side by side, one barrier, then each of the 8 waves finishes 2 of the
+    // 16 outputs of its lanes for both matrices: rounding, the SiLU-gated
+    // product, and the 32 x 32 tile of h in LDS (the staged limb area, free
+    // once every wave is past the barrier); one more barrier and one wave
+    // writes the tile as the down projection's limb tiles.
+    static_assert(W == 4, "8 waves, 2 outputs each");
+    __shared__ int64_t xs[2][W][16][64];
+    extern __shared__ __align__(16) uint8_t dyn[];
+    int64_t(*ht)[33] = reinterpret_cast<int64_t(*)[33]>(dyn);   // [token][row], padded rows
+#pragma unroll
+    for (int r = 0; r < 16; ++r) xs[m][wave][r][lane] = acc[0][r] + acc[NACC - 1][r];
+    __syncthreads();
+    bool good = true;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int r = 2 * wave_all + j;
+      int64_t g = 0, u = 0;
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        g += xs[0][w][r][lane];
+        u += xs[1][w][r][lane];
+      }
+      g = (g + ((int64_t)1 << 23)) >> 24;   // floor((acc + 2^23) / 2^24): no overflow below 2^62.01
+      u = (u + ((int64_t)1 << 23)) >> 24;
+      int64_t h = 0;
+      if (token(r) < a.t && row < a.n) good = silu_gate(g, u, a.lut, &h) && good;
+      ht[8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)][lane & 31] = h;
+    }
+    if (!good) flag(a.status, EI_DEV_OUT_RANGE);
+    __syncthreads();
+    if (wave_all == 0) {
+      // lane: token lane % 32, rows 16 (lane / 32) .. + 15 of the tile
+      const int64_t* src = &ht[lane & 31][16 * (lane >> 5)];
+      uint32_t words[3][4];
+      bool ok = true;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t v[4] = {src[4 * q], src[4 * q + 1], src[4 * q + 2], src[4 * q + 3]};
+        uint32_t w[3];
+        ok = limb_words<3>(v, w) && ok;
+#pragma unroll
+        for (int l = 0; l < 3; ++l) words[l][q] = w[l];
+      }
+      if (!ok) flag(a.status, EI_DEV_LIMB_RANGE);
+      const int64_t nb_out = a.n_pad / kTile;
+#pragma unroll
+      for (int l = 0; l < 3; ++l) {
+        const v4i v = {(int)words[l][0], (int)words[l][1], (int)words[l][2], (int)words[l][3]};
+        reinterpret_cast<v4i*>(a.limb_out)[((l * tgs + tg) * nb_out + rg) * 64 + lane] = v;
+      }
+    }
+    return;
+  } else if constexpr (L <= 3) {
     // Every wave turns its sums into the additive pair (h, r) of
     // acc = 2^24 h + r, the pairs meet in LDS, and wave w finishes the four
     // outputs 4w .. 4w + 3 of its lanes (all waves share the epilogue).
@@ -363,12 +419,15 @@ constexpr int kGateUpStage = 8;   // blocks per wave with the limb tiles staged 
 
 hipError_t launch_gemm_skinny_gateup(const GemmArgs& a, bool narrow, hipStream_t s) {
   const dim3 grid((unsigned)(a.n_pad / kTile), 1, (unsigned)(a.t_pad / kTile));
+  // narrow forms: dynamic LDS for the staged limb tiles, then the 32 x 33 int64 tile of h
+  const size_t h_tile = (size_t)kTile * 33 * 8;
+  const size_t staged = (size_t)a.nb * 3 * 1024;
   if (narrow && a.nb <= kSkinnyWaves * kGateUpStage)
     hipLaunchKernelGGL((gemm_skinny_kernel<3, kSkinnyWaves, kGateUpDepth, 2, true, kGateUpStage>), grid,
-                       dim3(64 * kSkinnyWaves * 2), (size_t)a.nb * 3 * 1024, s, a);
+                       dim3(64 * kSkinnyWaves * 2), staged > h_tile ? staged : h_tile, s, a);
   else if (narrow)
     hipLaunchKernelGGL((gemm_skinny_kernel<3, kSkinnyWaves, kGateUpDepth, 2, true>), grid, dim3(64 * kSkinnyWaves * 2),
-                       0, s, a);
+                       h_tile, s, a);
   else
     hipLaunchKernelGGL((gemm_skinny_kernel<3, kSkinnyWaves, kSkinnyDepth, 2, false>), grid, dim3(64 * kSkinnyWaves * 2),
                        0, s, a);
