@@ -181,21 +181,22 @@ def bench_q4_table(args, torch, np, ei, synth, dev) -> int:
             x = torch.from_numpy(synth.q4_d512_x(k, t)).to(dev)
             cases.append((f"{name}_t{t}", n, k, t, nd, sd, w, x, torch.empty((t, n), dtype=torch.int64, device=dev),
                           torch.empty((t, n), dtype=torch.int64, device=dev),
-                          torch.empty(max(ei.workspace_bytes(w, t), 1), dtype=torch.uint8, device=dev)))
+                          torch.empty(max(ei.workspace_bytes(w, t), 1), dtype=torch.uint8, device=dev),
+                          torch.empty(max(ei.q4_table_workspace_bytes(n, k, t), 1), dtype=torch.uint8, device=dev)))
     status = torch.zeros(1, dtype=torch.int32, device=dev)
 
     def step_table():
-        for _, n, k, t, nd, sd, w, x, yt, ym, ws in cases:
-            ei.gemm_q4_table(nd, sd, x, out=yt, status=status)
+        for _, n, k, t, nd, sd, w, x, yt, ym, ws, wt in cases:
+            ei.gemm_q4_table(nd, sd, x, out=yt, workspace=wt, status=status)
 
     def step_mfma():
-        for _, n, k, t, nd, sd, w, x, yt, ym, ws in cases:
+        for _, n, k, t, nd, sd, w, x, yt, ym, ws, wt in cases:
             ei.gemm_q4(w, x, out=ym, workspace=ws, status=status)
 
     ms_t, wall_t = _time_graph(torch, step_table, args.steps, args.warmup)
     ms_m, _ = _time_graph(torch, step_mfma, args.steps, args.warmup)
     ok = int(status.item()) == 0 and all(ei.digest(yt) == gold[name] and ei.digest(ym) == gold[name]
-                                         for name, n, k, t, nd, sd, w, x, yt, ym, ws in cases)
+                                         for name, n, k, t, nd, sd, w, x, yt, ym, ws, wt in cases)
     logical = sum(2.0 * t * n * k for _, n, k, t, *rest in cases)
     tops = logical / (ms_t * 1e-3) / 1e12
     alu_peak = 78.6   # int32 VALU lane-ops/s: 256 CUs x 4 SIMDs x 32 lanes x 2 issue x 2.4 GHz (fp32 157.3 TFLOP/s / 2)

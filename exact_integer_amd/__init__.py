@@ -64,7 +64,8 @@ SIGNATURES = {
     "output_digest": (I32, [P, SZ, P, P]),
     "ei_sha256_host": (None, [P, SZ, P]),
     "ei_topk_route": (I32, [P, I64, I64, I32, P, P]),
-    "int_gemm_q4_table": (I32, [P, P, P, P, I64, I64, I64, P, P]),
+    "int_gemm_q4_table": (I32, [P, P, P, P, I64, I64, I64, P, SZ, P, P]),
+    "ei_q4_table_workspace_bytes": (SZ, [I64, I64, I64]),
     "silu_lut_epilogue_radix16": (I32, [P, P, P, P, I64, P, P]),
     "ei_wide_packed_bytes": (SZ, [I64, I64]),
     "ei_wide_pack": (I32, [P, I64, I64, P, SZ, WP, P]),
@@ -254,7 +255,12 @@ def rmsnorm_q16(x: torch.Tensor, g: torch.Tensor, eps_q32: int, out=None, status
     return y
 
 
-def gemm_q4_table(nib: torch.Tensor, sme: torch.Tensor, x: torch.Tensor, out=None, status=None) -> torch.Tensor:
+def q4_table_workspace_bytes(n: int, k: int, t: int) -> int:
+    return int(lib().ei_q4_table_workspace_bytes(n, k, t))
+
+
+def gemm_q4_table(nib: torch.Tensor, sme: torch.Tensor, x: torch.Tensor, out=None, workspace=None,
+                  status=None) -> torch.Tensor:
     """The 4-bit projection by table reads, from the export format (int64 [t][n])."""
     s = _stream()
     n = nib.shape[0]
@@ -264,10 +270,14 @@ def gemm_q4_table(nib: torch.Tensor, sme: torch.Tensor, x: torch.Tensor, out=Non
     pn, ps, px = _dev(nib, torch.uint8, "nib"), _dev(sme, torch.uint8, "sme"), _dev(x, torch.int32, "x")
     y = out if out is not None else torch.empty((t, n), dtype=torch.int64, device=x.device)
     py = _dev(y, torch.int64, "y")
+    need = q4_table_workspace_bytes(n, k, t)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    pw, wb = (workspace.data_ptr(), workspace.numel() * workspace.element_size()) if workspace is not None else (None, 0)
     check = status is None
     if check:
         status = torch.zeros(1, dtype=torch.int32, device=x.device)
-    _check(lib().int_gemm_q4_table(pn, ps, px, py, n, k, t, status.data_ptr(), s), "int_gemm_q4_table")
+    _check(lib().int_gemm_q4_table(pn, ps, px, py, n, k, t, pw, wb, status.data_ptr(), s), "int_gemm_q4_table")
     if check:
         _raise_status(status, "int_gemm_q4_table")
     return y

@@ -20,6 +20,7 @@ constexpr int kSplitParts = 8;
 // 32-bit buffer offsets, and enough 128-row x 32-token workgroups to occupy the
 // chip (fewer go to the skinny kernel, which also splits K).
 constexpr int64_t kTiledMinT = 64, kTiledMinWorkgroups = 128;
+constexpr int64_t kMaxQ4TableK = kMaxK;   // the table-read projection: at most 1,024 chunks of 256 columns
 bool tiled_ok(const ei_weights* w, int64_t t, int limbs, int schedule) {
   if (limbs != 3 || t < kTiledMinT) return false;
   if (schedule != EI_SCHED_DEFAULT && schedule != EI_SCHED_CANONICAL) return false;
@@ -822,11 +823,19 @@ int ei_rmsnorm_q16(const int64_t* x, const int32_t* g, int64_t eps_q32, int64_t*
              : EI_EDEVICE;
 }
 
+size_t ei_q4_table_workspace_bytes(int64_t n, int64_t k, int64_t t) {
+  if (n < 1 || t < 1 || k < 32 || k % 32 != 0 || t > 65535 || k > kMaxQ4TableK) return 0;
+  return q4_table_workspace_bytes(n, k, t);
+}
+
 int int_gemm_q4_table(const uint8_t* nib, const uint8_t* sme, const int32_t* x, int64_t* y, int64_t n, int64_t k,
-                      int64_t t, int32_t* d_status, ei_stream stream) {
+                      int64_t t, void* workspace, size_t workspace_bytes, int32_t* d_status, ei_stream stream) {
   if (!nib || !sme || !x || !y || n < 1 || t < 1 || k < 32 || k % 32 != 0) return EI_EINVAL;
-  if (t > 65535) return EI_ERANGE;
-  return launch_q4_table(nib, sme, x, y, n, k, t, d_status, static_cast<hipStream_t>(stream)) == hipSuccess
+  if (t > 65535 || k > kMaxQ4TableK) return EI_ERANGE;
+  const size_t need = q4_table_workspace_bytes(n, k, t);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return EI_ENOSPACE;
+  if (need > 0 && !aligned(workspace, 16)) return EI_EINVAL;   // int128 sums
+  return launch_q4_table(nib, sme, x, y, n, k, t, workspace, d_status, static_cast<hipStream_t>(stream)) == hipSuccess
              ? EI_OK
              : EI_EDEVICE;
 }

@@ -167,8 +167,10 @@ hipError_t launch_wide_pack(const int32_t* codes, int64_t n, int64_t k, int64_t 
                             hipStream_t s);
 hipError_t launch_wide_gemm(const int8_t* wtiles, const int8_t* atiles, int64_t* y, int64_t n, int64_t t,
                             int64_t n_pad, int64_t t_pad, int64_t nb, int32_t* status, hipStream_t s);
+// workspace: q4_table_workspace_bytes(n, k, t) bytes (int128 chunk sums), or none for k <= 256
+size_t q4_table_workspace_bytes(int64_t n, int64_t k, int64_t t);
 hipError_t launch_q4_table(const uint8_t* nib, const uint8_t* sme, const int32_t* x, int64_t* y, int64_t n,
-                           int64_t k, int64_t t, int32_t* status, hipStream_t s);
+                           int64_t k, int64_t t, void* workspace, int32_t* status, hipStream_t s);
 hipError_t launch_silu_mul_radix16(const int64_t* g, const int64_t* u, const int32_t* lut, int64_t* h, int64_t n,
                                    int32_t* status, hipStream_t s);
 hipError_t launch_topk(const int64_t* scores, int64_t t, int64_t e, int k, int32_t* route, hipStream_t s);

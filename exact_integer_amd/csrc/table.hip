@@ -10,7 +10,9 @@
 // output rows (the pages' 4-row blocking reuses every table four times); per
 // group of 32 columns it sums the table reads and applies the group scale
 // m 2^e by shifts and adds (one add per set bit of the 4-bit mantissa, then a
-// shift by e).  Input is the export format itself: nibbles [n][k/2] (element
+// shift by e).  K is cut into 256-column chunks, one workgroup each, whose
+// exact int128 sums a second kernel adds (integer sums: any order gives the
+// same result).  Input is the export format itself: nibbles [n][k/2] (element
 // 2j in the low nibble of byte j, two's complement) and one scale byte per
 // group [n][k/32] (m in the low nibble, e in the high nibble).
 //
@@ -21,56 +23,58 @@
 
 namespace ei {
 
-constexpr int kTabCols = 256;     // columns per table chunk
-constexpr int kTabRows = 4;       // output rows per thread
-constexpr int kTabThreads = 256;
+constexpr int kTabCols = 256;     // columns per table chunk: one chunk per workgroup
+constexpr int kTabRows = 4;       // output rows per thread (each table entry read for four rows)
+constexpr int kTabThreads = 64;   // one wave: 256 rows per workgroup
 
+// Workgroup (row block, token, K chunk): the chunk's tables, then the exact
+// sums of its 4-row blocks.  With one chunk the result goes to y (checked to
+// fit int64); otherwise each chunk's int128 sums go to part[chunk][t][n] for
+// q4_table_combine_kernel.
 __global__ __launch_bounds__(kTabThreads) void q4_table_kernel(const uint8_t* __restrict__ nib,
                                                                const uint8_t* __restrict__ sme,
                                                                const int32_t* __restrict__ x, int64_t* __restrict__ y,
-                                                               int64_t n, int64_t k, int32_t* status) {
+                                                               __int128* __restrict__ part, int64_t n, int64_t k,
+                                                               int64_t t, int32_t* status) {
   __shared__ int64_t tab[kTabCols][16];   // tab[j][q + 8] = q * x_j
-  const int64_t tok = blockIdx.y;
+  const int64_t tok = blockIdx.y, chunk = blockIdx.z, c0 = chunk * kTabCols;
+  const int cols = (int)(k - c0 < kTabCols ? k - c0 : kTabCols);   // a multiple of 32
   const int64_t r0 = ((int64_t)blockIdx.x * kTabThreads + threadIdx.x) * kTabRows;
-  __int128 acc[kTabRows] = {};
-  for (int64_t c0 = 0; c0 < k; c0 += kTabCols) {
-    const int cols = (int)(k - c0 < kTabCols ? k - c0 : kTabCols);   // a multiple of 32
-    __syncthreads();   // the previous chunk's reads are done
-    for (int j = threadIdx.x; j < cols; j += kTabThreads) {
-      const int64_t xj = x[tok * k + c0 + j];
-      int64_t v = 0;
-      tab[j][8] = 0;
-      for (int q = 1; q <= 7; ++q) {
-        v += xj;
-        tab[j][8 + q] = v;
-      }
-      v = 0;
-      for (int q = 1; q <= 8; ++q) {
-        v -= xj;
-        tab[j][8 - q] = v;
-      }
+  for (int j = threadIdx.x; j < cols; j += kTabThreads) {
+    const int64_t xj = x[tok * k + c0 + j];
+    int64_t v = 0;
+    tab[j][8] = 0;
+    for (int q = 1; q <= 7; ++q) {
+      v += xj;
+      tab[j][8 + q] = v;
     }
-    __syncthreads();
-    for (int g = 0; g < cols / 32; ++g) {
+    v = 0;
+    for (int q = 1; q <= 8; ++q) {
+      v -= xj;
+      tab[j][8 - q] = v;
+    }
+  }
+  __syncthreads();
+  __int128 acc[kTabRows] = {};
+  for (int g = 0; g < cols / 32; ++g) {
 #pragma unroll
-      for (int rr = 0; rr < kTabRows; ++rr) {
-        const int64_t row = r0 + rr;
-        if (row >= n) continue;
-        const uint8_t* nb = nib + row * (k / 2) + (c0 + 32 * g) / 2;
-        int64_t gs = 0;
-        for (int jj = 0; jj < 16; ++jj) {   // byte jj: columns 2 jj (low nibble) and 2 jj + 1
-          const int b = nb[jj];
-          gs += tab[32 * g + 2 * jj][(b & 15) ^ 8];        // code c -> q = c - 16 [c >= 8]; index q + 8 = c ^ 8
-          gs += tab[32 * g + 2 * jj + 1][(b >> 4) ^ 8];
-        }
-        const int sc = sme[row * (k / 32) + (c0 / 32 + g)];
-        const int m = sc & 15, e = sc >> 4;
-        int64_t mg = 0;
-#pragma unroll
-        for (int bit = 0; bit < 4; ++bit)
-          if ((m >> bit) & 1) mg += gs << bit;
-        acc[rr] += (__int128)mg << e;
+    for (int rr = 0; rr < kTabRows; ++rr) {
+      const int64_t row = r0 + rr;
+      if (row >= n) continue;
+      const uint8_t* nb = nib + row * (k / 2) + (c0 + 32 * g) / 2;
+      int64_t gs = 0;
+      for (int jj = 0; jj < 16; ++jj) {   // byte jj: columns 2 jj (low nibble) and 2 jj + 1
+        const int b = nb[jj];
+        gs += tab[32 * g + 2 * jj][(b & 15) ^ 8];        // code c -> q = c - 16 [c >= 8]; index q + 8 = c ^ 8
+        gs += tab[32 * g + 2 * jj + 1][(b >> 4) ^ 8];
       }
+      const int sc = sme[row * (k / 32) + (c0 / 32 + g)];
+      const int m = sc & 15, e = sc >> 4;
+      int64_t mg = 0;
+#pragma unroll
+      for (int bit = 0; bit < 4; ++bit)
+        if ((m >> bit) & 1) mg += gs << bit;
+      acc[rr] += (__int128)mg << e;
     }
   }
   bool ok = true;
@@ -78,11 +82,32 @@ __global__ __launch_bounds__(kTabThreads) void q4_table_kernel(const uint8_t* __
   for (int rr = 0; rr < kTabRows; ++rr) {
     const int64_t row = r0 + rr;
     if (row >= n) continue;
-    int64_t out;
-    ok = fit_i64(acc[rr], &out) && ok;
-    y[tok * n + row] = out;
+    if (gridDim.z > 1) {
+      part[(chunk * t + tok) * n + row] = acc[rr];
+    } else {
+      int64_t out;
+      ok = fit_i64(acc[rr], &out) && ok;
+      y[tok * n + row] = out;
+    }
   }
   if (!ok) flag(status, EI_DEV_OUT_RANGE);
+}
+
+// y[e] = the sum of the chunks' int128 sums, checked to fit int64.
+__global__ void q4_table_combine_kernel(const __int128* __restrict__ part, int64_t chunks, int64_t* __restrict__ y,
+                                        int64_t tn, int32_t* status) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= tn) return;
+  __int128 v = 0;
+  for (int64_t c = 0; c < chunks; ++c) v += part[c * tn + e];
+  int64_t out;
+  if (!fit_i64(v, &out)) flag(status, EI_DEV_OUT_RANGE);
+  y[e] = out;
+}
+
+size_t q4_table_workspace_bytes(int64_t n, int64_t k, int64_t t) {
+  const int64_t chunks = (k + kTabCols - 1) / kTabCols;
+  return chunks > 1 ? (size_t)chunks * (size_t)t * (size_t)n * sizeof(__int128) : 0;
 }
 
 __global__ __launch_bounds__(256) void silu_mul_radix16_kernel(const int64_t* __restrict__ g,
@@ -112,10 +137,16 @@ __global__ __launch_bounds__(256) void silu_mul_radix16_kernel(const int64_t* __
 }
 
 hipError_t launch_q4_table(const uint8_t* nib, const uint8_t* sme, const int32_t* x, int64_t* y, int64_t n,
-                           int64_t k, int64_t t, int32_t* status, hipStream_t s) {
+                           int64_t k, int64_t t, void* workspace, int32_t* status, hipStream_t s) {
   const int64_t per = (int64_t)kTabThreads * kTabRows;
-  hipLaunchKernelGGL(q4_table_kernel, dim3((unsigned)((n + per - 1) / per), (unsigned)t), dim3(kTabThreads), 0, s,
-                     nib, sme, x, y, n, k, status);
+  const int64_t chunks = (k + kTabCols - 1) / kTabCols;
+  __int128* part = static_cast<__int128*>(workspace);
+  hipLaunchKernelGGL(q4_table_kernel, dim3((unsigned)((n + per - 1) / per), (unsigned)t, (unsigned)chunks),
+                     dim3(kTabThreads), 0, s, nib, sme, x, y, part, n, k, t, status);
+  if (chunks == 1) return hipGetLastError();
+  const int64_t tn = t * n;
+  hipLaunchKernelGGL(q4_table_combine_kernel, dim3((unsigned)((tn + 255) / 256)), dim3(256), 0, s, part, chunks, y,
+                     tn, status);
   return hipGetLastError();
 }
 

@@ -294,15 +294,23 @@ int silu_lut_epilogue(const int64_t* gate, const int64_t* up, const int32_t* lut
  * additions, one read per weight, four output rows per table, and the group
  * scale m 2^e applied by shifts and adds.  Reads the export format directly
  * and gives the same integers as int_gemm_q4 (a second implementation for
- * the two to be compared bit for bit; not the fast path).
+ * the two to be compared bit for bit; not the fast path).  K is cut into
+ * chunks of 256 columns, one workgroup each; their exact sums meet in the
+ * workspace.
  *   nib      device uint8 [n][k/2] (element 2j in the low nibble of byte j)
  *   sme      device uint8 [n][k/32] (m low nibble, e high nibble)
  *   x        device int32 [t][k];  y device int64 [t][n]
- * EI_EINVAL for null pointers, n < 1, t < 1, k % 32 != 0; EI_ERANGE for
- * t > 65535; a sum outside int64 sets EI_DEV_OUT_RANGE.
+ *   workspace device scratch of ei_q4_table_workspace_bytes(n, k, t) bytes,
+ *            16-byte aligned (none, and may be NULL, for k <= 256); owned by
+ *            the caller, not kept after the call's work completes on the stream
+ * EI_EINVAL for null pointers, n < 1, t < 1, k % 32 != 0, a misaligned
+ * workspace; EI_ERANGE for
+ * t > 65535 or k > 262,144; EI_ENOSPACE for a missing or short workspace; a
+ * sum outside int64 sets EI_DEV_OUT_RANGE.
  */
+size_t ei_q4_table_workspace_bytes(int64_t n, int64_t k, int64_t t);
 int int_gemm_q4_table(const uint8_t* nib, const uint8_t* sme, const int32_t* x, int64_t* y, int64_t n, int64_t k,
-                      int64_t t, int32_t* d_status, ei_stream stream);
+                      int64_t t, void* workspace, size_t workspace_bytes, int32_t* d_status, ei_stream stream);
 
 /*
  * silu_lut_epilogue with its runtime product lut[idx] * u formed as

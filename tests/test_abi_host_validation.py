@@ -118,8 +118,18 @@ def test_next_row_arguments(ei):
     wd = _desc(ei, 64, 32768 + 32, 3)
     assert L.int_gemm_wide(ctypes.byref(wd), FAKE, FAKE, 4, FAKE, 1 << 40, None, None) == EI_ERANGE
     assert L.int_gemm_wide(ctypes.byref(_desc(ei, 64, 64, 1)), FAKE, FAKE, 4, FAKE, 1 << 40, None, None) == EI_EINVAL
-    assert L.int_gemm_q4_table(FAKE, FAKE, FAKE, FAKE, 64, 96, 65536, None, None) == EI_ERANGE
-    assert L.int_gemm_q4_table(FAKE, FAKE, FAKE, FAKE, 64, 95, 4, None, None) == EI_EINVAL
+    assert L.int_gemm_q4_table(FAKE, FAKE, FAKE, FAKE, 64, 96, 65536, None, 0, None, None) == EI_ERANGE
+    assert L.int_gemm_q4_table(FAKE, FAKE, FAKE, FAKE, 64, 95, 4, None, 0, None, None) == EI_EINVAL
+    assert L.int_gemm_q4_table(FAKE, FAKE, FAKE, FAKE, 64, 262144 + 32, 4, FAKE, 1 << 40, None, None) == EI_ERANGE
+    # K in chunks of 256 columns: exact int128 sums per chunk, none for one chunk
+    assert L.ei_q4_table_workspace_bytes(64, 256, 4) == 0
+    assert L.ei_q4_table_workspace_bytes(64, 288, 4) == 2 * 4 * 64 * 16
+    assert L.ei_q4_table_workspace_bytes(1030, 2048, 7) == 8 * 7 * 1030 * 16
+    assert L.ei_q4_table_workspace_bytes(64, 95, 4) == 0
+    assert L.int_gemm_q4_table(FAKE, FAKE, FAKE, FAKE, 64, 288, 4, None, 0, None, None) == EI_ENOSPACE
+    assert L.int_gemm_q4_table(FAKE, FAKE, FAKE, FAKE, 64, 288, 4, FAKE, 2 * 4 * 64 * 16 - 1, None, None) == EI_ENOSPACE
+    odd = ctypes.c_void_p(0x1008)   # int128 sums need 16-byte alignment
+    assert L.int_gemm_q4_table(FAKE, FAKE, FAKE, FAKE, 64, 288, 4, odd, 1 << 20, None, None) == EI_EINVAL
     out = ei.Weights()
     assert L.ei_wide_pack(FAKE, 64, 95, FAKE, 1 << 30, ctypes.byref(out), None) == EI_EINVAL
     assert L.ei_wide_pack(FAKE, 64, 96, FAKE, 100, ctypes.byref(out), None) == EI_ENOSPACE

@@ -676,6 +676,24 @@ def test_q4_table_read_full_ranges(ei):
     assert (host(ei.gemm_q4_table(dev(nib), dev(sme), dev(x))) == oracle.q4(nib, sme, x)).all()
 
 
+def test_q4_table_read_overflow_is_flagged(ei):
+    # codes -8, m = 15, e = 15, x = -2^31: every group of 32 adds
+    # 15 * 2^15 * 32 * 2^34 = 15 * 2^54, so 64 groups (eight chunks of 256
+    # columns) reach 15 * 2^60 > 2^63; the int128 sums of the chunks meet in
+    # the combiner, which flags the result
+    N, K, T = 40, 2048, 2
+    nib = np.full((N, K // 2), 0x88, np.uint8)
+    sme = np.full((N, K // 32), 0xFF, np.uint8)
+    x = np.full((T, K), -(2**31), np.int32)
+    say("q4 table read overflow")
+    with pytest.raises(ei.EIError):
+        ei.gemm_q4_table(dev(nib), dev(sme), dev(x))
+    # 16 groups left (15 * 2^58): the sum fits again
+    x[:, K // 2:] = 0
+    x[:, : K // 4] = 0
+    assert (host(ei.gemm_q4_table(dev(nib), dev(sme), dev(x))) == oracle.q4(nib, sme, x)).all()
+
+
 def test_silu_mul_radix16_equals_silu_mul(ei, lut):
     r = np.random.default_rng(82)
     g = np.concatenate([r.integers(-(2**21), 2**21, 50000), r.integers(-(2**40), 2**40, 1000),
