@@ -110,6 +110,30 @@ struct GemvMulti {
   int count;
 };
 
+// Work item of a grouped (routed) launch over a grid of rbs x tiles_max
+// workgroups: the rbs * ntiles items in use go token tile by token tile
+// (w = tb * rbs + rb, row blocks fastest), so the workgroups that read one
+// token tile's activation limb tiles, and then the token tiles of one expert,
+// which read the same weight rows, run together.  Workgroup blk runs on XCD
+// blk % 8: each XCD takes a contiguous run of an eighth of the items in use,
+// so the unused tail of the grid is shared out evenly too.  False: no item.
+__device__ inline bool grouped_item(int64_t blk, int64_t grid, int64_t rbs, int64_t ntiles, int64_t* rb,
+                                    int64_t* tb) {
+  const int64_t active = rbs * ntiles;
+  int64_t w = blk;
+  if (grid % 8 == 0) {
+    const int64_t x = blk % 8, l = blk / 8;
+    const int64_t s0 = x * active / 8, s1 = (x + 1) * active / 8;
+    if (l >= s1 - s0) return false;
+    w = s0 + l;
+  } else if (blk >= active) {
+    return false;
+  }
+  *tb = w / rbs;
+  *rb = w % rbs;
+  return true;
+}
+
 // pos-th block visited by a kernel in the block range [b0, b1) of `a`.
 __device__ inline int64_t block_at(const GemmArgs& a, int64_t pos) {
   if (a.order == ORDER_DESC) return a.b1 - 1 - pos;

@@ -271,16 +271,23 @@ __global__ __launch_bounds__(256) void gemm_tiled_qreg_kernel(GemmArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // ---- tile of this workgroup: 128 rows x 32 tokens, XCD-contiguous order
+  // (dense: row blocks in runs, token tiles fastest; grouped: grouped_item)
   const int64_t tbs = kGrouped ? a.tiles_max : a.t_pad / kTile;
   const int64_t rbs = (a.n_pad + 127) / 128, ntiles = rbs * tbs;
-  int64_t g = blockIdx.x;
-  if (ntiles % 8 == 0) g = (g % 8) * (ntiles / 8) + g / 8;
-  const int64_t rb = g / tbs, tb = g % tbs;
+  int64_t rb, tb;
+  if (kGrouped) {
+    const int64_t used = *a.ntiles < a.tiles_max ? *a.ntiles : a.tiles_max;
+    if (!grouped_item(blockIdx.x, ntiles, rbs, used, &rb, &tb)) return;   // the whole workgroup: no tile
+  } else {
+    int64_t g = blockIdx.x;
+    if (ntiles % 8 == 0) g = (g % 8) * (ntiles / 8) + g / 8;
+    rb = g / tbs;
+    tb = g % tbs;
+  }
   const int64_t rgs = a.n_pad / kTile, tgs = kGrouped ? a.tiles_max : a.t_pad / kTile;
   const int8_t* codes = a.codes;
   const int32_t* scales = a.scales;
   if (kGrouped) {
-    if (tb >= *a.ntiles) return;   // the whole workgroup: no tile here
     const int64_t e = a.tile_expert[tb];
     codes += e * a.expert_stride;
     scales = reinterpret_cast<const int32_t*>(reinterpret_cast<const int8_t*>(scales) + e * a.expert_stride);
@@ -419,15 +426,13 @@ __global__ __launch_bounds__(kGuWaves * 64) __attribute__((amdgpu_waves_per_eu(4
   const int wr = wave & 3;              // row tile within the workgroup's 128 rows
   const bool is_up = wave >= 4;
   const int64_t tgs = a.tiles_max, rgs = a.n_pad / kTile;
-  // XCD-contiguous order (workgroup g runs on XCD g % 8): each XCD takes a
-  // contiguous run of (row block, token tile) pairs, token tiles fastest, so
-  // the token tiles of one expert, which read the same weight rows, share
-  // that XCD's L2 instead of fetching the rows once per XCD
-  const int64_t nwg = ((a.n_pad + 4 * kTile - 1) / (4 * kTile)) * tgs;
-  int64_t g = blockIdx.x;
-  if (nwg % 8 == 0) g = (g % 8) * (nwg / 8) + g / 8;
-  const int64_t rb = g / tgs, tb = g % tgs;
-  if (tb >= *a.ntiles) return;          // the whole workgroup: no tile here
+  // token tiles in turn, row blocks fastest, an eighth of the tiles in use
+  // per XCD (grouped_item): the row blocks of a token tile share its limb
+  // tiles, and the token tiles of one expert its weight rows, in one XCD's L2
+  const int64_t rbs = (a.n_pad + 4 * kTile - 1) / (4 * kTile);
+  int64_t rb, tb;
+  const int64_t used = *a.ntiles < tgs ? *a.ntiles : tgs;
+  if (!grouped_item(blockIdx.x, rbs * tgs, rbs, used, &rb, &tb)) return;   // the whole workgroup: no tile
   const int64_t ex = a.tile_expert[tb];
   const int8_t* codes[2] = {a.codes + ex * a.expert_stride, a.codes2 + ex * a.expert_stride};
   const int32_t* scales[2] = {
