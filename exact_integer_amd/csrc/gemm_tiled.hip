@@ -263,21 +263,32 @@ hipError_t launch_tiled_shape(const GemmArgs& a, hipStream_t s) {
 // input of the limb-0 product (every partial sum stays below 2^28 in
 // magnitude).  Then two int64 chains per output, S (P_0 + 2^8 P_1) and
 // (2^16 S) P_2, exact for narrow scales (narrow_scales).
-template <bool kExact, bool kGrouped>
+// XB (dense): each XCD takes a block of a quarter of the row blocks by half the
+// token tiles (token tiles fastest), so its share of the activation limb tiles
+// stays in its L2 while the code tiles stream; a code tile is fetched by two
+// XCDs.  Measured on the dense 14336 x 4096, T = 512 projection: 184.7 us mean
+// against 190.2 us for contiguous runs of row blocks with all their token tiles.
+template <bool kExact, bool kGrouped, bool XB = true>
 __global__ __launch_bounds__(256) void gemm_tiled_qreg_kernel(GemmArgs a) {
   constexpr int kBuf = 4 * 1024;   // per block: 3 limb tiles + 1 KB for the fourth wave's dummy copy
   extern __shared__ __align__(16) uint8_t lds[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // ---- tile of this workgroup: 128 rows x 32 tokens, XCD-contiguous order
-  // (dense: row blocks in runs, token tiles fastest; grouped: grouped_item)
+  // ---- tile of this workgroup: 128 rows x 32 tokens in an XCD-aware order
+  // (dense: XB blocks, else row blocks in runs, token tiles fastest; grouped:
+  // grouped_item)
   const int64_t tbs = kGrouped ? a.tiles_max : a.t_pad / kTile;
   const int64_t rbs = (a.n_pad + 127) / 128, ntiles = rbs * tbs;
   int64_t rb, tb;
   if (kGrouped) {
     const int64_t used = *a.ntiles < a.tiles_max ? *a.ntiles : a.tiles_max;
     if (!grouped_item(blockIdx.x, ntiles, rbs, used, &rb, &tb)) return;   // the whole workgroup: no tile
+  } else if (XB && rbs % 4 == 0 && tbs % 2 == 0) {
+    // XCD x: row blocks of quarter x / 2, token tiles of half x % 2, token tiles fastest
+    const int64_t x = blockIdx.x % 8, l = blockIdx.x / 8, th = tbs / 2;
+    rb = (x / 2) * (rbs / 4) + l / th;
+    tb = (x % 2) * th + l % th;
   } else {
     int64_t g = blockIdx.x;
     if (ntiles % 8 == 0) g = (g % 8) * (ntiles / 8) + g / 8;
