@@ -378,10 +378,14 @@ def bench_qwen_ffn(args, torch, np, ei, synth, dev, prenorm: bool = False) -> in
 
     final = bufs[(synth.QWEN_LAYERS - 1) % 2]
 
-    def step():   # layer l reads x_l and writes x_{l+1}; the first reads x0
-        if not prenorm:   # the whole stack in one call
+    def step():   # the whole stack in one call
+        if prenorm:
+            ei.ffn_q8_prenorm_chain(layers, norms, synth.QWEN_RMS_EPS_Q32, x0, lut, out=final, workspace=ws,
+                                    status=status)
+        else:
             ei.ffn_q8_chain(layers, x0, lut, out=final, workspace=ws, status=status)
-            return
+
+    def step_layers():   # the pre-norm stack as 24 layer calls: layer l reads x_l and writes x_{l+1}
         src = x0
         for i, (wg, wu, wd) in enumerate(layers):
             dst = bufs[i % 2]
@@ -389,10 +393,17 @@ def bench_qwen_ffn(args, torch, np, ei, synth, dev, prenorm: bool = False) -> in
                               status=status)
             src = dst
 
-    ms, wall_ms = _time_graph(torch, step, args.steps, args.warmup)
     gold = _json.load(open(os.path.join(ROOT, "tests", "golden", "oracle_digests.json")))[
         "qwen05b_ffn_prenorm" if prenorm else "qwen05b_ffn"]["layers"]
+    layer_calls_ms = None
+    if prenorm:
+        layer_calls_ms, _ = _time_graph(torch, step_layers, args.steps, args.warmup)
+        ok_layers = int(status.item()) == 0 and ei.digest(final) == gold[-1]["x_next"]
+        final.zero_()
+    ms, wall_ms = _time_graph(torch, step, args.steps, args.warmup)
     ok = int(status.item()) == 0 and ei.digest(final) == gold[-1]["x_next"]
+    if prenorm:
+        ok = ok and ok_layers
     wbytes = synth.QWEN_LAYERS * 3 * F * D * (1 + 4 / 32)
     gbs = wbytes / (ms * 1e-3) / 1e9
     print(json.dumps({
@@ -407,6 +418,7 @@ def bench_qwen_ffn(args, torch, np, ei, synth, dev, prenorm: bool = False) -> in
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "step_ms": round(ms, 4),
                      "weight_bytes": int(wbytes)},
+        **({"layer_calls_step_ms": round(layer_calls_ms, 4)} if prenorm else {}),
         "parity": {"final_digest_equals_oracle": ok}}))
     return 0 if ok else 1
 

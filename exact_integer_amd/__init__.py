@@ -76,6 +76,7 @@ SIGNATURES = {
     "ei_ffn_workspace_bytes": (SZ, [WP, WP, I64]),
     "int_ffn_q8": (I32, [WP, WP, WP, P, P, P, I64, P, SZ, P, P]),
     "int_ffn_q8_prenorm": (I32, [WP, WP, WP, P, I64, P, P, P, I64, P, SZ, P, P]),
+    "int_ffn_q8_prenorm_chain": (I32, [ctypes.POINTER(WP), I32, P, I64, P, P, P, I64, P, SZ, P, P]),
     "ei_ffn_chain_workspace_bytes": (SZ, [WP, WP, I64]),
     "int_ffn_q8_chain": (I32, [ctypes.POINTER(WP), I32, P, P, P, I64, P, SZ, P, P]),
     "ei_moe_ffn_workspace_bytes": (SZ, [WP, WP, I64, I32]),
@@ -426,6 +427,35 @@ def ffn_q8_prenorm(wg: PackedWeights, wu: PackedWeights, wd: PackedWeights, g_no
                                     status.data_ptr(), s), "int_ffn_q8_prenorm")
     if check:
         _raise_status(status, "int_ffn_q8_prenorm")
+    return y
+
+
+def ffn_q8_prenorm_chain(layers, g_norms, eps_q32: int, x: torch.Tensor, lut: torch.Tensor, out=None,
+                         workspace=None, status=None) -> torch.Tensor:
+    """A stack of pre-norm FFN layers: x_{l+1} = ffn_q8_prenorm(layer l, g_norms[l], x_l)."""
+    s = _stream()
+    t, d = x.shape
+    wg0, _, wd0 = layers[0]
+    if len(g_norms) != len(layers) or any(g.numel() != d for g in g_norms):
+        raise EIError("int_ffn_q8_prenorm_chain: one g_norm [d] per layer")
+    for wg, wu, wd in layers:
+        if d != wg.k or wu.k != wg.k or wu.n != wg.n or wd.k != wg.n or wd.n != wg.k or wg.n != wg0.n:
+            raise EIError("int_ffn_q8_prenorm_chain: every layer must be gate, up [f][d], down [d][f] of one shape")
+    descs = (WP * (3 * len(layers)))(*[ctypes.pointer(w.desc) for layer in layers for w in layer])
+    gptrs = (ctypes.c_void_p * len(g_norms))(*[_dev(g, torch.int32, "g_norm") for g in g_norms])
+    px, pl = _dev(x, torch.int64, "x"), _dev(lut, torch.int32, "lut")
+    y = out if out is not None else torch.empty_like(x)
+    py = _dev(y, torch.int64, "y")
+    if workspace is None:
+        workspace = torch.empty(max(ffn_chain_workspace_bytes(wg0, wd0, t), 1), dtype=torch.uint8, device=x.device)
+    check = status is None
+    if check:
+        status = torch.zeros(1, dtype=torch.int32, device=x.device)
+    _check(lib().int_ffn_q8_prenorm_chain(descs, len(layers), ctypes.cast(gptrs, ctypes.c_void_p), eps_q32, px, pl,
+                                          py, t, workspace.data_ptr(), workspace.numel(), status.data_ptr(), s),
+           "int_ffn_q8_prenorm_chain")
+    if check:
+        _raise_status(status, "int_ffn_q8_prenorm_chain")
     return y
 
 

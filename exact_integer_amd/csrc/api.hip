@@ -472,11 +472,12 @@ namespace {
 
 // y = x + FFN(x), or y = x + FFN(rmsnorm(x)) when gnorm is given.
 // in_limbs (fused path only): x's limb tiles are already there; out_limbs:
-// y's limb tiles for the next layer's gate/up pass are written there too.
+// y's limb tiles for the next layer's gate/up pass are written there too
+// (of rmsnorm(y, next_gnorm, eps_q32) when next_gnorm is given).
 int ffn_run(const ei_weights* wg, const ei_weights* wu, const ei_weights* wd, const int64_t* x,
             const int32_t* gnorm, int64_t eps_q32, const int32_t* lut, int64_t* y, int64_t t, void* workspace,
             size_t workspace_bytes, int32_t* d_status, hipStream_t s, const int8_t* in_limbs = nullptr,
-            int8_t* out_limbs = nullptr) {
+            int8_t* out_limbs = nullptr, const int32_t* next_gnorm = nullptr) {
   if (!x || !lut || !y || t < 1) return EI_EINVAL;
   const int c = ffn_check(wg, wu, wd);
   if (c != EI_OK) return c;
@@ -545,14 +546,20 @@ int ffn_run(const ei_weights* wg, const ei_weights* wu, const ei_weights* wd, co
       b.b1 = wd->nb;
       b.out_mode = OUT_PARTIAL;
       if (launch_gemm_skinny(b, 3, ld.splits, narrow_scales(wd->smax, wd->nb), s) != hipSuccess) return EI_EDEVICE;
-      return launch_combine_hr_tiles(part, ld.splits, y, t, wd->n, x, out_limbs, ld.t_pad, d_status, s) == hipSuccess
-                 ? EI_OK
-                 : EI_EDEVICE;
+      const hipError_t e =
+          next_gnorm ? launch_combine_rmsnorm_tiles(part, ld.splits, x, y, next_gnorm, eps_q32, out_limbs, t,
+                                                    ld.t_pad, wd->n, d_status, s)
+                     : launch_combine_hr_tiles(part, ld.splits, y, t, wd->n, x, out_limbs, ld.t_pad, d_status, s);
+      return e == hipSuccess ? EI_OK : EI_EDEVICE;
     }
     const int r = run_gemm(wd, nullptr, 0, y, t, 3, EI_SCHED_DEFAULT, 0, gws, gws_bytes, d_status, s, OUT_ROUND_Q24,
                            x, h_limbs);
     if (r != EI_OK || !out_limbs) return r;
-    return launch_limb_tiles(y, 0, t, wd->n, 3, out_limbs, ld.t_pad, d_status, s) == hipSuccess ? EI_OK : EI_EDEVICE;
+    const hipError_t e = next_gnorm
+                             ? launch_rmsnorm_limb_tiles(y, next_gnorm, eps_q32, out_limbs, t, ld.t_pad, wd->n,
+                                                         d_status, s)
+                             : launch_limb_tiles(y, 0, t, wd->n, 3, out_limbs, ld.t_pad, d_status, s);
+    return e == hipSuccess ? EI_OK : EI_EDEVICE;
   }
   const int64_t* xin = x;
   if (gnorm) {
@@ -633,6 +640,44 @@ int int_ffn_q8_prenorm(const ei_weights* wg, const ei_weights* wu, const ei_weig
   if (!g_norm) return EI_EINVAL;
   return ffn_run(wg, wu, wd, x, g_norm, eps_q32, lut, y, t, workspace, workspace_bytes, d_status,
                  static_cast<hipStream_t>(stream));
+}
+
+int int_ffn_q8_prenorm_chain(const ei_weights* const* layers, int n_layers, const int32_t* const* g_norms,
+                             int64_t eps_q32, const int64_t* x, const int32_t* lut, int64_t* y, int64_t t,
+                             void* workspace, size_t workspace_bytes, int32_t* d_status, ei_stream stream) {
+  if (!layers || n_layers < 1 || !g_norms || !x || !lut || !y || t < 1) return EI_EINVAL;
+  for (int l = 0; l < n_layers; ++l) {
+    const ei_weights *wg = layers[3 * l], *wu = layers[3 * l + 1], *wd = layers[3 * l + 2];
+    const int c = ffn_check(wg, wu, wd);
+    if (c != EI_OK) return c;
+    if (wg->n != layers[0]->n || wg->k != layers[0]->k) return EI_EINVAL;   // one shape for the whole chain
+    if (!g_norms[l]) return EI_EINVAL;
+  }
+  const ei_weights *g0 = layers[0], *d0 = layers[2];
+  if (g0->k > 65536 || eps_q32 < 1 || eps_q32 > ((int64_t)1 << 32)) return EI_ERANGE;
+  const FfnLayout f = ffn_layout(g0, d0, t);
+  if (!workspace || workspace_bytes < ei_ffn_chain_workspace_bytes(g0, d0, t)) return EI_ENOSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  int64_t* xbuf = reinterpret_cast<int64_t*>(ws + f.total);
+  int8_t* limbs = reinterpret_cast<int8_t*>(ws + f.total + align_up(sizeof(int64_t) * (size_t)t * (size_t)g0->k));
+  const int64_t t_pad = round_up(t, kTile);
+  // as int_ffn_q8_chain; on the fused path the first layer's normalized input
+  // goes into `limbs` here and every later layer's as its predecessor's
+  // residual stream is formed
+  if (f.fused && launch_rmsnorm_limb_tiles(x, g_norms[0], eps_q32, limbs, t, t_pad, g0->k, d_status, s) != hipSuccess)
+    return EI_EDEVICE;
+  const int64_t* in = x;
+  for (int l = 0; l < n_layers; ++l) {
+    int64_t* out = ((n_layers - 1 - l) % 2 == 0) ? y : xbuf;
+    const bool last = l == n_layers - 1;
+    const int r = ffn_run(layers[3 * l], layers[3 * l + 1], layers[3 * l + 2], in, g_norms[l], eps_q32, lut, out, t,
+                          workspace, f.total, d_status, s, f.fused ? limbs : nullptr,
+                          f.fused && !last ? limbs : nullptr, f.fused && !last ? g_norms[l + 1] : nullptr);
+    if (r != EI_OK) return r;
+    in = out;
+  }
+  return EI_OK;
 }
 
 size_t ei_moe_ffn_workspace_bytes(const ei_weights* wg, const ei_weights* wd, int64_t rows, int topk) {

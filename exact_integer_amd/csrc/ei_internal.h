@@ -202,6 +202,10 @@ hipError_t launch_rmsnorm_q16(const int64_t* x, const int32_t* g, int64_t eps, i
                               int32_t* status, hipStream_t s);
 hipError_t launch_rmsnorm_limb_tiles(const int64_t* x, const int32_t* g, int64_t eps, int8_t* tiles, int64_t t,
                                      int64_t t_pad, int64_t d, int32_t* status, hipStream_t s);   // d % 32 == 0
+// y = resid + combined (h, r) partials [nparts][2][t][d]; tiles = limb tiles of rmsnorm(y, g, eps); d % 32 == 0
+hipError_t launch_combine_rmsnorm_tiles(const int64_t* part, int nparts, const int64_t* resid, int64_t* y,
+                                        const int32_t* g, int64_t eps, int8_t* tiles, int64_t t, int64_t t_pad,
+                                        int64_t d, int32_t* status, hipStream_t s);
 hipError_t launch_requant(const int64_t* c, int64_t m, int k, int64_t* y, int64_t n, int32_t* status,
                           hipStream_t s);
 hipError_t launch_shadow(const int8_t* q, const int32_t* s, const int64_t* x, float* y, int64_t n, int64_t k,

@@ -123,6 +123,90 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_q16_kernel(const int64_t
   }
 }
 
+// The residual stream between two pre-norm layers, in one pass per token:
+// y = resid + (the down projection's split-K (h, r) partials, rounded), then
+// y's RMSNorm with the next layer's weight g, written as that layer's 3-limb
+// activation tiles (layout and padding rows as rmsnorm_q16_kernel<true>).
+// Each thread owns groups of four consecutive columns 4i .. 4i+3 in both
+// passes, so the second pass re-reads only its own stores of y.
+__global__ __launch_bounds__(kNormThreads) void combine_rmsnorm_tiles_kernel(
+    const int64_t* __restrict__ part, int nparts, const int64_t* __restrict__ resid, int64_t* __restrict__ y,
+    const int32_t* __restrict__ g, int64_t eps, int8_t* __restrict__ tiles, int64_t t, int64_t t_pad, int64_t d,
+    int32_t* status) {
+  __shared__ uint64_t wsum[kNormThreads / 64];
+  __shared__ uint64_t inv_s;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t tok = blockIdx.x, nb = d / 32, tg = tok / kTile, tgs = t_pad / kTile;
+  const int tl = (int)(tok % kTile);
+  if (tok >= t) {   // padding token of the last tile: zero limbs
+    const v4i z = {0, 0, 0, 0};
+    for (int64_t c = tid; c < 2 * nb; c += kNormThreads)
+#pragma unroll
+      for (int l = 0; l < 3; ++l)
+        reinterpret_cast<v4i*>(tiles)[((l * tgs + tg) * nb + c / 2) * 64 + tl + 32 * (c & 1)] = z;
+    return;
+  }
+  const int64_t tn = t * d;
+  int64_t* yrow = y + tok * d;
+  const int64_t* rrow = resid + tok * d;
+  uint64_t ss = 0;
+  bool fit = true, in_range = true;
+  for (int64_t i = tid; i < d / 4; i += kNormThreads) {
+    int64_t h[4] = {0, 0, 0, 0}, r[4] = {0, 0, 0, 0};
+    for (int p = 0; p < nparts; ++p) {
+      const int64_t* ph = part + (int64_t)(2 * p) * tn + tok * d + 4 * i;
+      const int64_t* pr = part + (int64_t)(2 * p + 1) * tn + tok * d + 4 * i;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        h[j] += ph[j];
+        r[j] += pr[j];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int64_t out;
+      fit = finish_hr(h[j], r[j], OUT_ROUND_Q24, &out) && fit;
+      fit = fit_i64((__int128)rrow[4 * i + j] + out, &out) && fit;
+      yrow[4 * i + j] = out;
+      const bool in = out >= -((int64_t)1 << 23) && out <= ((int64_t)1 << 23);
+      in_range = in_range && in;
+      ss += in ? (uint64_t)(out * out) : 0;
+    }
+  }
+  if (!fit) flag(status, EI_DEV_OUT_RANGE);
+  if (!in_range) flag(status, EI_DEV_LIMB_RANGE);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)ss, o, 64), hi = __shfl_xor((uint32_t)(ss >> 32), o, 64);
+    ss += ((uint64_t)hi << 32) | lo;
+  }
+  if (lane == 0) wsum[wave] = ss;
+  __syncthreads();
+  if (tid == 0) {
+    uint64_t tot = 0;
+    for (int w = 0; w < kNormThreads / 64; ++w) tot += wsum[w];
+    inv_s = rms_inverse(tot, d, eps);
+  }
+  __syncthreads();
+  const uint64_t inv = inv_s;
+  bool range_ok = true, sfit = true;
+  for (int64_t i = tid; i < d / 4; i += kNormThreads) {
+    int64_t v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)   // this thread's own stores of y
+      sfit = shift_half_away((__int128)(yrow[4 * i + j] * (int64_t)g[4 * i + j]) * (__int128)inv, kRmsShift, &v[j]) &&
+             sfit;
+    uint32_t w[3];
+    range_ok = limb_words<3>(v, w) && range_ok;
+    const int64_t lane16 = tl + 32 * ((i >> 2) & 1);
+#pragma unroll
+    for (int l = 0; l < 3; ++l)
+      reinterpret_cast<uint32_t*>(tiles)[(((l * tgs + tg) * nb + (i >> 3)) * 64 + lane16) * 4 + (i & 3)] = w[l];
+  }
+  if (!sfit) flag(status, EI_DEV_OUT_RANGE);
+  if (!range_ok) flag(status, EI_DEV_LIMB_RANGE);
+}
+
 __global__ void requant_kernel(const int64_t* __restrict__ c, int64_t m, int k, int64_t* __restrict__ y, int64_t n,
                                int32_t* status) {
   const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -143,6 +227,14 @@ hipError_t launch_rmsnorm_limb_tiles(const int64_t* x, const int32_t* g, int64_t
                                      int64_t t_pad, int64_t d, int32_t* status, hipStream_t s) {
   hipLaunchKernelGGL(rmsnorm_q16_kernel<true>, dim3((unsigned)t_pad), dim3(kNormThreads), 0, s, x, g, eps,
                      (int64_t*)nullptr, tiles, t, t_pad, d, status);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_rmsnorm_tiles(const int64_t* part, int nparts, const int64_t* resid, int64_t* y,
+                                        const int32_t* g, int64_t eps, int8_t* tiles, int64_t t, int64_t t_pad,
+                                        int64_t d, int32_t* status, hipStream_t s) {
+  hipLaunchKernelGGL(combine_rmsnorm_tiles_kernel, dim3((unsigned)t_pad), dim3(kNormThreads), 0, s, part, nparts,
+                     resid, y, g, eps, tiles, t, t_pad, d, status);
   return hipGetLastError();
 }
 

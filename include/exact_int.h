@@ -457,6 +457,24 @@ int int_ffn_q8_prenorm(const ei_weights* wg, const ei_weights* wu, const ei_weig
                        void* workspace, size_t workspace_bytes, int32_t* d_status, ei_stream stream);
 
 /*
+ * A stack of pre-norm layers in one call: x_{l+1} = int_ffn_q8_prenorm(layer
+ * l, g_norms[l], x_l) for l = 0 .. n_layers - 1, y = x_{n_layers}; results
+ * equal n_layers calls of int_ffn_q8_prenorm.  Where the fused gate/up pass
+ * and a split-K down projection apply, one kernel per token forms each
+ * layer's output (residual plus the combined partials) and writes the next
+ * layer's RMSNorm of it as that layer's activation limb tiles.
+ *   layers   host array of 3 * n_layers descriptors as int_ffn_q8_chain
+ *   g_norms  host array of n_layers device pointers, each int32 [d], Q16
+ *   eps_q32  in [1, 2^32];  d <= 65536
+ *   x, y     device int64 [t][d]; y must not overlap x
+ * Workspace: ei_ffn_chain_workspace_bytes(gate, down, t).  Errors as
+ * int_ffn_q8_chain and int_ffn_q8_prenorm.
+ */
+int int_ffn_q8_prenorm_chain(const ei_weights* const* layers, int n_layers, const int32_t* const* g_norms,
+                             int64_t eps_q32, const int64_t* x, const int32_t* lut, int64_t* y, int64_t t,
+                             void* workspace, size_t workspace_bytes, int32_t* d_status, ei_stream stream);
+
+/*
  * The routed (mixture-of-experts) feed-forward layer ([tritify] 3.2
  * "Mixture-of-Experts": each selected expert is an exact-integer MLP; the
  * gate as in [Handshake] C1 and C4): for every pair (r, s), with

@@ -103,6 +103,13 @@ def test_routed_and_ffn_arguments(ei):
     layers = (WP * 3)(ctypes.pointer(g), ctypes.pointer(u), ctypes.pointer(dn))
     assert L.int_ffn_q8_chain(layers, 0, FAKE, FAKE, FAKE, 3, FAKE, 1 << 30, None, None) == EI_EINVAL
     assert L.int_ffn_q8_chain(layers, 1, FAKE, FAKE, FAKE, 3, FAKE, 0, None, None) == EI_ENOSPACE
+    gns = (ctypes.c_void_p * 1)(0x1000)
+    assert L.int_ffn_q8_prenorm_chain(layers, 0, gns, 1 << 20, FAKE, FAKE, FAKE, 3, FAKE, 1 << 30, None, None) == EI_EINVAL
+    assert L.int_ffn_q8_prenorm_chain(layers, 1, None, 1 << 20, FAKE, FAKE, FAKE, 3, FAKE, 1 << 30, None, None) == EI_EINVAL
+    nulls = (ctypes.c_void_p * 1)(None)
+    assert L.int_ffn_q8_prenorm_chain(layers, 1, nulls, 1 << 20, FAKE, FAKE, FAKE, 3, FAKE, 1 << 30, None, None) == EI_EINVAL
+    assert L.int_ffn_q8_prenorm_chain(layers, 1, gns, 0, FAKE, FAKE, FAKE, 3, FAKE, 1 << 30, None, None) == EI_ERANGE
+    assert L.int_ffn_q8_prenorm_chain(layers, 1, gns, 1 << 20, FAKE, FAKE, FAKE, 3, FAKE, 0, None, None) == EI_ENOSPACE
 
 
 def test_next_row_arguments(ei):

@@ -334,6 +334,41 @@ def test_qwen_ffn_24_layers_chain(ei):
     assert ei.digest(y) == GOLDEN["qwen05b_ffn"]["layers"][-1]["x_next"]
 
 
+@pytest.mark.parametrize("shape", [(96, 64, 3), (160, 96, 30), (4096, 64, 30), (4096, 64, 50), (2048, 96, 33),
+                                   (96, 160, 70)])
+def test_ffn_q8_prenorm_chain_matches_oracle(ei, lut, shape):
+    # three pre-norm layers in one call: with a K-split down projection each
+    # layer's output and the next layer's normalized limb tiles come from one
+    # kernel per token; other shapes take the per-layer paths
+    F, D, T = shape
+    r = np.random.default_rng(F * 3 + D + T)
+    layers = [[(synth.q8_codes(r, F, D), synth.q8_scales(r, F, D)), (synth.q8_codes(r, F, D), synth.q8_scales(r, F, D)),
+               (synth.q8_codes(r, D, F), synth.q8_scales(r, D, F))] for _ in range(3)]
+    norms = [r.integers(1 << 14, 1 << 17, D).astype(np.int32) for _ in range(3)]
+    eps = 1 << 20
+    x = synth.q16_acts(r, T, D)
+    packed = [tuple(ei.pack_q8(dev(c), dev(sc)) for c, sc in layer) for layer in layers]
+    say("ffn prenorm chain", shape)
+    y = host(ei.ffn_q8_prenorm_chain(packed, [dev(g) for g in norms], eps, dev(x), dev(lut)))
+    ref = x
+    for (wg, wu, wd), gn in zip(layers, norms):
+        *_, ref = oracle.ffn_layer_prenorm(ref, gn, eps, wg, wu, wd, lut)
+    assert (y == ref).all()
+
+
+def test_qwen_ffn_24_layers_prenorm_chain(ei):
+    lut = ei.silu_lut()
+    gold = GOLDEN["qwen05b_ffn_prenorm"]
+    packed, norms = [], []
+    for layer in range(synth.QWEN_LAYERS):
+        (gc, gs), (uc, us), (dc, ds) = synth.qwen_ffn_layer(layer)
+        packed.append((ei.pack_q8(dev(gc), dev(gs)), ei.pack_q8(dev(uc), dev(us)), ei.pack_q8(dev(dc), dev(ds))))
+        norms.append(dev(synth.qwen_norm_weight(layer)))
+    say("prenorm ffn chain 24 layers")
+    y = ei.ffn_q8_prenorm_chain(packed, norms, gold["eps_q32"], dev(synth.qwen_ffn_x0()), lut)
+    assert ei.digest(y) == gold["layers"][-1]["x_next"]
+
+
 def test_qwen_ffn_24_layers_prenorm(ei):
     lut = ei.silu_lut()
     x = dev(synth.qwen_ffn_x0())
