@@ -153,14 +153,27 @@ __global__ __launch_bounds__(kNormThreads) void combine_rmsnorm_tiles_kernel(
   bool fit = true, in_range = true;
   for (int64_t i = tid; i < d / 4; i += kNormThreads) {
     int64_t h[4] = {0, 0, 0, 0}, r[4] = {0, 0, 0, 0};
-    for (int p = 0; p < nparts; ++p) {
-      const int64_t* ph = part + (int64_t)(2 * p) * tn + tok * d + 4 * i;
-      const int64_t* pr = part + (int64_t)(2 * p + 1) * tn + tok * d + 4 * i;
+    for (int p0 = 0; p0 < nparts; p0 += 4) {   // four partials' loads in flight (past nparts: the last, not added)
+      int64_t vh[4][4], vr[4][4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        h[j] += ph[j];
-        r[j] += pr[j];
+      for (int q = 0; q < 4; ++q) {
+        const int64_t p = p0 + q < nparts ? p0 + q : nparts - 1;
+        const int64_t* ph = part + 2 * p * tn + tok * d + 4 * i;
+        const int64_t* pr = part + (2 * p + 1) * tn + tok * d + 4 * i;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          vh[q][j] = ph[j];
+          vr[q][j] = pr[j];
+        }
       }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (p0 + q < nparts)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            h[j] += vh[q][j];
+            r[j] += vr[q][j];
+          }
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
