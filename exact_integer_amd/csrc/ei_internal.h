@@ -44,6 +44,12 @@ inline bool narrow_scales(uint32_t smax, int64_t nb) {
   return smax < 32768u && (uint64_t)smax * (uint64_t)nb <= ((uint64_t)1 << 27);
 }
 
+// Bytes of the code tiles of an n_pad x k packed matrix: (n_pad / 32) row
+// groups of nb 1 KB tiles, i.e. one byte per code.  Kernels size the buffer
+// resource over a whole matrix's codes with this (host checks keep it below
+// 2^32).
+__host__ __device__ inline int64_t code_bytes(int64_t n_pad, int64_t nb) { return n_pad * nb * 32; }
+
 inline size_t packed_bytes(int64_t n, int64_t k) {
   int64_t n_pad = round_up(n, kTile);
   return (size_t)kHeaderBytes + (size_t)n_pad * (size_t)k + (size_t)n_pad * (size_t)(k / 32) * 4u;

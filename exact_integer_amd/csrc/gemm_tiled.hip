@@ -82,7 +82,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs a) {
   // tiles, so that every wave has the same number of loads per block.  Row
   // and token groups past the matrix re-read the last one (results unused).
   // Scalar offsets of tile j at block 0; block b adds b * 1 KB.
-  const __amdgpu_buffer_rsrc_t rcode = make_rsrc(codes, (uint32_t)(a.n_pad * a.nb * 1024));
+  const __amdgpu_buffer_rsrc_t rcode = make_rsrc(codes, (uint32_t)code_bytes(a.n_pad, a.nb));
   const __amdgpu_buffer_rsrc_t rlimb = make_rsrc(a.limb_tiles, (uint32_t)(3 * tgs * a.nb * 1024));
   const __amdgpu_buffer_rsrc_t rscal = make_rsrc(scales, (uint32_t)(a.n_pad * a.nb * 4));
   uint32_t soff[Sh::kPerWave];
@@ -464,7 +464,7 @@ __global__ __launch_bounds__(kGuWaves * 64) __attribute__((amdgpu_waves_per_eu(4
     if (j < 8) {
       int64_t rg = 4 * rb + (j & 3);
       rg = rg < rgs ? rg : rgs - 1;
-      rsrc[i] = make_rsrc(codes[j >> 2], (uint32_t)(a.n_pad * nb * 1024));
+      rsrc[i] = make_rsrc(codes[j >> 2], (uint32_t)code_bytes(a.n_pad, nb));
       soff[i] = (uint32_t)(rg * nb * 1024);
       dst[i] = j * 1024;
     } else {   // j < kCopies is checked where the copy is issued

@@ -14,11 +14,27 @@ Sources, cited by page title and section:
               Arithmetic, and Verifiable Distributed Inference as Its
               Consequence" (arXiv 2611.13730), sections 3.1, 3.2, 3.4, 4.
 
-Parity status of each function (what pins it is in tests/test_oracle_*.py):
-  q8, q4, silu_mul, limb_split, silu_lut, ffn_layer, moe_pairs, topk_route,
-  requant, rms_inverse, rmsnorm_q16, wide_gemm -- pinned;
-  q8_fp32 (the float negative control) -- canonical and tree_walk orders are
-  pinned against numpy float32 sequences; the other orders: parity unpinned.
+Parity status of each function and the test that pins it:
+  q8          brute force with Python integers, reductions to numpy integer
+              matmul, crafted rounding ties, schedule invariance
+              (test_oracle_pins.py, test_oracle_mutations.py);
+  q4          brute force, m = 1 / e = 0 reductions, the table-read
+              derivation;
+  silu_lut, silu_mul   closed forms, float64 and page clip figures, brute force;
+  limb_split  exhaustive over the 3-limb range;
+  ffn_layer   composed from brute-force q8 and silu_mul (test_ffn_layer_*);
+  ffn_layer_prenorm    composed from a Fraction/Decimal RMSNorm and brute-force
+              q8 and silu_mul, with planted mistakes (residual from the norm,
+              skipped norm, misindexed norm weight) caught
+              (test_ffn_layer_prenorm_*);
+  moe_pairs   per-pair brute force on tiny shapes with unsorted and repeated
+              experts, with planted mistakes (slot for token, shifted slot,
+              transposed route, swapped gate and up) caught (test_moe_pairs_*);
+  topk_route  brute force with ties; requant, rms_inverse, rmsnorm_q16
+              exact rationals and decimal square roots; wide_gemm brute force;
+  q8_fp32     (the float negative control) every order against numpy float32
+              sequences, the shuffled order with a splitmix64 / Fisher-Yates
+              of the test's own (test_fp32_shadow_*).
 """
 from __future__ import annotations
 
@@ -208,8 +224,19 @@ def ffn_layer(x: np.ndarray, wg, wu, wd, lut: np.ndarray, threads: int = 1):
     u = q8(wu[0], wu[1], x, threads=threads)
     h = silu_mul(g, u, lut)
     d = q8(wd[0], wd[1], h, threads=threads)
-    xn = x + d
+    xn = add_i64(x, d)
     return g, u, h, d, xn
+
+
+def add_i64(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """a + b elementwise for int64 arrays, raising OracleError if a sum leaves
+    int64 (numpy's own add would wrap without a word)."""
+    a, b = np.asarray(a, np.int64), np.asarray(b, np.int64)
+    s = a + b   # wraps on overflow; detected below
+    over = ((a >= 0) == (b >= 0)) & ((s >= 0) != (a >= 0))
+    if over.any():
+        raise OracleError("add_i64: sum outside int64")
+    return s
 
 
 def requant(c, m: int, k: int):
@@ -317,36 +344,41 @@ def ffn_layer_prenorm(x: np.ndarray, g_norm: np.ndarray, eps_q32: int, wg, wu, w
     (n, d, x_next)."""
     n = rmsnorm_q16(x, g_norm, eps_q32)
     _, _, _, d, _ = ffn_layer(n, wg, wu, wd, lut, threads=threads)
-    return n, d, x + d
+    return n, d, add_i64(x, d)
 
 
 def moe_pairs(x: np.ndarray, route: np.ndarray, experts, lut: np.ndarray, pairs=None,
               down_rows=None, threads: int = 1) -> np.ndarray:
-    """Routed expert FFNs: out[t][k] = Wd_e (silu(Wg_e x_t) * (Wu_e x_t) >> 16)
-    for e = route[t][k] ([tritify] 3.2 "Mixture-of-Experts": each selected
-    expert is an exact-integer MLP).  No combine: the router weights are not
-    part of this workload.
+    """Routed expert FFNs: out[p] = Wd_e (silu(Wg_e x_t) * (Wu_e x_t) >> 16)
+    for pair p = (t, k) and e = route[t][k] ([tritify] 3.2 "Mixture-of-Experts":
+    each selected expert is an exact-integer MLP).  No combine: the router
+    weights are not part of this workload.
 
     experts(e) -> ((gc, gs), (uc, us), (dc, ds)).  pairs: optional list of
-    (t, k) to compute; down_rows: optional subset of output rows.  Returns
-    an int64 array [len(pairs)][n_rows]."""
+    (t, k) to compute (default: every pair, t-major); down_rows: optional
+    subset of output rows.  Returns an int64 array [len(pairs)][n_rows].
+
+    The pairs of one expert go through q8 together, one activation row per
+    pair: every output of q8 depends on its own row alone, so this is the
+    per-pair definition evaluated a batch at a time."""
     T, topk = route.shape
     if pairs is None:
         pairs = [(t, k) for t in range(T) for k in range(topk)]
-    outs = []
-    cache = {}
-    for (t, k) in pairs:
-        e = int(route[t, k])
-        if e not in cache:
-            cache.clear()
-            cache[e] = experts(e)
-        (gc, gs), (uc, us), (dc, ds) = cache[e]
-        xt = x[t:t + 1]
-        g = q8(gc, gs, xt, threads=threads)
-        u = q8(uc, us, xt, threads=threads)
+    by_expert = {}
+    for p, (t, k) in enumerate(pairs):
+        by_expert.setdefault(int(route[t, k]), []).append(p)
+    out = None
+    for e in sorted(by_expert):
+        idx = by_expert[e]
+        (gc, gs), (uc, us), (dc, ds) = experts(e)
+        if down_rows is not None:
+            dc, ds = dc[down_rows], ds[down_rows]
+        xe = x[[pairs[p][0] for p in idx]]
+        g = q8(gc, gs, xe, threads=threads)
+        u = q8(uc, us, xe, threads=threads)
         h = silu_mul(g, u, lut)
-        if down_rows is None:
-            outs.append(q8(dc, ds, h, threads=threads)[0])
-        else:
-            outs.append(q8(dc[down_rows], ds[down_rows], h, threads=threads)[0])
-    return np.stack(outs) if outs else np.zeros((0, 0), np.int64)
+        d = q8(dc, ds, h, threads=threads)
+        if out is None:
+            out = np.zeros((len(pairs), d.shape[1]), np.int64)
+        out[idx] = d
+    return out if out is not None else np.zeros((0, 0), np.int64)

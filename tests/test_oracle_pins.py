@@ -7,6 +7,7 @@ pages state (schedule invariance, row-order = column-stream), and brute
 force with Python's arbitrary-precision integers on tiny inputs.
 """
 import itertools
+import zlib
 import math
 import os
 
@@ -21,7 +22,7 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
 def _rng(tag):
-    return np.random.default_rng(abs(hash(tag)) % (2**32))
+    return np.random.default_rng(zlib.crc32(repr(tag).encode()))
 
 
 def _rand_q8(r, N, K, T, extreme=False):
