@@ -44,7 +44,8 @@ def main(threads: int = 8) -> None:
     for layer in range(synth.QWEN_LAYERS):
         wg, wu, wd = synth.qwen_ffn_layer(layer)
         g, u, h, d, x = oracle.ffn_layer(x, wg, wu, wd, lut, threads=threads)
-        layers.append({"d": oracle.digest(d), "x_next": oracle.digest(x)})
+        layers.append({"g": oracle.digest(g), "u": oracle.digest(u), "h": oracle.digest(h),
+                       "d": oracle.digest(d), "x_next": oracle.digest(x)})
         print("ffn layer", layer, layers[-1]["x_next"][:16], flush=True)
     out["qwen05b_ffn"] = {"layers": layers}
 
@@ -63,12 +64,22 @@ def main(threads: int = 8) -> None:
 
     (rc, rs), xo = synth.olmoe_router(), synth.olmoe_x()
     scores = oracle.q8(rc, rs, xo, threads=threads)
-    out["olmoe_router"] = {"scores": oracle.digest(scores),
-                           "route": oracle.digest(oracle.topk_route(scores, synth.OLMOE_TOPK))}
+    iroute = oracle.topk_route(scores, synth.OLMOE_TOPK)
+    print("olmoe step, integer route", flush=True)
+    out["olmoe_router"] = {"scores": oracle.digest(scores), "route": oracle.digest(iroute),
+                           "y": oracle.digest(oracle.moe_pairs(xo, iroute, synth.olmoe_expert, lut,
+                                                               threads=threads))}
+    # the whole routed step (every one of the 4096 token-expert pairs), with
+    # the seeded route
+    print("olmoe step, seeded route", flush=True)
+    out["olmoe_step"] = {"y": oracle.digest(oracle.moe_pairs(xo, synth.olmoe_route(), synth.olmoe_expert, lut,
+                                                             threads=threads))}
 
     w, s = synth.dense_w()
     x1 = synth.dense_x(1)
-    out["dense_14336x4096"] = {"t1_y": oracle.digest(oracle.q8(w, s, x1, threads=threads))}
+    print("dense 14336x4096, T = 1 and 512", flush=True)
+    out["dense_14336x4096"] = {"t1_y": oracle.digest(oracle.q8(w, s, x1, threads=threads)),
+                               "t512_y": oracle.digest(oracle.q8(w, s, synth.dense_x(512), threads=threads))}
 
     with open(os.path.join(HERE, "oracle_digests.json"), "w") as f:
         json.dump(out, f, indent=1, sort_keys=True)

@@ -216,11 +216,14 @@ def test_q4_small_all_schedules(ei, shape):
 # ------------------------------------------------------------------ workloads
 
 def test_q8_896x896_gemv(ei):
+    # the single 896x896 GEMV under every schedule ([Handshake] Schedule gate)
     (q, s), x = synth.q8_896_inputs()
     w = ei.pack_q8(dev(q), dev(s))
-    say("q8 896x896 T=1")
-    y = ei.gemm_q8(w, dev(x))
-    assert ei.digest(y) == GOLDEN["q8_896x896"]["y"] == oracle.digest(oracle.q8(q, s, x))
+    assert GOLDEN["q8_896x896"]["y"] == oracle.digest(oracle.q8(q, s, x))
+    xd = dev(x)
+    for sched in SCHEDS:
+        say("q8 896x896 T=1", sched)
+        assert ei.digest(ei.gemm_q8(w, xd, 3, sched)) == GOLDEN["q8_896x896"]["y"], sched
 
 
 def test_qkv_schedule_gate(ei):
@@ -240,9 +243,11 @@ def test_q4_d512(ei):
         nib, sme = synth.q4_d512_matrix(name)
         w = ei.pack_q4(dev(nib), dev(sme))
         for t in (1, 64):
-            say("q4 d512", name, t)
-            y = ei.gemm_q4(w, dev(synth.q4_d512_x(k, t)))
-            assert ei.digest(y) == GOLDEN["q4_d512"][f"{name}_t{t}"]
+            xd = dev(synth.q4_d512_x(k, t))
+            for sched in SCHEDS:
+                say("q4 d512", name, t, sched)
+                y = ei.gemm_q4(w, xd, 3, sched)
+                assert ei.digest(y) == GOLDEN["q4_d512"][f"{name}_t{t}"], sched
 
 
 def test_qwen_ffn_24_layers(ei):
@@ -259,6 +264,28 @@ def test_qwen_ffn_24_layers(ei):
         x = x + d
         exp = GOLDEN["qwen05b_ffn"]["layers"][layer]
         assert ei.digest(d) == exp["d"], layer
+        assert ei.digest(x) == exp["x_next"], layer
+
+
+def test_qwen_ffn_schedule_gate(ei):
+    # every projection of the 24 Qwen-shaped layers (gate, up 4864x896; down
+    # 896x4864; T=30) under the five schedules: g, u, h and d digests equal
+    # the oracle's, layer by layer ([Handshake] Schedule gate)
+    lut = ei.silu_lut()
+    x = dev(synth.qwen_ffn_x0())
+    for layer in range(synth.QWEN_LAYERS):
+        (gc, gs), (uc, us), (dc, ds) = synth.qwen_ffn_layer(layer)
+        wg, wu, wd = ei.pack_q8(dev(gc), dev(gs)), ei.pack_q8(dev(uc), dev(us)), ei.pack_q8(dev(dc), dev(ds))
+        exp = GOLDEN["qwen05b_ffn"]["layers"][layer]
+        for sched in SCHEDS:
+            say("qwen schedule gate, layer", layer, sched)
+            g = ei.gemm_q8(wg, x, 3, sched)
+            u = ei.gemm_q8(wu, x, 3, sched)
+            h = ei.silu_mul(g, u, lut)
+            d = ei.gemm_q8(wd, h, 3, sched)
+            assert (ei.digest(g), ei.digest(u), ei.digest(h), ei.digest(d)) == \
+                (exp["g"], exp["u"], exp["h"], exp["d"]), (layer, sched)
+        x = x + d
         assert ei.digest(x) == exp["x_next"], layer
 
 
@@ -451,35 +478,42 @@ def test_q8_multi_sixteen_matrices(ei):
         assert (y == oracle.q8(q, s, x)).all()
 
 
-def test_dense_t1(ei):
+@pytest.fixture(scope="module")
+def dense(ei):
     q, s = synth.dense_w()
-    w = ei.pack_q8(dev(q), dev(s))
-    say("dense T=1")
-    y = ei.gemm_q8(w, dev(synth.dense_x(1)))
-    assert ei.digest(y) == GOLDEN["dense_14336x4096"]["t1_y"]
+    return q, s, ei.pack_q8(dev(q), dev(s))
 
 
-def test_dense_t512_sampled_rows_and_schedules(ei):
-    q, s = synth.dense_w()
+def test_dense_t1(ei, dense):
+    # the whole T=1 output against the oracle's digest, under every schedule
+    q, s, w = dense
+    xd = dev(synth.dense_x(1))
+    for sched in SCHEDS:
+        say("dense T=1", sched)
+        assert ei.digest(ei.gemm_q8(w, xd, 3, sched)) == GOLDEN["dense_14336x4096"]["t1_y"], sched
+
+
+def test_dense_t512_full_output_all_schedules(ei, dense):
+    # all 512 x 14336 outputs against the oracle's digest ([Handshake]
+    # Falsifier 3: a single mismatched cell at any scale), under every
+    # schedule including the pairwise tree (22.5 GB of per-block terms)
+    q, s, w = dense
     x = synth.dense_x(512)
-    w = ei.pack_q8(dev(q), dev(s))
     xd = dev(x)
     say("dense T=512 default")
     y = host(ei.gemm_q8(w, xd))
-    rows = np.random.default_rng(9).choice(q.shape[0], 48, replace=False)
-    rows = np.concatenate([rows, [0, 31, 32, 14335]])
-    ref = oracle.q8(q[rows], s[rows], x, threads=8)
-    assert (y[:, rows] == ref).all()
-    # properties that hold at any size: every schedule gives the same bytes
-    d0 = oracle.digest(y)
-    for sched in ("reversed", "split_k", "tiled_shuffled"):
+    assert oracle.digest(y) == GOLDEN["dense_14336x4096"]["t512_y"]
+    rows = np.array([0, 31, 32, 14335])
+    assert (y[:, rows] == oracle.q8(q[rows], s[rows], x, threads=8)).all()
+    del y
+    for sched in SCHEDS[1:]:
         say("dense T=512", sched)
-        assert ei.digest(ei.gemm_q8(w, xd, 3, sched)) == d0, sched
+        assert ei.digest(ei.gemm_q8(w, xd, 3, sched)) == GOLDEN["dense_14336x4096"]["t512_y"], sched
+        torch.cuda.empty_cache()
 
 
-def test_repeat_runs_identical(ei):
-    q, s = synth.dense_w()
-    w = ei.pack_q8(dev(q), dev(s))
+def test_repeat_runs_identical(ei, dense):
+    q, s, w = dense
     for t in (1, 64):
         xd = dev(synth.dense_x(t))
         say("repeat", t)
@@ -516,6 +550,66 @@ def test_q8_tiled_narrow_scales_at_the_edge(ei, N):
     w = ei.pack_q8(dev(q), dev(s))
     assert w.desc.smax == 32767
     assert (host(ei.gemm_q8(w, dev(x))) == oracle.q8(q, s, x)).all()
+
+
+# Wide scales (|S| >= 2^15) send the tiled kernels to their per-limb form,
+# which addresses a whole matrix's code tiles through one buffer resource.
+# At n_pad * k = 2^27 (16384 x 8192) that size must not wrap: a wrapped size
+# reads every code as zero.
+WRAP_N, WRAP_K = 16384, 8192
+
+
+def _wide_scale_matrix(r, n, k):
+    q = synth.q8_codes(r, n, k)
+    s = r.integers(-(2**16), 2**16 + 1, (n, k // 32)).astype(np.int32)
+    s[0, 0] = 2**16   # never narrow
+    return q, s
+
+
+def test_q8_tiled_wide_scales_at_the_code_size_wrap(ei):
+    r = np.random.default_rng(31)
+    q, s = _wide_scale_matrix(r, WRAP_N, WRAP_K)
+    x = synth.q16_acts(r, 64, WRAP_K)
+    say("tiled wide scales at n_pad*k = 2^27")
+    w = ei.pack_q8(dev(q), dev(s))
+    assert w.desc.smax == 2**16
+    y = host(ei.gemm_q8(w, dev(x)))
+    rows = np.concatenate([r.choice(WRAP_N, 12, replace=False), [0, 31, WRAP_N - 32, WRAP_N - 1]])
+    assert (y[:, rows] == oracle.q8(q[rows], s[rows], x, threads=8)).all()
+    assert (y[:, rows] != 0).any()
+
+
+def test_grouped_wide_scales_at_the_code_size_wrap(ei, lut):
+    # two experts of 16384 x 8192 (gate, up) and 8192 x 16384 (down): the
+    # routed projection and the fused gate/up pass in their per-limb form
+    r = np.random.default_rng(32)
+    E, rows, topk = 2, 48, 2
+    F, D = WRAP_N, WRAP_K
+    mats = [[_wide_scale_matrix(r, F, D), _wide_scale_matrix(r, F, D), _wide_scale_matrix(r, D, F)]
+            for _ in range(E)]
+    x = r.integers(-(2**12), 2**12 + 1, (rows, D)).astype(np.int64)
+    route = np.stack([r.permutation(E)[:topk] for _ in range(rows)]).astype(np.int32)
+
+    def stack(m):
+        return (dev(np.stack([mm[m][0] for mm in mats])), dev(np.stack([mm[m][1] for mm in mats])))
+    say("grouped wide scales: pack")
+    wg, wu, wd = (ei.pack_q8_stacked(*stack(m)) for m in range(3))
+    assert wg.desc.smax == 2**16
+    xd, rd = dev(x), dev(route)
+    say("grouped wide scales: gate projection")
+    g = host(ei.gemm_q8_grouped(wg, xd, rd))
+    pick = [(0, 0), (0, 1), (17, 0), (rows - 1, 1)]
+    for (t, k) in pick:
+        e = int(route[t, k])
+        want = oracle.q8(mats[e][0][0], mats[e][0][1], x[t:t + 1], threads=8)[0]
+        assert (g[t * topk + k] == want).all(), (t, k)
+    say("grouped wide scales: routed FFN")
+    y = host(ei.moe_ffn_q8(wg, wu, wd, xd, rd, dev(lut)))
+    down_rows = [0, 1, 4095, D - 1]
+    ref = oracle.moe_pairs(x, route, lambda e: mats[e], lut, pairs=pick, down_rows=down_rows, threads=8)
+    for (t, k), want in zip(pick, ref):
+        assert (y[t * topk + k][down_rows] == want).all(), (t, k)
+    assert (y != 0).any()
 
 
 @pytest.mark.parametrize("emax", [14, 15])
@@ -650,41 +744,60 @@ def test_q8_grouped_bad_expert_is_flagged(ei):
         ei.gemm_q8_grouped(w, dev(synth.q16_acts(r, rows, K)), dev(route))
 
 
-def test_olmoe_grouped_ffn_sampled_pairs(ei, lut):
-    # 64 experts (gate/up 1024x2048, down 2048x1024), 512 tokens, top-8: the
-    # full routed FFN on the GPU, sampled pairs against the oracle
-    E, H, I = synth.OLMOE_E, synth.OLMOE_H, synth.OLMOE_I
+@pytest.fixture(scope="module")
+def olmoe(ei):
+    # 64 experts (gate/up 1024x2048, down 2048x1024), 512 tokens, top-8
+    E = synth.OLMOE_E
     mats = [synth.olmoe_expert(e) for e in range(E)]
-    gc = np.stack([m[0][0] for m in mats]); gs = np.stack([m[0][1] for m in mats])
-    uc = np.stack([m[1][0] for m in mats]); us = np.stack([m[1][1] for m in mats])
-    dc = np.stack([m[2][0] for m in mats]); ds = np.stack([m[2][1] for m in mats])
-    x, route = synth.olmoe_x(), synth.olmoe_route()
+
+    def stacked(m):
+        return ei.pack_q8_stacked(dev(np.stack([mm[m][0] for mm in mats])), dev(np.stack([mm[m][1] for mm in mats])))
     say("olmoe pack")
-    wg, wu, wd = ei.pack_q8_stacked(dev(gc), dev(gs)), ei.pack_q8_stacked(dev(uc), dev(us)), \
-        ei.pack_q8_stacked(dev(dc), dev(ds))
+    return mats, stacked(0), stacked(1), stacked(2), synth.olmoe_x(), synth.olmoe_route()
+
+
+def test_olmoe_grouped_ffn_full_output(ei, lut, olmoe):
+    # the full routed FFN on the GPU: all 4096 x 2048 outputs against the
+    # oracle's digest, by three grouped calls and by the one-call routed FFN
+    mats, wg, wu, wd, x, route = olmoe
     xd, rd = dev(x), dev(route)
     say("olmoe grouped ffn")
     g = ei.gemm_q8_grouped(wg, xd, rd)
     u = ei.gemm_q8_grouped(wu, xd, rd)
     h = ei.silu_mul(g, u, ei.silu_lut())
-    out = host(ei.gemm_q8_grouped(wd, h, rd.reshape(-1, 1)))
-    assert out.shape == (synth.OLMOE_T * synth.OLMOE_TOPK, H)
-    rs = np.random.default_rng(23)
-    pairs = [(int(t), int(k)) for t, k in zip(rs.integers(0, synth.OLMOE_T, 16), rs.integers(0, 8, 16))]
-    pairs += [(0, 0), (511, 7)]
+    out = ei.gemm_q8_grouped(wd, h, rd.reshape(-1, 1))
+    assert tuple(out.shape) == (synth.OLMOE_T * synth.OLMOE_TOPK, synth.OLMOE_H)
+    assert ei.digest(out) == GOLDEN["olmoe_step"]["y"]
+    pairs = [(0, 0), (511, 7), (200, 3)]
     ref = oracle.moe_pairs(x, route, lambda e: mats[e], lut, pairs=pairs, threads=8)
+    outh = host(out)
     for (t, k), want in zip(pairs, ref):
-        assert (out[t * 8 + k] == want).all(), (t, k)
-    # the gate projection of one expert equals the dense projection of that
-    # expert on its routed tokens (a property that holds at any size)
-    e = int(route[3, 0])
-    tt, kk = np.nonzero(route == e)
-    dense = host(ei.gemm_q8(ei.pack_q8(dev(gc[e]), dev(gs[e])), dev(x[tt])))
-    assert (host(g)[tt * 8 + kk] == dense).all()
-    # the one-call routed FFN (one grouping for the three projections) gives
-    # the same rows as the three grouped calls
+        assert (outh[t * 8 + k] == want).all(), (t, k)
     say("olmoe routed ffn, one call")
-    assert (host(ei.moe_ffn_q8(wg, wu, wd, xd, rd, dev(lut))) == out).all()
+    assert ei.digest(ei.moe_ffn_q8(wg, wu, wd, xd, rd, dev(lut))) == GOLDEN["olmoe_step"]["y"]
+
+
+def test_olmoe_expert_schedule_gate(ei, olmoe):
+    # each expert's three projections on the rows routed to it, run as plain
+    # projections under the five schedules, equal the grouped outputs row for
+    # row (whose whole digest equals the oracle's above)
+    mats, wg, wu, wd, x, route = olmoe
+    xd, rd = dev(x), dev(route)
+    g = ei.gemm_q8_grouped(wg, xd, rd)
+    u = ei.gemm_q8_grouped(wu, xd, rd)
+    h = ei.silu_mul(g, u, ei.silu_lut())
+    out = ei.gemm_q8_grouped(wd, h, rd.reshape(-1, 1))
+    for e in range(synth.OLMOE_E):
+        tt, kk = np.nonzero(route == e)
+        pr = torch.from_numpy(tt * synth.OLMOE_TOPK + kk).cuda()
+        (gc, gs), (uc, us), (dc, ds) = mats[e]
+        pg, pu, pd = ei.pack_q8(dev(gc), dev(gs)), ei.pack_q8(dev(uc), dev(us)), ei.pack_q8(dev(dc), dev(ds))
+        xe, he = xd[torch.from_numpy(tt).cuda()].contiguous(), h[pr].contiguous()
+        for sched in SCHEDS:
+            say("olmoe expert", e, "rows", len(tt), sched)
+            assert torch.equal(ei.gemm_q8(pg, xe, 3, sched), g[pr]), (e, sched, "gate")
+            assert torch.equal(ei.gemm_q8(pu, xe, 3, sched), u[pr]), (e, sched, "up")
+            assert torch.equal(ei.gemm_q8(pd, he, 3, sched), out[pr]), (e, sched, "down")
 
 
 # ------------------------------------- second derivations (table reads)
@@ -852,6 +965,16 @@ def test_olmoe_integer_router(ei):
     route = ei.topk_route(scores, synth.OLMOE_TOPK)
     assert ei.digest(scores) == GOLDEN["olmoe_router"]["scores"]
     assert ei.digest(route) == GOLDEN["olmoe_router"]["route"]
+
+
+def test_olmoe_step_with_integer_router(ei, lut, olmoe):
+    # the routed FFN behind the integer router: the whole output = oracle's
+    _, wg, wu, wd, x, _ = olmoe
+    (rc, rs) = synth.olmoe_router()
+    xd = dev(x)
+    say("olmoe step with the integer router")
+    route = ei.topk_route(ei.gemm_q8(ei.pack_q8(dev(rc), dev(rs)), xd), synth.OLMOE_TOPK)
+    assert ei.digest(ei.moe_ffn_q8(wg, wu, wd, xd, route, dev(lut))) == GOLDEN["olmoe_router"]["y"]
 
 
 # ------------------------------------------------------------- FP32 shadow
