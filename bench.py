@@ -7,14 +7,19 @@ dense projection; synthetic seeded codes, Q24 scales and Q16 activations).
 
 One step = one decode pass (a T=1 projection over each of `--copies` distinct
 resident copies of the weights, so the 256 MB Infinity Cache cannot serve
-them) followed by one T=512 prefill projection.  Both are recorded once as
-HIP graphs and replayed; HIP events on the launch stream time every replay.
-After timing, the outputs are checked bit-exactly against the CPU oracle
-(full digest at T=1, sampled rows at T=512).
+them), one T=512 prefill projection, the 24-layer Qwen2.5-0.5B-shaped FFN
+chain (T=30) and the OLMoE-shaped routed FFN (64 experts, 512 tokens, top-8).
+Each part is recorded once as a HIP graph and replayed; HIP events on the
+launch stream time every part of every step.  After timing, every output is
+checked bit-exactly against the CPU oracle: whole-output digests (all 14336
+T=1 outputs of every copy, all 512 x 14336 prefill outputs, the chain's final
+activations, all 4096 x 2048 routed outputs), and the prefill element by
+element against the oracle run of the CPU baseline.
 
 Prints ONE JSON line.  `value` is the decode weight bandwidth (GB/s); the
-prefill rate, both roofline fractions, and the oracle timed on the host cores
-(`cpu_baseline`) ride along in the same line.
+prefill rate, the chain and routed FFN rates, their roofline fractions, and
+the oracle timed on the host cores (`cpu_baseline`) ride along in the same
+line.
 """
 from __future__ import annotations
 
@@ -42,6 +47,7 @@ GEMM_KERNEL = "gemm_tiled_qreg_kernel"   # the T=512 kernel for narrow scales (t
 # is used only while that file is unchanged
 KERNEL_SOURCES = {GEMV_KERNEL: "gemv.hip", GEMM_KERNEL: "gemm_tiled.hip"}
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+GOLDEN = os.path.join(ROOT, "tests", "golden", "oracle_digests.json")
 
 
 def kernel_source_hash(kernel: str) -> str:
@@ -97,30 +103,81 @@ def summarize_counters(fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy
     return 0
 
 
-def cpu_baseline(q, s, x1, x512, rows: int, decode_seconds: float = 8.0):
-    """The CPU oracle, as it stands, on the host cores: T=1 passes over the whole
-    matrix repeated for about `decode_seconds`, and one T=512 pass over the
-    first `rows` rows.  Threads own disjoint output rows."""
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or the platform string."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or platform.machine()
+
+
+def cpu_threads() -> int:
+    """Threads for the multi-threaded oracle leg: the CPUs this process may run
+    on, capped at OMP_NUM_THREADS when that is set (a shared host gives each
+    GPU's jobs a share of its cores, 16 per GPU on the MI355X boxes here)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    cap = os.environ.get("OMP_NUM_THREADS")
+    return max(1, min(n, int(cap))) if cap and cap.isdigit() else n
+
+
+def cpu_baseline(q, s, x1, x512, runs: int = 3, t1_seconds: float = 1.0, t512_rows_1thread: int = 256):
+    """The CPU oracle, as it stands, on the host cores, on the same input
+    bytes; median of `runs` runs of each leg (GEMM loops only):
+      * T=1 over the whole matrix, repeated for about `t1_seconds` per run,
+        with one thread and with cpu_threads() threads (disjoint output rows);
+      * T=512 over all rows with cpu_threads() threads (its output is kept for
+        the full-output parity check), and over the first `t512_rows_1thread`
+        rows with one thread.
+    Returns (record, y at T=1, y at T=512)."""
+    import statistics
     import oracle
-    cores = min(os.cpu_count() or 1, 16)
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        y1 = oracle.q8(q, s, x1, threads=cores)
-        reps += 1
-        if time.perf_counter() - t0 >= decode_seconds:
-            break
-    t_dec = (time.perf_counter() - t0) / reps
-    t0 = time.perf_counter()
-    oracle.q8(q[:rows], s[:rows], x512, threads=cores)
-    t_pre = time.perf_counter() - t0
-    useful = LIMBS * 2.0 * 512 * rows * K
+    nt = cpu_threads()
+
+    def t1(threads):
+        times = []
+        for _ in range(runs):
+            reps, t0 = 0, time.perf_counter()
+            while True:
+                y = oracle.q8(q, s, x1, threads=threads)
+                reps += 1
+                if time.perf_counter() - t0 >= t1_seconds:
+                    break
+            times.append((time.perf_counter() - t0) / reps)
+        return statistics.median(times), y
+
+    def t512(threads, rows):
+        times = []
+        for _ in range(runs):
+            t0 = time.perf_counter()
+            y = oracle.q8(q[:rows], s[:rows], x512, threads=threads)
+            times.append(time.perf_counter() - t0)
+        return statistics.median(times), y
+
+    d1_n, y1 = t1(nt)
+    d1_1, _ = t1(1)
+    p_n, y512 = t512(nt, N)
+    p_1, _ = t512(1, t512_rows_1thread)
+    use_n = LIMBS * 2.0 * 512 * N * K
+    use_1 = LIMBS * 2.0 * 512 * t512_rows_1thread * K
     return {
-        "value": W_BYTES / t_dec / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
-        "sample": f"T=1: all {N} rows x {reps} passes ({reps * t_dec:.1f} s); "
-                  f"T=512: rows 0..{rows - 1} of {N}, one pass ({t_pre:.1f} s)",
-        "t1_ms": t_dec * 1e3, "t512_useful_tops": useful / t_pre / 1e12,
-        "t512_logical_tops": useful / LIMBS / t_pre / 1e12, "t512_sample_s": t_pre,
-    }, y1
+        "value": W_BYTES / d1_n / 1e9, "unit": "GB/s", "cores": nt, "kind": "oracle",
+        "sample": f"median of {runs} runs per leg. T=1: all {N} rows, passes repeated for ~{t1_seconds:g} s per run, "
+                  f"{nt} threads and 1 thread; T=512: all {N} rows with {nt} threads, rows 0..{t512_rows_1thread - 1} "
+                  f"with 1 thread",
+        "cpu_model": cpu_model(), "host_logical_cpus": os.cpu_count(),
+        "threads_note": "threads = the CPUs this process may use, capped at OMP_NUM_THREADS (the box's per-GPU share)",
+        "t1_ms": d1_n * 1e3, "t1_ms_1thread": d1_1 * 1e3, "value_1thread": W_BYTES / d1_1 / 1e9,
+        "t512_s": p_n, "t512_useful_tops": use_n / p_n / 1e12, "t512_logical_tops": use_n / LIMBS / p_n / 1e12,
+        "t512_1thread_s_per_row_sample": p_1, "t512_useful_tops_1thread": use_1 / p_1 / 1e12,
+        "t512_logical_tops_1thread": use_1 / LIMBS / p_1 / 1e12,
+    }, y1, y512
 
 
 def copy_calibration(torch, dev) -> int:
@@ -199,7 +256,11 @@ def bench_q4_table(args, torch, np, ei, synth, dev) -> int:
                                          for name, n, k, t, nd, sd, w, x, yt, ym, ws, wt in cases)
     logical = sum(2.0 * t * n * k for _, n, k, t, *rest in cases)
     tops = logical / (ms_t * 1e-3) / 1e12
-    alu_peak = 78.6   # int32 VALU lane-ops/s: 256 CUs x 4 SIMDs x 32 lanes x 2 issue x 2.4 GHz (fp32 157.3 TFLOP/s / 2)
+    # int32 VALU peak in lane-ops/s: 256 CUs x 4 SIMDs x 16 lanes per clock x 2.4 GHz = 39.3 T (a wave64
+    # instruction issues over 4 clocks; the 157.3 TFLOP/s fp32 figure counts an FMA as 2 and packed fp32 as 2
+    # more, neither of which an int32 add or shift has).  `achieved` counts logical ops 2*T*N*K, while a
+    # table read spends at least one table read and one add per logical multiply-add.
+    alu_peak = 256 * 4 * 16 * 2.4e9 / 1e12
     print(json.dumps({
         "metric": "4-bit projection by table reads: logical int TOPS", "value": round(tops, 3), "unit": "TOPS",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall_t, 4),
@@ -207,7 +268,7 @@ def bench_q4_table(args, torch, np, ei, synth, dev) -> int:
         "data": "synthetic (seeded 4-bit codes and m*2^e scale bytes, int32 activations)",
         "config": {"workload": "q4_d512_table_read", "shapes": list(synth.Q4_SHAPES.values()), "tokens": [1, 64],
                    "parallelism": "single-gpu"},
-        "roofline": {"bound": "alu", "achieved": round(tops, 3), "peak": alu_peak, "unit": "TOP/s",
+        "roofline": {"bound": "alu", "achieved": round(tops, 3), "peak": round(alu_peak, 2), "unit": "TOP/s",
                      "frac": round(tops / alu_peak, 4), "traffic": None, "step_ms": round(ms_t, 4)},
         "mfma_path_step_ms": round(ms_m, 4),
         "parity": {"table_read_and_mfma_digests_equal_oracle": ok}}))
@@ -254,17 +315,16 @@ def bench_olmoe_router(args, torch, np, ei, synth, dev) -> int:
     """The OLMoE-shaped routed FFN behind an integer router: the router's Q8
     projection (64 x 2048) of the 512 tokens, integer top-8, then the routed
     FFN on that route, all inside the timed step."""
-    import oracle
     E, H, I, T, TOPK = synth.OLMOE_E, synth.OLMOE_H, synth.OLMOE_I, synth.OLMOE_T, synth.OLMOE_TOPK
     mats = [synth.olmoe_expert(e) for e in range(E)]
 
     def stack(m, k):
         return torch.from_numpy(np.ascontiguousarray(np.stack([mm[m][k] for mm in mats]))).to(dev)
     wg, wu, wd = (ei.pack_q8_stacked(stack(m, 0), stack(m, 1)) for m in range(3))
+    del mats
     rc, rs = synth.olmoe_router()
     wr = ei.pack_q8(torch.from_numpy(rc).to(dev), torch.from_numpy(rs).to(dev))
-    x = synth.olmoe_x()
-    xd = torch.from_numpy(x).to(dev)
+    xd = torch.from_numpy(synth.olmoe_x()).to(dev)
     scores = torch.empty((T, E), dtype=torch.int64, device=dev)
     route = torch.empty((T, TOPK), dtype=torch.int32, device=dev)
     out = torch.empty((T * TOPK, H), dtype=torch.int64, device=dev)
@@ -279,14 +339,9 @@ def bench_olmoe_router(args, torch, np, ei, synth, dev) -> int:
         ei.moe_ffn_q8(wg, wu, wd, xd, route, lut, out=out, workspace=ws, status=status)
 
     ms, wall_ms = _time_graph(torch, step, args.steps, args.warmup)
-    gold = json.load(open(os.path.join(ROOT, "tests", "golden", "oracle_digests.json")))["olmoe_router"]
+    gold = json.load(open(GOLDEN))["olmoe_router"]
     route_ok = int(status.item()) == 0 and ei.digest(route) == gold["route"]
-    rs_ = np.random.default_rng(6)
-    pairs = [(int(t), int(k)) for t, k in zip(rs_.integers(0, T, 6), rs_.integers(0, TOPK, 6))]
-    ref = oracle.moe_pairs(x, route.cpu().numpy(), lambda e: mats[e], oracle.silu_lut(), pairs=pairs,
-                           threads=min(os.cpu_count() or 1, 16))
-    got = out.cpu().numpy()
-    ok = route_ok and all((got[t * TOPK + k] == r).all() for (t, k), r in zip(pairs, ref))
+    ok = route_ok and ei.digest(out) == gold["y"]
     wbytes = 3 * E * I * H * (1 + 4 / 32) + E * H * (1 + 4 / 32)
     gbs = wbytes / (ms * 1e-3) / 1e9
     print(json.dumps({
@@ -300,67 +355,69 @@ def bench_olmoe_router(args, torch, np, ei, synth, dev) -> int:
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "step_ms": round(ms, 4),
                      "weight_bytes": int(wbytes)},
-        "parity": {"route_digest_equals_oracle": route_ok, "sampled_pairs_equal_oracle": ok,
-                   "pairs_checked": len(pairs)}}))
+        "parity": {"route_digest_equals_oracle": route_ok, "full_output_digest_equals_oracle": ok}}))
     return 0 if ok else 1
 
 
-def bench_olmoe(args, torch, np, ei, synth, dev) -> int:
+def setup_olmoe(torch, np, ei, synth, dev):
     """The OLMoE-shaped routed FFN: 64 experts (gate/up 1024x2048, down
-    2048x1024, Q8), 512 tokens, top-8: grouped gate and up projections, the
-    SiLU-gated product, grouped down projection.  HBM-bound: every expert's
-    weights are read once per step."""
-    import oracle
+    2048x1024, Q8), 512 tokens, top-8: grouped gate and up projections in one
+    pass with the SiLU-gated product, then the grouped down projection, in one
+    int_moe_ffn_q8 call.  HBM-bound: every expert's weights are read once per
+    step.  Returns the step, its parity check (the whole output's digest
+    against the oracle's) and the byte / op counts."""
     E, H, I, T, TOPK = synth.OLMOE_E, synth.OLMOE_H, synth.OLMOE_I, synth.OLMOE_T, synth.OLMOE_TOPK
     mats = [synth.olmoe_expert(e) for e in range(E)]
 
     def stack(m, k):
         return torch.from_numpy(np.ascontiguousarray(np.stack([mm[m][k] for mm in mats]))).to(dev)
     wg, wu, wd = (ei.pack_q8_stacked(stack(m, 0), stack(m, 1)) for m in range(3))
-    x, route = synth.olmoe_x(), synth.olmoe_route()
-    xd, rd = torch.from_numpy(x).to(dev), torch.from_numpy(route).to(dev)
+    del mats
+    xd, rd = torch.from_numpy(synth.olmoe_x()).to(dev), torch.from_numpy(synth.olmoe_route()).to(dev)
     P = T * TOPK
     out = torch.empty((P, H), dtype=torch.int64, device=dev)
     ws = torch.empty(ei.moe_ffn_workspace_bytes(wg, wd, T, TOPK), dtype=torch.uint8, device=dev)
     lut = ei.silu_lut(dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
+    gold = json.load(open(GOLDEN))["olmoe_step"]["y"]
 
     def step():
         ei.moe_ffn_q8(wg, wu, wd, xd, rd, lut, out=out, workspace=ws, status=status)
 
-    ms, wall_ms = _time_graph(torch, step, args.steps, args.warmup)
-    if int(status.item()) != 0:
-        print(f"bench.py: device status {int(status.item())}", file=sys.stderr)
-        return 1
-    rs = np.random.default_rng(5)
-    pairs = [(int(t), int(k)) for t, k in zip(rs.integers(0, T, 6), rs.integers(0, TOPK, 6))]
-    ref = oracle.moe_pairs(x, route, lambda e: mats[e], oracle.silu_lut(), pairs=pairs,
-                           threads=min(os.cpu_count() or 1, 16))
-    got = out.cpu().numpy()
-    ok = all((got[t * TOPK + k] == r).all() for (t, k), r in zip(pairs, ref))
-    wbytes = 3 * E * I * H * (1 + 4 / 32)
-    useful = LIMBS * 2.0 * P * 3 * I * H
-    gbs = wbytes / (ms * 1e-3) / 1e9
+    def check() -> bool:
+        return int(status.item()) == 0 and ei.digest(out) == gold
+
+    return {"step": step, "check": check, "wbytes": 3 * E * I * H * (1 + 4 / 32),
+            "useful": LIMBS * 2.0 * P * 3 * I * H, "config": {"experts": E, "hidden": H, "intermediate": I,
+                                                              "tokens": T, "top_k": TOPK}}
+
+
+def bench_olmoe(args, torch, np, ei, synth, dev) -> int:
+    """The routed FFN alone (see setup_olmoe)."""
+    o = setup_olmoe(torch, np, ei, synth, dev)
+    ms, wall_ms = _time_graph(torch, o["step"], args.steps, args.warmup)
+    ok = o["check"]()
+    gbs = o["wbytes"] / (ms * 1e-3) / 1e9
     print(json.dumps({
         "metric": "routed expert FFN: weight GB/s", "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall_ms, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "int8xint8->int32, int64 accumulate",
         "data": "synthetic (seeded Q8 experts, Q16 activations, uniform top-8 routing)",
-        "config": {"workload": "olmoe_grouped_ffn", "experts": E, "hidden": H, "intermediate": I, "tokens": T,
-                   "top_k": TOPK, "parallelism": "single-gpu"},
+        "config": {"workload": "olmoe_grouped_ffn", **o["config"], "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "step_ms": round(ms, 4),
-                     "weight_bytes": int(wbytes)},
-        "useful_tops": round(useful / (ms * 1e-3) / 1e12, 2),
-        "parity": {"sampled_pairs_equal_oracle": ok, "pairs_checked": len(pairs)}}))
+                     "weight_bytes": int(o["wbytes"])},
+        "useful_tops": round(o["useful"] / (ms * 1e-3) / 1e12, 2),
+        "parity": {"full_output_digest_equals_oracle": ok}}))
     return 0 if ok else 1
 
 
-def bench_qwen_ffn(args, torch, np, ei, synth, dev, prenorm: bool = False) -> int:
+def setup_qwen(torch, ei, synth, dev, prenorm: bool = False):
     """The Qwen2.5-0.5B-shaped FFN chain: 24 layers of gate and up (4864x896)
     and down (896x4864) Q8 projections at T=30 with the SiLU-gated product and
-    the residual add, fresh weights per layer (353 MB, read once per step)."""
-    import json as _json
+    the residual add (pre-norm: an integer RMSNorm in front of every layer),
+    fresh weights per layer (353 MB, read once per step), run as one chain
+    call.  Parity: the final layer's output digest against the oracle's."""
     layers = []
     for layer in range(synth.QWEN_LAYERS):
         (gc, gs), (uc, us), (dc, ds) = synth.qwen_ffn_layer(layer)
@@ -373,10 +430,9 @@ def bench_qwen_ffn(args, torch, np, ei, synth, dev, prenorm: bool = False) -> in
                          ei.ffn_chain_workspace_bytes(layers[0][0], layers[0][2], T), 1), dtype=torch.uint8, device=dev)
     lut = ei.silu_lut(dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
-
     norms = [torch.from_numpy(synth.qwen_norm_weight(i)).to(dev) for i in range(synth.QWEN_LAYERS)]
-
     final = bufs[(synth.QWEN_LAYERS - 1) % 2]
+    gold = json.load(open(GOLDEN))["qwen05b_ffn_prenorm" if prenorm else "qwen05b_ffn"]["layers"][-1]["x_next"]
 
     def step():   # the whole stack in one call
         if prenorm:
@@ -393,31 +449,38 @@ def bench_qwen_ffn(args, torch, np, ei, synth, dev, prenorm: bool = False) -> in
                               status=status)
             src = dst
 
-    gold = _json.load(open(os.path.join(ROOT, "tests", "golden", "oracle_digests.json")))[
-        "qwen05b_ffn_prenorm" if prenorm else "qwen05b_ffn"]["layers"]
-    layer_calls_ms = None
-    if prenorm:
-        layer_calls_ms, _ = _time_graph(torch, step_layers, args.steps, args.warmup)
-        ok_layers = int(status.item()) == 0 and ei.digest(final) == gold[-1]["x_next"]
+    def check() -> bool:
+        ok = int(status.item()) == 0 and ei.digest(final) == gold
         final.zero_()
-    ms, wall_ms = _time_graph(torch, step, args.steps, args.warmup)
-    ok = int(status.item()) == 0 and ei.digest(final) == gold[-1]["x_next"]
+        return ok
+
+    return {"step": step, "step_layers": step_layers, "check": check,
+            "wbytes": synth.QWEN_LAYERS * 3 * F * D * (1 + 4 / 32),
+            "useful": LIMBS * 2.0 * T * 3 * F * D * synth.QWEN_LAYERS,
+            "config": {"tokens": T, "hidden": D, "intermediate": F, "layers": synth.QWEN_LAYERS}}
+
+
+def bench_qwen_ffn(args, torch, np, ei, synth, dev, prenorm: bool = False) -> int:
+    """The FFN chain alone (see setup_qwen); with prenorm, also as 24 layer calls."""
+    qw = setup_qwen(torch, ei, synth, dev, prenorm)
+    layer_calls_ms, ok_layers = None, True
     if prenorm:
-        ok = ok and ok_layers
-    wbytes = synth.QWEN_LAYERS * 3 * F * D * (1 + 4 / 32)
-    gbs = wbytes / (ms * 1e-3) / 1e9
+        layer_calls_ms, _ = _time_graph(torch, qw["step_layers"], args.steps, args.warmup)
+        ok_layers = qw["check"]()
+    ms, wall_ms = _time_graph(torch, qw["step"], args.steps, args.warmup)
+    ok = qw["check"]() and ok_layers
+    gbs = qw["wbytes"] / (ms * 1e-3) / 1e9
     print(json.dumps({
         "metric": ("24-layer pre-norm Q8 FFN chain" if prenorm else "24-layer Q8 FFN chain") + ": weight GB/s",
         "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall_ms, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "int8xint8->int32, int64 accumulate",
         "data": "synthetic (seeded Q8 layers, Q16 activations)",
-        "config": {"workload": "qwen05b_ffn_24_layers" + ("_prenorm" if prenorm else ""), "tokens": T,
-                   "hidden": D, "intermediate": F,
-                   "layers": synth.QWEN_LAYERS, "parallelism": "single-gpu"},
+        "config": {"workload": "qwen05b_ffn_24_layers" + ("_prenorm" if prenorm else ""), **qw["config"],
+                   "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "step_ms": round(ms, 4),
-                     "weight_bytes": int(wbytes)},
+                     "weight_bytes": int(qw["wbytes"])},
         **({"layer_calls_step_ms": round(layer_calls_ms, 4)} if prenorm else {}),
         "parity": {"final_digest_equals_oracle": ok}}))
     return 0 if ok else 1
@@ -430,7 +493,6 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--copies", type=int, default=12, help="distinct resident weight copies for the T=1 pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=N, help="rows of the T=512 oracle sample")
     ap.add_argument("--profile", action="store_true", help="short run for rocprofv3 (no baseline, few steps)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 256 MiB, 5 times (the reference for HBM byte counters)")
@@ -479,6 +541,7 @@ def main() -> int:
     def to_dev(a):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
+    gold = json.load(open(GOLDEN))
     q, s = synth.dense_w()
     x1, x512 = synth.dense_x(1), synth.dense_x(512)
     w0 = ei.pack_q8(to_dev(q), to_dev(s))
@@ -493,6 +556,8 @@ def main() -> int:
     y512 = torch.empty((512, N), dtype=torch.int64, device=dev)
     ws = torch.empty(max(ei.workspace_bytes(w0, 512, LIMBS), 1), dtype=torch.uint8, device=dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
+    qw = setup_qwen(torch, ei, synth, dev)
+    om = setup_olmoe(torch, np, ei, synth, dev)
     torch.cuda.synchronize()
 
     def decode():
@@ -502,29 +567,41 @@ def main() -> int:
     def prefill():
         ei.gemm_q8(w0, x512d, LIMBS, out=y512, workspace=ws, status=status)
 
-    # eager run first (also the graph's warm-up)
-    decode(); prefill()
+    # One step: the T=1 decode pass over the copies, the T=512 prefill, the
+    # 24-layer Qwen-shaped FFN chain (SiLU epilogue, residual) and the
+    # OLMoE-shaped routed FFN (grouping, grouped projections): every part of
+    # the path.  Each part is a HIP graph; events on the launch stream
+    # bracket each part of each step.
+    parts = [("decode", decode), ("prefill", prefill), ("qwen", qw["step"]), ("olmoe", om["step"])]
+    graphs = []
+    for _, fn in parts:   # eager run first (also the graph's warm-up)
+        fn()
     torch.cuda.synchronize()
-    g_dec, g_pre = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_dec):
-        decode()
-    with torch.cuda.graph(g_pre):
-        prefill()
+    for _, fn in parts:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        graphs.append(g)
     torch.cuda.synchronize()
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)] for _ in range(args.steps)]
     for _ in range(args.warmup):
-        g_dec.replay(); g_pre.replay()
+        for g in graphs:
+            g.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for e0, e1, e2 in ev:
-        e0.record(); g_dec.replay(); e1.record(); g_pre.replay(); e2.record()
+    for e in ev:
+        e[0].record()
+        for i, g in enumerate(graphs):
+            g.replay()
+            e[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    dec_ms = sorted(a.elapsed_time(b) for a, b, _ in ev)
-    pre_ms = sorted(b.elapsed_time(c) for _, b, c in ev)
-    dec_med, pre_med = dec_ms[len(dec_ms) // 2], pre_ms[len(pre_ms) // 2]
+    med = {}
+    for i, (name, _) in enumerate(parts):
+        ms = sorted(e[i].elapsed_time(e[i + 1]) for e in ev)
+        med[name] = ms[len(ms) // 2]
+    dec_med, pre_med = med["decode"], med["prefill"]
     if int(status.item()) != 0:
         print(f"bench.py: device status {int(status.item())}", file=sys.stderr)
         return 1
@@ -532,29 +609,37 @@ def main() -> int:
     # ---- the same decode pass as batched launches (int_gemm_q8_multi, up to
     # 16 matrices sharing x per launch): reported beside `value`, not in it
     yb = [torch.empty((1, N), dtype=torch.int64, device=dev) for _ in copies]
-    batched = {}
+    batched, batched_ok = {}, True
     for group in (2, 16):   # 2: gate and up of one FFN layer; 16: the largest batch
         def decode_batched():
             for i in range(0, len(copies), group):
                 ei.gemm_q8_multi(copies[i:i + group], x1d, LIMBS, outs=yb[i:i + group], status=status)
 
         batched[group], _ = _time_graph(torch, decode_batched, args.steps, args.warmup)
-        if {ei.digest(y) for y in yb} != {json.load(open(os.path.join(ROOT, "tests", "golden", "oracle_digests.json")))[
-                "dense_14336x4096"]["t1_y"]}:
-            print(json.dumps({"error": "parity failure (batched decode)", "group": group}))
-            return 1
+        batched_ok = batched_ok and {ei.digest(y) for y in yb} == {gold["dense_14336x4096"]["t1_y"]}
         yb = [torch.empty((1, N), dtype=torch.int64, device=dev) for _ in copies]
 
-    # ---- parity of what was timed
-    import oracle
-    gold = json.load(open(os.path.join(ROOT, "tests", "golden", "oracle_digests.json")))["dense_14336x4096"]["t1_y"]
+    # ---- the oracle on the host cores (it also yields every T=512 row)
+    base = y512_ref = None
+    if not args.no_cpu_baseline:
+        base, _, y512_ref = cpu_baseline(q, s, x1, x512)
+
+    # ---- parity of what was timed: whole outputs against the oracle
     dig = {ei.digest(y1[c]) for c in range(args.copies)}
-    rows = np.concatenate([np.random.default_rng(11).choice(N, 24, replace=False), [0, N - 1]])
-    ref = oracle.q8(q[rows], s[rows], x512, threads=min(os.cpu_count() or 1, 16))
-    ok512 = bool((y512.cpu().numpy()[:, rows] == ref).all())
-    parity = {"t1_digest_equals_oracle": dig == {gold}, "t512_sampled_rows_equal_oracle": ok512,
-              "t512_rows_checked": int(rows.size), "t1_batched_digests_equal_oracle": True}
-    if not (parity["t1_digest_equals_oracle"] and ok512):
+    y512h = y512.cpu().numpy()
+    parity = {
+        "t1_digest_equals_oracle": dig == {gold["dense_14336x4096"]["t1_y"]},
+        "t512_full_digest_equals_oracle": oracle_digest(y512h) == gold["dense_14336x4096"]["t512_y"],
+        "t512_rows_checked_elementwise": 0,
+        "t1_batched_digests_equal_oracle": batched_ok,
+        "qwen_ffn_final_digest_equals_oracle": qw["check"](),
+        "olmoe_full_output_digest_equals_oracle": om["check"](),
+    }
+    if y512_ref is not None:
+        ok = bool((y512h == y512_ref).all())
+        parity["t512_rows_checked_elementwise"] = N if ok else -1
+    if not all(v for k, v in parity.items() if k != "t512_rows_checked_elementwise") or \
+            parity["t512_rows_checked_elementwise"] < 0:
         print(json.dumps({"error": "parity failure", "parity": parity}))
         return 1
 
@@ -566,13 +651,24 @@ def main() -> int:
     useful = LIMBS * 2.0 * 512 * N * K
     pre_tops = useful / (pre_med * 1e-3) / 1e12
     tr_dec, tr_pre = stored_traffic(GEMV_KERNEL), stored_traffic(GEMM_KERNEL)
+
+    def hbm_part(name, rec):
+        ms = med[name]
+        gbs = rec["wbytes"] / (ms * 1e-3) / 1e9
+        return {"ms": round(ms, 4), **rec["config"],
+                "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                             "weight_bytes": int(rec["wbytes"])},
+                "useful_tops": round(rec["useful"] / (ms * 1e-3) / 1e12, 2)}
+
     out = {
         "metric": METRIC, "value": round(dec_gbs, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8xint8->int32, int64 accumulate",
         "data": "synthetic (seeded Q8 codes, Q24 block scales, Q16 activations; no checkpoint)",
         "config": {"workload": "dense_14336x4096_q8", "t_decode": 1, "t_prefill": 512, "weight_copies": args.copies,
-                   "act_limbs": LIMBS, "parallelism": "single-gpu"},
+                   "act_limbs": LIMBS, "step_also_runs": ["qwen05b_ffn_24_layers", "olmoe_grouped_ffn"],
+                   "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "achieved": round(ach_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(ach_gbs / HBM_PEAK_GBS, 4), "traffic": tr_dec, "kernel": GEMV_KERNEL,
                      "launch_us": round(per_gemv_ms * 1e3, 3), "algorithmic_bytes": algo_bytes},
@@ -591,12 +687,21 @@ def main() -> int:
                          "frac": round(pre_tops / I8_PEAK_TOPS, 4), "traffic": tr_pre, "kernel": GEMM_KERNEL,
                          "note": "useful i8 ops = 3 limbs x 2*T*N*K; the event span covers the limb split and the MFMA kernel"},
         },
+        "qwen05b_ffn_24_layers": hbm_part("qwen", qw),
+        "olmoe_grouped_ffn": hbm_part("olmoe", om),
         "parity": parity,
     }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"], _ = cpu_baseline(q, s, x1, x512, args.cpu_rows)
+    if base is not None:
+        out["cpu_baseline"] = base
     print(json.dumps(out))
     return 0
+
+
+def oracle_digest(a) -> str:
+    """SHA-256 of an array's little-endian bytes (the oracle's digest layout)."""
+    import numpy as np
+    a = np.ascontiguousarray(a)
+    return hashlib.sha256(a.astype(a.dtype.newbyteorder("<"), copy=False).tobytes()).hexdigest()
 
 
 if __name__ == "__main__":
