@@ -18,7 +18,7 @@ from functools import lru_cache
 import torch
 
 __all__ = [
-    "EIError", "PackedWeights", "lib", "pack_q8", "pack_q4", "pack_q8_stacked", "gemm_q8", "gemm_q4",
+    "EIError", "PackedWeights", "lib", "pack_q8", "pack_q4", "pack_q8_stacked", "gemm_q8", "gemm_q8_noalloc", "gemm_q4",
     "gemm_q8_grouped", "fp32_shadow", "limb_split", "silu_lut", "silu_mul", "digest", "sha256_host", "workspace_bytes",
     "grouped_workspace_bytes", "SCHEDULES", "DEV_LIMB_RANGE", "DEV_OUT_RANGE", "DEV_ROUTE",
 ]
@@ -57,6 +57,7 @@ SIGNATURES = {
     "ei_gemm_workspace_bytes": (SZ, [WP, I64, I32, I32]),
     "int_gemm_q8": (I32, [WP, P, P, I64, I32, I32, U64, P, SZ, P, P]),
     "int_gemm_q8_multi": (I32, [P, I32, P, P, I64, I32, P, P]),
+    "int_gemm_q8_noalloc": (I32, [WP, P, P, I64, I32, P, P]),
     "int_gemm_q4": (I32, [WP, P, P, I64, I32, I32, U64, P, SZ, P, P]),
     "ei_silu_lut_build": (I32, [P, P]),
     "silu_lut_epilogue": (I32, [P, P, P, P, I64, P, P]),
@@ -526,6 +527,26 @@ def gemm_q8(w: PackedWeights, x: torch.Tensor, limbs: int = 3, schedule: str = "
             out=None, workspace=None, status=None) -> torch.Tensor:
     """y = (sum_b S sum_j q x + 2^23) >> 24 for Q16 int64 activations x [t][k]."""
     return _gemm("int_gemm_q8", w, x, torch.int64, limbs, schedule, seed, out, workspace, status)
+
+
+def gemm_q8_noalloc(w: PackedWeights, x: torch.Tensor, limbs: int = 3, out=None, status=None) -> torch.Tensor:
+    """gemm_q8 under the default schedule with the library's own scratch array
+    (int_gemm_q8_noalloc): no workspace argument, nothing allocated by the call."""
+    s = _stream()
+    t, k = x.shape
+    if k != w.k:
+        raise EIError(f"int_gemm_q8_noalloc: x has k={k}, weights k={w.k}")
+    px = _dev(x, torch.int64, "x")
+    y = out if out is not None else torch.empty((t, w.n), dtype=torch.int64, device=x.device)
+    py = _dev(y, torch.int64, "y")
+    check = status is None
+    if check:
+        status = torch.zeros(1, dtype=torch.int32, device=x.device)
+    _check(lib().int_gemm_q8_noalloc(ctypes.byref(w.desc), px, py, t, limbs, status.data_ptr(), s),
+           "int_gemm_q8_noalloc")
+    if check:
+        _raise_status(status, "int_gemm_q8_noalloc")
+    return y
 
 
 def gemm_q8_multi(ws, x: torch.Tensor, limbs: int = 3, outs=None, status=None):

@@ -3,6 +3,7 @@
 // arithmetic runs in the kernels of the other translation units.
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "ei_internal.h"
 
@@ -739,6 +740,55 @@ int int_gemm_q8(const ei_weights* w, const int64_t* x, int64_t* y, int64_t t, in
                   static_cast<hipStream_t>(stream), OUT_ROUND_Q24);
 }
 
+// ------------------------------------------------ allocation-free projection
+// Scratch memory of int_gemm_q8_noalloc: one array per device, in the code
+// object, held until the process ends.  Host code never uses the symbol's
+// name as an address: the device address comes from hipGetSymbolAddress,
+// once per device, and is cached below.
+}  // extern "C"
+
+namespace {
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;   // 32 MiB
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's copy of `scratch`, looked up on the first call made
+// with that device current.
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return EI_EDEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return EI_EDEVICE;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return EI_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int int_gemm_q8_noalloc(const ei_weights* w, const int64_t* x, int64_t* y, int64_t t, int limbs,
+                        int32_t* d_status, ei_stream stream) {
+  const int c = check_weights(w, EI_FORMAT_Q8);
+  if (c != EI_OK) return c;
+  if (!x || !y || t < 1 || limbs < 1 || limbs > 8) return EI_EINVAL;
+  if (limbs > kMaxLimbs) return EI_ERANGE;
+  const size_t need = layout_for(w, t, limbs, EI_SCHED_DEFAULT).total;
+  if (need > kNoAllocScratchBytes) return EI_ENOSPACE;
+  void* ws = nullptr;
+  if (need > 0) {
+    const int sc = scratch_of_current_device(&ws);
+    if (sc != EI_OK) return sc;
+  }
+  return run_gemm(w, x, 0, y, t, limbs, EI_SCHED_DEFAULT, 0, ws, need, d_status, static_cast<hipStream_t>(stream),
+                  OUT_ROUND_Q24);
+}
+
 int int_gemm_q8_multi(const ei_weights* const* w, int count, const int64_t* x, int64_t* const* y, int64_t t,
                       int limbs, int32_t* d_status, ei_stream stream) {
   if (!w || !y || !x || count < 1 || count > kMultiMax) return EI_EINVAL;
@@ -944,6 +994,6 @@ const char* ei_status_string(int code) {
   }
 }
 
-int ei_version(void) { return 108; }
+int ei_version(void) { return 109; }
 
 }  // extern "C"

@@ -42,8 +42,9 @@
  *   - No entry point allocates device memory except where a comment says
  *     so; scratch space is the caller's `workspace` of at least the size
  *     the matching *_workspace_bytes() returns.
- *   - The library holds no mutable global state; calls on different streams
- *     may run concurrently.  Calls that share a workspace must be ordered.
+ *   - The library holds no mutable global state apart from the scratch
+ *     array of int_gemm_q8_noalloc; calls on different streams may run
+ *     concurrently.  Calls that share a workspace must be ordered.
  *   - Weight matrices have K (the reduction dimension) a multiple of 32:
  *     the block structure of the formats.  N and T may be anything >= 1.
  */
@@ -218,6 +219,25 @@ int int_gemm_q8(const ei_weights* w, const int64_t* x, int64_t* y, int64_t t, in
 int int_gemm_q4(const ei_weights* w, const int32_t* x, int64_t* y, int64_t t, int limbs,
                 int schedule, uint64_t shuffle_seed, void* workspace, size_t workspace_bytes,
                 int32_t* d_status, ei_stream stream);
+
+/*
+ * int_gemm_q8 under EI_SCHED_DEFAULT for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same definition and the same bits, with no workspace
+ * argument.  The scratch space it needs (activation limb tiles, workgroup
+ * partials) is a fixed 32 MiB array inside the library's code object, one per
+ * device, held until the process ends; the device current at the call is the
+ * one used.  Nothing is allocated or freed by the call.
+ *   w, x, y, t, limbs, d_status, stream   as int_gemm_q8
+ * EI_ENOSPACE if ei_gemm_workspace_bytes(w, t, limbs, EI_SCHED_DEFAULT)
+ * exceeds 32 MiB (e.g. k = 4096 with more than about 2,700 tokens); other
+ * errors as int_gemm_q8.  All calls on one device share the array: calls
+ * that overlap in time on one device (different streams, or threads) race
+ * and must be ordered by the caller.  Every call writes all the scratch it
+ * reads, so no clearing between calls is needed.
+ */
+int int_gemm_q8_noalloc(const ei_weights* w, const int64_t* x, int64_t* y, int64_t t, int limbs,
+                        int32_t* d_status, ei_stream stream);
 
 /*
  * Several Q8 projections of the same activations in one launch, for decode

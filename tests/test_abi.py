@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
     for name in _declared():
         assert hasattr(lib, name), name
     assert set(ei.SIGNATURES) >= _declared(), sorted(_declared() - set(ei.SIGNATURES))
-    assert lib.ei_version() == 108
+    assert lib.ei_version() == 109
 
 
 def test_host_sha256_matches_hashlib():
