@@ -46,6 +46,10 @@ GEMM_KERNEL = "gemm_tiled_qreg_kernel"   # the T=512 kernel for narrow scales (t
 # the source file each timed kernel is built from: a stored HBM-traffic figure
 # is used only while that file is unchanged
 KERNEL_SOURCES = {GEMV_KERNEL: "gemv.hip", GEMM_KERNEL: "gemm_tiled.hip"}
+# the template instance each timed kernel runs as in the bench step (the routed
+# FFN in the same step runs other instances of the same templates)
+KERNEL_MATCH = {GEMV_KERNEL: "gemv_kernel<3, 1, long, 8, 2, false>",
+                GEMM_KERNEL: "gemm_tiled_qreg_kernel<false, false, true>"}
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 GOLDEN = os.path.join(ROOT, "tests", "golden", "oracle_digests.json")
 
@@ -89,8 +93,8 @@ def summarize_counters(fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy
     fetch, write = per_kernel(fetch_dir), per_kernel(write_dir)
     out = {"_calibration": {"copy_bytes": 256 << 20, "fetch_scale": round(f_fac, 4), "write_scale": round(w_fac, 4)}}
     for kern in (GEMV_KERNEL, GEMM_KERNEL):
-        fk = [v for k, vs in fetch.items() if kern in k for v in vs]
-        wk = [v for k, vs in write.items() if kern in k for v in vs]
+        fk = [v for k, vs in fetch.items() if KERNEL_MATCH[kern] in k for v in vs]
+        wk = [v for k, vs in write.items() if KERNEL_MATCH[kern] in k for v in vs]
         if not fk or not wk:
             continue
         f_b, w_b = statistics.median(fk) * 1024 * f_fac, statistics.median(wk) * 1024 * w_fac
@@ -101,6 +105,58 @@ def summarize_counters(fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy
         f.write("\n")
     print(json.dumps(out))
     return 0
+
+
+SQ_JSON = os.path.join(ROOT, "profiles", "sq_counters.json")
+XCDS, SIMDS = 8, 1024   # MI355X: GRBM_GUI_ACTIVE is summed over 8 XCDs; 256 CUs x 4 SIMDs
+
+
+def summarize_sq(pass1: str, pass2: str) -> int:
+    """Two rocprofv3 --pmc runs of `bench.py --profile` (SQ instruction and
+    busy counters) -> per-kernel medians, VALU / MFMA busy fractions, the
+    engine clock under load and the VALU ceiling (the launch's VALU
+    instructions at one per 4 cycles on each of the 1024 SIMDs), written to
+    profiles/sq_counters.json."""
+    import csv
+    import statistics
+
+    vals = {}
+    for d in (pass1, pass2):
+        for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))):
+            for kern in (GEMM_KERNEL,):
+                if KERNEL_MATCH[kern] in r["Kernel_Name"]:
+                    v = vals.setdefault(kern, {})
+                    v.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+                    v.setdefault("_ns", []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    out = {}
+    for kern, v in vals.items():
+        m = {k: statistics.median(x) for k, x in v.items()}
+        us = m["_ns"] / 1e3
+        cyc = m["GRBM_GUI_ACTIVE"] / XCDS
+        clock = cyc / (us * 1e-6) / 1e9
+        valu_ceiling_us = m["SQ_INSTS_VALU"] * 4 / SIMDS / (clock * 1e9) * 1e6
+        out[kern] = {
+            "duration_us": round(us, 2), "clock_ghz": round(clock, 3),
+            "valu_insts": int(m["SQ_INSTS_VALU"]), "valu_int64_insts": int(m.get("SQ_INSTS_VALU_INT64", 0)),
+            "mfma_insts": int(m["SQ_INSTS_MFMA"]), "lds_insts": int(m["SQ_INSTS_LDS"]),
+            "valu_busy": round(m["SQ_ACTIVE_INST_VALU"] * 4 / SIMDS / cyc, 4),
+            "mfma_busy": round(m["SQ_VALU_MFMA_BUSY_CYCLES"] / SIMDS / cyc, 4),
+            "valu_ceiling_us": round(valu_ceiling_us, 2),
+            "lds_bank_conflicts": int(m.get("SQ_LDS_BANK_CONFLICT", 0)),
+            "source_sha": kernel_source_hash(kern)}
+    with open(SQ_JSON, "w") as f:
+        json.dump(out, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps(out))
+    return 0
+
+
+def stored_sq(kernel: str):
+    """The committed SQ counter summary of `kernel`, if taken on the current source."""
+    if not os.path.exists(SQ_JSON):
+        return None
+    rec = json.load(open(SQ_JSON)).get(kernel)
+    return rec if rec and rec.get("source_sha") == kernel_source_hash(kernel) else None
 
 
 def cpu_model() -> str:
@@ -498,6 +554,8 @@ def main() -> int:
                     help="only run a plain device copy of 256 MiB, 5 times (the reference for HBM byte counters)")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="rocprofv3 --pmc output directories -> profiles/traffic.json (no GPU needed)")
+    ap.add_argument("--summarize-sq", nargs=2, metavar=("PASS1", "PASS2"),
+                    help="two rocprofv3 --pmc output directories of SQ counters -> profiles/sq_counters.json")
     ap.add_argument("--workload", choices=("dense", "olmoe", "olmoe_router", "qwen_ffn", "qwen_ffn_prenorm", "wide",
                                            "q4_table"),
                     default="dense",
@@ -509,6 +567,8 @@ def main() -> int:
     args = ap.parse_args()
     if args.summarize_counters:
         return summarize_counters(*args.summarize_counters)
+    if args.summarize_sq:
+        return summarize_sq(*args.summarize_sq)
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the projection would shard by rows across GPUs, see the design notes)", file=sys.stderr)
@@ -652,6 +712,35 @@ def main() -> int:
     pre_tops = useful / (pre_med * 1e-3) / 1e12
     tr_dec, tr_pre = stored_traffic(GEMV_KERNEL), stored_traffic(GEMM_KERNEL)
 
+    def valu_ceiling(step_ms):
+        # the prefill kernel is bound by its per-block VALU epilogue (exact
+        # int64 scale multiply-adds): its VALU instructions at one per 4 cycles
+        # on every SIMD, at the clock measured under load, give its ceiling
+        sq = stored_sq(GEMM_KERNEL)
+        if sq is None:
+            return None
+        return {"bound": "valu", "ceiling_us": sq["valu_ceiling_us"], "kernel_us_profiled": sq["duration_us"],
+                "frac": round(sq["valu_ceiling_us"] / sq["duration_us"], 4),
+                "valu_busy": sq["valu_busy"], "mfma_busy": sq["mfma_busy"], "clock_ghz": sq["clock_ghz"],
+                "valu_insts_per_launch": sq["valu_insts"],
+                "valu_insts_per_wave_block": round(sq["valu_insts"] / (512 // 32 * N // 32 * (K // 32)), 1),
+                "step_us_this_run": round(step_ms * 1e3, 1),
+                "source": "profiles/sq_counters.json (rocprofv3 --pmc of bench.py --profile)"}
+
+    # a plain device copy: the measured HBM ceiling beside the datasheet's
+    csrc_t = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    cdst_t = torch.empty_like(csrc_t)
+    cdst_t.copy_(csrc_t)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(10):
+        cdst_t.copy_(csrc_t)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * (256 << 20) * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del csrc_t, cdst_t
+
     def hbm_part(name, rec):
         ms = med[name]
         gbs = rec["wbytes"] / (ms * 1e-3) / 1e9
@@ -686,7 +775,10 @@ def main() -> int:
             "roofline": {"bound": "mfma", "achieved": round(pre_tops, 2), "peak": I8_PEAK_TOPS, "unit": "TOPS",
                          "frac": round(pre_tops / I8_PEAK_TOPS, 4), "traffic": tr_pre, "kernel": GEMM_KERNEL,
                          "note": "useful i8 ops = 3 limbs x 2*T*N*K; the event span covers the limb split and the MFMA kernel"},
+            "valu_ceiling": valu_ceiling(pre_med),
         },
+        "measured_ceilings": {"hbm_copy_gbs_read_plus_write": round(copy_gbs, 1),
+                              "note": "a 256 MiB device copy timed in this run (bytes read + written per second)"},
         "qwen05b_ffn_24_layers": hbm_part("qwen", qw),
         "olmoe_grouped_ffn": hbm_part("olmoe", om),
         "parity": parity,
