@@ -268,9 +268,12 @@ hipError_t launch_tiled_shape(const GemmArgs& a, hipStream_t s) {
 // stays in its L2 while the code tiles stream; a code tile is fetched by two
 // XCDs.  Measured on the dense 14336 x 4096, T = 512 projection: 184.7 us mean
 // against 190.2 us for contiguous runs of row blocks with all their token tiles.
-template <bool kExact, bool kGrouped, bool XB = true>
+// PF: blocks of operands in flight ahead of the one consumed (an LDS ring of
+// PF + 1 one-block buffers, PF + 1 register sets).
+template <bool kExact, bool kGrouped, bool XB = true, int PF = 1>
 __global__ __launch_bounds__(256) void gemm_tiled_qreg_kernel(GemmArgs a) {
   constexpr int kBuf = 4 * 1024;   // per block: 3 limb tiles + 1 KB for the fourth wave's dummy copy
+  constexpr int kRing = PF + 1;
   extern __shared__ __align__(16) uint8_t lds[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -313,32 +316,21 @@ __global__ __launch_bounds__(256) void gemm_tiled_qreg_kernel(GemmArgs a) {
   const int64_t tg = tb < tgs ? tb : tgs - 1;
   const uint32_t lsoff = (uint32_t)(((int64_t)(wave < 3 ? wave : 0) * tgs + tg) * a.nb * 1024);
   const int ldst = wave * 1024;
-  auto issue = [&](int64_t b) {
-    copy16_to_lds(rlimb, lds + (int)(b & 1) * kBuf + ldst, lane * 16, lsoff + (uint32_t)b * 1024u);
+  const int64_t nb = a.nb;
+  // block b's operands (b < nb): its limb tiles into LDS slot b % kRing (every
+  // wave one copy), its code tile and scales into a register set: 3 requests
+  auto fetch = [&](int64_t b, v4i& q, int32_t& S) {
+    copy16_to_lds(rlimb, lds + (int)(b % kRing) * kBuf + ldst, lane * 16, lsoff + (uint32_t)b * 1024u);
+    q = __builtin_amdgcn_raw_buffer_load_b128(rcode, lane * 16, (int)b * 1024, 0);
+    S = __builtin_amdgcn_raw_buffer_load_b32(rscal, (lane & 31) * 4, (int)b * 128, 0);
   };
 
   int64_t acc0[16], acc1[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc0[r] = acc1[r] = 0;
   const v16i zero = {};
-  const int64_t nb = a.nb;
-  v4i qn = {};
-  int32_t Sn = 0;
-  if (nb > 0) {
-    issue(0);
-    qn = __builtin_amdgcn_raw_buffer_load_b128(rcode, lane * 16, 0, 0);
-    Sn = __builtin_amdgcn_raw_buffer_load_b32(rscal, (lane & 31) * 4, 0, 0);
-  }
-  for (int64_t b = 0; b < nb; ++b) {
-    barrier_after_vmcnt<0>();   // block b: limb tiles in LDS (every wave), code tile and scales in registers
-    const v4i q = qn;
-    const int32_t S = Sn;
-    if (b + 1 < nb) {
-      issue(b + 1);             // into the buffer block b - 1 used: every wave is past it
-      qn = __builtin_amdgcn_raw_buffer_load_b128(rcode, lane * 16, (int)(b + 1) * 1024, 0);
-      Sn = __builtin_amdgcn_raw_buffer_load_b32(rscal, (lane & 31) * 4, (int)(b + 1) * 128, 0);
-    }
-    const uint8_t* blk = lds + (int)(b & 1) * kBuf;
+  auto consume = [&](int64_t b, const v4i& q, int32_t S) {
+    const uint8_t* blk = lds + (int)(b % kRing) * kBuf;
     const v4i d0 = *reinterpret_cast<const v4i*>(blk + 0 * 1024 + lane * 16);
     const v4i d1 = *reinterpret_cast<const v4i*>(blk + 1 * 1024 + lane * 16);
     const v4i d2 = *reinterpret_cast<const v4i*>(blk + 2 * 1024 + lane * 16);
@@ -353,6 +345,46 @@ __global__ __launch_bounds__(256) void gemm_tiled_qreg_kernel(GemmArgs a) {
       acc0[r] += (int64_t)S * P01[r];
       acc1[r] += (int64_t)S16 * P2[r];
     }
+  };
+  if constexpr (PF == 1) {
+    // one block ahead: the loop the dense prefill was tuned with (block b's
+    // copies waited for, block b + 1 requested, block b consumed)
+    v4i qn = {};
+    int32_t Sn = 0;
+    if (nb > 0) fetch(0, qn, Sn);
+    for (int64_t b = 0; b < nb; ++b) {
+      barrier_after_vmcnt<0>();   // block b: limb tiles in LDS (every wave), code tile and scales in registers
+      const v4i q = qn;
+      const int32_t S = Sn;
+      if (b + 1 < nb) fetch(b + 1, qn, Sn);   // into the buffer block b - 1 used: every wave is past it
+      consume(b, q, S);
+    }
+  } else {
+  v4i qs[kRing];
+  int32_t Ss[kRing];
+#pragma unroll
+  for (int j = 0; j < PF; ++j)
+    if (j < nb) fetch(j, qs[j], Ss[j]);
+  // iteration b: wait until only the PF - 1 newer fetches are out, so block
+  // b has landed for every wave, then fetch block b + PF into the slot block
+  // b - 1 used (every wave is past it) and consume block b.  Near the end
+  // nothing is fetched and the wait covers everything still out, so no copy
+  // into LDS is in flight once the loop ends.
+  for (int64_t b0 = 0; b0 < nb; b0 += kRing) {
+#pragma unroll
+    for (int j = 0; j < kRing; ++j) {
+      const int64_t b = b0 + j;
+      if (b < nb) {
+        if (b + PF < nb) {
+          barrier_after_vmcnt<(PF - 1) * 3>();
+          fetch(b + PF, qs[(j + PF) % kRing], Ss[(j + PF) % kRing]);
+        } else {
+          barrier_after_vmcnt<0>();
+        }
+        consume(b, qs[j], Ss[j]);
+      }
+    }
+  }
   }
 
   // ---- store: lane holds row 32 (4 rb + wave) + lane % 32 and tokens
@@ -375,20 +407,26 @@ __global__ __launch_bounds__(256) void gemm_tiled_qreg_kernel(GemmArgs a) {
   }
 }
 
+// Prefetch depth: the dense prefill's code tiles are mostly L2 hits (each is
+// read by the token tiles that share its XCD), one block ahead suffices; a
+// routed projection's expert weights serve only a few token tiles and stream
+// from HBM, so its loads go further ahead.
+constexpr int kDensePF = 1, kGroupedPF = 3;
+
 hipError_t launch_gemm_tiled_qreg(const GemmArgs& a, bool grouped, hipStream_t s) {
   const int64_t rbs = (a.n_pad + 127) / 128;
   const int64_t tbs = grouped ? a.tiles_max : a.t_pad / kTile;
   const dim3 grid((unsigned)(rbs * tbs)), block(256);
   const bool exact = a.out_mode == OUT_EXACT;
-  const size_t lds = 2 * 4 * 1024;
+  const size_t lds = (size_t)((grouped ? kGroupedPF : kDensePF) + 1) * 4 * 1024;
   if (grouped && exact)
-    hipLaunchKernelGGL((gemm_tiled_qreg_kernel<true, true>), grid, block, lds, s, a);
+    hipLaunchKernelGGL((gemm_tiled_qreg_kernel<true, true, true, kGroupedPF>), grid, block, lds, s, a);
   else if (grouped)
-    hipLaunchKernelGGL((gemm_tiled_qreg_kernel<false, true>), grid, block, lds, s, a);
+    hipLaunchKernelGGL((gemm_tiled_qreg_kernel<false, true, true, kGroupedPF>), grid, block, lds, s, a);
   else if (exact)
-    hipLaunchKernelGGL((gemm_tiled_qreg_kernel<true, false>), grid, block, lds, s, a);
+    hipLaunchKernelGGL((gemm_tiled_qreg_kernel<true, false, true, kDensePF>), grid, block, lds, s, a);
   else
-    hipLaunchKernelGGL((gemm_tiled_qreg_kernel<false, false>), grid, block, lds, s, a);
+    hipLaunchKernelGGL((gemm_tiled_qreg_kernel<false, false, true, kDensePF>), grid, block, lds, s, a);
   return hipGetLastError();
 }
 
@@ -427,6 +465,7 @@ constexpr int kGuScaleOff = kGuLimbOff + 3 * 1024;
 constexpr int kGuBlockBytes = kGuScaleOff + 8 * 128;
 constexpr int kGuNbuf = 2;
 constexpr int kGuTileBytes = 32 * 33 * 8;          // one wave's 32 x 32 int64 exchange tile (padded rows)
+constexpr int kGateUpPF = 3;                        // narrow form: blocks of operands in flight ahead (ring of 4 x 3 KB)
 
 // NARROW: two int64 accumulators per output, as in the register-fed tiled kernel.
 template <bool NARROW>
@@ -504,26 +543,19 @@ __global__ __launch_bounds__(kGuWaves * 64) __attribute__((amdgpu_waves_per_eu(4
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(codes[is_up ? 1 : 0] + rg * nb * 1024, (uint32_t)(nb * 1024));
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(scales[is_up ? 1 : 0] + rg * nb * 32, (uint32_t)(nb * 128));
     const uint32_t lsoff = (uint32_t)(((int64_t)(wave < 3 ? wave : 0) * tgs + tb) * nb * 1024);
-    auto issue_limb = [&](int64_t b) {
-      if (wave < 3) copy16_to_lds(rlimb, lds + (int)(b & 1) * 3072 + wave * 1024, lane * 16, lsoff + (uint32_t)b * 1024u);
+    // block b (b < nb): limb tiles into LDS slot b % kRing (waves 0-2 copy one
+    // each), code tile and scales into a register set, kGateUpPF blocks ahead:
+    // a wave's fetch is 3 requests for waves 0-2, 2 for the others
+    constexpr int PF = kGateUpPF, kRing = PF + 1;
+    static_assert(kRing * 3072 <= 4 * kGuTileBytes, "the ring fits the allocation of the exchange tiles");
+    auto fetch = [&](int64_t b, v4i& q, int32_t& S) {
+      if (wave < 3)
+        copy16_to_lds(rlimb, lds + (int)(b % kRing) * 3072 + wave * 1024, lane * 16, lsoff + (uint32_t)b * 1024u);
+      q = __builtin_amdgcn_raw_buffer_load_b128(rc, lane * 16, (int)b * 1024, 0);
+      S = __builtin_amdgcn_raw_buffer_load_b32(rs, (lane & 31) * 4, (int)b * 128, 0);
     };
-    v4i qn = {};
-    int32_t Sn = 0;
-    if (nb > 0) {
-      issue_limb(0);
-      qn = __builtin_amdgcn_raw_buffer_load_b128(rc, lane * 16, 0, 0);
-      Sn = __builtin_amdgcn_raw_buffer_load_b32(rs, (lane & 31) * 4, 0, 0);
-    }
-    for (int64_t b = 0; b < nb; ++b) {
-      barrier_after_vmcnt<0>();   // block b: limb tiles in LDS, code tile and scales in registers
-      const v4i q = qn;
-      const int32_t S = Sn;
-      if (b + 1 < nb) {
-        issue_limb(b + 1);        // into the buffer block b - 1 used: every wave is past it
-        qn = __builtin_amdgcn_raw_buffer_load_b128(rc, lane * 16, (int)(b + 1) * 1024, 0);
-        Sn = __builtin_amdgcn_raw_buffer_load_b32(rs, (lane & 31) * 4, (int)(b + 1) * 128, 0);
-      }
-      const uint8_t* blk = lds + (int)(b & 1) * 3072;
+    auto consume = [&](int64_t b, const v4i& q, int32_t S) {
+      const uint8_t* blk = lds + (int)(b % kRing) * 3072;
       const v4i d0 = *reinterpret_cast<const v4i*>(blk + lane * 16);
       const v4i d1 = *reinterpret_cast<const v4i*>(blk + 1024 + lane * 16);
       const v4i d2 = *reinterpret_cast<const v4i*>(blk + 2048 + lane * 16);
@@ -537,6 +569,33 @@ __global__ __launch_bounds__(kGuWaves * 64) __attribute__((amdgpu_waves_per_eu(4
       for (int r = 0; r < 16; ++r) {
         acc[0][r] += (int64_t)S * P01[r];
         acc[NACC - 1][r] += (int64_t)S16 * P2[r];
+      }
+    };
+    v4i qs[kRing];
+    int32_t Ss[kRing];
+#pragma unroll
+    for (int j = 0; j < PF; ++j)
+      if (j < nb) fetch(j, qs[j], Ss[j]);
+    // as in the register-fed kernel: block b has landed for every wave once
+    // only the PF - 1 newer fetches are out; near the end nothing is fetched
+    // and the wait covers everything, so no LDS copy is in flight when the
+    // exchange below reuses this memory
+    for (int64_t b0 = 0; b0 < nb; b0 += kRing) {
+#pragma unroll
+      for (int j = 0; j < kRing; ++j) {
+        const int64_t b = b0 + j;
+        if (b < nb) {
+          if (b + PF < nb) {
+            if (wave < 3)
+              barrier_after_vmcnt<(PF - 1) * 3>();
+            else
+              barrier_after_vmcnt<(PF - 1) * 2>();
+            fetch(b + PF, qs[(j + PF) % kRing], Ss[(j + PF) % kRing]);
+          } else {
+            barrier_after_vmcnt<0>();
+          }
+          consume(b, qs[j], Ss[j]);
+        }
       }
     }
   } else {

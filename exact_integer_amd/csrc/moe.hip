@@ -164,6 +164,109 @@ __global__ __launch_bounds__(kMoeSortThreads) void moe_sort_kernel(const int32_t
   if (tid == 0) *ntiles = (int32_t)total;
 }
 
+// The same grouping for up to kMoeFastExperts experts by a stable counting
+// sort.  The pairs are cut into 16 contiguous wave ranges.  A wave ranks its
+// keys 64 at a time: lanes with the same bucket (expert, or E for an id
+// outside [0, E)) find each other with one ballot per bucket bit, a key's rank
+// is the wave's running count of its bucket plus the matching lanes before it,
+// and the first lane of each bucket adds the group's size to that count.  A
+// scan over the waves per bucket and one over the buckets then place every key:
+// position = bucket start + keys of the bucket in earlier waves + rank in its
+// wave, which is the order (bucket, pair index).  Five barriers in all, against
+// two scans per two-bit pass of the radix sort.
+constexpr int kMoeFastExperts = 255;      // buckets 0 .. E fit 8 bits
+constexpr int kMoeWaves = kMoeSortThreads / 64;
+
+__global__ __launch_bounds__(kMoeSortThreads) void moe_count_sort_kernel(
+    const int32_t* __restrict__ route, int64_t pairs, int64_t experts, int32_t* __restrict__ sorted_pair,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ tile_expert, int32_t* __restrict__ tile_row0,
+    int32_t* __restrict__ tile_rows, int32_t* __restrict__ ntiles, int32_t* status) {
+  __shared__ uint16_t rank_of[kMoeMaxPairs];    // rank of pair i among its bucket's keys in its wave range
+  __shared__ uint8_t bucket_of[kMoeMaxPairs];
+  __shared__ uint16_t cnt[kMoeWaves][256];      // keys per (wave, bucket); then the exclusive base over waves
+  __shared__ uint64_t seg[256];                 // (keys, tiles) of bucket b, then their exclusive prefix
+  __shared__ uint64_t wave_tot[kMoeWaves];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = tid >> 6;
+  const int nb = (int)experts + 1;               // buckets
+  const int per = (int)((pairs + kMoeWaves - 1) / kMoeWaves);   // keys per wave range
+  for (int b = lane; b < 256; b += 64) cnt[wave][b] = 0;
+  // every key's bucket, all route loads in flight at once
+  bool bad = false;
+  for (int i = tid; i < pairs; i += kMoeSortThreads) {
+    const int32_t e = route[i];
+    const int b = (e >= 0 && e < experts) ? e : (int)experts;
+    bad |= b == (int)experts;
+    bucket_of[i] = (uint8_t)b;
+  }
+  if (bad) flag(status, EI_DEV_ROUTE);
+  __syncthreads();
+  const int i0 = wave * per, i1 = (int)(i0 + per < pairs ? i0 + per : pairs);
+  const uint64_t lt = ((uint64_t)1 << lane) - 1;
+  for (int base = i0; base < i1; base += 64) {
+    const int i = base + lane;
+    const bool valid = i < i1;
+    const int b = valid ? bucket_of[i] : 0;
+    uint64_t match = __ballot(valid);
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {
+      const uint64_t ones = __ballot(valid && ((b >> bit) & 1));
+      match &= ((b >> bit) & 1) ? ones : ~ones;
+    }
+    if (valid) {
+      const int prior = cnt[wave][b];
+      rank_of[i] = (uint16_t)(prior + __popcll(match & lt));
+      if ((match & lt) == 0) cnt[wave][b] = (uint16_t)(prior + __popcll(match));   // the bucket's first lane
+    }
+  }
+  __syncthreads();
+  // per bucket: exclusive base over the waves, the bucket's total and tile count
+  uint64_t v = 0;
+  if (tid < 256) {
+    int run = 0;
+    for (int w = 0; w < kMoeWaves; ++w) {
+      const int c = cnt[w][tid];
+      cnt[w][tid] = (uint16_t)run;
+      run += c;
+    }
+    const int tiles = tid < experts ? (run + kTile - 1) / kTile : 0;
+    v = (uint64_t)run | ((uint64_t)tiles << 32);
+  }
+  // exclusive scan of (keys, tiles) over the buckets: threads 0 .. 255 are waves 0 .. 3
+  uint64_t inc = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint64_t u = __shfl_up(inc, d, 64);
+    if (lane >= d) inc += u;
+  }
+  if (lane == 63) wave_tot[wave] = inc;
+  __syncthreads();
+  if (tid < 256) {
+    uint64_t pre = inc - v;
+    for (int w = 0; w < wave; ++w) pre += wave_tot[w];
+    seg[tid] = pre;
+    if (tid <= experts) offsets[tid] = (int32_t)(pre & 0xFFFFFFFFu);
+    if (tid < experts) {
+      const int start = (int)(pre & 0xFFFFFFFFu), keys = (int)(v & 0xFFFFFFFFu);
+      const int t0 = (int)(pre >> 32), nt = (int)(v >> 32);
+      for (int s2 = 0; s2 < nt; ++s2) {
+        const int left = keys - s2 * kTile;
+        tile_expert[t0 + s2] = tid;
+        tile_row0[t0 + s2] = start + s2 * kTile;
+        tile_rows[t0 + s2] = left < kTile ? left : kTile;
+      }
+    }
+    if (tid == 0) *ntiles = (int32_t)((wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3]) >> 32);
+  }
+  __syncthreads();
+  for (int i = tid; i < pairs; i += kMoeSortThreads) {
+    const int b = bucket_of[i];
+    const int w = i / per;
+    sorted_pair[(int)(seg[b] & 0xFFFFFFFFu) + cnt[w][b] + rank_of[i]] = i;
+  }
+  (void)nb;
+}
+
 // Limb tiles of the grouped activations: thread (tile j, block b, lane) takes
 // the 16 activations of half lane / 32 of block b of the row of the pair at
 // sorted position tile_row0[j] + lane % 32 (zeros past the tile's pairs).
@@ -208,6 +311,11 @@ __global__ void grouped_limb_tiles_kernel(const int64_t* __restrict__ x, int64_t
 hipError_t launch_moe_sort(const int32_t* route, int64_t pairs, int64_t experts, int32_t* sorted_pair,
                            int32_t* offsets, int32_t* tile_expert, int32_t* tile_row0, int32_t* tile_rows,
                            int32_t* ntiles, int32_t* status, hipStream_t s) {
+  if (experts <= kMoeFastExperts && pairs <= kMoeMaxPairs) {
+    hipLaunchKernelGGL(moe_count_sort_kernel, dim3(1), dim3(kMoeSortThreads), 0, s, route, pairs, experts,
+                       sorted_pair, offsets, tile_expert, tile_row0, tile_rows, ntiles, status);
+    return hipGetLastError();
+  }
   const int64_t per = (pairs + kMoeSortThreads - 1) / kMoeSortThreads;
   hipLaunchKernelGGL(moe_sort_kernel, dim3(1), dim3(kMoeSortThreads), (size_t)(per * kMoeSortThreads) * 4, s, route,
                      pairs, experts,
