@@ -49,7 +49,7 @@ KERNEL_SOURCES = {GEMV_KERNEL: "gemv.hip", GEMM_KERNEL: "gemm_tiled.hip"}
 # the template instance each timed kernel runs as in the bench step (the routed
 # FFN in the same step runs other instances of the same templates)
 KERNEL_MATCH = {GEMV_KERNEL: "gemv_kernel<3, 1, long, 8, 2, false>",
-                GEMM_KERNEL: "gemm_tiled_qreg_kernel<false, false, true>"}
+                GEMM_KERNEL: "gemm_tiled_qreg_kernel<false, false, true, 1>"}
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 GOLDEN = os.path.join(ROOT, "tests", "golden", "oracle_digests.json")
 
