@@ -714,11 +714,13 @@ def test_q8_grouped_skewed_and_extreme(ei):
     assert (y == _grouped_reference(codes, scales, x, route)).all()
 
 
-@pytest.mark.parametrize("shape", [(100, 1500, 2, 32, 64), (1, 70, 3, 40, 32), (7, 8192, 2, 32, 32)])
+@pytest.mark.parametrize("shape", [(100, 1500, 2, 32, 64), (1, 70, 3, 40, 32), (7, 8192, 2, 32, 32),
+                                   (300, 200, 2, 32, 32)])
 def test_q8_grouped_sort_sizes(ei, shape):
     # pair counts that leave ragged per-thread runs in the grouping sort, up to
     # the 2^14-pair maximum; a single expert; 100 experts (a non-power-of-two
-    # expert field); unsorted routes that may repeat an expert within a row
+    # expert field); 300 experts (more buckets than the counting sort has: the
+    # radix sort); unsorted routes that may repeat an expert within a row
     E, rows, topk, N, K = shape
     r = np.random.default_rng(E + rows)
     codes = np.stack([synth.q8_codes(r, N, K) for _ in range(E)])
@@ -731,14 +733,15 @@ def test_q8_grouped_sort_sizes(ei, shape):
     assert (y == _grouped_reference(codes, scales, x, route)).all()
 
 
-def test_q8_grouped_bad_expert_is_flagged(ei):
-    E, rows, topk, N, K = 3, 8, 2, 32, 64
+@pytest.mark.parametrize("E", [3, 300])   # the counting sort and the radix sort
+def test_q8_grouped_bad_expert_is_flagged(ei, E):
+    rows, topk, N, K = 8, 2, 32, 64
     r = np.random.default_rng(22)
     codes = np.stack([synth.q8_codes(r, N, K) for _ in range(E)])
     scales = np.stack([synth.q8_scales(r, N, K) for _ in range(E)])
     route = np.tile(np.array([[0, 1]], np.int32), (rows, 1))
-    route[3, 1] = 3
-    say("grouped bad expert")
+    route[3, 1] = E
+    say("grouped bad expert", E)
     w = ei.pack_q8_stacked(dev(codes), dev(scales))
     with pytest.raises(ei.EIError):
         ei.gemm_q8_grouped(w, dev(synth.q16_acts(r, rows, K)), dev(route))
