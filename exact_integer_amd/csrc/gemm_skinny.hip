@@ -378,13 +378,15 @@ __global__ __launch_bounds__(64 * W * G) void gemm_skinny_kernel(GemmArgs a) {
 
 constexpr int kSkinnyWaves = 4, kSkinnyDepth = 2;
 
-// Workgroup K splits: about 160 workgroups in all when the row tiles alone are
+// Workgroup K splits: about 140 workgroups in all when the row tiles alone are
 // fewer than 128.  (On the 896 x 4864, T = 30 projection, 6 splits measured
-// 8.5 us with the partial combiner, 9 splits 9.1 us, one split 11.9 us.)
+// 8.5 us with the partial combiner, 9 splits 9.1 us, one split 11.9 us; in the
+// 24-layer FFN chain 3, 4, 5, 6 and 8 splits measured 481, 453, 450, 455 and
+// 459 us.)
 int skinny_splits(int64_t n_pad, int64_t t_pad, int64_t nb) {
   const int64_t wgs = (n_pad / kTile) * (t_pad / kTile);
   if (wgs >= 128) return 1;   // enough row tiles: no partials
-  int64_t ks = (160 + wgs - 1) / wgs;
+  int64_t ks = (140 + wgs - 1) / wgs;
   const int64_t cap = nb / (kSkinnyWaves * 2 * kSkinnyDepth);   // >= two batches per wave
   if (ks > cap) ks = cap;
   if (ks > 64) ks = 64;
