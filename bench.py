@@ -174,7 +174,7 @@ def cpu_model() -> str:
 def cpu_threads() -> int:
     """Threads for the multi-threaded oracle leg: the CPUs this process may run
     on, capped at OMP_NUM_THREADS when that is set (a shared host gives each
-    GPU's jobs a share of its cores, 16 per GPU on the MI355X boxes here)."""
+    GPU's jobs a share of its cores)."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
@@ -228,7 +228,7 @@ def cpu_baseline(q, s, x1, x512, runs: int = 3, t1_seconds: float = 1.0, t512_ro
                   f"{nt} threads and 1 thread; T=512: all {N} rows with {nt} threads, rows 0..{t512_rows_1thread - 1} "
                   f"with 1 thread",
         "cpu_model": cpu_model(), "host_logical_cpus": os.cpu_count(),
-        "threads_note": "threads = the CPUs this process may use, capped at OMP_NUM_THREADS (the box's per-GPU share)",
+        "threads_note": "threads = the CPUs this process may use, capped at OMP_NUM_THREADS (the host's share of CPUs per GPU)",
         "t1_ms": d1_n * 1e3, "t1_ms_1thread": d1_1 * 1e3, "value_1thread": W_BYTES / d1_1 / 1e9,
         "t512_s": p_n, "t512_useful_tops": use_n / p_n / 1e12, "t512_logical_tops": use_n / LIMBS / p_n / 1e12,
         "t512_1thread_s_per_row_sample": p_1, "t512_useful_tops_1thread": use_1 / p_1 / 1e12,
@@ -570,8 +570,8 @@ def main() -> int:
     if args.summarize_sq:
         return summarize_sq(*args.summarize_sq)
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the projection would shard by rows across GPUs, see the design notes)", file=sys.stderr)
+        print(f"bench.py: runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the projection would shard by rows across GPUs)", file=sys.stderr)
         return 2
     if args.profile:
         args.steps, args.warmup, args.no_cpu_baseline = 5, 2, True

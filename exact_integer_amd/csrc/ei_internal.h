@@ -19,7 +19,7 @@ constexpr int kHeaderBytes = 256;
 constexpr int kTile = 32;                   // rows per row group, tokens per token group, columns per block
 constexpr int kTileBytes = 1024;            // one 32x32 int8 tile in MFMA lane order
 constexpr int64_t kMaxK = 262144;           // per-limb int64 sums exact up to here (2^13 blocks x 2^50)
-constexpr int kMaxLimbs = 4;                // limb counts instantiated by this build
+constexpr int kMaxLimbs = 4;                // the largest limb count the kernels are instantiated for
 
 // The packed weight buffer starts with this header (device memory).
 struct PackedHeader {
