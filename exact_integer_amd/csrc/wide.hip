@@ -152,7 +152,7 @@ __global__ __launch_bounds__(256) void wide_gemm_kernel(const int8_t* __restrict
     for (int s = 0; s < kWideDigits + kWideActLimbs - 1; ++s) v += (__int128)acc[s][r] << (8 * s);
     int64_t out;
     ok = fit_i64(v, &out) && ok;
-    y[tok * n + row] = out;
+    __builtin_nontemporal_store(out, y + tok * n + row);   // written once, not read here
   }
   if (!ok) flag(status, EI_DEV_OUT_RANGE);
 }
