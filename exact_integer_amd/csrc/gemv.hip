@@ -21,7 +21,11 @@
 // read back as 16-byte broadcasts (all 32 lanes of a half-wave read the same
 // address).  No workgroup barrier separates staging from use: a wave's LDS
 // operations complete in order.  Large K is staged in chunks of `a.chunk`
-// blocks per wave.
+// blocks per wave.  When the first chunk's activations fit two items of four
+// per lane (T = 1 up to 16 blocks per wave) they are requested before the
+// code tiles, so that their split runs while the code tiles are in flight
+// (loads complete in issue order: issued after the codes, they would be
+// waited for behind them).
 //
 // Scales.  In the ascending order a wave's blocks are contiguous, so the
 // scales of a chunk (128 B per block) arrive in at most four 1 KB wave loads
@@ -102,9 +106,8 @@ __device__ inline void gemv_rows(const GemmArgs& a, int64_t rg, uint8_t* lds) {
     for (int l = 0; l < L; ++l) acc[t][l] = 0;
 
   // Two register batches of D blocks alternate: while one is consumed the
-  // other is in flight, and a consumed batch is refilled at once.  Positions
-  // past the wave's last visit load that block again and count with a zero
-  // scale.
+  // other is in flight.  Positions of a batch past the wave's last visit load
+  // that block again and count with a zero scale.
   v4i qa[D], qb[D];
   int32_t Sa[D], Sb[D];
   auto load = [&](v4i (&q)[D], int32_t (&S)[D], int64_t m0) {
@@ -160,9 +163,27 @@ __device__ inline void gemv_rows(const GemmArgs& a, int64_t rg, uint8_t* lds) {
   };
 
   bool ok = true;
-  // the first two batches go out before anything else
-  // (loads are unconditional so that a refilled batch lands in the registers
-  // the next iteration reads, with no copy that would wait for it)
+  // the first chunk's activations are requested first (at most kXPre items
+  // of 4 per lane, held in registers) so that their split can run while the
+  // code tiles are in flight; then the first two batches of code tiles
+  constexpr int kXPre = 2;
+  const int cb0 = (int)(cnt < chunk ? cnt : chunk);
+  const bool pre = cb0 * T * 8 <= 64 * kXPre;
+  int64_t xv[kXPre][4];
+  if (pre) {
+    const XT* x = static_cast<const XT*>(a.x);
+#pragma unroll
+    for (int i = 0; i < kXPre; ++i) {
+      const int e = lane + 64 * i;
+      if (e < cb0 * T * 8) {
+        const int g = e & 7, t = (e >> 3) % T, s = (e >> 3) / T;
+        const XT* src = x + (int64_t)t * a.k + visit<kGeneric>(a, p0 + s) * 32 + 4 * g;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xv[i][j] = (int64_t)src[j];
+      }
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
   if (cnt > 0) {
     load(qa, Sa, 0);
     load(qb, Sb, D);
@@ -178,16 +199,33 @@ __device__ inline void gemv_rows(const GemmArgs& a, int64_t rg, uint8_t* lds) {
     for (int i = 0; i < kGemvScaleLoads; ++i)
       if (i < nsl)
         sc[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16, (int)(a.b0 + p0 + c0) * 128 + i * 1024, kStream);
-    ok &= stage_limbs<L, T, XT, kGeneric>(a, p0, c0, cb, my, lane);
+    if (pre && c0 == 0) {
+#pragma unroll
+      for (int i = 0; i < kXPre; ++i) {
+        const int e = lane + 64 * i;
+        if (e < cb * T * 8) {
+          const int g = e & 7, t = (e >> 3) % T, s = (e >> 3) / T;
+          uint32_t w[L];
+          ok &= limb_words<L>(xv[i], w);
+#pragma unroll
+          for (int l = 0; l < L; ++l)
+            *reinterpret_cast<uint32_t*>(my + ((s * L + l) * T + t) * 32 + 4 * g) = w[l];
+        }
+      }
+    } else {
+      ok &= stage_limbs<L, T, XT, kGeneric>(a, p0, c0, cb, my, lane);
+    }
 #pragma unroll
     for (int i = 0; i < kGemvScaleLoads; ++i)
       if (i < nsl && lane * 16 + i * 1024 < cb * 128) *reinterpret_cast<v4i*>(mysc + lane * 16 + i * 1024) = sc[i];
     __builtin_amdgcn_wave_barrier();
+    // a consumed batch is refilled at once, up to the wave's last block (no
+    // request past it: with the non-temporal policy its lines may be gone)
     for (int64_t m = c0; m < c0 + cb; m += 2 * D) {
       consume(qa, Sa, m, c0);
-      load(qa, Sa, m + 2 * D);
+      if (m + 2 * D < cnt) load(qa, Sa, m + 2 * D);
       consume(qb, Sb, m + D, c0);
-      load(qb, Sb, m + 3 * D);
+      if (m + 3 * D < cnt) load(qb, Sb, m + 3 * D);
     }
     __builtin_amdgcn_wave_barrier();
   }
@@ -203,8 +241,8 @@ __device__ inline void gemv_rows(const GemmArgs& a, int64_t rg, uint8_t* lds) {
       const int lo = __shfl_xor((int)(uint32_t)v, 32), hi = __shfl_xor((int)(v >> 32), 32);
       acc[t][l] = v + (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
     }
-  __syncthreads();   // every wave is done with its limb slice
-  int64_t* red = reinterpret_cast<int64_t*>(lds);   // [W][32][T][L]
+  // the waves' sums meet in an LDS area of their own, after the limbs and scales
+  int64_t* red = reinterpret_cast<int64_t*>(lds + (size_t)W * chunk * (kSlot + 128));   // [W][32][T][L]
   if (lane < 32) {
 #pragma unroll
     for (int t = 0; t < T; ++t)
@@ -275,8 +313,7 @@ static hipError_t gemv_launch(GemmArgs a, hipStream_t s) {
   if (chunk > per_wave) chunk = per_wave;
   a.chunk = (int)chunk;
   const size_t red = (size_t)W * 32 * T * L * 8;
-  size_t lds = (size_t)W * chunk * (kSlot + 128);   // limbs, then the scales
-  if (lds < red) lds = red;
+  const size_t lds = (size_t)W * chunk * (kSlot + 128) + red;   // limbs, scales, then the waves' sums
   const dim3 grid((unsigned)(a.n_pad / kTile)), block(W * 64);
   const bool generic = a.order != ORDER_ASC || a.out_mode == OUT_TERMS;
   if (a.x_is_i32) {
@@ -308,8 +345,7 @@ static hipError_t gemv_multi_launch(GemmArgs a, const GemvMulti& mm, hipStream_t
   if (chunk > per_wave) chunk = per_wave;
   a.chunk = (int)chunk;
   const size_t red = (size_t)W * 32 * T * L * 8;
-  size_t lds = (size_t)W * chunk * (kSlot + 128);
-  if (lds < red) lds = red;
+  const size_t lds = (size_t)W * chunk * (kSlot + 128) + red;
   hipLaunchKernelGGL((gemv_multi_kernel<L, T, W, D>), dim3((unsigned)mm.rg0[mm.count]), dim3(W * 64), lds, s, a,
                      mm);
   return hipGetLastError();
