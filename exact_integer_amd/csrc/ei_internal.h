@@ -314,11 +314,24 @@ __device__ inline void copy16_to_lds(__amdgpu_buffer_rsrc_t r, uint8_t* dst, uin
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)dst, 16, voffset, soffset, 0, 0);
 }
 
+// Wait until at most N of this wave's vector-memory operations are
+// outstanding, as an instruction the compiler's own wait insertion takes into
+// account (it cannot see into inline asm, and would otherwise add a wait of
+// its own, down to zero, before the first use of a register loaded N
+// requests back).  s_waitcnt fields: vmcnt bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8; the last two are left at their maxima (no wait).
+template <int N>
+__device__ inline void vmcnt_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit count");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Workgroup barrier once at most N of this wave's vector-memory operations
 // (direct-to-LDS copies of later blocks) are outstanding and its LDS reads
 // are done.  __syncthreads would wait for every copy in flight.
 template <int N>
 __device__ inline void barrier_after_vmcnt() {
+  vmcnt_wait<N>();
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 

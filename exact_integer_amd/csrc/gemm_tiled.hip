@@ -317,10 +317,10 @@ __global__ __launch_bounds__(256) void gemm_tiled_qreg_kernel(GemmArgs a) {
   const uint32_t lsoff = (uint32_t)(((int64_t)(wave < 3 ? wave : 0) * tgs + tg) * a.nb * 1024);
   const int ldst = wave * 1024;
   const int64_t nb = a.nb;
-  // block b's operands (b < nb): its limb tiles into LDS slot b % kRing (every
+  // block b's operands (b < nb): its limb tiles into LDS slot `slot` (every
   // wave one copy), its code tile and scales into a register set: 3 requests
-  auto fetch = [&](int64_t b, v4i& q, int32_t& S) {
-    copy16_to_lds(rlimb, lds + (int)(b % kRing) * kBuf + ldst, lane * 16, lsoff + (uint32_t)b * 1024u);
+  auto fetch = [&](int slot, int64_t b, v4i& q, int32_t& S) {
+    copy16_to_lds(rlimb, lds + slot * kBuf + ldst, lane * 16, lsoff + (uint32_t)b * 1024u);
     q = __builtin_amdgcn_raw_buffer_load_b128(rcode, lane * 16, (int)b * 1024, 0);
     S = __builtin_amdgcn_raw_buffer_load_b32(rscal, (lane & 31) * 4, (int)b * 128, 0);
   };
@@ -329,8 +329,8 @@ __global__ __launch_bounds__(256) void gemm_tiled_qreg_kernel(GemmArgs a) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc0[r] = acc1[r] = 0;
   const v16i zero = {};
-  auto consume = [&](int64_t b, const v4i& q, int32_t S) {
-    const uint8_t* blk = lds + (int)(b % kRing) * kBuf;
+  auto consume = [&](int slot, const v4i& q, int32_t S) {
+    const uint8_t* blk = lds + slot * kBuf;
     const v4i d0 = *reinterpret_cast<const v4i*>(blk + 0 * 1024 + lane * 16);
     const v4i d1 = *reinterpret_cast<const v4i*>(blk + 1 * 1024 + lane * 16);
     const v4i d2 = *reinterpret_cast<const v4i*>(blk + 2 * 1024 + lane * 16);
@@ -351,40 +351,45 @@ __global__ __launch_bounds__(256) void gemm_tiled_qreg_kernel(GemmArgs a) {
     // copies waited for, block b + 1 requested, block b consumed)
     v4i qn = {};
     int32_t Sn = 0;
-    if (nb > 0) fetch(0, qn, Sn);
+    if (nb > 0) fetch(0, 0, qn, Sn);
     for (int64_t b = 0; b < nb; ++b) {
       barrier_after_vmcnt<0>();   // block b: limb tiles in LDS (every wave), code tile and scales in registers
       const v4i q = qn;
       const int32_t S = Sn;
-      if (b + 1 < nb) fetch(b + 1, qn, Sn);   // into the buffer block b - 1 used: every wave is past it
-      consume(b, q, S);
+      if (b + 1 < nb) fetch((int)((b + 1) % kRing), b + 1, qn, Sn);   // into the buffer block b - 1 used: every wave is past it
+      consume((int)(b % kRing), q, S);
     }
   } else {
+  // Ring turns: iteration b waits until only the PF - 1 newer fetches are
+  // out, so block b has landed for every wave, fetches block b + PF into the
+  // slot block b - 1 used (every wave is past it) and consumes block b.  No
+  // fetch sits under a branch -- one the compiler cannot rule out would make
+  // it drain every load before the first use of a register set -- so the
+  // loop runs whole turns of the ring: fetches past the last block re-read
+  // it, and blocks past the last are consumed with scale 0 (adding nothing).
   v4i qs[kRing];
   int32_t Ss[kRing];
+  // (scheduling barriers keep each fetch in its place: requests in block
+  // order, and no load moved across the multiply-adds it would keep
+  // registers live through)
 #pragma unroll
-  for (int j = 0; j < PF; ++j)
-    if (j < nb) fetch(j, qs[j], Ss[j]);
-  // iteration b: wait until only the PF - 1 newer fetches are out, so block
-  // b has landed for every wave, then fetch block b + PF into the slot block
-  // b - 1 used (every wave is past it) and consume block b.  Near the end
-  // nothing is fetched and the wait covers everything still out, so no copy
-  // into LDS is in flight once the loop ends.
-  for (int64_t b0 = 0; b0 < nb; b0 += kRing) {
+  for (int j = 0; j < PF; ++j) {
+    fetch(j, j < nb ? j : nb - 1, qs[j], Ss[j]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const int64_t turns = (nb + kRing - 1) / kRing;
+  for (int64_t t = 0; t < turns; ++t) {
 #pragma unroll
     for (int j = 0; j < kRing; ++j) {
-      const int64_t b = b0 + j;
-      if (b < nb) {
-        if (b + PF < nb) {
-          barrier_after_vmcnt<(PF - 1) * 3>();
-          fetch(b + PF, qs[(j + PF) % kRing], Ss[(j + PF) % kRing]);
-        } else {
-          barrier_after_vmcnt<0>();
-        }
-        consume(b, qs[j], Ss[j]);
-      }
+      const int64_t b = t * kRing + j;
+      barrier_after_vmcnt<(PF - 1) * 3>();
+      fetch((j + PF) % kRing, b + PF < nb ? b + PF : nb - 1, qs[(j + PF) % kRing], Ss[(j + PF) % kRing]);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(j, qs[j], b < nb ? Ss[j] : 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
+  vmcnt_wait<0>();   // the re-reads past the end have landed before the wave ends
   }
 
   // ---- store: lane holds row 32 (4 rb + wave) + lane % 32 and tokens
@@ -545,19 +550,24 @@ __global__ __launch_bounds__(kGuWaves * 64) __attribute__((amdgpu_waves_per_eu(4
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(codes[is_up ? 1 : 0] + rg * nb * 1024, (uint32_t)(nb * 1024));
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(scales[is_up ? 1 : 0] + rg * nb * 32, (uint32_t)(nb * 128));
     const uint32_t lsoff = (uint32_t)(((int64_t)(wave < 3 ? wave : 0) * tgs + tb) * nb * 1024);
-    // block b (b < nb): limb tiles into LDS slot b % kRing (waves 0-2 copy one
-    // each), code tile and scales into a register set, kGateUpPF blocks ahead:
-    // a wave's fetch is 3 requests for waves 0-2, 2 for the others
+    // block b (b < nb): limb tiles into LDS slot `slot` (waves 0-2 copy one
+    // each; the others issue the same copy against an empty buffer range,
+    // which reads nothing, into a spare kilobyte, so that every wave issues
+    // the same three requests per block on one path, and the compiler's wait
+    // tracking follows that count), code tile and scales into a register
+    // set, kGateUpPF blocks ahead
     constexpr int PF = kGateUpPF, kRing = PF + 1;
-    static_assert(kRing * 3072 <= 4 * kGuTileBytes, "the ring fits the allocation of the exchange tiles");
-    auto fetch = [&](int64_t b, v4i& q, int32_t& S) {
-      if (wave < 3)
-        copy16_to_lds(rlimb, lds + (int)(b % kRing) * 3072 + wave * 1024, lane * 16, lsoff + (uint32_t)b * 1024u);
+    constexpr int kSlot = 4 * 1024;
+    static_assert(kRing * kSlot <= 4 * kGuTileBytes, "the ring fits the allocation of the exchange tiles");
+    const __amdgpu_buffer_rsrc_t rcopy = wave < 3 ? rlimb : make_rsrc(a.limb_tiles, 0u);
+    const int cdst = (wave < 3 ? wave : 3) * 1024;
+    auto fetch = [&](int slot, int64_t b, v4i& q, int32_t& S) {
+      copy16_to_lds(rcopy, lds + slot * kSlot + cdst, lane * 16, lsoff + (uint32_t)b * 1024u);
       q = __builtin_amdgcn_raw_buffer_load_b128(rc, lane * 16, (int)b * 1024, 0);
       S = __builtin_amdgcn_raw_buffer_load_b32(rs, (lane & 31) * 4, (int)b * 128, 0);
     };
-    auto consume = [&](int64_t b, const v4i& q, int32_t S) {
-      const uint8_t* blk = lds + (int)(b % kRing) * 3072;
+    auto consume = [&](int slot, const v4i& q, int32_t S) {
+      const uint8_t* blk = lds + slot * kSlot;
       const v4i d0 = *reinterpret_cast<const v4i*>(blk + lane * 16);
       const v4i d1 = *reinterpret_cast<const v4i*>(blk + 1024 + lane * 16);
       const v4i d2 = *reinterpret_cast<const v4i*>(blk + 2048 + lane * 16);
@@ -573,33 +583,33 @@ __global__ __launch_bounds__(kGuWaves * 64) __attribute__((amdgpu_waves_per_eu(4
         acc[NACC - 1][r] += (int64_t)S16 * P2[r];
       }
     };
+    // Ring turns as in the register-fed kernel: iteration b waits until only
+    // the PF - 1 newer fetches are out (block b has landed for every wave),
+    // fetches block b + PF into the slot block b - 1 used (every wave is past
+    // it) and consumes block b.  No fetch sits under a branch (one the
+    // compiler cannot rule out would make it drain every load before a first
+    // use); fetches past the last block re-read it.
     v4i qs[kRing];
     int32_t Ss[kRing];
 #pragma unroll
-    for (int j = 0; j < PF; ++j)
-      if (j < nb) fetch(j, qs[j], Ss[j]);
-    // as in the register-fed kernel: block b has landed for every wave once
-    // only the PF - 1 newer fetches are out; near the end nothing is fetched
-    // and the wait covers everything, so no LDS copy is in flight when the
-    // exchange below reuses this memory
-    for (int64_t b0 = 0; b0 < nb; b0 += kRing) {
+    for (int j = 0; j < PF; ++j) {
+      fetch(j, j < nb ? j : nb - 1, qs[j], Ss[j]);
+      __builtin_amdgcn_sched_barrier(0);   // requests in block order
+    }
+    const int64_t turns = (nb + kRing - 1) / kRing;
+    for (int64_t t = 0; t < turns; ++t) {
 #pragma unroll
       for (int j = 0; j < kRing; ++j) {
-        const int64_t b = b0 + j;
-        if (b < nb) {
-          if (b + PF < nb) {
-            if (wave < 3)
-              barrier_after_vmcnt<(PF - 1) * 3>();
-            else
-              barrier_after_vmcnt<(PF - 1) * 2>();
-            fetch(b + PF, qs[(j + PF) % kRing], Ss[(j + PF) % kRing]);
-          } else {
-            barrier_after_vmcnt<0>();
-          }
-          consume(b, qs[j], Ss[j]);
-        }
+        const int64_t b = t * kRing + j;
+        if (b >= nb) break;
+        barrier_after_vmcnt<(PF - 1) * 3>();
+        fetch((j + PF) % kRing, b + PF < nb ? b + PF : nb - 1, qs[(j + PF) % kRing], Ss[(j + PF) % kRing]);
+        __builtin_amdgcn_sched_barrier(0);
+        consume(j, qs[j], Ss[j]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
+    barrier_after_vmcnt<0>();   // no LDS copy in flight when the exchange below reuses this memory
   } else {
     if (nb > 0) issue(0);
     for (int64_t b = 0; b < nb; ++b) {
