@@ -148,19 +148,44 @@ __global__ __launch_bounds__(64 * W * G) void gemm_skinny_kernel(GemmArgs a) {
         }
       }
     };
-    // no load past the range: a copy still in flight at the reduction's
-    // barrier would hold every wave until it lands
     SkinnyBatch<L, D> A, B;
-    load(A, w0);
-    for (int64_t pos = w0;; pos += 2 * D) {
-      const bool more_b = pos + D < w1;
-      if (more_b) load(B, pos + D);
-      compute(A, pos);
-      if (!more_b) break;
-      const bool more_a = pos + 2 * D < w1;
-      if (more_a) load(A, pos + 2 * D);
-      compute(B, pos + D);
-      if (!more_a) break;
+    if constexpr (G == 1) {
+      // two batches in flight, a consumed batch refilled at once; no load
+      // sits under a branch (the compiler's own waits would otherwise assume
+      // the fewest requests after a load and wait for nearly all of them), so
+      // past the range the refills re-read the last block (cache hits).
+      // Scheduling barriers keep every load where it is written: the
+      // scheduler would otherwise sink a batch's loads to its first use.
+      load(A, w0);
+      __builtin_amdgcn_sched_barrier(0);
+      load(B, w0 + D);
+      __builtin_amdgcn_sched_barrier(0);
+      for (int64_t pos = w0;; pos += 2 * D) {
+        compute(A, pos);
+        if (pos + D >= w1) break;
+        __builtin_amdgcn_sched_barrier(0);
+        load(A, pos + 2 * D);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(B, pos + D);
+        __builtin_amdgcn_sched_barrier(0);
+        load(B, pos + 3 * D);   // before the exit test: no path back to the top skips it
+        __builtin_amdgcn_sched_barrier(0);
+        if (pos + 2 * D >= w1) break;
+      }
+    } else {
+      // the gate/up pair at 256 VGPRs: batches loaded only inside the range
+      // (the form above spills here)
+      load(A, w0);
+      for (int64_t pos = w0;; pos += 2 * D) {
+        const bool more_b = pos + D < w1;
+        if (more_b) load(B, pos + D);
+        compute(A, pos);
+        if (!more_b) break;
+        const bool more_a = pos + 2 * D < w1;
+        if (more_a) load(A, pos + 2 * D);
+        compute(B, pos + D);
+        if (!more_a) break;
+      }
     }
   }
 
