@@ -301,10 +301,19 @@ __global__ __launch_bounds__(256) void gemm_tiled_qreg_kernel(GemmArgs a) {
   const int64_t rgs = a.n_pad / kTile, tgs = kGrouped ? a.tiles_max : a.t_pad / kTile;
   const int8_t* codes = a.codes;
   const int32_t* scales = a.scales;
+  int trows = kTile;   // pairs in this token tile
   if (kGrouped) {
     const int64_t e = a.tile_expert[tb];
     codes += e * a.expert_stride;
     scales = reinterpret_cast<const int32_t*>(reinterpret_cast<const int8_t*>(scales) + e * a.expert_stride);
+    // the output rows of the tile's tokens, copied now into this wave's 256 B
+    // after the ring (lanes 32-63 repeat lanes 0-31) and read at the end: no
+    // dependent load in the epilogue, and no register held through the loop
+    trows = a.tile_rows[tb];
+    const int l = lane & 31;
+    const __amdgpu_buffer_rsrc_t rpair = make_rsrc(a.sorted_pair, (uint32_t)(a.t * 4));   // a.t: the pairs
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rpair, (lds_ptr)(lds + kRing * kBuf + wave * 256), 4,
+                                             (uint32_t)(a.tile_row0[tb] + (l < trows ? l : trows - 1)) * 4u, 0, 0, 0);
   }
   int64_t rg = 4 * rb + wave;     // this wave's row tile (past the matrix: the last one, results unused)
   rg = rg < rgs ? rg : rgs - 1;
@@ -331,19 +340,38 @@ __global__ __launch_bounds__(256) void gemm_tiled_qreg_kernel(GemmArgs a) {
   const v16i zero = {};
   auto consume = [&](int slot, const v4i& q, int32_t S) {
     const uint8_t* blk = lds + slot * kBuf;
-    const v4i d0 = *reinterpret_cast<const v4i*>(blk + 0 * 1024 + lane * 16);
-    const v4i d1 = *reinterpret_cast<const v4i*>(blk + 1 * 1024 + lane * 16);
-    const v4i d2 = *reinterpret_cast<const v4i*>(blk + 2 * 1024 + lane * 16);
-    v16i c = __builtin_amdgcn_mfma_i32_32x32x32_i8(d1, q, zero, 0, 0, 0);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) c[r] = (int)((uint32_t)c[r] << 8);
-    const v16i P01 = __builtin_amdgcn_mfma_i32_32x32x32_i8(d0, q, c, 0, 0, 0);   // P_0 + 2^8 P_1
-    const v16i P2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(d2, q, zero, 0, 0, 0);
     const int32_t S16 = (int32_t)((uint32_t)S << 16);
+    const v4i d2 = *reinterpret_cast<const v4i*>(blk + 2 * 1024 + lane * 16);
+    if constexpr (kGrouped) {
+      // (2^16 S) P_2 first, then S (P_0 + 2^8 P_1): one product tile live at
+      // a time, which leaves room for the grouped launch's ring depth (117
+      // VGPRs against 130, 4 waves per SIMD instead of 3); the dense loop is
+      // as fast either way and keeps the other order
+      const v16i P2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(d2, q, zero, 0, 0, 0);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      acc0[r] += (int64_t)S * P01[r];
-      acc1[r] += (int64_t)S16 * P2[r];
+      for (int r = 0; r < 16; ++r) acc1[r] += (int64_t)S16 * P2[r];
+      __builtin_amdgcn_sched_barrier(0);
+      const v4i d0 = *reinterpret_cast<const v4i*>(blk + 0 * 1024 + lane * 16);
+      const v4i d1 = *reinterpret_cast<const v4i*>(blk + 1 * 1024 + lane * 16);
+      v16i c = __builtin_amdgcn_mfma_i32_32x32x32_i8(d1, q, zero, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) c[r] = (int)((uint32_t)c[r] << 8);
+      const v16i P01 = __builtin_amdgcn_mfma_i32_32x32x32_i8(d0, q, c, 0, 0, 0);   // P_0 + 2^8 P_1
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc0[r] += (int64_t)S * P01[r];
+    } else {
+      const v4i d0 = *reinterpret_cast<const v4i*>(blk + 0 * 1024 + lane * 16);
+      const v4i d1 = *reinterpret_cast<const v4i*>(blk + 1 * 1024 + lane * 16);
+      v16i c = __builtin_amdgcn_mfma_i32_32x32x32_i8(d1, q, zero, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) c[r] = (int)((uint32_t)c[r] << 8);
+      const v16i P01 = __builtin_amdgcn_mfma_i32_32x32x32_i8(d0, q, c, 0, 0, 0);   // P_0 + 2^8 P_1
+      const v16i P2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(d2, q, zero, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        acc0[r] += (int64_t)S * P01[r];
+        acc1[r] += (int64_t)S16 * P2[r];
+      }
     }
   };
   if constexpr (PF == 1) {
@@ -401,8 +429,8 @@ __global__ __launch_bounds__(256) void gemm_tiled_qreg_kernel(GemmArgs a) {
     const int tloc = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
     int64_t orow;
     if (kGrouped) {
-      if (tloc >= a.tile_rows[tb]) continue;
-      orow = a.sorted_pair[a.tile_row0[tb] + tloc];
+      if (tloc >= trows) continue;
+      orow = reinterpret_cast<const int32_t*>(lds + kRing * kBuf + wave * 256)[tloc];
     } else {
       orow = tb * kTile + tloc;
       if (orow >= a.t) continue;
@@ -425,7 +453,8 @@ hipError_t launch_gemm_tiled_qreg(const GemmArgs& a, bool grouped, hipStream_t s
   const int64_t tbs = grouped ? a.tiles_max : a.t_pad / kTile;
   const dim3 grid((unsigned)(rbs * tbs)), block(256);
   const bool exact = a.out_mode == OUT_EXACT;
-  const size_t lds = (size_t)((grouped ? kGroupedPF : kDensePF) + 1) * 4 * 1024;
+  // the ring; grouped: and 256 B per wave for the tile's output rows
+  const size_t lds = (size_t)((grouped ? kGroupedPF : kDensePF) + 1) * 4 * 1024 + (grouped ? 4 * 256 : 0);
   if (grouped && exact)
     hipLaunchKernelGGL((gemm_tiled_qreg_kernel<true, true, true, kGroupedPF>), grid, block, lds, s, a);
   else if (grouped)
