@@ -526,6 +526,30 @@ int ffn_run(const ei_weights* wg, const ei_weights* wu, const ei_weights* wd, co
       return EI_EDEVICE;
     const int8_t* h_limbs = reinterpret_cast<const int8_t*>(ws + f.h_off);
     const WsLayout ld = layout_for(wd, t, 3, EI_SCHED_DEFAULT);
+    if (!next_gnorm && narrow_scales(wd->smax, wd->nb) && skinny16_finish_fits(wd->n, wd->nb, t)) {
+      // the down projection in one launch on 16 x 16 tiles: y = x + result,
+      // and the next layer's input limb tiles, with no split-K combiner
+      GemmArgs b;
+      std::memset(&b, 0, sizeof b);
+      const uint8_t* bd = static_cast<const uint8_t*>(wd->packed);
+      b.codes = reinterpret_cast<const int8_t*>(bd + kHeaderBytes);
+      b.scales = reinterpret_cast<const int32_t*>(bd + kHeaderBytes + wd->n_pad * wd->k);
+      b.limb_tiles = h_limbs;
+      b.resid = x;
+      b.y = y;
+      b.limb_out = out_limbs;
+      b.status = d_status;
+      b.n = wd->n;
+      b.k = wd->k;
+      b.t = t;
+      b.n_pad = wd->n_pad;
+      b.t_pad = lay.t_pad;
+      b.nb = wd->nb;
+      b.b0 = 0;
+      b.b1 = wd->nb;
+      b.out_mode = OUT_ROUND_Q24;
+      return launch_skinny16_finish(b, s) == hipSuccess ? EI_OK : EI_EDEVICE;
+    }
     if (out_limbs && ld.path == PATH_SKINNY && ld.splits > 1) {
       // split-K down projection whose combiner also writes the next input's limb tiles
       GemmArgs b;

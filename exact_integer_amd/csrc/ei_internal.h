@@ -189,6 +189,12 @@ hipError_t launch_combine_hr_tiles(const int64_t* part, int nparts, int64_t* y, 
                                    hipStream_t s);   // Q8 rounding; n % 32 == 0
 hipError_t launch_add_residual(int64_t* y, const int64_t* resid, int64_t n, int32_t* status, hipStream_t s);
 hipError_t launch_gemm_skinny_gateup(const GemmArgs& a, bool narrow, hipStream_t s);   // 3 limbs, one split
+// A projection with narrow scales at t <= 64 in one launch on 16 x 16 tiles:
+// y = resid + Q8-rounded result, and, if a.limb_out is set, y's limb tiles
+// [3][t_pad/32][n/32][1 KB] (n % 32 == 0).  skinny16_finish_fits: the shapes
+// it takes.
+bool skinny16_finish_fits(int64_t n, int64_t nb, int64_t t);
+hipError_t launch_skinny16_finish(const GemmArgs& a, hipStream_t s);
 hipError_t launch_tree_terms(int64_t* terms, int64_t nb, int64_t* y, int64_t t, int64_t n,
                              int limbs, int out_mode, int32_t* status, hipStream_t s);
 hipError_t launch_make_perm(int32_t* perm, int64_t n, uint64_t seed, hipStream_t s);

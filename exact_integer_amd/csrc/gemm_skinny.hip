@@ -465,3 +465,138 @@ hipError_t launch_gemm_skinny_gateup(const GemmArgs& a, bool narrow, hipStream_t
 }
 
 }  // namespace ei
+
+namespace ei {
+
+// ================================================================ finishing down projection, 16 x 16 tiles
+// The down projection of an FFN layer at up to 32 tokens, without a split of
+// K across workgroups, so that no combiner launch follows it.  A 32-row tile
+// gives too few workgroups (28 for 896 rows) to pull the weights, so this
+// kernel works on 16-row x 16-token tiles with v_mfma_i32_16x16x32_i8 (lane
+// l holds A[l % 16][8 (l / 16) .. +7] of the 16 x 32 limb operand,
+// B[8 (l / 16) .. +7][l % 16] of the 32 x 16 code operand and D[4 (l / 16) +
+// i][l % 16] of the result): 56 x 2 workgroups for 896 rows and 30 tokens.
+// The operands are read straight from the 1 KB tiles of the 32 x 32 layout
+// (an 8-byte piece of a lane's 16 bytes there).  The W waves of a workgroup
+// split the K blocks; each wave requests all of its blocks at once (past its
+// range the loads point outside the buffers and read nothing), accumulates
+// the narrow form's two chains, and the waves' int64 totals meet in LDS.  One
+// thread per output then forms y = resid + floor((acc + 2^23) / 2^24) and, if
+// asked, y's balanced base-256 digits as the next layer's limb tiles (tile
+// (l, token / 32, row / 32), lane (token % 32) + 32 ((row % 32) / 16), byte
+// row % 16) -- the work of the split-K combiner.  Narrow scales only.
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+constexpr int kNonTemporal = 2;   // buffer-load cache policy bit: the weights are read once
+constexpr int kF16Waves = 16;
+constexpr int kF16MaxBlocks = 10;   // blocks per wave at most (K <= 16 x 10 x 32 = 5,120)
+
+// MB: blocks per wave at most (the launch takes the smallest instance that
+// holds ceil(nb / W)); every slot is computed, past cnt with scale 0, so the
+// loop has no branch for the compiler to wait around
+template <int MB>
+__global__ __launch_bounds__(64 * kF16Waves) void skinny16_finish_kernel(GemmArgs a) {
+  constexpr int W = kF16Waves;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t rt = blockIdx.x, th = blockIdx.y;   // 16-row tile, 16-token half
+  const int64_t rg = rt >> 1, rh = rt & 1;           // its 32-row group and half
+  const int64_t nb = a.nb, tgs = a.t_pad / kTile;
+  const int64_t w0 = wave * nb / W, cnt = (wave + 1) * nb / W - w0;   // cnt <= MB (checked on the host)
+  const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.codes + rg * nb * 1024, (uint32_t)(nb * 1024));
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scales + rg * nb * 32, (uint32_t)(nb * 128));
+  const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.limb_tiles, (uint32_t)(3 * tgs * nb * 1024));
+  const int vo_end = (int)(3 * tgs * nb * 1024);   // at or past the end of all three ranges
+  const int q = lane >> 4;
+  // token 16 th + lane % 16 of the 32-token tile th / 2, k piece q
+  const int64_t tg = th >> 1;
+  const int vo_limb = (int)(((16 * (th & 1) + (lane & 15)) + 32 * (q >> 1)) * 16 + 8 * (q & 1));
+  const int vo_code = (int)(((16 * rh + (lane & 15)) + 32 * (q >> 1)) * 16 + 8 * (q & 1));
+  const int vo_scale = (int)((16 * rh + (lane & 15)) * 4);
+
+  // the residual of this thread's output (threads 0-255, one output each),
+  // requested first so that the epilogue does not wait for it
+  const int tl = (threadIdx.x >> 4) & 15, rl16 = threadIdx.x & 15;   // token tl of the half, row rl16 of the tile
+  const int64_t tok = 16 * th + tl, row = 16 * rt + rl16;
+  const bool mine = threadIdx.x < 256 && tok < a.t && row < a.n;
+  const int64_t resid = mine ? a.resid[tok * a.n + row] : 0;
+  int64_t code[MB], d[MB][3];
+  int32_t S[MB];
+#pragma unroll
+  for (int u = 0; u < MB; ++u) {
+    const bool live = u < cnt;
+    const int b = live ? (int)(w0 + u) : 0;
+    const v2u c2 = __builtin_amdgcn_raw_buffer_load_b64(rc, live ? vo_code : vo_end, b * 1024, kNonTemporal);
+    code[u] = (int64_t)(((uint64_t)c2[1] << 32) | c2[0]);
+    S[u] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, live ? vo_scale : vo_end, b * 128, kNonTemporal);
+#pragma unroll
+    for (int l = 0; l < 3; ++l) {
+      const v2u d2 = __builtin_amdgcn_raw_buffer_load_b64(rl, live ? vo_limb : vo_end,
+                                                           (int)(((l * tgs + tg) * nb + b) * 1024), 0);
+      d[u][l] = (int64_t)(((uint64_t)d2[1] << 32) | d2[0]);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // requests in block order: block u is waited for alone
+  }
+  int64_t acc0[4] = {0, 0, 0, 0}, acc1[4] = {0, 0, 0, 0};
+  const v4i zero = {0, 0, 0, 0};
+#pragma unroll
+  for (int u = 0; u < MB; ++u) {
+    const int32_t Su = u < cnt ? S[u] : 0;
+    v4i c = __builtin_amdgcn_mfma_i32_16x16x32_i8(d[u][1], code[u], zero, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c[i] = (int)((uint32_t)c[i] << 8);
+    const v4i P01 = __builtin_amdgcn_mfma_i32_16x16x32_i8(d[u][0], code[u], c, 0, 0, 0);   // P_0 + 2^8 P_1
+    const v4i P2 = __builtin_amdgcn_mfma_i32_16x16x32_i8(d[u][2], code[u], zero, 0, 0, 0);
+    const int32_t S16 = (int32_t)((uint32_t)Su << 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc0[i] += (int64_t)Su * P01[i];
+      acc1[i] += (int64_t)S16 * P2[i];
+    }
+  }
+
+  // the waves' totals (each a sum over a subset of blocks: |.| < 2^62.01)
+  __shared__ int64_t red[W][4][64];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) red[wave][i][lane] = acc0[i] + acc1[i];
+  __syncthreads();
+  if (!mine) return;
+  const int src_lane = rl16 + 16 * (tl >> 2), src_i = tl & 3;
+  int64_t v = 0;
+#pragma unroll
+  for (int w = 0; w < W; ++w) v += red[w][src_i][src_lane];
+  const int64_t e = tok * a.n + row;
+  int64_t out;
+  bool ok = fit_i64((__int128)resid + ((v + ((int64_t)1 << 23)) >> 24), &out);   // |v| < 2^62.01: no overflow
+  a.y[e] = out;
+  if (a.limb_out) {
+    // balanced digits: the bytes of out + 0x808080, each less 0x80
+    const uint64_t u = (uint64_t)out + 0x808080u;
+    if (u >> 24) flag(a.status, EI_DEV_LIMB_RANGE);
+    const int64_t nbo = a.n / 32, lane16 = (tok % 32) + 32 * ((row % 32) / 16);
+#pragma unroll
+    for (int l = 0; l < 3; ++l)
+      a.limb_out[((((int64_t)l * tgs + tg) * nbo + row / 32) * 64 + lane16) * 16 + (row % 16)] =
+          (int8_t)(((u >> (8 * l)) & 0xFF) ^ 0x80);
+  }
+  if (!ok) flag(a.status, EI_DEV_OUT_RANGE);
+}
+
+bool skinny16_finish_fits(int64_t n, int64_t nb, int64_t t) {
+  return n % 32 == 0 && t <= 2 * kTile && nb <= (int64_t)kF16Waves * kF16MaxBlocks && nb >= kF16Waves;
+}
+
+hipError_t launch_skinny16_finish(const GemmArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)(a.n / 16), (unsigned)((a.t + 15) / 16)), block(64 * kF16Waves);
+  const int64_t per = (a.nb + kF16Waves - 1) / kF16Waves;   // blocks of the busiest wave
+  if (per <= 4)
+    hipLaunchKernelGGL(skinny16_finish_kernel<4>, grid, block, 0, s, a);
+  else if (per <= 6)
+    hipLaunchKernelGGL(skinny16_finish_kernel<6>, grid, block, 0, s, a);
+  else if (per <= 8)
+    hipLaunchKernelGGL(skinny16_finish_kernel<8>, grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL(skinny16_finish_kernel<kF16MaxBlocks>, grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace ei

@@ -290,14 +290,18 @@ def test_qwen_ffn_schedule_gate(ei):
 
 
 @pytest.mark.parametrize("shape", [(96, 64, 1), (96, 64, 3), (160, 96, 30), (128, 64, 40), (64, 4096, 30),
-                                   (4096, 64, 30), (96, 160, 70), (32, 320, 5), (4096, 1024, 30), (4096, 1056, 30)])
+                                   (4096, 64, 30), (96, 160, 70), (32, 320, 5), (4096, 1024, 30), (4096, 1056, 30),
+                                   (1056, 64, 17), (5120, 96, 16), (800, 64, 40), (5152, 64, 30)])
 def test_ffn_q8_matches_the_separate_steps(ei, lut, shape):
     # one layer through int_ffn_q8 against the oracle's gate, up, SiLU
     # product, down projection and residual: the fused gate/up pass (5..63
     # tokens with one workgroup split), the GEMV path, the tiled path, the
     # unfused path, and split-K partials (with the residual) on the down
     # projection; K = 1024 is the largest the fused pass stages in LDS
-    # (152 KB with its exchange buffers), K = 1056 the smallest it does not
+    # (152 KB with its exchange buffers), K = 1056 the smallest it does not.
+    # The one-launch down projection on 16 x 16 tiles takes 16..160 blocks:
+    # 33 (ragged over its 16 waves), 160 (the most), 25 (a token half of 8),
+    # and 161 blocks falls back to split-K
     F, D, T = shape
     r = np.random.default_rng(F + D + T)
     mats = [(synth.q8_codes(r, F, D), synth.q8_scales(r, F, D)), (synth.q8_codes(r, F, D), synth.q8_scales(r, F, D)),
