@@ -21,7 +21,12 @@ Parity status of each function and the test that pins it:
   q4          brute force, m = 1 / e = 0 reductions, the table-read
               derivation;
   silu_lut, silu_mul   closed forms, float64 and page clip figures, brute force;
-  limb_split  exhaustive over the 3-limb range;
+  limb_split  exhaustive over the 3-limb range, and with the 4-bit offset
+              over the whole int16 range;
+  q4_row_offsets       equal to q4 at x = 128 everywhere, and the two-limb
+              form (q4 of each digit vector, weighted, plus the offsets)
+              equal to q4, with planted mistakes caught
+              (test_q4_row_offsets_*, test_q4_offset_mutants_are_caught);
   ffn_layer   composed from brute-force q8 and silu_mul (test_ffn_layer_*);
   ffn_layer_prenorm    composed from a Fraction/Decimal RMSNorm and brute-force
               q8 and silu_mul, with planted mistakes (residual from the norm,
@@ -144,6 +149,34 @@ def q4(nib: np.ndarray, sme: np.ndarray, x: np.ndarray, derivation: str = "defin
     return y
 
 
+Q4_OFFSET = 128
+
+
+def q4_row_offsets(nib: np.ndarray, sme: np.ndarray, offset: int = Q4_OFFSET) -> np.ndarray:
+    """R[i] = offset * sum_j m 2^e q[i][j], the row's weight sum times offset.
+
+    The 4-bit projection ([UORLUT01] "One projection (definition)") is linear
+    in x, so with x' = x - offset every output is y = sum_j w x' + R[i].  For
+    int32 activations in [-2^15, 2^15), x - 128 lies in [-32896, 32639], the
+    exact range of two balanced base-256 digits, which is what lets the 4-bit
+    projection run on two activation limbs instead of three.
+    nib uint8 [N][K/2], sme uint8 [N][K/32] -> int64 [N].  Group sums of q are
+    at most 256 in magnitude, a group term m 2^e sum q below 2^27, the row sum
+    below 2^40 for K <= 262144, so int64 holds every step.
+    """
+    nib, sme = _c(nib, np.uint8), _c(sme, np.uint8)
+    N, K = nib.shape[0], nib.shape[1] * 2
+    assert sme.shape == (N, K // 32) and abs(offset) <= 128
+    q = np.empty((N, K), dtype=np.int64)
+    q[:, 0::2] = nib & 15          # element 2j: low nibble of byte j
+    q[:, 1::2] = nib >> 4
+    q = np.where(q >= 8, q - 16, q)   # two's-complement nibbles
+    m = (sme & 15).astype(np.int64)
+    e = (sme >> 4).astype(np.int64)
+    groups = q.reshape(N, K // 32, 32).sum(axis=2)
+    return np.int64(offset) * ((m * groups) << e).sum(axis=1)
+
+
 def silu_mul(g: np.ndarray, u: np.ndarray, lut: np.ndarray) -> np.ndarray:
     """h = floor(LUT[clamp(floor((g+16)/32), +-32768) + 32768] * u / 2^16)."""
     g, u, lut = _c(g, np.int64), _c(u, np.int64), _c(lut, np.int32)
@@ -153,11 +186,17 @@ def silu_mul(g: np.ndarray, u: np.ndarray, lut: np.ndarray) -> np.ndarray:
     return h
 
 
-def limb_split(x: np.ndarray, L: int) -> tuple[np.ndarray, bool]:
-    """Balanced base-256 digits d [L][n] in [-128, 127], x = sum 256^l d_l.
+def limb_split(x: np.ndarray, L: int, offset: int = 0) -> tuple[np.ndarray, bool]:
+    """Balanced base-256 digits d [L][n] in [-128, 127], x - offset = sum 256^l d_l.
 
-    Returns (digits, in_range)."""
+    offset 0 is the plain split; the two-limb form of the 4-bit projection
+    splits x - Q4_OFFSET (see q4_row_offsets).  Returns (digits, in_range)."""
     x = _c(x.reshape(-1), np.int64)
+    if offset:
+        lo, hi = -(2**63) + max(offset, 0), 2**63 - 1 + min(offset, 0)
+        if x.size and (int(x.min()) < lo or int(x.max()) > hi):
+            raise OracleError("limb_split: x - offset leaves int64")
+        x = x - np.int64(offset)
     d = np.zeros((L, x.size), dtype=np.int8)
     st = _lib().orc_limb_split(x.ctypes.data, d.ctypes.data, x.size, L)
     if st not in (ORC_OK, ORC_ERANGE):

@@ -208,3 +208,38 @@ def test_rms_mutants_are_caught(name):
     rq = {"half_even": _requant_half_even, "floor": _requant_floor}.get(name, oracle.requant)
     ri = {"no_d": _rms_no_d, "eps_unscaled": _rms_eps_unscaled}.get(name, oracle.rms_inverse)
     assert not _rms_checks(rq, ri), name
+
+
+# ------------------------------------------- 4-bit row offsets (Python oracle)
+
+def _q4_offset_checks(row_offsets) -> bool:
+    """The row-offset pins, applied to a candidate implementation."""
+    r = np.random.default_rng(45)
+    for N, K in ((3, 32), (9, 96)):
+        nib = r.integers(0, 256, size=(N, K // 2)).astype(np.uint8)
+        sme = (r.integers(0, 16, size=(N, K // 32)) | (r.integers(0, 16, size=(N, K // 32)) << 4)).astype(np.uint8)
+        if not (oracle.q4(nib, sme, np.full((1, K), 128, np.int32))[0] == row_offsets(nib, sme)).all():
+            return False
+    return True
+
+
+def _roff_mutant(kind):
+    def f(nib, sme):
+        N, K = nib.shape[0], nib.shape[1] * 2
+        q = np.empty((N, K), dtype=np.int64)
+        q[:, 0::2], q[:, 1::2] = nib & 15, nib >> 4
+        q = np.where(q > 8 if kind == "sign" else q >= 8, q - 16, q)
+        sm = np.roll(sme, 1, axis=1) if kind == "scale_group" else sme
+        m = (sm & 15).astype(np.int64)
+        e = (sm >> 4).astype(np.int64)
+        g = q.reshape(N, K // 32, 32).sum(axis=2)
+        if kind == "exponent":
+            return 128 * (m * g).sum(axis=1)
+        return (127 if kind == "offset" else 128) * ((m * g) << e).sum(axis=1)
+    return f
+
+
+@pytest.mark.parametrize("kind", ["scale_group", "sign", "exponent", "offset"])
+def test_q4_offset_mutants_are_caught(kind):
+    assert _q4_offset_checks(oracle.q4_row_offsets)
+    assert not _q4_offset_checks(_roff_mutant(kind)), kind

@@ -316,6 +316,48 @@ def test_limb_split_matches_bigint_random():
         assert d[:, e].tolist() == bigint.limbs(int(x[e]), 8)[0]
 
 
+def test_limb_split_offset_covers_int16():
+    # two digits of x - 128 cover exactly the int16 range [-2^15, 2^15)
+    x = np.arange(-(2**15), 2**15, dtype=np.int64)
+    d, ok = oracle.limb_split(x, 2, offset=oracle.Q4_OFFSET)
+    assert ok
+    rec = d[0].astype(np.int64) + 256 * d[1].astype(np.int64) + 128
+    assert (rec == x).all()
+    for v in (2**15, -(2**15) - 1):
+        assert not oracle.limb_split(np.array([v], np.int64), 2, offset=oracle.Q4_OFFSET)[1]
+    # without the offset two digits stop short of the top of the range
+    assert not oracle.limb_split(np.array([2**15 - 1], np.int64), 2)[1]
+
+
+def _rand_q4(r, N, K):
+    nib = r.integers(0, 256, size=(N, K // 2), dtype=np.int64).astype(np.uint8)
+    sme = (r.integers(0, 16, size=(N, K // 32)) | (r.integers(0, 16, size=(N, K // 32)) << 4)).astype(np.uint8)
+    return nib, sme
+
+
+@pytest.mark.parametrize("N,K", [(1, 32), (7, 64), (33, 160)])
+def test_q4_row_offsets_equal_q4_at_the_offset(N, K):
+    # with every activation equal to the offset, y = R exactly
+    nib, sme = _rand_q4(_rng(("roff", N, K)), N, K)
+    x = np.full((1, K), oracle.Q4_OFFSET, dtype=np.int32)
+    assert (oracle.q4(nib, sme, x)[0] == oracle.q4_row_offsets(nib, sme)).all()
+
+
+@pytest.mark.parametrize("N,K,T", [(5, 32, 3), (40, 96, 4), (17, 320, 2)])
+def test_q4_row_offsets_two_limb_form_equals_q4(N, K, T):
+    # y = q4(d_0) + 256 q4(d_1) + R with d the digits of x - 128: the two-limb form
+    r = _rng(("two-limb", N, K, T))
+    nib, sme = _rand_q4(r, N, K)
+    x = r.integers(-(2**15), 2**15, size=(T, K)).astype(np.int32)
+    x[0, :4] = [-(2**15), 2**15 - 1, 0, 128]
+    d, ok = oracle.limb_split(x.astype(np.int64), 2, offset=oracle.Q4_OFFSET)
+    assert ok
+    d0 = d[0].reshape(T, K).astype(np.int32)
+    d1 = d[1].reshape(T, K).astype(np.int32)
+    y = oracle.q4(nib, sme, d0) + 256 * oracle.q4(nib, sme, d1) + oracle.q4_row_offsets(nib, sme)[None, :]
+    assert (y == oracle.q4(nib, sme, x)).all()
+
+
 # ------------------------------------------------------------ Q16 reading
 
 def test_q16_semantics_page_values():
