@@ -574,9 +574,11 @@ def gemm_q8_multi(ws, x: torch.Tensor, limbs: int = 3, outs=None, status=None):
     return ys
 
 
-def gemm_q4(w: PackedWeights, x: torch.Tensor, limbs: int = 3, schedule: str = "default", seed: int = 0xE1,
+def gemm_q4(w: PackedWeights, x: torch.Tensor, limbs: int = 2, schedule: str = "default", seed: int = 0xE1,
             out=None, workspace=None, status=None) -> torch.Tensor:
-    """y = sum_g m 2^e sum_j q x (exact) for int32 activations x [t][k]."""
+    """y = sum_g m 2^e sum_j q x (exact) for int32 activations x [t][k].
+
+    limbs 2 (the default) is the two-limb form for x in [-2^15, 2^15)."""
     return _gemm("int_gemm_q4", w, x, torch.int32, limbs, schedule, seed, out, workspace, status)
 
 

@@ -99,9 +99,13 @@ int check_weights(const ei_weights* w, int format) {
 // their own).
 // With pre_limbs (T > 4 only), x is already split: its limb tiles
 // [limbs][t_pad/32][nb][1 KB] are read from there.
+// With row_off (exact outputs), x_off is subtracted from every activation
+// before its split and row_off[i] added to output row i (the two-limb 4-bit
+// form).
 int run_gemm(const ei_weights* w, const void* x, int x_is_i32, int64_t* y, int64_t t, int limbs, int schedule,
              uint64_t seed, void* ws, size_t ws_bytes, int32_t* status, hipStream_t s, int out_mode,
-             const int64_t* resid = nullptr, const int8_t* pre_limbs = nullptr) {
+             const int64_t* resid = nullptr, const int8_t* pre_limbs = nullptr, const int64_t* row_off = nullptr,
+             int64_t x_off = 0) {
   if ((!x && !pre_limbs) || !y || t < 1) return EI_EINVAL;
   if (limbs < 1 || limbs > 8) return EI_EINVAL;
   if (limbs > kMaxLimbs) return EI_ERANGE;
@@ -130,6 +134,8 @@ int run_gemm(const ei_weights* w, const void* x, int x_is_i32, int64_t* y, int64
   a.b1 = w->nb;
   a.out_mode = out_mode;
   a.order = ORDER_ASC;
+  a.row_off = row_off;
+  a.x_off = x_off;
 
   hipError_t e = hipSuccess;
   if (lay.mfma && pre_limbs) {
@@ -137,7 +143,7 @@ int run_gemm(const ei_weights* w, const void* x, int x_is_i32, int64_t* y, int64
   } else if (lay.mfma) {
     a.limb_tiles = reinterpret_cast<const int8_t*>(wsb + lay.limb_off);
     e = launch_limb_tiles(x, x_is_i32, t, w->k, limbs, reinterpret_cast<int8_t*>(wsb + lay.limb_off), lay.t_pad,
-                          status, s);
+                          status, s, x_off);
     if (e != hipSuccess) return EI_EDEVICE;
   } else if (pre_limbs) {
     return EI_EINVAL;
@@ -157,8 +163,10 @@ int run_gemm(const ei_weights* w, const void* x, int x_is_i32, int64_t* y, int64
           a.out_mode = OUT_PARTIAL;
           e = launch_gemm_skinny(a, limbs, lay.splits, limbs == 3 && narrow_scales(w->smax, w->nb), s);
           if (e == hipSuccess)
-            e = limbs <= 3 ? launch_combine_hr(part, lay.splits, y, t, w->n, out_mode, resid, status, s)
-                           : launch_combine_partials(part, lay.splits, y, t, w->n, limbs, out_mode, resid, status, s);
+            e = limbs <= 3
+                    ? launch_combine_hr(part, lay.splits, y, t, w->n, out_mode, resid, status, s, row_off)
+                    : launch_combine_partials(part, lay.splits, y, t, w->n, limbs, out_mode, resid, status, s,
+                                              row_off);
         } else {
           a.resid = resid;
           e = launch_gemm_skinny(a, limbs, 1, limbs == 3 && narrow_scales(w->smax, w->nb), s);
@@ -192,7 +200,8 @@ int run_gemm(const ei_weights* w, const void* x, int x_is_i32, int64_t* y, int64
         a.part_index = p;
         e = launch(a);
       }
-      if (e == hipSuccess) e = launch_combine_partials(part, kSplitParts, y, t, w->n, limbs, out_mode, resid, status, s);
+      if (e == hipSuccess)
+        e = launch_combine_partials(part, kSplitParts, y, t, w->n, limbs, out_mode, resid, status, s, row_off);
       return e == hipSuccess ? EI_OK : EI_EDEVICE;
     }
     case EI_SCHED_TREE: {
@@ -200,7 +209,7 @@ int run_gemm(const ei_weights* w, const void* x, int x_is_i32, int64_t* y, int64
       a.part = terms;
       a.out_mode = OUT_TERMS;
       e = launch(a);
-      if (e == hipSuccess) e = launch_tree_terms(terms, w->nb, y, t, w->n, limbs, out_mode, status, s);
+      if (e == hipSuccess) e = launch_tree_terms(terms, w->nb, y, t, w->n, limbs, out_mode, status, s, row_off);
       break;
     }
   }
@@ -852,8 +861,12 @@ int int_gemm_q4(const ei_weights* w, const int32_t* x, int64_t* y, int64_t t, in
                 uint64_t shuffle_seed, void* workspace, size_t workspace_bytes, int32_t* d_status, ei_stream stream) {
   const int c = check_weights(w, EI_FORMAT_Q4);
   if (c != EI_OK) return c;
+  // two limbs: the split takes x - 128 and every row gets its R_i back
+  const int64_t* roff =
+      limbs == 2 ? reinterpret_cast<const int64_t*>(static_cast<const uint8_t*>(w->packed) + row_offsets_at(w->n_pad, w->k))
+                 : nullptr;
   return run_gemm(w, x, 1, y, t, limbs, schedule, shuffle_seed, workspace, workspace_bytes, d_status,
-                  static_cast<hipStream_t>(stream), OUT_EXACT);
+                  static_cast<hipStream_t>(stream), OUT_EXACT, nullptr, nullptr, roff, roff ? kQ4Offset : 0);
 }
 
 int ei_topk_route(const int64_t* scores, int64_t t, int64_t e, int k, int32_t* route, ei_stream stream) {

@@ -29,6 +29,7 @@ struct PackedHeader {
   uint32_t smax;     // max |scale| (written by the pack pass with atomicMax)
   uint32_t pad0;
   int64_t codes_off, scales_off;
+  int64_t roff_off;  // row offsets, int64 [n_pad] (4-bit images; zero in Q8 images)
 };
 static_assert(sizeof(PackedHeader) <= kHeaderBytes, "header too large");
 
@@ -50,10 +51,20 @@ inline bool narrow_scales(uint32_t smax, int64_t nb) {
 // 2^32).
 __host__ __device__ inline int64_t code_bytes(int64_t n_pad, int64_t nb) { return n_pad * nb * 32; }
 
-inline size_t packed_bytes(int64_t n, int64_t k) {
-  int64_t n_pad = round_up(n, kTile);
+// header, code tiles, scales [n_pad/32][nb][32] int32, row offsets [n_pad] int64
+__host__ __device__ inline size_t row_offsets_at(int64_t n_pad, int64_t k) {
   return (size_t)kHeaderBytes + (size_t)n_pad * (size_t)k + (size_t)n_pad * (size_t)(k / 32) * 4u;
 }
+inline size_t packed_bytes(int64_t n, int64_t k) {
+  const int64_t n_pad = round_up(n, kTile);
+  return row_offsets_at(n_pad, k) + (size_t)n_pad * 8u;
+}
+
+// The 4-bit projection's two-limb form: activations are split as x - kQ4Offset
+// (two balanced base-256 digits hold exactly [-2^15, 2^15) then), and row i's
+// output gets R_i = kQ4Offset * (row i's weight sum) added back, since the
+// projection is linear in x.
+constexpr int64_t kQ4Offset = 128;
 
 // Output modes of the projection kernels.
 enum OutMode : int {
@@ -102,6 +113,10 @@ struct GemmArgs {
   const int32_t* lut;
   const int64_t* resid;
   int8_t* limb_out;          // fused gate/up: h as limb tiles [3][t_pad/32][n/32][1 KB]
+  // two-limb 4-bit form: x_off is subtracted from every (int32) activation
+  // before its split, row_off[i] added to output row i as it is finished
+  int64_t x_off;
+  const int64_t* row_off;
 };
 
 // Matrices of one batched GEMV launch (same k, same activations): matrix m
@@ -154,8 +169,9 @@ hipError_t launch_pack_q4(const uint8_t* nib, const uint8_t* sme, int64_t n, int
                           void* packed, hipStream_t s);
 hipError_t launch_limb_split_flat(const int64_t* x, int8_t* d, int64_t n, int limbs,
                                   int32_t* status, hipStream_t s);
+// x_off: subtracted from every activation before its split (int32 x only)
 hipError_t launch_limb_tiles(const void* x, int x_is_i32, int64_t t, int64_t k, int limbs,
-                             int8_t* tiles, int64_t t_pad, int32_t* status, hipStream_t s);
+                             int8_t* tiles, int64_t t_pad, int32_t* status, hipStream_t s, int64_t x_off = 0);
 hipError_t launch_gemv(const GemmArgs& a, int limbs, hipStream_t s);
 // a carries k, t, x, the block range and status; mm the matrices and outputs
 hipError_t launch_gemv_multi(const GemmArgs& a, const GemvMulti& mm, int limbs, hipStream_t s);
@@ -180,10 +196,13 @@ hipError_t launch_moe_sort(const int32_t* route, int64_t pairs, int64_t experts,
 hipError_t launch_grouped_limb_tiles(const int64_t* x, int64_t k, int topk, const int32_t* sorted_pair,
                                      const int32_t* tile_row0, const int32_t* tile_rows, const int32_t* ntiles,
                                      int64_t tiles_max, int8_t* tiles, int32_t* status, hipStream_t s);
+// row_off (exact outputs only): row_off[i] is added to output row i
 hipError_t launch_combine_partials(const int64_t* part, int nparts, int64_t* y, int64_t t, int64_t n,
-                                   int limbs, int out_mode, const int64_t* resid, int32_t* status, hipStream_t s);
+                                   int limbs, int out_mode, const int64_t* resid, int32_t* status, hipStream_t s,
+                                   const int64_t* row_off = nullptr);
 hipError_t launch_combine_hr(const int64_t* part, int nparts, int64_t* y, int64_t t, int64_t n, int out_mode,
-                             const int64_t* resid, int32_t* status, hipStream_t s);   // (h, r) partials
+                             const int64_t* resid, int32_t* status, hipStream_t s,
+                             const int64_t* row_off = nullptr);   // (h, r) partials
 hipError_t launch_combine_hr_tiles(const int64_t* part, int nparts, int64_t* y, int64_t t, int64_t n,
                                    const int64_t* resid, int8_t* tiles, int64_t t_pad, int32_t* status,
                                    hipStream_t s);   // Q8 rounding; n % 32 == 0
@@ -196,7 +215,8 @@ hipError_t launch_gemm_skinny_gateup(const GemmArgs& a, bool narrow, hipStream_t
 bool skinny16_finish_fits(int64_t n, int64_t nb, int64_t t);
 hipError_t launch_skinny16_finish(const GemmArgs& a, hipStream_t s);
 hipError_t launch_tree_terms(int64_t* terms, int64_t nb, int64_t* y, int64_t t, int64_t n,
-                             int limbs, int out_mode, int32_t* status, hipStream_t s);
+                             int limbs, int out_mode, int32_t* status, hipStream_t s,
+                             const int64_t* row_off = nullptr);
 hipError_t launch_make_perm(int32_t* perm, int64_t n, uint64_t seed, hipStream_t s);
 hipError_t launch_silu_lut(int32_t* lut, hipStream_t s);
 hipError_t launch_wide_pack(const int32_t* codes, int64_t n, int64_t k, int64_t n_pad, int8_t* tiles, uint32_t* bad,

@@ -77,7 +77,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a) {
 #pragma unroll
       for (int l = 0; l < L; ++l) a.part[(((int64_t)a.part_index * L + l) * a.t + tok) * a.n + row] = acc[l][r];
     } else {
-      __int128 v = 0;
+      __int128 v = a.row_off ? (__int128)a.row_off[row] : 0;   // the two-limb 4-bit form's R_i
 #pragma unroll
       for (int l = 0; l < L; ++l) v += (__int128)acc[l][r] << (8 * l);
       int64_t out;

@@ -355,7 +355,9 @@ __global__ __launch_bounds__(64 * W * G) void gemm_skinny_kernel(GemmArgs a) {
           a.part[((part * 2 + 1) * a.t + tok) * a.n + row] = rs[j];
         } else {
           int64_t out;
-          bool ok = finish_hr(hs[j], rs[j], a.out_mode, &out);
+          bool ok = a.row_off   // exact outputs of the two-limb 4-bit form: + R_i
+                        ? fit_i64((__int128)hs[j] * ((__int128)1 << 24) + rs[j] + a.row_off[row], &out)
+                        : finish_hr(hs[j], rs[j], a.out_mode, &out);
           if (a.resid) ok = fit_i64((__int128)a.resid[tok * a.n + row] + out, &out) && ok;
           if (!ok) flag(a.status, EI_DEV_OUT_RANGE);
           a.y[tok * a.n + row] = out;
@@ -391,7 +393,7 @@ __global__ __launch_bounds__(64 * W * G) void gemm_skinny_kernel(GemmArgs a) {
 #pragma unroll
         for (int l = 0; l < L; ++l) a.part[((part * L + l) * a.t + tok) * a.n + row] = acc[l][r];
       } else {
-        __int128 v = 0;
+        __int128 v = a.row_off ? (__int128)a.row_off[row] : 0;
 #pragma unroll
         for (int l = 0; l < L; ++l) v += (__int128)acc[l][r] << (8 * l);
         int64_t out;

@@ -57,6 +57,9 @@ constexpr int kGemvScaleLoads = 4;       // 1 KB scale loads per chunk: at most 
 // default policy.
 constexpr int kStream = 2;
 
+template <typename XT>
+constexpr bool kIsI32 = sizeof(XT) == 4;   // int32 (4-bit form) activations
+
 // Block visited at position pos: the plain ascending order unless the launch
 // is one of the schedule variants (kGeneric).
 template <bool kGeneric>
@@ -75,7 +78,8 @@ __device__ inline bool stage_limbs(const GemmArgs& a, int64_t p0, int64_t c0, in
     const int g = e & 7, t = (e >> 3) % T, s = (e >> 3) / T;
     const int64_t b = visit<kGeneric>(a, p0 + c0 + s);
     const XT* src = x + (int64_t)t * a.k + b * 32 + 4 * g;
-    const int64_t v[4] = {(int64_t)src[0], (int64_t)src[1], (int64_t)src[2], (int64_t)src[3]};
+    const int64_t xo = kIsI32<XT> ? a.x_off : 0;   // the two-limb 4-bit form splits x - x_off
+    const int64_t v[4] = {(int64_t)src[0] - xo, (int64_t)src[1] - xo, (int64_t)src[2] - xo, (int64_t)src[3] - xo};
     uint32_t w[L];
     ok &= limb_words<L>(v, w);
 #pragma unroll
@@ -190,7 +194,7 @@ __device__ inline void gemv_rows(const GemmArgs& a, int64_t rg, uint8_t* lds) {
         const int g = e & 7, t = (e >> 3) % T, s = (e >> 3) / T;
         const XT* src = x + (int64_t)t * a.k + visit<kGeneric>(a, p0 + s) * 32 + 4 * g;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) xv[i][j] = (int64_t)src[j];
+        for (int j = 0; j < 4; ++j) xv[i][j] = (int64_t)src[j] - (kIsI32<XT> ? a.x_off : 0);
       }
     }
   }
@@ -283,7 +287,7 @@ __device__ inline void gemv_rows(const GemmArgs& a, int64_t rg, uint8_t* lds) {
 #pragma unroll
         for (int l = 0; l < L; ++l) a.part[(((int64_t)a.part_index * L + l) * a.t + t) * a.n + orow] = sum[l];
       } else {
-        __int128 v = 0;
+        __int128 v = a.row_off ? (__int128)a.row_off[orow] : 0;   // the two-limb 4-bit form's R_i
 #pragma unroll
         for (int l = 0; l < L; ++l) v += (__int128)sum[l] << (8 * l);
         int64_t out;

@@ -49,9 +49,10 @@ __global__ void limb_split_flat_kernel(const int64_t* __restrict__ x, int8_t* __
 // 16 bytes of each of the L limb tiles (l, tg, b).  Consecutive threads write
 // consecutive 16-byte pieces of a tile; each reads one 128-byte (int64) or
 // 64-byte (int32) run of x.
+// x_off is subtracted from every activation first (the two-limb 4-bit form).
 template <int L, typename XT>
 __global__ void limb_tiles_kernel(const XT* __restrict__ x, int64_t t, int64_t k, int8_t* __restrict__ tiles,
-                                  int64_t t_pad, int32_t* status) {
+                                  int64_t t_pad, int32_t* status, int64_t x_off) {
   const int64_t nb = k / 32;
   int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= t_pad * nb * 2) return;
@@ -66,12 +67,13 @@ __global__ void limb_tiles_kernel(const XT* __restrict__ x, int64_t t, int64_t k
 #pragma unroll
     for (int w = 0; w < 4; ++w) words[l][w] = 0;
   bool ok = true;
+  if (sizeof(XT) != 4) x_off = 0;   // the offset is for int32 (4-bit form) activations only
   if (tok < t) {
     const XT* src = x + tok * k + b * 32 + 16 * h;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int64_t v[4] = {(int64_t)src[4 * q], (int64_t)src[4 * q + 1], (int64_t)src[4 * q + 2],
-                            (int64_t)src[4 * q + 3]};
+      const int64_t v[4] = {(int64_t)src[4 * q] - x_off, (int64_t)src[4 * q + 1] - x_off,
+                            (int64_t)src[4 * q + 2] - x_off, (int64_t)src[4 * q + 3] - x_off};
       uint32_t w[L];
       ok &= limb_words<L>(v, w);
 #pragma unroll
@@ -105,23 +107,31 @@ hipError_t launch_limb_split_flat(const int64_t* x, int8_t* d, int64_t n, int li
 
 template <typename XT>
 static void launch_tiles_t(const XT* x, int64_t t, int64_t k, int limbs, int8_t* tiles, int64_t t_pad,
-                           int32_t* status, hipStream_t s) {
+                           int32_t* status, hipStream_t s, int64_t x_off) {
   const int64_t threads = t_pad * (k / 32) * 2;
   const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
   switch (limbs) {
-    case 1: hipLaunchKernelGGL((limb_tiles_kernel<1, XT>), grid, block, 0, s, x, t, k, tiles, t_pad, status); break;
-    case 2: hipLaunchKernelGGL((limb_tiles_kernel<2, XT>), grid, block, 0, s, x, t, k, tiles, t_pad, status); break;
-    case 3: hipLaunchKernelGGL((limb_tiles_kernel<3, XT>), grid, block, 0, s, x, t, k, tiles, t_pad, status); break;
-    default: hipLaunchKernelGGL((limb_tiles_kernel<4, XT>), grid, block, 0, s, x, t, k, tiles, t_pad, status); break;
+    case 1:
+      hipLaunchKernelGGL((limb_tiles_kernel<1, XT>), grid, block, 0, s, x, t, k, tiles, t_pad, status, x_off);
+      break;
+    case 2:
+      hipLaunchKernelGGL((limb_tiles_kernel<2, XT>), grid, block, 0, s, x, t, k, tiles, t_pad, status, x_off);
+      break;
+    case 3:
+      hipLaunchKernelGGL((limb_tiles_kernel<3, XT>), grid, block, 0, s, x, t, k, tiles, t_pad, status, x_off);
+      break;
+    default:
+      hipLaunchKernelGGL((limb_tiles_kernel<4, XT>), grid, block, 0, s, x, t, k, tiles, t_pad, status, x_off);
+      break;
   }
 }
 
 hipError_t launch_limb_tiles(const void* x, int x_is_i32, int64_t t, int64_t k, int limbs, int8_t* tiles,
-                             int64_t t_pad, int32_t* status, hipStream_t s) {
+                             int64_t t_pad, int32_t* status, hipStream_t s, int64_t x_off) {
   if (x_is_i32)
-    launch_tiles_t(static_cast<const int32_t*>(x), t, k, limbs, tiles, t_pad, status, s);
+    launch_tiles_t(static_cast<const int32_t*>(x), t, k, limbs, tiles, t_pad, status, s, x_off);
   else
-    launch_tiles_t(static_cast<const int64_t*>(x), t, k, limbs, tiles, t_pad, status, s);
+    launch_tiles_t(static_cast<const int64_t*>(x), t, k, limbs, tiles, t_pad, status, s, x_off);
   return hipGetLastError();
 }
 

@@ -5,7 +5,8 @@
 // rg*32 + l%32 and columns b*32 + 16*(l/32) .. +15, 16 contiguous bytes.  The
 // same tile feeds the GEMV (one 16-byte load per lane) and the MFMA B operand
 // (one 16-byte load per lane, no shuffles).  Scales follow as
-// [n_pad/32][nb][32] int32.  Rows beyond n are zero (zero codes, zero scales),
+// [n_pad/32][nb][32] int32, then the row offsets [n_pad] int64 (4-bit images;
+// zero in Q8 images).  Rows beyond n are zero (zero codes, zero scales),
 // so padded rows contribute nothing and are never written back.
 #include "ei_internal.h"
 
@@ -100,6 +101,36 @@ __global__ void pack_q4_scales_kernel(const uint8_t* __restrict__ sme, int64_t n
   atomicMax(smax, (uint32_t)s);
 }
 
+// Row offsets of a 4-bit image, one thread per row: R_i = 128 * sum_j m 2^e q
+// (the row's weight sum times kQ4Offset; |R_i| < 2^47 for k <= 262,144).
+// The two-limb form adds R_i back after splitting x - 128.  Rows >= n get 0.
+__global__ void pack_q4_row_offsets_kernel(const uint8_t* __restrict__ nib, const uint8_t* __restrict__ sme,
+                                           int64_t n, int64_t k, int64_t nb, int64_t n_pad,
+                                           int64_t* __restrict__ roff) {
+  const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (row >= n_pad) return;
+  int64_t sum = 0;
+  if (row < n) {
+    for (int64_t b = 0; b < nb; ++b) {
+      const uint8_t* src = nib + row * (k / 2) + b * 16;
+      int g = 0;   // sum of the block's 32 codes, |g| <= 256
+      for (int p = 0; p < 16; ++p) {
+        const int lo = src[p] & 15, hi = src[p] >> 4;
+        g += (lo >= 8 ? lo - 16 : lo) + (hi >= 8 ? hi - 16 : hi);
+      }
+      const int sc = sme[row * nb + b];
+      sum += (int64_t)((sc & 15) * g) << (sc >> 4);
+    }
+  }
+  roff[row] = kQ4Offset * sum;
+}
+
+// Q8 images carry the row-offset area too (one layout for both formats): zeros.
+__global__ void zero_i64_kernel(int64_t* __restrict__ p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
 __global__ void pack_header_kernel(PackedHeader* h, int32_t format, int64_t n, int64_t k, int64_t n_pad, int64_t nb) {
   if (threadIdx.x != 0 || blockIdx.x != 0) return;
   h->magic = kMagic;
@@ -112,6 +143,7 @@ __global__ void pack_header_kernel(PackedHeader* h, int32_t format, int64_t n, i
   h->pad0 = 0;
   h->codes_off = kHeaderBytes;
   h->scales_off = kHeaderBytes + n_pad * k;
+  h->roff_off = (int64_t)row_offsets_at(n_pad, k);
 }
 
 static hipError_t launch_pack(int format, const void* codes, const void* scales, int64_t n, int64_t k,
@@ -120,6 +152,8 @@ static hipError_t launch_pack(int format, const void* codes, const void* scales,
   PackedHeader* h = static_cast<PackedHeader*>(packed);
   int8_t* tiles = static_cast<int8_t*>(packed) + kHeaderBytes;
   int32_t* sc = reinterpret_cast<int32_t*>(tiles + n_pad * k);
+  int64_t* roff = reinterpret_cast<int64_t*>(static_cast<uint8_t*>(packed) + row_offsets_at(n_pad, k));
+  const unsigned g3 = (unsigned)((n_pad + 255) / 256);
   hipLaunchKernelGGL(pack_header_kernel, dim3(1), dim3(64), 0, s, h, format, n, k, n_pad, nb);
   const int64_t ncode = (n_pad / kTile) * nb * 64, nsc = (n_pad / kTile) * nb * 32;
   const unsigned g1 = (unsigned)((ncode + 255) / 256), g2 = (unsigned)((nsc + 255) / 256);
@@ -128,11 +162,14 @@ static hipError_t launch_pack(int format, const void* codes, const void* scales,
                        nb, n_pad, tiles);
     hipLaunchKernelGGL(pack_q8_scales_kernel, dim3(g2), dim3(256), 0, s, static_cast<const int32_t*>(scales), n, nb,
                        n_pad, sc, &h->smax);
+    hipLaunchKernelGGL(zero_i64_kernel, dim3(g3), dim3(256), 0, s, roff, n_pad);
   } else {
     hipLaunchKernelGGL(pack_q4_codes_kernel, dim3(g1), dim3(256), 0, s, static_cast<const uint8_t*>(codes),
                        static_cast<const uint8_t*>(scales), n, k, nb, n_pad, tiles);
     hipLaunchKernelGGL(pack_q4_scales_kernel, dim3(g2), dim3(256), 0, s, static_cast<const uint8_t*>(scales), n, nb,
                        n_pad, sc, &h->smax);
+    hipLaunchKernelGGL(pack_q4_row_offsets_kernel, dim3(g3), dim3(256), 0, s, static_cast<const uint8_t*>(codes),
+                       static_cast<const uint8_t*>(scales), n, k, nb, n_pad, roff);
   }
   return hipGetLastError();
 }

@@ -9,10 +9,12 @@ namespace ei {
 
 // y[t][i] from per-limb partials part[p][l][t][i]; each partial sum is exact
 // in int64.  With resid,
-// y = resid + (that result), checked to fit int64.
+// y = resid + (that result), checked to fit int64; with row_off (exact
+// outputs), row_off[i] is added to the exact sum.
 __global__ void combine_partials_kernel(const int64_t* __restrict__ part, int nparts, int64_t* __restrict__ y,
                                         int64_t t, int64_t n, int limbs, int out_mode,
-                                        const int64_t* __restrict__ resid, int32_t* status) {
+                                        const int64_t* __restrict__ resid, int32_t* status,
+                                        const int64_t* __restrict__ row_off) {
   int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= t * n) return;
   const int64_t tn = t * n;
@@ -35,7 +37,7 @@ __global__ void combine_partials_kernel(const int64_t* __restrict__ part, int np
   if (limbs <= 3 && out_mode == OUT_ROUND_Q24) {
     out = round_q24_3(sum[0], limbs > 1 ? sum[1] : 0, limbs > 2 ? sum[2] : 0);
   } else {
-    __int128 v = 0;
+    __int128 v = row_off ? (__int128)row_off[e % n] : 0;
 #pragma unroll
     for (int l = 0; l < kMaxLimbs; ++l)
       if (l < limbs) v += (__int128)sum[l] << (8 * l);
@@ -49,7 +51,8 @@ __global__ void combine_partials_kernel(const int64_t* __restrict__ part, int np
 // y[t][i] from (h, r) partials part[p][2][t][i] (acc = 2^24 sum h + sum r;
 // the r are below 3 * 2^24 each), plus resid when given.
 __global__ void combine_hr_kernel(const int64_t* __restrict__ part, int nparts, int64_t* __restrict__ y, int64_t t,
-                                  int64_t n, int out_mode, const int64_t* __restrict__ resid, int32_t* status) {
+                                  int64_t n, int out_mode, const int64_t* __restrict__ resid, int32_t* status,
+                                  const int64_t* __restrict__ row_off) {
   int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= t * n) return;
   const int64_t tn = t * n;
@@ -69,7 +72,11 @@ __global__ void combine_hr_kernel(const int64_t* __restrict__ part, int nparts, 
     }
   }
   int64_t out;
-  bool ok = finish_hr(h, r, out_mode, &out);
+  bool ok;
+  if (row_off)   // exact outputs: acc = 2^24 h + r + row_off[i]
+    ok = fit_i64((__int128)h * ((__int128)1 << 24) + r + row_off[e % n], &out);
+  else
+    ok = finish_hr(h, r, out_mode, &out);
   if (resid) ok = fit_i64((__int128)resid[e] + out, &out) && ok;
   if (!ok) flag(status, EI_DEV_OUT_RANGE);
   y[e] = out;
@@ -129,7 +136,8 @@ __global__ void add_residual_kernel(int64_t* __restrict__ y, const int64_t* __re
 // (2,3), ... at every level, an odd last term passes up unchanged.  Each
 // thread owns one (t, i) and reduces its L columns in place.
 __global__ void tree_terms_kernel(int64_t* __restrict__ terms, int64_t nb, int64_t* __restrict__ y, int64_t t,
-                                  int64_t n, int limbs, int out_mode, int32_t* status) {
+                                  int64_t n, int limbs, int out_mode, int32_t* status,
+                                  const int64_t* __restrict__ row_off) {
   int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= t * n) return;
   const int64_t stride = (int64_t)limbs * t * n;   // between consecutive blocks
@@ -145,6 +153,7 @@ __global__ void tree_terms_kernel(int64_t* __restrict__ terms, int64_t nb, int64
     }
     v += (__int128)(nb > 0 ? col[0] : 0) << (8 * l);
   }
+  if (row_off) v += row_off[e % n];
   int64_t out;
   if (!finish_output(v, out_mode, &out)) flag(status, EI_DEV_OUT_RANGE);
   y[e] = out;
@@ -170,18 +179,19 @@ __global__ void make_perm_kernel(int32_t* perm, int64_t n, uint64_t seed) {
 }
 
 hipError_t launch_combine_partials(const int64_t* part, int nparts, int64_t* y, int64_t t, int64_t n, int limbs,
-                                   int out_mode, const int64_t* resid, int32_t* status, hipStream_t s) {
+                                   int out_mode, const int64_t* resid, int32_t* status, hipStream_t s,
+                                   const int64_t* row_off) {
   const int64_t total = t * n;
   hipLaunchKernelGGL(combine_partials_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, part, nparts, y,
-                     t, n, limbs, out_mode, resid, status);
+                     t, n, limbs, out_mode, resid, status, row_off);
   return hipGetLastError();
 }
 
 hipError_t launch_combine_hr(const int64_t* part, int nparts, int64_t* y, int64_t t, int64_t n, int out_mode,
-                             const int64_t* resid, int32_t* status, hipStream_t s) {
+                             const int64_t* resid, int32_t* status, hipStream_t s, const int64_t* row_off) {
   const int64_t total = t * n;
   hipLaunchKernelGGL(combine_hr_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, part, nparts, y, t, n,
-                     out_mode, resid, status);
+                     out_mode, resid, status, row_off);
   return hipGetLastError();
 }
 
@@ -201,10 +211,10 @@ hipError_t launch_add_residual(int64_t* y, const int64_t* resid, int64_t n, int3
 }
 
 hipError_t launch_tree_terms(int64_t* terms, int64_t nb, int64_t* y, int64_t t, int64_t n, int limbs, int out_mode,
-                             int32_t* status, hipStream_t s) {
+                             int32_t* status, hipStream_t s, const int64_t* row_off) {
   const int64_t total = t * n;
   hipLaunchKernelGGL(tree_terms_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, terms, nb, y, t, n,
-                     limbs, out_mode, status);
+                     limbs, out_mode, status, row_off);
   return hipGetLastError();
 }
 

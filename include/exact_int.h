@@ -111,7 +111,8 @@ typedef struct ei_weights {
 
 /* ------------------------------------------------------------ weights */
 
-/* Bytes of device memory ei_q8_pack / ei_q4_pack need for an n x k matrix. */
+/* Bytes of device memory ei_q8_pack / ei_q4_pack need for an n x k matrix
+ * (one layout for both formats; see ei_q8_pack). */
 size_t ei_packed_bytes(int64_t n, int64_t k);
 
 /*
@@ -123,7 +124,8 @@ size_t ei_packed_bytes(int64_t n, int64_t k);
  *           after the call it holds a 256-byte header, then the code tiles
  *           [n_pad/32][k/32][64 lanes][16 B] (lane l holds row l%32 and
  *           columns 16*(l/32) .. +15 of the block), then the scales
- *           [n_pad/32][k/32][32] int32; rows >= n are zero.
+ *           [n_pad/32][k/32][32] int32, then a row-offset area [n_pad]
+ *           int64 (used by 4-bit images, zero here); rows >= n are zero.
  *   out     host: the descriptor to pass to the GEMM entry points.
  * Synchronous (it reads back the largest scale).  Errors: EI_EINVAL for a
  * null pointer, n < 1, k < 32 or k % 32 != 0; EI_ENOSPACE if packed_bytes is
@@ -140,7 +142,9 @@ int ei_q8_pack(const int8_t* codes, const int32_t* scales, int64_t n, int64_t k,
  *   sme     device uint8 [n][k/32]: m in the low nibble, e in the high nibble
  * The mantissa is folded into the codes (m q lies in [-120, 105], an int8)
  * and the scale kept as 2^e, so sum_g m 2^e sum_j q x is computed exactly
- * as sum_g 2^e sum_j (m q) x.  Layout, sync and errors as ei_q8_pack.
+ * as sum_g 2^e sum_j (m q) x.  The row-offset area holds R_i = 128 sum_j
+ * m 2^e q[i][j] (|R_i| < 2^47), which the two-limb form of int_gemm_q4 adds
+ * back.  Layout, sync and errors as ei_q8_pack.
  */
 int ei_q4_pack(const uint8_t* nib, const uint8_t* sme, int64_t n, int64_t k,
                void* packed, size_t packed_bytes, ei_weights* out, ei_stream stream);
@@ -210,9 +214,14 @@ int int_gemm_q8(const ei_weights* w, const int64_t* x, int64_t* y, int64_t t, in
  * 4-bit projection ([UORLUT01] "One projection (definition)"), exact, not
  * rounded:  y[t][i] = sum_g m[i][g] 2^e[i][g] sum_{j in g} q[i][j] x[t][j]
  *   w        descriptor from ei_q4_pack (format EI_FORMAT_Q4)
- *   x        device int32 [t][k]; limbs as in int_gemm_q8 (3 covers
- *            |x| < 2^23; the workload's x in [-2^15, 2^15) needs 3 too, as
- *            2 limbs stop at 32639)
+ *   x        device int32 [t][k]
+ *   limbs    2: the two-limb form for x in [-2^15, 2^15): the split takes the
+ *            digits of x - 128 (two balanced base-256 digits hold exactly
+ *            [-32896, 32639]) and row i gets R_i = 128 sum_j w[i][j] from
+ *            the packed image back, which is exact because the projection
+ *            is linear in x; an x outside [-2^15, 2^15) sets
+ *            EI_DEV_LIMB_RANGE.  Any other L in 1..4 splits x itself, as
+ *            int_gemm_q8 does (3 covers |x| < 2^23).
  *   y        device int64 [t][n]
  * Other arguments and errors as int_gemm_q8.
  */

@@ -35,7 +35,7 @@ def _desc(ei, n, k, fmt=1, experts=1):
 
 def test_packed_and_workspace_sizes(ei):
     L = ei.lib()
-    assert L.ei_packed_bytes(100, 96) == 256 + 128 * 96 + 128 * 3 * 4
+    assert L.ei_packed_bytes(100, 96) == 256 + 128 * 96 + 128 * 3 * 4 + 128 * 8   # header, codes, scales, row offsets
     assert L.ei_packed_bytes(100, 95) == 0
     assert L.ei_wide_packed_bytes(100, 96) == 256 + 128 * 96 * 3
     d = _desc(ei, 896, 4864)

@@ -213,6 +213,52 @@ def test_q4_small_all_schedules(ei, shape):
         assert (host(ei.gemm_q4(w, dev(x), 3, sched)) == ref).all(), sched
 
 
+@pytest.mark.parametrize("shape", [(37, 96, 1), (100, 320, 4), (64, 288, 64), (33, 512, 7), (50, 4096, 12),
+                                   (300, 1024, 100)])
+def test_q4_two_limbs_all_schedules(ei, shape):
+    # the two-limb form: x - 128 split into two digits, R_i added back as
+    # each row is finished (GEMV, skinny with and without K splits, the
+    # generic MFMA kernel and every schedule's reducer); activations at both
+    # ends of [-2^15, 2^15)
+    N, K, T = shape
+    r = np.random.default_rng(N + 5 * K + T)
+    nib, sme, x = synth.q4_codes_packed(r, N, K), synth.q4_scale_bytes(r, N, K), synth.i32_acts(r, T, K)
+    x[0, :4] = [-(2**15), 2**15 - 1, 128, 127]
+    x[T - 1, K - 2:] = [2**15 - 1, -(2**15)]
+    ref = oracle.q4(nib, sme, x)
+    w = ei.pack_q4(dev(nib), dev(sme))
+    for sched in SCHEDS:
+        say("q4 two limbs", shape, sched)
+        assert (host(ei.gemm_q4(w, dev(x), 2, sched)) == ref).all(), sched
+
+
+def test_q4_row_offsets_in_the_image(ei):
+    # the packed 4-bit image carries R_i = 128 * row weight sum after the scales
+    N, K = 70, 160
+    r = np.random.default_rng(70)
+    nib, sme = synth.q4_codes_packed(r, N, K), synth.q4_scale_bytes(r, N, K)
+    w = ei.pack_q4(dev(nib), dev(sme))
+    n_pad = (N + 31) // 32 * 32
+    at = 256 + n_pad * K + n_pad * (K // 32) * 4
+    roff = host(w.buf[at:at + 8 * n_pad].view(torch.int64))
+    assert (roff[:N] == oracle.q4_row_offsets(nib, sme)).all()
+    assert (roff[N:] == 0).all()
+
+
+def test_q4_two_limb_range_is_flagged(ei):
+    r = np.random.default_rng(9)
+    nib, sme = synth.q4_codes_packed(r, 32, 64), synth.q4_scale_bytes(r, 32, 64)
+    w = ei.pack_q4(dev(nib), dev(sme))
+    for T in (1, 8):
+        for v in (2**15, -(2**15) - 1):   # one past [-2^15, 2^15) either side
+            x = np.zeros((T, 64), np.int32)
+            x[T - 1, 7] = v
+            say("q4 two-limb range flag", T, v)
+            with pytest.raises(ei.EIError):
+                ei.gemm_q4(w, dev(x), 2)
+            assert (host(ei.gemm_q4(w, dev(x), 3)) == oracle.q4(nib, sme, x)).all()
+
+
 # ------------------------------------------------------------------ workloads
 
 def test_q8_896x896_gemv(ei):
@@ -244,10 +290,11 @@ def test_q4_d512(ei):
         w = ei.pack_q4(dev(nib), dev(sme))
         for t in (1, 64):
             xd = dev(synth.q4_d512_x(k, t))
-            for sched in SCHEDS:
-                say("q4 d512", name, t, sched)
-                y = ei.gemm_q4(w, xd, 3, sched)
-                assert ei.digest(y) == GOLDEN["q4_d512"][f"{name}_t{t}"], sched
+            for limbs in (2, 3):
+                for sched in SCHEDS:
+                    say("q4 d512", name, t, limbs, sched)
+                    y = ei.gemm_q4(w, xd, limbs, sched)
+                    assert ei.digest(y) == GOLDEN["q4_d512"][f"{name}_t{t}"], (limbs, sched)
 
 
 def test_qwen_ffn_24_layers(ei):
