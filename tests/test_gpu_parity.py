@@ -232,6 +232,23 @@ def test_q4_two_limbs_all_schedules(ei, shape):
         assert (host(ei.gemm_q4(w, dev(x), 2, sched)) == ref).all(), sched
 
 
+@pytest.mark.parametrize("shape", [(1, 32, 1), (1, 32, 5), (1, 32, 64), (3, 32, 100), (1, 64, 4)])
+def test_single_row_single_block(ei, shape):
+    # the degenerate sizes: one output row (31 padded rows in its tile), one or
+    # two blocks along K (most waves, K splits and split-K partials empty),
+    # every schedule, Q8 at three limbs and the two-limb 4-bit form
+    N, K, T = shape
+    r = np.random.default_rng(N * 1000 + K + T)
+    q, s, x = synth.q8_codes(r, N, K), synth.q8_scales(r, N, K), synth.q16_acts(r, T, K)
+    nib, sme, x4 = synth.q4_codes_packed(r, N, K), synth.q4_scale_bytes(r, N, K), synth.i32_acts(r, T, K)
+    w8, w4 = ei.pack_q8(dev(q), dev(s)), ei.pack_q4(dev(nib), dev(sme))
+    ref8, ref4 = oracle.q8(q, s, x), oracle.q4(nib, sme, x4)
+    for sched in SCHEDS:
+        say("single row/block", shape, sched)
+        assert (host(ei.gemm_q8(w8, dev(x), 3, sched)) == ref8).all(), sched
+        assert (host(ei.gemm_q4(w4, dev(x4), 2, sched)) == ref4).all(), sched
+
+
 def test_q4_row_offsets_in_the_image(ei):
     # the packed 4-bit image carries R_i = 128 * row weight sum after the scales
     N, K = 70, 160
