@@ -256,14 +256,17 @@ def copy_calibration(torch, dev) -> int:
     return 0
 
 
-def _time_graph(torch, fn, steps: int, warmup: int):
-    """Record fn once as a HIP graph, replay it warmup + steps times; median ms
-    per replay from HIP events on the capturing stream."""
+def _time_graph(torch, fn, steps: int, warmup: int, reps: int = 1):
+    """Record fn (reps times in a row) as a HIP graph, replay it warmup + steps
+    times; median ms per call of fn from HIP events on the capturing stream.
+    Work of a few microseconds needs reps > 1: a replay's events also see the
+    host's submission of the graph when the device finishes first."""
     fn()
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        fn()
+        for _ in range(reps):
+            fn()
     torch.cuda.synchronize()
     for _ in range(warmup):
         g.replay()
@@ -274,7 +277,7 @@ def _time_graph(torch, fn, steps: int, warmup: int):
         a.record(); g.replay(); b.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    ms = sorted(a.elapsed_time(b) / reps for a, b in ev)
     return ms[len(ms) // 2], wall / steps * 1e3
 
 
@@ -308,11 +311,11 @@ def bench_q4_table(args, torch, np, ei, synth, dev) -> int:
                 ei.gemm_q4(w, x, limbs, out=ym, workspace=ws, status=status)
         return f
 
-    ms_t, wall_t = _time_graph(torch, step_table, args.steps, args.warmup)
+    ms_t, wall_t = _time_graph(torch, step_table, args.steps, args.warmup, reps=10)
     ok = True
     ms_m = {}
     for limbs in (3, 2):   # the two-limb form (x - 128 split, row offsets added back) last
-        ms_m[limbs], _ = _time_graph(torch, step_mfma(limbs), args.steps, args.warmup)
+        ms_m[limbs], _ = _time_graph(torch, step_mfma(limbs), args.steps, args.warmup, reps=10)
         ok = ok and all(ei.digest(ym) == gold[name] for name, n, k, t, nd, sd, w, x, yt, ym, ws, wt in cases)
     ok = ok and int(status.item()) == 0 and all(ei.digest(yt) == gold[name]
                                                 for name, n, k, t, nd, sd, w, x, yt, ym, ws, wt in cases)
@@ -334,6 +337,77 @@ def bench_q4_table(args, torch, np, ei, synth, dev) -> int:
                      "frac": round(tops / alu_peak, 4), "traffic": None, "step_ms": round(ms_t, 4)},
         "mfma_path_step_ms": round(ms_m[2], 4), "mfma_path_3_limbs_step_ms": round(ms_m[3], 4),
         "parity": {"table_read_and_mfma_digests_equal_oracle": ok}}))
+    return 0 if ok else 1
+
+
+def bench_schedule_gate(args, torch, np, ei, synth, dev) -> int:
+    """The two small workloads, timed per schedule: the single 896x896 Q8
+    projection at T=1, and the schedule gate's Q (896x896), K and V (128x896)
+    projections of a 4-token prefix (also as one batched launch of the three).
+    Both are cache-resident and launch-bound, so they are reported in
+    microseconds.  Parity: every schedule's digest equals the oracle's; the
+    float32 shadow of Q/K/V is run in the five orders for contrast and its
+    distinct digests are counted (the integer ones must be one per matrix)."""
+    import json as _json
+    gold = _json.load(open(os.path.join(ROOT, "tests", "golden", "oracle_digests.json")))
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    scheds = ("canonical", "reversed", "tiled_shuffled", "split_k", "tree_walk")
+
+    def prepare(c, sc, x):
+        w = ei.pack_q8(torch.from_numpy(c).to(dev), torch.from_numpy(sc).to(dev))
+        t = x.shape[0]
+        return {"w": w, "y": torch.empty((t, w.n), dtype=torch.int64, device=dev),
+                "ws": {sd: torch.empty(max(ei.workspace_bytes(w, t, 3, sd), 1), dtype=torch.uint8, device=dev)
+                       for sd in ("default",) + scheds}}
+
+    (c0, s0), x0 = synth.q8_896_inputs()
+    x0d = torch.from_numpy(x0).to(dev)
+    m0 = prepare(c0, s0, x0)
+    mats, xq = synth.qkv_inputs()
+    xqd = torch.from_numpy(xq).to(dev)
+    mq = {name: prepare(c, sc, xq) for name, (c, sc) in mats.items()}
+    out, ok = {"q8_896x896_t1": {}, "qkv_t4": {}}, True
+    for sd in ("default",) + scheds:
+        def one():
+            ei.gemm_q8(m0["w"], x0d, 3, sd, 0xE1, out=m0["y"], workspace=m0["ws"][sd], status=status)
+
+        def qkv():
+            for m in mq.values():
+                ei.gemm_q8(m["w"], xqd, 3, sd, 0xE1, out=m["y"], workspace=m["ws"][sd], status=status)
+
+        ms, _ = _time_graph(torch, one, args.steps, args.warmup, reps=20)
+        out["q8_896x896_t1"][sd] = round(ms * 1e3, 2)
+        ok = ok and ei.digest(m0["y"]) == gold["q8_896x896"]["y"]
+        ms, _ = _time_graph(torch, qkv, args.steps, args.warmup, reps=20)
+        out["qkv_t4"][sd] = round(ms * 1e3, 2)
+        ok = ok and all(ei.digest(m["y"]) == gold["qkv_gate"][name] for name, m in mq.items())
+    outs = [m["y"] for m in mq.values()]
+
+    def qkv_batched():
+        ei.gemm_q8_multi([m["w"] for m in mq.values()], xqd, 3, outs=outs, status=status)
+
+    ms_b, _ = _time_graph(torch, qkv_batched, args.steps, args.warmup, reps=20)
+    ok = ok and all(ei.digest(m["y"]) == gold["qkv_gate"][name] for name, m in mq.items())
+    shadow = {}
+    for name, (c, sc) in mats.items():
+        cd, scd = torch.from_numpy(c).to(dev), torch.from_numpy(sc).to(dev)
+        shadow[name] = len({ei.digest(ei.fp32_shadow(cd, scd, xqd, sd, seed=0xE1)) for sd in scheds})
+    ok = ok and int(status.item()) == 0
+    wbytes = 896 * 896 * (1 + 4 / 32)
+    us = out["q8_896x896_t1"]["default"]
+    print(json.dumps({
+        "metric": "896x896 Q8 projection at T=1 (default schedule): microseconds per launch", "value": us,
+        "unit": "us", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(us / 1e3, 5),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8xint8->int32, int64 accumulate",
+        "data": "synthetic (seeded Q8 codes, Q24 block scales, Q16 activations)",
+        "config": {"workload": "q8_896x896_t1_and_qkv_schedule_gate", "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "achieved": round(wbytes / (us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(wbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                     "note": "0.9 MB of weights: cache-resident and launch-bound, so the fraction is not its bound"},
+        "us_per_schedule": out, "qkv_t4_batched_us": round(ms_b * 1e3, 2),
+        "fp32_shadow_distinct_digests_of_5": shadow,
+        "parity": {"every_schedule_digest_equals_oracle": ok}}))
     return 0 if ok else 1
 
 
@@ -563,13 +637,14 @@ def main() -> int:
     ap.add_argument("--summarize-sq", nargs=2, metavar=("PASS1", "PASS2"),
                     help="two rocprofv3 --pmc output directories of SQ counters -> profiles/sq_counters.json")
     ap.add_argument("--workload", choices=("dense", "olmoe", "olmoe_router", "qwen_ffn", "qwen_ffn_prenorm", "wide",
-                                           "q4_table"),
+                                           "q4_table", "schedule_gate"),
                     default="dense",
                     help="dense: the 14336x4096 decode + prefill step (default); olmoe / qwen_ffn: the routed "
                          "expert FFN or the 24-layer FFN chain, timed the same way; olmoe_router: the routed "
                          "FFN behind the integer router; qwen_ffn_prenorm: the chain with an integer RMSNorm "
                          "in front of every layer; wide: the 12-trit wide-code GEMM (896x896, 4096 rows); q4_table: the "
-                         "4-bit projections by table reads against the MFMA path")
+                         "4-bit projections by table reads against the MFMA path; schedule_gate: the 896x896 projection at T=1 "
+                         "and the Q/K/V schedule gate, per schedule")
     args = ap.parse_args()
     if args.summarize_counters:
         return summarize_counters(*args.summarize_counters)
@@ -597,6 +672,8 @@ def main() -> int:
         return bench_olmoe(args, torch, np, ei, synth, dev)
     if args.workload == "q4_table":
         return bench_q4_table(args, torch, np, ei, synth, dev)
+    if args.workload == "schedule_gate":
+        return bench_schedule_gate(args, torch, np, ei, synth, dev)
     if args.workload == "wide":
         return bench_wide(args, torch, np, ei, synth, dev)
     if args.workload == "olmoe_router":
