@@ -496,7 +496,9 @@ int orc_limb_split(const int64_t* x, int8_t* d, int64_t n, int L) {
  *   split_k        8 partials over contiguous block ranges (ascending), then
  *                  0 + p7 + p6 + ... + p0;
  *   tree_walk      per-block sums (ascending), then a pairwise tree.
- * Parity unpinned: the pages print no float values for synthetic inputs.
+ * The pages print float values only for their checkpoint, not for synthetic
+ * inputs; each order is pinned instead against float32 sequences formed
+ * independently in the tests.
  */
 static float shadow_w(const int8_t* q, const int32_t* s, int64_t K, int64_t i, int64_t j) {
   return (float)((double)((int64_t)s[i * (K / 32) + j / 32] * q[i * K + j]) * (1.0 / 16777216.0));
