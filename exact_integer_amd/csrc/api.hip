@@ -66,8 +66,11 @@ WsLayout layout_for(const ei_weights* w, int64_t t, int limbs, int schedule) {
   if (L.path == PATH_SKINNY) {
     L.splits = skinny_splits(w->n_pad, L.t_pad, w->nb);
     if (L.splits > 1) {
+      // the workgroups' partials: an (h, r) pair per output for up to three
+      // limbs (two int64 even for one limb), one int64 per limb for four
+      const size_t slots = limbs <= 3 ? 2 : (size_t)limbs;
       L.part_off = off;
-      off = align_up(off + sizeof(int64_t) * (size_t)L.splits * limbs * (size_t)t * (size_t)w->n);
+      off = align_up(off + sizeof(int64_t) * (size_t)L.splits * slots * (size_t)t * (size_t)w->n);
     }
   }
   if (schedule == EI_SCHED_TILED_SHUFFLED) {

@@ -43,6 +43,13 @@ def test_packed_and_workspace_sizes(ei):
     assert L.ei_gemm_workspace_bytes(ctypes.byref(d), 30, 3, 0) > 3 * 32 * 4864
     assert L.ei_gemm_workspace_bytes(ctypes.byref(d), 1, 3, 0) == 0          # the GEMV needs none
     assert L.ei_wide_workspace_bytes(ctypes.byref(_desc(ei, 896, 896, 3)), 4096) == 4 * 4096 * 896
+    # the skinny path splits 64 x 1024 at T=5 over two workgroups: their (h, r)
+    # pairs take two int64 per output whatever the limb count up to three, so
+    # one and two limbs differ only in the limb tiles (32 tokens x 1024 bytes)
+    d = _desc(ei, 64, 1024)
+    w1, w2 = L.ei_gemm_workspace_bytes(ctypes.byref(d), 5, 1, 0), L.ei_gemm_workspace_bytes(ctypes.byref(d), 5, 2, 0)
+    assert w2 - w1 == 32 * 1024
+    assert w1 >= 32 * 1024 + 2 * 2 * 5 * 64 * 8
 
 
 def test_projection_arguments(ei):
