@@ -1,0 +1,113 @@
+"""GPU parity on seeded random shapes: projections, FFN layers and routed FFNs.
+
+Each case draws its shape, limb count, schedule and scale range from one
+seeded generator and compares the whole output with the oracle.  The draws
+reach combinations the hand-picked shapes do not: every limb count on every
+path, wide scales on the skinny and generic kernels, K splits of every count,
+FFN layers on and off the fused path, routed FFNs with 1-23 experts.  One
+fixed case, a one-limb projection whose skinny pass splits K over eight
+workgroups, once wrote its (h, r) partials past a workspace sized one int64
+per output; it runs first.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+SCH = ["default", "canonical", "reversed", "tiled_shuffled", "split_k", "tree_walk"]
+LIMB = {1: (-128, 127), 2: (-32896, 32639), 3: (-8421504, 8355711), 4: (-2155905152, 2139062143)}
+CASES = 400
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    return t.cpu().numpy()
+
+
+@pytest.fixture(scope="module")
+def ei():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    import exact_integer_amd
+    return exact_integer_amd
+
+
+def _q8(ei, r, n, k, t, L, sched, wide):
+    q = synth.q8_codes(r, n, k)
+    if wide:
+        s = r.integers(-(2**31), 2**31, size=(n, k // 32), dtype=np.int64).astype(np.int32)
+    else:
+        s = synth.q8_scales(r, n, k)
+    lo, hi = LIMB[L]
+    x = r.integers(lo, hi + 1, size=(t, k)).astype(np.int64)
+    seed = int(r.integers(0, 2**32))
+    print("q8", n, k, t, L, sched, "wide" if wide else "", flush=True)
+    y = host(ei.gemm_q8(ei.pack_q8(dev(q), dev(s)), dev(x), L, sched, seed))
+    assert (y == oracle.q8(q, s, x, threads=8)).all(), (n, k, t, L, sched, wide)
+
+
+def test_one_limb_skinny_split_partials(ei):
+    _q8(ei, np.random.default_rng(30), 45, 4224, 32, 1, "canonical", False)
+
+
+def test_random_shapes(ei, lut):
+    r = np.random.default_rng(20261203)
+    lut_d = ei.silu_lut()
+
+    def pick_t():
+        c = r.integers(0, 3)
+        return int(r.integers(1, 5)) if c == 0 else int(r.integers(5, 64)) if c == 1 else int(r.integers(64, 320))
+
+    for _ in range(CASES):
+        kind = str(r.choice(["q8", "q4", "ffn", "moe"], p=[0.45, 0.25, 0.15, 0.15]))
+        if kind in ("q8", "q4"):
+            t = pick_t()
+            k = 32 * int(r.integers(1, 160))
+            n = int(r.integers(1, max(2, min(3000, 3e8 // (k * t)))))
+            sched = str(r.choice(SCH))
+            if kind == "q8":
+                _q8(ei, r, n, k, t, int(r.choice([1, 2, 3, 3, 3, 4])), sched, bool(r.random() < 0.2))
+            else:
+                L = int(r.choice([2, 3]))
+                nib, sme, x = synth.q4_codes_packed(r, n, k), synth.q4_scale_bytes(r, n, k), synth.i32_acts(r, t, k)
+                print("q4", n, k, t, L, sched, flush=True)
+                y = host(ei.gemm_q4(ei.pack_q4(dev(nib), dev(sme)), dev(x), L, sched))
+                assert (y == oracle.q4(nib, sme, x, threads=8)).all(), (n, k, t, L, sched)
+        elif kind == "ffn":
+            D, F, T = 32 * int(r.integers(1, 40)), 32 * int(r.integers(1, 160)), int(r.integers(1, 80))
+            mats = [(synth.q8_codes(r, F, D), synth.q8_scales(r, F, D)),
+                    (synth.q8_codes(r, F, D), synth.q8_scales(r, F, D)),
+                    (synth.q8_codes(r, D, F), synth.q8_scales(r, D, F))]
+            x = synth.q16_acts(r, T, D)
+            print("ffn", D, F, T, flush=True)
+            _, _, h, _, xn = oracle.ffn_layer(x, mats[0], mats[1], mats[2], lut, threads=8)
+            wg, wu, wd = (ei.pack_q8(dev(c), dev(sc)) for c, sc in mats)
+            lo, hi = LIMB[3]
+            if h.min() < lo or h.max() > hi:   # the down projection's input leaves its 3-limb range
+                with pytest.raises(ei.EIError):
+                    ei.ffn_q8(wg, wu, wd, dev(x), lut_d)
+            else:
+                assert (host(ei.ffn_q8(wg, wu, wd, dev(x), lut_d)) == xn).all(), (D, F, T)
+        else:
+            E = int(r.integers(1, 24))
+            topk = int(r.integers(1, min(E, 8) + 1))
+            rows, D, F = int(r.integers(1, 200)), 32 * int(r.integers(1, 24)), 32 * int(r.integers(1, 24))
+            mats = [[(synth.q8_codes(r, F, D), synth.q8_scales(r, F, D)),
+                     (synth.q8_codes(r, F, D), synth.q8_scales(r, F, D)),
+                     (synth.q8_codes(r, D, F), synth.q8_scales(r, D, F))] for _ in range(E)]
+            x = synth.q16_acts(r, rows, D)
+            route = r.integers(0, E, (rows, topk)).astype(np.int32)
+            print("moe", E, topk, rows, D, F, flush=True)
+
+            def stack(m):
+                return (dev(np.stack([mm[m][0] for mm in mats])), dev(np.stack([mm[m][1] for mm in mats])))
+            wg, wu, wd = (ei.pack_q8_stacked(*stack(m)) for m in range(3))
+            y = host(ei.moe_ffn_q8(wg, wu, wd, dev(x), dev(route), lut_d))
+            assert (y == oracle.moe_pairs(x, route, lambda e: mats[e], lut, threads=8)).all(), (E, topk, rows, D, F)
