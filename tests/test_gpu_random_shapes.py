@@ -111,3 +111,97 @@ def test_random_shapes(ei, lut):
             wg, wu, wd = (ei.pack_q8_stacked(*stack(m)) for m in range(3))
             y = host(ei.moe_ffn_q8(wg, wu, wd, dev(x), dev(route), lut_d))
             assert (y == oracle.moe_pairs(x, route, lambda e: mats[e], lut, threads=8)).all(), (E, topk, rows, D, F)
+
+
+def test_random_shapes_other_entry_points(ei, lut):
+    # the batched GEMV (1-16 matrices, 1-4 limbs), the routed projection
+    # (ragged rows, repeated experts), FFN chains plain and pre-norm (1-5
+    # layers, fused and unfused paths), the allocation-free projection and
+    # projections large enough for the tiled kernels (narrow, wide and 4-bit)
+    r = np.random.default_rng(20261204)
+    lut_d = ei.silu_lut()
+    lo3, hi3 = LIMB[3]
+    for _ in range(120):
+        kind = str(r.choice(["multi", "grouped", "chain", "prenorm", "noalloc", "tiled"]))
+        if kind == "multi":
+            L, t, k = int(r.choice([1, 2, 3, 4])), int(r.integers(1, 5)), 32 * int(r.integers(1, 200))
+            mats = [(synth.q8_codes(r, n, k), synth.q8_scales(r, n, k))
+                    for n in [int(r.integers(1, 3000)) for _ in range(int(r.integers(1, 17)))]]
+            lo, hi = LIMB[L]
+            x = r.integers(lo, hi + 1, size=(t, k)).astype(np.int64)
+            print("multi", L, t, k, [q.shape[0] for q, _ in mats], flush=True)
+            ys = ei.gemm_q8_multi([ei.pack_q8(dev(q), dev(s)) for q, s in mats], dev(x), L)
+            for (q, s), y in zip(mats, ys):
+                assert (host(y) == oracle.q8(q, s, x, threads=8)).all()
+        elif kind == "grouped":
+            E = int(r.integers(1, 40))
+            topk, rows = int(r.integers(1, min(E, 8) + 1)), int(r.integers(1, 300))
+            n = 32 * int(r.integers(1, 40)) if r.random() < 0.5 else int(r.integers(1, 1200))
+            k = 32 * int(r.integers(1, 40))
+            mats = [(synth.q8_codes(r, n, k), synth.q8_scales(r, n, k)) for _ in range(E)]
+            x = synth.q16_acts(r, rows, k)
+            route = r.integers(0, E, (rows, topk)).astype(np.int32)
+            print("grouped", E, topk, rows, n, k, flush=True)
+            w = ei.pack_q8_stacked(dev(np.stack([m[0] for m in mats])), dev(np.stack([m[1] for m in mats])))
+            y = host(ei.gemm_q8_grouped(w, dev(x), dev(route)))
+            for e in range(E):
+                pr = [(i, s) for i in range(rows) for s in range(topk) if route[i, s] == e]
+                if pr:
+                    ye = oracle.q8(mats[e][0], mats[e][1], x[[i for i, _ in pr]], threads=8)
+                    assert all((y[i * topk + s] == ye[j]).all() for j, (i, s) in enumerate(pr)), (E, e)
+        elif kind in ("chain", "prenorm"):
+            D, F, T, nl = 32 * int(r.integers(1, 33)), 32 * int(r.integers(1, 130)), int(r.integers(1, 80)), \
+                int(r.integers(1, 6))
+            layers = [[(synth.q8_codes(r, F, D), synth.q8_scales(r, F, D)),
+                       (synth.q8_codes(r, F, D), synth.q8_scales(r, F, D)),
+                       (synth.q8_codes(r, D, F), synth.q8_scales(r, D, F))] for _ in range(nl)]
+            x = synth.q16_acts(r, T, D)
+            gns = [np.rint(r.normal(1.0, 0.2, D) * 2**16).astype(np.int32) for _ in range(nl)]
+            eps = int(r.integers(1, 2**20))
+            print(kind, D, F, T, nl, flush=True)
+            xi, in_range = x, True
+            for li, m in enumerate(layers):
+                if kind == "prenorm":   # the normalized input, the gated product and x + d
+                    src, _, xn = oracle.ffn_layer_prenorm(xi, gns[li], eps, *m, lut, threads=8)
+                    h = oracle.ffn_layer(src, *m, lut, threads=8)[2]
+                else:
+                    src = xi
+                    _, _, h, _, xn = oracle.ffn_layer(xi, *m, lut, threads=8)
+                # what the library splits into limbs: each layer's input (or its norm) and h
+                in_range = in_range and lo3 <= src.min() and src.max() <= hi3 and lo3 <= h.min() and h.max() <= hi3
+                xi = xn
+            x_next = xi
+            pk = [tuple(ei.pack_q8(dev(c), dev(s)) for c, s in m) for m in layers]
+            run = (lambda: ei.ffn_q8_prenorm_chain(pk, [dev(g) for g in gns], eps, dev(x), lut_d)) \
+                if kind == "prenorm" else (lambda: ei.ffn_q8_chain(pk, dev(x), lut_d))
+            if in_range:
+                assert (host(run()) == x_next).all(), (kind, D, F, T, nl)
+            else:
+                with pytest.raises(ei.EIError):
+                    run()
+        elif kind == "noalloc":
+            t, k = int(r.integers(1, 320)), 32 * int(r.integers(1, 160))
+            n = int(r.integers(1, max(2, min(4000, 3e8 // (k * t)))))
+            q, s, x = synth.q8_codes(r, n, k), synth.q8_scales(r, n, k), synth.q16_acts(r, t, k)
+            print("noalloc", n, k, t, flush=True)
+            w = ei.pack_q8(dev(q), dev(s))
+            if ei.workspace_bytes(w, t) > 32 << 20:
+                with pytest.raises(ei.EIError):
+                    ei.gemm_q8_noalloc(w, dev(x))
+            else:
+                assert (host(ei.gemm_q8_noalloc(w, dev(x))) == oracle.q8(q, s, x, threads=8)).all()
+        else:
+            fmt, t, k = str(r.choice(["q8", "q8", "q4"])), int(r.integers(64, 700)), 32 * int(r.integers(1, 24))
+            need = (128 * 128 * 32) // ((t + 31) // 32 * 32)
+            n = int(r.integers(min(max(1, need - 200), 5999), 6000))
+            print("tiled", fmt, n, k, t, flush=True)
+            if fmt == "q8":
+                q = synth.q8_codes(r, n, k)
+                s = (r.integers(-(2**31), 2**31, size=(n, k // 32), dtype=np.int64).astype(np.int32)
+                     if r.random() < 0.3 else synth.q8_scales(r, n, k))
+                x = synth.q16_acts(r, t, k)
+                assert (host(ei.gemm_q8(ei.pack_q8(dev(q), dev(s)), dev(x), 3)) == oracle.q8(q, s, x, threads=8)).all()
+            else:
+                nib, sme, x = synth.q4_codes_packed(r, n, k), synth.q4_scale_bytes(r, n, k), synth.i32_acts(r, t, k)
+                y = host(ei.gemm_q4(ei.pack_q4(dev(nib), dev(sme)), dev(x), 3))
+                assert (y == oracle.q4(nib, sme, x, threads=8)).all()
