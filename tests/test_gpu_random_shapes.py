@@ -205,3 +205,80 @@ def test_random_shapes_other_entry_points(ei, lut):
                 nib, sme, x = synth.q4_codes_packed(r, n, k), synth.q4_scale_bytes(r, n, k), synth.i32_acts(r, t, k)
                 y = host(ei.gemm_q4(ei.pack_q4(dev(nib), dev(sme)), dev(x), 3))
                 assert (y == oracle.q4(nib, sme, x, threads=8)).all()
+
+
+def test_random_shapes_wide_scales_and_large_routes(ei, lut):
+    # FFN layers, chains and routed FFNs with block scales past the narrow
+    # bound (|S| up to 2^17: the per-limb gate/up and down forms), routed FFNs
+    # with up to 319 experts (the radix grouping) and 2,048 rows, and 4-bit
+    # and Q8 projections of up to 1,024 tokens; an h or input outside the
+    # 3-limb range must be flagged
+    r = np.random.default_rng(20261205)
+    lut_d = ei.silu_lut()
+    lo3, hi3 = LIMB[3]
+
+    def scales(n, k, wide):
+        if not wide:
+            return synth.q8_scales(r, n, k)
+        lim = int(r.choice([2**15, 2**16, 2**17]))
+        return r.integers(-lim, lim + 1, size=(n, k // 32), dtype=np.int64).astype(np.int32)
+
+    def mats_for(F, D, wide):
+        return [(synth.q8_codes(r, F, D), scales(F, D, wide)), (synth.q8_codes(r, F, D), scales(F, D, wide)),
+                (synth.q8_codes(r, D, F), scales(D, F, wide))]
+
+    for _ in range(60):
+        kind = str(r.choice(["chain", "moe", "big"]))
+        if kind == "chain":
+            D, F, T, nl = 32 * int(r.integers(1, 33)), 32 * int(r.integers(1, 130)), int(r.integers(1, 80)), \
+                int(r.integers(1, 5))
+            layers = [mats_for(F, D, bool(r.random() < 0.6)) for _ in range(nl)]
+            x = synth.q16_acts(r, T, D)
+            print("chain", D, F, T, nl, flush=True)
+            xi, in_range = x, True
+            for m in layers:
+                _, _, h, _, xn = oracle.ffn_layer(xi, *m, lut, threads=8)
+                in_range = in_range and lo3 <= xi.min() and xi.max() <= hi3 and lo3 <= h.min() and h.max() <= hi3
+                xi = xn
+            pk = [tuple(ei.pack_q8(dev(c), dev(s)) for c, s in m) for m in layers]
+            if in_range:
+                assert (host(ei.ffn_q8_chain(pk, dev(x), lut_d)) == xi).all(), (D, F, T, nl)
+            else:
+                with pytest.raises(ei.EIError):
+                    ei.ffn_q8_chain(pk, dev(x), lut_d)
+        elif kind == "moe":
+            E = int(r.integers(1, 64)) if r.random() < 0.5 else int(r.integers(200, 320))
+            topk = int(r.integers(1, min(E, 8) + 1))
+            rows, D, F = int(r.integers(1, 2049)), 32 * int(r.integers(1, 12)), 32 * int(r.integers(1, 12))
+            wide = bool(r.random() < 0.5)
+            mats = [mats_for(F, D, wide) for _ in range(E)]
+            x = synth.q16_acts(r, rows, D)
+            route = r.integers(0, E, (rows, topk)).astype(np.int32)
+            print("moe", E, topk, rows, D, F, wide, flush=True)
+            in_range = True
+            for e in range(E):
+                idx = np.nonzero((route == e).any(axis=1))[0]
+                if len(idx):
+                    h = oracle.ffn_layer(x[idx], *mats[e], lut, threads=8)[2]
+                    in_range = in_range and lo3 <= h.min() and h.max() <= hi3
+
+            def stack(i):
+                return (dev(np.stack([mm[i][0] for mm in mats])), dev(np.stack([mm[i][1] for mm in mats])))
+            wg, wu, wd = (ei.pack_q8_stacked(*stack(i)) for i in range(3))
+            if in_range:
+                y = host(ei.moe_ffn_q8(wg, wu, wd, dev(x), dev(route), lut_d))
+                assert (y == oracle.moe_pairs(x, route, lambda e: mats[e], lut, threads=8)).all(), (E, topk, rows)
+            else:
+                with pytest.raises(ei.EIError):
+                    ei.moe_ffn_q8(wg, wu, wd, dev(x), dev(route), lut_d)
+        else:
+            t, k, n = int(r.integers(64, 1025)), 32 * int(r.integers(1, 16)), int(r.integers(1, 8000))
+            print("big", n, k, t, flush=True)
+            if r.random() < 0.5:
+                q, s, x = synth.q8_codes(r, n, k), scales(n, k, bool(r.random() < 0.3)), synth.q16_acts(r, t, k)
+                assert (host(ei.gemm_q8(ei.pack_q8(dev(q), dev(s)), dev(x), 3)) == oracle.q8(q, s, x, threads=8)).all()
+            else:
+                L = int(r.choice([2, 3]))
+                nib, sme, x = synth.q4_codes_packed(r, n, k), synth.q4_scale_bytes(r, n, k), synth.i32_acts(r, t, k)
+                y = host(ei.gemm_q4(ei.pack_q4(dev(nib), dev(sme)), dev(x), L))
+                assert (y == oracle.q4(nib, sme, x, threads=8)).all(), (n, k, t, L)
