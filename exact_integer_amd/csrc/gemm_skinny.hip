@@ -72,9 +72,10 @@ __global__ __launch_bounds__(64 * W * G) void gemm_skinny_kernel(GemmArgs a) {
   if constexpr (STAGE > 0) {
     extern __shared__ __align__(16) uint8_t stage[];   // limb tile (b, l) at (3 b + l) KB
     const v16i zero = {};
-    if (m == 0) {   // the gate waves copy the limb tiles of their blocks
+    {   // the gate and up waves of one block range copy its limb tiles, half each
       const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.limb_tiles, (uint32_t)(3 * tgs * a.nb * 1024));
-      for (int64_t b = w0; b < w1; ++b)
+      const int64_t mid = w0 + (w1 - w0 + 1) / 2;
+      for (int64_t b = m == 0 ? w0 : mid; b < (m == 0 ? mid : w1); ++b)
 #pragma unroll
         for (int l = 0; l < 3; ++l)
           copy16_to_lds(rl, stage + (3 * b + l) * 1024, lane * 16, (uint32_t)(((l * tgs + tg) * a.nb + b) * 1024));
